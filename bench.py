@@ -1,0 +1,207 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one chunked prefill of the layer-shaped workload (T = 8192 tokens,
+48 value heads sharing 16 key heads, d_k = d_v = 128, chunk 32, bf16 q/k/v/a/b,
+fp32 state): gates and normalisation, chunk prologue, forward substitution,
+WY factors, the inter-chunk state scan and the outputs, all inside one kernel
+launch.  ``value`` is prefill tokens/s over the K timed steps.  The decode leg
+(256 sequences x 48 heads, fp32 state 256x48x128x128 carried in place over 64
+single-token recurrent steps) is timed in the same run and reported under
+"decode" as achieved HBM GB/s.  Inputs are seeded synthetic tensors drawn on
+the GPU; they are resident in HBM before the timed region starts.
+
+Prints ONE JSON line (rank 0, N = 1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (T=8192, 48 heads) + decode HBM GB/s, % of roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+
+def prefill_flops(T, H_k, H_v, d_k, d_v, C):
+    """Algorithmic matrix flops of the chunked form (lower triangles counted
+    half, no redundant recompute): per chunk of c tokens
+    H_v [c(c+1)(d_k + 2 d_v) + 6 c d_k d_v] + H_k [2 c^2 d_k]."""
+    total = 0
+    t = 0
+    while t < T:
+        c = min(C, T - t)
+        total += H_v * (c * (c + 1) * (d_k + 2 * d_v) + 6 * c * d_k * d_v) + H_k * 2 * c * c * d_k
+        t += c
+    return total
+
+
+def prefill_bytes(T, N, H_k, H_v, d_k, d_v, elem=2, s0=False):
+    """Algorithmic HBM bytes of one fused pass: q, k, v, a, b read once, o
+    written once in the input dtype, the fp32 state written (and read if given)."""
+    per_tok = (2 * H_k * d_k + H_v * d_v + 2 * H_v) * elem + H_v * d_v * elem
+    return T * per_tok + N * H_v * d_k * d_v * 4 * (2 if s0 else 1)
+
+
+def decode_bytes(N, H_k, H_v, d_k, d_v, elem=2):
+    """Algorithmic HBM bytes of one decode step: the fp32 state read and
+    written once, q, k, v, a, b read, o written, A_log and dt_bias read."""
+    return (N * H_v * d_k * d_v * 4 * 2 + N * (2 * H_k * d_k + H_v * d_v) * elem
+            + N * H_v * 2 * elem + N * H_v * d_v * elem + 8 * H_v)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=48,
+                    help="value heads of the prefill workload the oracle runs for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the rule runs without collectives and this build "
+              "has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_68_amd as gdr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ------------------------------------------------------------ prefill
+    w = synth.workload("prefill")
+    inp = synth.make_inputs(w, 0, device=dev)
+    T, N = w.total_tokens, 1
+    o = torch.empty((T, w.H_v, w.d_v), dtype=w.torch_dtype, device=dev)
+    S = torch.empty((N, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+
+    def prefill_step():
+        gdr.chunked_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"],
+                        inp["dt_bias"], None, chunk=w.chunk, num_seqs=1, o=o, final_state=S)
+
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        prefill_step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = T * args.steps / (total_ms / 1e3)
+    flops = prefill_flops(T, w.H_k, w.H_v, w.d_k, w.d_v, w.chunk)
+    pbytes = prefill_bytes(T, N, w.H_k, w.H_v, w.d_k, w.d_v, 2, s0=False)
+    avg_s = (sum(per_launch_ms) / len(per_launch_ms)) / 1e3
+    achieved_tf = flops / avg_s / 1e12
+
+    # ------------------------------------------------------------ decode
+    wd = synth.workload("decode")
+    dinp = synth.make_inputs(wd, 0, device=dev)
+    state = dinp["initial_state"].clone()
+    od = torch.empty((wd.num_seqs, wd.H_v, wd.d_v), dtype=wd.torch_dtype, device=dev)
+    nsteps = min(args.decode_steps, wd.steps)
+
+    def decode_step(s):
+        gdr.recurrent_fwd(dinp["q"][s], dinp["k"][s], dinp["v"][s], dinp["a"][s], dinp["b"][s],
+                          dinp["A_log"], dinp["dt_bias"], state, num_seqs=wd.num_seqs, o=od,
+                          inplace=True)
+
+    for s in range(2):  # warm-up, then restore the initial state
+        decode_step(s)
+    state.copy_(dinp["initial_state"])
+    torch.cuda.synchronize(dev)
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+    dev_ev[0].record(stream)
+    for s in range(nsteps):
+        decode_step(s)
+        dev_ev[s + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    step_ms = sorted(dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(nsteps))
+    dmean_ms = dev_ev[0].elapsed_time(dev_ev[-1]) / nsteps
+    dmed_ms = step_ms[len(step_ms) // 2]
+    dbytes = decode_bytes(wd.num_seqs, wd.H_k, wd.H_v, wd.d_k, wd.d_v, 2)
+    dgbs = dbytes / (dmean_ms / 1e3) / 1e9
+
+    # ------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        heads = max(1, min(args.cpu_heads, w.H_v))
+        threads = min(16, os.cpu_count() or 1)
+        q64, k64, v64, a64, b64 = (oracle.f64(inp[x]) for x in ("q", "k", "v", "a", "b"))
+        A64, D64 = oracle.f64(inp["A_log"]), oracle.f64(inp["dt_bias"])
+        pairs = [(0, h) for h in range(heads)]
+        c0 = time.perf_counter()
+        oracle.fwd(q64, k64, v64, a64, b64, A64, D64, num_seqs=1, pairs=pairs, n_threads=threads)
+        c_s = time.perf_counter() - c0
+        layer_s = c_s * w.H_v / heads
+        cpu = {"value": T / layer_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"fp64 sequential oracle on {heads} of {w.H_v} value heads x {T} tokens "
+                         f"of the prefill workload ({c_s:.1f} s wall), scaled to the "
+                         f"{w.H_v}-head layer"}
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": gdr_chunked_dtype(gdr, w),
+        "data": "synthetic",
+        "config": {"workload": "prefill layer: 1 sequence x 8192 tokens, 48 value heads sharing "
+                               "16 key heads, d_k=d_v=128, chunk 32, bf16 inputs, fp32 state",
+                   "global_batch": 1, "seq_len": T, "H_v": w.H_v, "H_k": w.H_k, "d": w.d_k,
+                   "chunk": w.chunk},
+        "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "chunked prefill", "flop_per_launch": flops,
+                     "avg_launch_ms": avg_s * 1e3,
+                     "hbm_view": {"bytes_per_launch": pbytes,
+                                  "achieved_GBs": pbytes / avg_s / 1e9,
+                                  "frac": pbytes / avg_s / 1e9 / PEAK_HBM_GBS}},
+        "decode": {"workload": "256 sequences x 48 value heads (16 key heads), d_k=d_v=128, "
+                               "fp32 state in place, bf16 inputs, single-token steps",
+                   "steps": nsteps, "mean_step_ms": dmean_ms, "median_step_ms": dmed_ms,
+                   "tokens_per_s": wd.num_seqs / (dmean_ms / 1e3),
+                   "roofline": {"bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS, "traffic": None,
+                                "bytes_per_launch": dbytes}},
+        "wall_s_prefill_timed": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def gdr_chunked_dtype(gdr, w):
+    """Arithmetic type of the chunked kernel the library picks for ``w``."""
+    fn = getattr(gdr, "chunked_path", None)
+    if fn is None:
+        return "f32"
+    return "bf16" if fn(w) == "mfma" else "f32"
+
+
+if __name__ == "__main__":
+    main()

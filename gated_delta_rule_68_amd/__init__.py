@@ -1,0 +1,285 @@
+"""Gated delta rule on AMD MI355X (gfx950): Python binding of libgdr.so.
+
+This module only marshals arguments: it checks torch tensors, allocates the
+outputs with torch (PyTorch provides device memory and the stream), and calls
+the C ABI declared in ``include/gdr.h`` through ctypes.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built (``python -m gated_delta_rule_68_amd.build``) every
+call raises.
+
+Entry points (same names as the C ABI):
+  gates(q, k, a, b, A_log, dt_bias)             -> q_hat, k_hat, g, beta
+  recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, ...) -> o, final_state
+  chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, chunk=32, ...) -> o, final_state
+  fwd(...)  picks the form on the step count, as the GatedDeltaRule.ixx File
+            Reference ("Detailed Description") describes the backend doing:
+            sequences no longer than one chunk run the recurrence, longer
+            ones the chunked form.
+
+Layouts: q, k [total, H_k, d_k]; v [total, H_v, d_v]; a, b [total, H_v]
+(all fp32 or all bf16); A_log, dt_bias [H_v] fp32; states
+[N, H_v, d_k, d_v] fp32; o [total, H_v, d_v] in the input dtype.  A dense
+batch passes num_seqs (equal-length sequences back to back) or 4-D
+[N, T, H, d] / 3-D [N, T, H] tensors; a packed batch passes cu_seqlens
+(int32 [N + 1] on the device).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["gates", "recurrent_fwd", "chunked_fwd", "fwd", "library_path", "lib",
+           "GdrError", "abi_version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_F32, GDR_BF16 = 0, 1
+_STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_SHAPE", 3: "GDR_ERR_UNSUPPORTED",
+           4: "GDR_ERR_ALIGN", 5: "GDR_ERR_LAUNCH", 6: "GDR_ERR_ALIAS"}
+
+
+class GdrError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class GdrShape(ctypes.Structure):
+    """Mirror of ``gdr_shape`` in include/gdr.h."""
+    _fields_ = [("num_seqs", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64), ("cu_seqlens", ctypes.c_void_p),
+                ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("l2_eps", ctypes.c_float)]
+
+
+_lib = None
+_load_error: Optional[str] = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _bind(lib):
+    vp = ctypes.c_void_p
+    sp = ctypes.POINTER(GdrShape)
+    lib.gdr_gates.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdr_gates.restype = ctypes.c_int
+    lib.gdr_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdr_recurrent_fwd.restype = ctypes.c_int
+    lib.gdr_chunked_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdr_chunked_fwd.restype = ctypes.c_int
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_abi_version.argtypes = []
+    lib.gdr_abi_version.restype = ctypes.c_int
+    return lib
+
+
+def lib():
+    """The loaded libgdr.so; raises if it is missing or fails to load."""
+    global _lib, _load_error
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"libgdr.so is not built ({_LIB_PATH} missing): run "
+                "`python -m gated_delta_rule_68_amd.build` (there is no non-HIP fallback)")
+        try:
+            _lib = _bind(ctypes.CDLL(_LIB_PATH))
+        except OSError as e:  # pragma: no cover - depends on the box
+            _load_error = str(e)
+            raise RuntimeError(f"failed to load {_LIB_PATH}: {e}") from e
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().gdr_abi_version())
+
+
+# ------------------------------------------------------------------ marshalling
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return GDR_F32
+    if dt == torch.bfloat16:
+        return GDR_BF16
+    raise TypeError(f"unsupported dtype {dt}: q, k, v, a, b must be float32 or bfloat16")
+
+
+def _check(t: torch.Tensor, name: str, device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _flatten(x: torch.Tensor, tail: int) -> torch.Tensor:
+    """[N, T, ...] -> [N*T, ...] for dense 4-D/3-D inputs (view, no copy)."""
+    if x.dim() == tail + 2:
+        return x.reshape((-1,) + tuple(x.shape[2:]))
+    return x
+
+
+def _make_shape(total, H_k, H_v, d_k, d_v, cu_seqlens, num_seqs, dtype_code, chunk, scale,
+                l2_eps, dense_T=None):
+    s = GdrShape()
+    if cu_seqlens is not None:
+        s.num_seqs = cu_seqlens.numel() - 1
+        s.seq_len = 0
+        s.cu_seqlens = cu_seqlens.data_ptr()
+    else:
+        if num_seqs is None:
+            num_seqs = 1 if dense_T is None else total // dense_T
+        if num_seqs < 0 or (num_seqs > 0 and total % num_seqs != 0) or (num_seqs == 0 and total):
+            raise ValueError(f"total tokens {total} is not a multiple of num_seqs {num_seqs}")
+        s.num_seqs = num_seqs
+        s.seq_len = total // num_seqs if num_seqs else 0
+        s.cu_seqlens = None
+    s.total_tokens = total
+    s.H_k, s.H_v, s.d_k, s.d_v = H_k, H_v, d_k, d_v
+    s.dtype = dtype_code
+    s.chunk = chunk
+    s.scale = 0.0 if scale is None else float(scale)
+    s.l2_eps = float(l2_eps)
+    return s
+
+
+def _raise(fn: str, rc: int):
+    if rc != 0:
+        msg = lib().gdr_status_string(rc).decode()
+        raise GdrError(fn, rc, msg)
+
+
+def gates(q, k, a, b, A_log, dt_bias, *, scale=None, l2_eps=1e-6, num_seqs=None,
+          outputs=("q_hat", "k_hat", "g", "beta")) -> Tuple:
+    """beta = sigmoid(b), g = -exp(A_log)*softplus(a + dt_bias) (fp32) and the
+    normalised q (times scale) and k (input dtype).  Outputs not named in
+    ``outputs`` are returned as None and not computed."""
+    dense_T = q.shape[1] if q.dim() == 4 else None
+    q, k = _flatten(q, 2), _flatten(k, 2)
+    a, b = _flatten(a, 1), _flatten(b, 1)
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    total, H_k, d_k = q.shape
+    H_v = a.shape[1]
+    for t, n in ((q, "q"), (k, "k")):
+        _check(t, n, dev, dt, (total, H_k, d_k))
+    for t, n in ((a, "a"), (b, "b")):
+        _check(t, n, dev, dt, (total, H_v))
+    _check(A_log, "A_log", dev, torch.float32, (H_v,))
+    _check(dt_bias, "dt_bias", dev, torch.float32, (H_v,))
+    q_hat = torch.empty_like(q) if "q_hat" in outputs else None
+    k_hat = torch.empty_like(k) if "k_hat" in outputs else None
+    g = torch.empty((total, H_v), dtype=torch.float32, device=dev) if "g" in outputs else None
+    beta = torch.empty((total, H_v), dtype=torch.float32, device=dev) if "beta" in outputs else None
+    shape = _make_shape(total, H_k, H_v, d_k, d_k, None, num_seqs, code, 32, scale, l2_eps,
+                        dense_T)
+    rc = lib().gdr_gates(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(a), _ptr(b), _ptr(A_log),
+                         _ptr(dt_bias), _ptr(q_hat), _ptr(k_hat), _ptr(g), _ptr(beta),
+                         _stream(dev))
+    _raise("gdr_gates", rc)
+    return q_hat, k_hat, g, beta
+
+
+def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_seqs, chunk,
+         scale, l2_eps, o, final_state, output_final_state, inplace):
+    dense_T = q.shape[1] if q.dim() == 4 else None
+    q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
+    a, b = _flatten(a, 1), _flatten(b, 1)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"{fn_name}: tensors must be on a GPU (got {dev})")
+    dt = q.dtype
+    code = _dtype_code(dt)
+    total, H_k, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    _check(q, "q", dev, dt)
+    _check(k, "k", dev, dt, (total, H_k, d_k))
+    _check(v, "v", dev, dt, (total, H_v, d_v))
+    _check(a, "a", dev, dt, (total, H_v))
+    _check(b, "b", dev, dt, (total, H_v))
+    _check(A_log, "A_log", dev, torch.float32, (H_v,))
+    _check(dt_bias, "dt_bias", dev, torch.float32, (H_v,))
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    shape = _make_shape(total, H_k, H_v, d_k, d_v, cu_seqlens, num_seqs, code, chunk, scale,
+                        l2_eps, dense_T)
+    N = shape.num_seqs
+    st_shape = (N, H_v, d_k, d_v)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, st_shape)
+    if o is None:
+        o = torch.empty((total, H_v, d_v), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dev, dt, (total, H_v, d_v))
+    if inplace:
+        if initial_state is None:
+            raise ValueError("inplace=True needs an initial_state to update")
+        final_state = initial_state
+    elif final_state is None and output_final_state:
+        final_state = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", dev, torch.float32, st_shape)
+    fn = getattr(lib(), fn_name)
+    rc = fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+            _ptr(dt_bias), _ptr(initial_state), _ptr(o), _ptr(final_state), _stream(dev))
+    _raise(fn_name, rc)
+    if dense_T is not None:
+        o = o.view(N, dense_T, H_v, d_v)
+    return o, final_state
+
+
+def recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, cu_seqlens=None,
+                  num_seqs=None, scale=None, l2_eps=1e-6, o=None, final_state=None,
+                  output_final_state=True, inplace=False):
+    """Sequential (decode) form; ``inplace=True`` updates initial_state."""
+    return _fwd("gdr_recurrent_fwd", q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens,
+                num_seqs, 32, scale, l2_eps, o, final_state, output_final_state, inplace)
+
+
+def chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32, cu_seqlens=None,
+                num_seqs=None, scale=None, l2_eps=1e-6, o=None, final_state=None,
+                output_final_state=True, inplace=False):
+    """Chunked (prefill) form with ``chunk`` tokens per triangular solve."""
+    return _fwd("gdr_chunked_fwd", q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens,
+                num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state, inplace)
+
+
+def fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32, cu_seqlens=None,
+        num_seqs=None, max_seqlen=None, **kw):
+    """Pick the form on the step count: recurrent when no sequence is longer
+    than one chunk, chunked otherwise.  For a packed batch pass ``max_seqlen``
+    to avoid reading cu_seqlens back to the host."""
+    if max_seqlen is None:
+        if cu_seqlens is not None:
+            cu = cu_seqlens.detach().to("cpu")
+            max_seqlen = int((cu[1:] - cu[:-1]).max()) if cu.numel() > 1 else 0
+        elif q.dim() == 4:
+            max_seqlen = q.shape[1]
+        else:
+            n = 1 if num_seqs is None else num_seqs
+            max_seqlen = q.shape[0] // n if n else 0
+    if max_seqlen <= chunk:
+        return recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens=cu_seqlens,
+                             num_seqs=num_seqs, **kw)
+    return chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state, chunk=chunk,
+                       cu_seqlens=cu_seqlens, num_seqs=num_seqs, **kw)

@@ -1,0 +1,192 @@
+// C-ABI entry points: synchronous validation, then dispatch to a kernel
+// family.  Nothing here allocates, frees or synchronises.
+#include <cmath>
+#include <cstdint>
+
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t elem_size(gdr_dtype t) { return t == GDR_F32 ? 4 : 2; }
+
+// Resolve and check the shape; fills `pr`.
+gdr_status resolve(const gdr_shape *s, Problem &pr) {
+  if (s == nullptr) return GDR_ERR_NULL;
+  if (s->num_seqs < 0 || s->H_k <= 0 || s->H_v <= 0 || s->d_k <= 0 || s->d_v <= 0 ||
+      s->total_tokens < 0)
+    return GDR_ERR_SHAPE;
+  if (s->H_v % s->H_k != 0) return GDR_ERR_SHAPE;
+  if (s->cu_seqlens == nullptr) {
+    if (s->seq_len < 0) return GDR_ERR_SHAPE;
+    if ((int64_t)s->num_seqs * s->seq_len != s->total_tokens) return GDR_ERR_SHAPE;
+  }
+  if (s->dtype != GDR_F32 && s->dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+  if (!head_dim_ok(s->d_k) || !head_dim_ok(s->d_v)) return GDR_ERR_UNSUPPORTED;
+  if (!(s->l2_eps >= 0.0f) || !std::isfinite(s->l2_eps)) return GDR_ERR_SHAPE;
+  if (!std::isfinite(s->scale)) return GDR_ERR_SHAPE;
+  // element offsets are computed in 64-bit; grid sizes must fit a launch
+  if ((int64_t)s->num_seqs * s->H_v * (s->d_v / 16) > 0x7fffffffLL) return GDR_ERR_UNSUPPORTED;
+  pr.num_seqs = s->num_seqs;
+  pr.seq_len = s->cu_seqlens ? 0 : s->seq_len;
+  pr.total = s->total_tokens;
+  pr.cu = s->cu_seqlens;
+  pr.H_k = s->H_k;
+  pr.H_v = s->H_v;
+  pr.d_k = s->d_k;
+  pr.d_v = s->d_v;
+  pr.dtype = static_cast<gdr_dtype>(s->dtype);
+  pr.chunk = s->chunk;
+  pr.scale = s->scale > 0.0f ? s->scale : 1.0f / std::sqrt((float)s->d_k);
+  pr.eps = s->l2_eps;
+  return GDR_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void *p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
+
+gdr_status check_fwd(const Problem &pr, const FwdArgs &x) {
+  if (!x.A_log || !x.dt_bias) return GDR_ERR_NULL;
+  if (pr.total > 0 && (!x.q || !x.k || !x.v || !x.a || !x.b || !x.o)) return GDR_ERR_NULL;
+  // row tensors are read and written in 16-byte vectors; per-token scalars
+  // (a, b) and the per-head parameters need only their element alignment
+  const void *rows[] = {x.q, x.k, x.v, x.s0, x.o, x.sT};
+  for (const void *p : rows)
+    if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+  const size_t es = elem_size(pr.dtype);
+  const void *scalars[] = {x.a, x.b};
+  for (const void *p : scalars)
+    if (p && !aligned_to(p, es)) return GDR_ERR_ALIGN;
+  const void *words[] = {x.A_log, x.dt_bias, pr.cu};
+  for (const void *p : words)
+    if (p && !aligned_to(p, 4)) return GDR_ERR_ALIGN;
+  const size_t T = (size_t)pr.total;
+  const size_t state_bytes = (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4;
+  const Range ins[] = {
+      span(x.q, T * pr.H_k * pr.d_k * es), span(x.k, T * pr.H_k * pr.d_k * es),
+      span(x.v, T * pr.H_v * pr.d_v * es), span(x.a, T * pr.H_v * es),
+      span(x.b, T * pr.H_v * es),          span(x.A_log, (size_t)pr.H_v * 4),
+      span(x.dt_bias, (size_t)pr.H_v * 4), span(pr.cu, pr.cu ? (size_t)(pr.num_seqs + 1) * 4 : 0)};
+  const Range o = span(x.o, T * pr.H_v * pr.d_v * es);
+  const Range sT = span(x.sT, x.sT ? state_bytes : 0);
+  const Range s0 = span(x.s0, x.s0 ? state_bytes : 0);
+  for (const Range &r : ins) {
+    if (r.lo == 0 || r.hi == r.lo) continue;
+    if (x.o && o.hi > o.lo && overlap(r, o)) return GDR_ERR_ALIAS;
+    if (x.sT && sT.hi > sT.lo && overlap(r, sT)) return GDR_ERR_ALIAS;
+  }
+  if (x.o && x.sT && o.hi > o.lo && sT.hi > sT.lo && overlap(o, sT)) return GDR_ERR_ALIAS;
+  if (x.o && x.s0 && o.hi > o.lo && s0.hi > s0.lo && overlap(o, s0)) return GDR_ERR_ALIAS;
+  // final_state may be exactly initial_state, but not a shifted overlap of it
+  if (x.s0 && x.sT && x.s0 != x.sT && overlap(s0, sT)) return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
+gdr_status launched(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH; }
+
+}  // namespace
+}  // namespace gdr
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char *gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_NULL: return "a required pointer is NULL";
+    case GDR_ERR_SHAPE: return "inconsistent shape";
+    case GDR_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case GDR_ERR_ALIGN: return "tensor pointer breaks its alignment rule";
+    case GDR_ERR_LAUNCH: return "kernel launch failed";
+    case GDR_ERR_ALIAS: return "an output overlaps an input it may not alias";
+  }
+  return "unknown status";
+}
+
+gdr_status gdr_gates(const gdr_shape *shape, const void *q, const void *k, const void *a,
+                     const void *b, const float *A_log, const float *dt_bias, void *q_hat,
+                     void *k_hat, float *g, float *beta, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (pr.total > 0) {
+    if (q_hat && !q) return GDR_ERR_NULL;
+    if (k_hat && !k) return GDR_ERR_NULL;
+    if ((g || beta) && (!a || !b || !A_log || !dt_bias)) return GDR_ERR_NULL;
+  }
+  const size_t es = elem_size(pr.dtype);
+  const void *rows[] = {q, k, q_hat, k_hat};
+  for (const void *p : rows)
+    if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+  const void *scalars[] = {a, b};
+  for (const void *p : scalars)
+    if (p && !aligned_to(p, es)) return GDR_ERR_ALIGN;
+  const void *words[] = {A_log, dt_bias, g, beta};
+  for (const void *p : words)
+    if (p && !aligned_to(p, 4)) return GDR_ERR_ALIGN;
+  const size_t T = (size_t)pr.total;
+  const Range ins[] = {span(q, T * pr.H_k * pr.d_k * es), span(k, T * pr.H_k * pr.d_k * es),
+                       span(a, T * pr.H_v * es), span(b, T * pr.H_v * es)};
+  const Range outs[] = {span(q_hat, T * pr.H_k * pr.d_k * es),
+                        span(k_hat, T * pr.H_k * pr.d_k * es), span(g, T * pr.H_v * 4),
+                        span(beta, T * pr.H_v * 4)};
+  for (const Range &o : outs) {
+    if (o.lo == 0 || o.hi == o.lo) continue;
+    for (const Range &i : ins)
+      if (i.lo != 0 && overlap(i, o)) return GDR_ERR_ALIAS;
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[i].lo && outs[j].lo && outs[i].hi > outs[i].lo && outs[j].hi > outs[j].lo &&
+          overlap(outs[i], outs[j]))
+        return GDR_ERR_ALIAS;
+  GatesArgs x{q, k, a, b, A_log, dt_bias, q_hat, k_hat, g, beta};
+  return launched(launch_gates(pr, x, stream));
+}
+
+gdr_status gdr_recurrent_fwd(const gdr_shape *shape, const void *q, const void *k, const void *v,
+                             const void *a, const void *b, const float *A_log,
+                             const float *dt_bias, const float *initial_state, void *o,
+                             float *final_state, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (!recurrent_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
+  st = check_fwd(pr, x);
+  if (st != GDR_OK) return st;
+  return launched(launch_recurrent(pr, x, stream));
+}
+
+gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k, const void *v,
+                           const void *a, const void *b, const float *A_log, const float *dt_bias,
+                           const float *initial_state, void *o, float *final_state,
+                           hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
+  FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
+  st = check_fwd(pr, x);
+  if (st != GDR_OK) return st;
+  if (chunked_mfma_supports(pr)) return launched(launch_chunked_mfma(pr, x, stream));
+  if (!chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  return launched(launch_chunked_vec(pr, x, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "gdr.h"
+
+namespace gdr {
+
+// A validated copy of gdr_shape with the defaults resolved.
+struct Problem {
+  int num_seqs;
+  int seq_len;             // dense batches only
+  int64_t total;           // tokens in the batch
+  const int32_t *cu;       // device prefix sums, or nullptr for a dense batch
+  int H_k, H_v, d_k, d_v;
+  gdr_dtype dtype;
+  int chunk;
+  float scale;             // resolved: never <= 0
+  float eps;
+};
+
+// Pointers of one forward call (types erased; dtype in Problem).
+struct FwdArgs {
+  const void *q, *k, *v, *a, *b;
+  const float *A_log, *dt_bias;
+  const float *s0;  // may be nullptr (zeros)
+  void *o;
+  float *sT;        // may be nullptr (dropped); may equal s0
+};
+
+struct GatesArgs {
+  const void *q, *k, *a, *b;
+  const float *A_log, *dt_bias;
+  void *q_hat, *k_hat;
+  float *g, *beta;
+};
+
+hipError_t launch_gates(const Problem &p, const GatesArgs &x, hipStream_t s);
+hipError_t launch_recurrent(const Problem &p, const FwdArgs &x, hipStream_t s);
+hipError_t launch_chunked_vec(const Problem &p, const FwdArgs &x, hipStream_t s);
+hipError_t launch_chunked_mfma(const Problem &p, const FwdArgs &x, hipStream_t s);
+
+// Shapes each kernel family is instantiated for.
+bool recurrent_supports(const Problem &p);
+bool chunked_vec_supports(const Problem &p);
+bool chunked_mfma_supports(const Problem &p);
+
+}  // namespace gdr

@@ -1,0 +1,231 @@
+// Sequential (decode) form of the gated delta rule.
+//
+// GatedDeltaRule.ixx File Reference, "Detailed Description": per value head an
+// fp32 state S [d_k, d_v]; per token S <- S*exp(g); delta <- (v - k^T S)*beta;
+// S <- S + k (outer) delta; o <- q^T S, with q, k L2-normalised and q scaled.
+// Decode runs this sequential form, so its cost is one read and one write of S
+// per (sequence, head) per call -- a pure stream of the state through HBM.
+//
+// One workgroup per (sequence, value head) holds the whole [d_k, d_v] state in
+// registers for the whole call.  Thread (rg, cg) owns columns 4cg..4cg+3 of rows
+// rg, rg + RG, rg + 2RG, ...; consecutive threads own consecutive 16-byte
+// column groups, so each wave loads and stores whole rows (fully coalesced).
+//
+// Per token, with the state taken BEFORE the decay (all reassociations of the
+// stated order):
+//   u_j = k^T S[:, j],  w_j = q^T S[:, j]       (raw q, k; two column reductions)
+//   k_hat = k / |k|,  q_hat = scale * q / |q|
+//   delta_j = beta * (v_j - alpha * u_j / |k|)
+//   o_j     = alpha * scale * w_j / |q| + (q_hat . k_hat) * delta_j
+//   S[i, j] = alpha * S[i, j] + k_hat_i * delta_j
+// so the state is read once and written once, and the norms and q.k ride along
+// in the same reduction as u and w.
+#include "device_common.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+template <int DK, int DV>
+struct RecGeom {
+  static constexpr int CG = DV / 4;                               // column groups
+  static constexpr int RG = (DK < 256 / CG) ? DK : 256 / CG;      // row groups
+  static constexpr int NT = CG * RG;                              // threads
+  static constexpr int RPT = DK / RG;                             // rows per thread
+  static constexpr int NW = (NT + 63) / 64;                       // waves
+  static constexpr int RG_PER_WAVE = (64 / CG < RG) ? 64 / CG : RG;
+  static constexpr int NRED = 11;  // u[4], w[4], |k|^2, |q|^2, q.k
+  static_assert(DV % 4 == 0 && DK % RG == 0, "bad geometry");
+};
+
+template <typename T>
+struct RecParams {
+  const T *q, *k, *v, *a, *b;
+  const float *A_log, *dt_bias;
+  const float *s0;
+  T *o;
+  float *sT;
+  const int32_t *cu;
+  int seq_len;
+  int H_k, H_v;
+  float scale, eps;
+};
+
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__((RecGeom<DK, DV>::NT)) void recurrent_kernel(RecParams<T> p) {
+  using G = RecGeom<DK, DV>;
+  constexpr int CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW, NRED = G::NRED;
+  __shared__ float red[2][NW > 1 ? NW : 1][CG][NRED];
+
+  const int n = blockIdx.x / p.H_v;
+  const int h = blockIdx.x % p.H_v;
+  const int hk = h / (p.H_v / p.H_k);
+  const int tid = threadIdx.x;
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  const int wave = tid / 64;
+
+  int64_t t0, t1;
+  seq_bounds(p.cu, p.seq_len, n, t0, t1);
+
+  const size_t state_off = ((size_t)n * p.H_v + h) * DK * DV;
+  float4 S[RPT];
+  if (p.s0) {
+    const float *src = p.s0 + state_off + 4 * cg;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) S[i] = load4(src + (size_t)(rg + RG * i) * DV);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float neg_exp_A = -expf(p.A_log[h]);
+  const float dtb = p.dt_bias[h];
+
+  for (int64_t t = t0; t < t1; ++t) {
+    const T *kr = p.k + (t * p.H_k + hk) * DK;
+    const T *qr = p.q + (t * p.H_k + hk) * DK;
+    float kv[RPT], qv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      kv[i] = to_f32(kr[rg + RG * i]);
+      qv[i] = to_f32(qr[rg + RG * i]);
+    }
+    const float4 vv = load4(p.v + (t * p.H_v + h) * DV + 4 * cg);
+    const float a_t = to_f32(p.a[t * p.H_v + h]);
+    const float b_t = to_f32(p.b[t * p.H_v + h]);
+
+    float r[NRED];
+#pragma unroll
+    for (int j = 0; j < NRED; ++j) r[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      r[0] += kv[i] * S[i].x;
+      r[1] += kv[i] * S[i].y;
+      r[2] += kv[i] * S[i].z;
+      r[3] += kv[i] * S[i].w;
+      r[4] += qv[i] * S[i].x;
+      r[5] += qv[i] * S[i].y;
+      r[6] += qv[i] * S[i].z;
+      r[7] += qv[i] * S[i].w;
+      r[8] += kv[i] * kv[i];
+      r[9] += qv[i] * qv[i];
+      r[10] += qv[i] * kv[i];
+    }
+    // reduce over the row groups of this wave (lanes that differ by multiples of CG)
+#pragma unroll
+    for (int off = CG; off < CG * G::RG_PER_WAVE; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < NRED; ++j) r[j] += __shfl_xor(r[j], off, 64);
+    }
+    if constexpr (NW > 1) {
+      const int buf = (int)((t - t0) & 1);
+      if (tid % 64 < CG) {
+#pragma unroll
+        for (int j = 0; j < NRED; ++j) red[buf][wave][cg][j] = r[j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NRED; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s += red[buf][w][cg][j];
+        r[j] = s;
+      }
+    }
+    const float ik = rsqrtf(r[8] + p.eps);
+    const float iq = rsqrtf(r[9] + p.eps) * p.scale;
+    const float qk = r[10] * ik * iq;
+    const float g = log_decay(neg_exp_A, a_t, dtb);
+    const float alpha = expf(g);
+    const float beta = sigmoid_f32(b_t);
+    const float au = alpha * ik;
+    float4 d;
+    d.x = beta * (vv.x - au * r[0]);
+    d.y = beta * (vv.y - au * r[1]);
+    d.z = beta * (vv.z - au * r[2]);
+    d.w = beta * (vv.w - au * r[3]);
+    if (rg == 0) {
+      const float aw = alpha * iq;
+      float4 o;
+      o.x = aw * r[4] + qk * d.x;
+      o.y = aw * r[5] + qk * d.y;
+      o.z = aw * r[6] + qk * d.z;
+      o.w = aw * r[7] + qk * d.w;
+      store4(p.o + (t * p.H_v + h) * DV + 4 * cg, o);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float kh = kv[i] * ik;
+      S[i].x = alpha * S[i].x + kh * d.x;
+      S[i].y = alpha * S[i].y + kh * d.y;
+      S[i].z = alpha * S[i].z + kh * d.z;
+      S[i].w = alpha * S[i].w + kh * d.w;
+    }
+  }
+  if (p.sT) {
+    float *dst = p.sT + state_off + 4 * cg;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) store4(dst + (size_t)(rg + RG * i) * DV, S[i]);
+  }
+}
+
+template <int DK, int DV, typename T>
+hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
+  RecParams<T> p;
+  p.q = static_cast<const T *>(x.q);
+  p.k = static_cast<const T *>(x.k);
+  p.v = static_cast<const T *>(x.v);
+  p.a = static_cast<const T *>(x.a);
+  p.b = static_cast<const T *>(x.b);
+  p.A_log = x.A_log;
+  p.dt_bias = x.dt_bias;
+  p.s0 = x.s0;
+  p.o = static_cast<T *>(x.o);
+  p.sT = x.sT;
+  p.cu = pr.cu;
+  p.seq_len = pr.seq_len;
+  p.H_k = pr.H_k;
+  p.H_v = pr.H_v;
+  p.scale = pr.scale;
+  p.eps = pr.eps;
+  const int64_t grid = (int64_t)pr.num_seqs * pr.H_v;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((recurrent_kernel<DK, DV, T>), dim3((unsigned)grid),
+                     dim3(RecGeom<DK, DV>::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DK, typename T>
+hipError_t launch_dv(const Problem &pr, const FwdArgs &x, hipStream_t s) {
+  switch (pr.d_v) {
+    case 16: return launch_typed<DK, 16, T>(pr, x, s);
+    case 32: return launch_typed<DK, 32, T>(pr, x, s);
+    case 64: return launch_typed<DK, 64, T>(pr, x, s);
+    case 128: return launch_typed<DK, 128, T>(pr, x, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_dk(const Problem &pr, const FwdArgs &x, hipStream_t s) {
+  switch (pr.d_k) {
+    case 16: return launch_dv<16, T>(pr, x, s);
+    case 32: return launch_dv<32, T>(pr, x, s);
+    case 64: return launch_dv<64, T>(pr, x, s);
+    case 128: return launch_dv<128, T>(pr, x, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool recurrent_supports(const Problem &p) {
+  auto ok = [](int d) { return d == 16 || d == 32 || d == 64 || d == 128; };
+  return ok(p.d_k) && ok(p.d_v);
+}
+
+hipError_t launch_recurrent(const Problem &pr, const FwdArgs &x, hipStream_t s) {
+  return pr.dtype == GDR_F32 ? launch_dk<float>(pr, x, s) : launch_dk<bf16>(pr, x, s);
+}
+
+}  // namespace gdr

@@ -1,0 +1,167 @@
+/*
+ * gdr.h -- C ABI of the gated delta rule library for AMD MI355X (gfx950).
+ *
+ * The operation (GatedDeltaRule.ixx File Reference, "Detailed Description"):
+ * per (sequence, value head) an fp32 state S of shape [d_k, d_v] that does not
+ * grow with context; for every token t
+ *     S     <- S * exp(g_t)
+ *     delta <- (v_t - k_t^T S) * beta_t
+ *     S     <- S + k_t (outer) delta
+ *     o_t   <- q_t^T S
+ * where q_t and k_t are L2-normalised and q_t is further scaled by
+ * 1/sqrt(d_k), and the gates are derived inside the library from the raw
+ * projections a, b and the per-head parameters A_log, dt_bias:
+ *     beta_t = sigmoid(b_t),   g_t = -exp(A_log) * softplus(a_t + dt_bias).
+ * The same page states the two forms this library exports -- the sequential
+ * recurrence for decode and a chunked (UT-transform) form for prefill with one
+ * triangular solve per chunk of 32 steps -- which agree up to float
+ * reassociation, and that the layer is inference-only (no backward).
+ * The Track L pull request (tessera #77, "Numerics finding") adds that the rule
+ * is well conditioned only with L2-normalised keys and fp32 state; this
+ * library therefore always normalises q and k and always keeps S in fp32.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers to dense, row-major, contiguous
+ *   memory.  q, k, v, o, q_hat, k_hat and the states must be 16-byte aligned
+ *   (they move in 16-byte vectors); a, b, g, beta, A_log, dt_bias and
+ *   cu_seqlens need only the alignment of their element type.  The caller
+ *   owns every buffer and the stream.
+ * - Layouts (total = number of tokens in the batch):
+ *     q, k          [total, H_k, d_k]   dtype
+ *     v             [total, H_v, d_v]   dtype
+ *     a, b          [total, H_v]        dtype
+ *     A_log, dt_bias[H_v]               fp32
+ *     states        [num_seqs, H_v, d_k, d_v]  fp32
+ *     o             [total, H_v, d_v]   dtype
+ *   Value head h reads key head h / (H_v / H_k) (H_v consecutive value heads
+ *   share one key head).  Dense batches hold num_seqs sequences of seq_len
+ *   tokens one after another; packed batches give cu_seqlens.
+ * - Every call is asynchronous on `stream`.  The library never allocates,
+ *   frees or synchronises, holds no global state, and is thread-safe.
+ * - Shape, dtype, pointer and alignment checks are synchronous: on failure
+ *   nothing is launched and nothing is written.  Faults inside a kernel show
+ *   up at the caller's next synchronisation.  GDR_ERR_LAUNCH reports a failed
+ *   kernel launch.
+ * - The contents of cu_seqlens are trusted (device memory is not read on the
+ *   host): cu[0] = 0, nondecreasing, cu[num_seqs] = total_tokens.
+ * - Outputs are fully overwritten.  final_state may be the same buffer as
+ *   initial_state (in-place decode); no other aliasing is allowed.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+/* Symbols of this header are the only ones the shared library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define GDR_API __attribute__((visibility("default")))
+#else
+#define GDR_API
+#endif
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  GDR_ERR_SHAPE = 2,       /* inconsistent sizes (H_v % H_k, totals, negatives)  */
+  GDR_ERR_UNSUPPORTED = 3, /* a valid shape this build has no kernel for         */
+  GDR_ERR_ALIGN = 4,       /* a tensor pointer breaks its alignment rule         */
+  GDR_ERR_LAUNCH = 5,      /* the HIP runtime refused a kernel launch            */
+  GDR_ERR_ALIAS = 6        /* an output overlaps an input it may not alias       */
+} gdr_status;
+
+typedef enum gdr_dtype {
+  GDR_F32 = 0,  /* IEEE binary32                                         */
+  GDR_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit stored mantissa)       */
+} gdr_dtype;
+
+/*
+ * Problem description, passed by pointer to every call (read only during the
+ * call; the library keeps no reference to it).
+ */
+typedef struct gdr_shape {
+  int32_t num_seqs;          /* N >= 0: sequences in the batch                        */
+  int32_t seq_len;           /* dense batches: tokens per sequence (>= 0);            */
+                             /*   ignored when cu_seqlens != NULL                     */
+  int64_t total_tokens;      /* tokens in the batch; dense: num_seqs * seq_len        */
+  const int32_t *cu_seqlens; /* device [num_seqs + 1] prefix sums of the lengths, or  */
+                             /*   NULL for a dense batch                              */
+  int32_t H_k;               /* key heads (>= 1)                                      */
+  int32_t H_v;               /* value heads, a multiple of H_k                        */
+  int32_t d_k;               /* key/query head size: 16, 32, 64 or 128                */
+  int32_t d_v;               /* value head size: 16, 32, 64 or 128                    */
+  int32_t dtype;             /* gdr_dtype of q, k, v, a, b and o                      */
+  int32_t chunk;             /* chunked form: tokens per chunk, 16, 32 or 64          */
+                             /*   (ignored by the recurrent form and the gates)       */
+  float scale;               /* extra factor on q; <= 0 selects 1/sqrt(d_k)           */
+  float l2_eps;              /* normalisation x / sqrt(sum x^2 + l2_eps), >= 0        */
+} gdr_shape;
+
+/*
+ * gdr_gates -- the gates and the normalised q, k, as the component derives
+ * them (GatedDeltaRule.ixx File Reference, "Detailed Description"):
+ *   beta = sigmoid(b), g = -exp(A_log[h]) * softplus(a + dt_bias[h])   [total, H_v] fp32
+ *   q_hat = scale * q / sqrt(|q|^2 + l2_eps),  k_hat = k / sqrt(|k|^2 + l2_eps)
+ *                                                          [total, H_k, d_k] dtype
+ * Any of q_hat, k_hat, g, beta may be NULL (that output is skipped); the
+ * inputs an output needs must then be non-NULL.  The forward entry points do
+ * not call this (they derive the same quantities inside their own kernels);
+ * it is exported for callers that want the gates themselves.
+ */
+GDR_API gdr_status gdr_gates(const gdr_shape *shape, const void *q, const void *k, const void *a,
+                     const void *b, const float *A_log, const float *dt_bias, void *q_hat,
+                     void *k_hat, float *g, float *beta, hipStream_t stream);
+
+/*
+ * gdr_recurrent_fwd -- the sequential (decode) form: each token updates the
+ * state once, in order (GatedDeltaRule.ixx File Reference, "Detailed
+ * Description": decode runs the sequential recurrence).  Works for any
+ * sequence length; a decode step is a call with seq_len = 1 and
+ * final_state == initial_state.
+ *   initial_state : fp32 [N, H_v, d_k, d_v], or NULL for zeros
+ *   o             : dtype [total, H_v, d_v]
+ *   final_state   : fp32 [N, H_v, d_k, d_v], or NULL to drop it; may equal
+ *                   initial_state
+ */
+GDR_API gdr_status gdr_recurrent_fwd(const gdr_shape *shape, const void *q, const void *k, const void *v,
+                             const void *a, const void *b, const float *A_log,
+                             const float *dt_bias, const float *initial_state, void *o,
+                             float *final_state, hipStream_t stream);
+
+/*
+ * gdr_chunked_fwd -- the chunked (prefill) form: the same arithmetic regrouped
+ * per chunk of `chunk` tokens into dense contractions plus one forward
+ * substitution of (I + A) per chunk (GatedDeltaRule.ixx File Reference,
+ * "Detailed Description"; Track L pull request, L2: chunk-parallel
+ * UT-transform whose only non-GEMM step is the (I + A)^-1 forward
+ * substitution).  Chunks restart at every sequence start; the last chunk of a
+ * sequence may be partial.  Arguments as gdr_recurrent_fwd.
+ * bf16 with d_k = d_v = 128 and chunk = 32 runs on the matrix cores with bf16
+ * operands and fp32 accumulation and state; every other supported shape runs
+ * a vector fp32 kernel.
+ */
+GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k, const void *v,
+                           const void *a, const void *b, const float *A_log, const float *dt_bias,
+                           const float *initial_state, void *o, float *final_state,
+                           hipStream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+GDR_API const char *gdr_status_string(gdr_status status);
+
+/* GDR_ABI_VERSION of the loaded library. */
+GDR_API int gdr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,178 @@
+"""The C-ABI library on the CPU: it loads, exports exactly what include/gdr.h
+declares, its Python mirror of gdr_shape matches the C layout, and its
+synchronous validation rejects bad calls before any launch (every call below
+fails validation, so no kernel is ever launched without a GPU)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+@pytest.fixture(scope="module")
+def gdr():
+    import gated_delta_rule_68_amd as g
+    if not os.path.exists(g.library_path()):
+        from gated_delta_rule_68_amd import build
+        build.build(verbose=False)
+    g.lib()
+    return g
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GDR_API\s+[\w\s\*]+?\b(gdr_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_gates",
+                                  "gdr_recurrent_fwd", "gdr_status_string"]
+
+
+def test_library_exports_every_declared_symbol(gdr):
+    lib = gdr.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), f"{name} not exported"
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", gdr.library_path()],
+                             capture_output=True, text=True, check=True).stdout
+        exported = sorted(set(re.findall(r"\sT\s(gdr_\w+)", out)))
+        assert exported == declared_symbols(), "library exports symbols the header does not declare"
+
+
+def test_abi_version_matches_header(gdr):
+    m = re.search(r"#define GDR_ABI_VERSION (\d+)", open(HEADER).read())
+    assert gdr.abi_version() == int(m.group(1))
+
+
+def test_status_strings(gdr):
+    lib = gdr.lib()
+    seen = set()
+    for code in range(7):
+        s = lib.gdr_status_string(code).decode()
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 7
+    assert lib.gdr_status_string(99).decode() == "unknown status"
+
+
+def test_shape_struct_layout_matches_c(gdr, tmp_path):
+    """Compile a probe against the header with gcc and compare offsets."""
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or ROCm headers missing")
+    src = tmp_path / "probe.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "gdr.h"\n'
+        "int main(void){printf(\"%zu\", sizeof(gdr_shape));"
+        + "".join(f'printf(" %zu", offsetof(gdr_shape, {f}));'
+                  for f, _ in gdr.GdrShape._fields_) + "return 0;}\n")
+    exe = tmp_path / "probe"
+    subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include", "-I/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True, capture_output=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(gdr.GdrShape)
+    for (name, _), off in zip(gdr.GdrShape._fields_, vals[1:]):
+        assert getattr(gdr.GdrShape, name).offset == off, name
+
+
+# ------------------------------------------------------------ validation paths
+def shape(gdr, **kw):
+    s = gdr.GdrShape()
+    d = dict(num_seqs=1, seq_len=4, total_tokens=4, cu_seqlens=None, H_k=1, H_v=2, d_k=16,
+             d_v=16, dtype=0, chunk=16, scale=0.0, l2_eps=1e-6)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(s, k, v)
+    return s
+
+
+# Fake, never-dereferenced device addresses: every case below fails validation.
+BASE = 0x7f0000000000
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * 0x100000 + off)
+
+
+def call(gdr, fn, s, ptrs=None):
+    p = [fake(i) for i in range(10)] if ptrs is None else ptrs
+    f = getattr(gdr.lib(), fn)
+    arg = ctypes.byref(s) if s is not None else None
+    if fn == "gdr_gates":
+        return f(arg, *p[:10], None)
+    return f(arg, *p[:10], None)
+
+
+@pytest.mark.parametrize("fn", ["gdr_recurrent_fwd", "gdr_chunked_fwd", "gdr_gates"])
+def test_null_shape(gdr, fn):
+    assert call(gdr, fn, None) == 1
+
+
+@pytest.mark.parametrize("fn", ["gdr_recurrent_fwd", "gdr_chunked_fwd", "gdr_gates"])
+@pytest.mark.parametrize("bad,code", [
+    (dict(H_v=3, H_k=2), 2),            # H_v not a multiple of H_k
+    (dict(num_seqs=-1), 2),
+    (dict(total_tokens=5), 2),          # dense: total != N * T
+    (dict(d_k=24), 3),                  # unsupported head size
+    (dict(d_v=256), 3),
+    (dict(dtype=7), 3),
+    (dict(l2_eps=-1.0), 2),
+    (dict(scale=float("nan")), 2),
+])
+def test_shape_errors(gdr, fn, bad, code):
+    assert call(gdr, fn, shape(gdr, **bad)) == code
+
+
+def test_chunk_size_checked(gdr):
+    assert call(gdr, "gdr_chunked_fwd", shape(gdr, chunk=48)) == 3
+    assert call(gdr, "gdr_chunked_fwd", shape(gdr, chunk=0)) == 3
+
+
+def test_null_inputs(gdr):
+    p = [fake(i) for i in range(10)]
+    p[0] = None  # q
+    assert call(gdr, "gdr_recurrent_fwd", shape(gdr), p) == 1
+    p = [fake(i) for i in range(10)]
+    p[5] = None  # A_log
+    assert call(gdr, "gdr_chunked_fwd", shape(gdr), p) == 1
+
+
+def test_misaligned(gdr):
+    p = [fake(i) for i in range(10)]
+    p[2] = fake(2, off=4)  # v: row tensors need 16 bytes
+    assert call(gdr, "gdr_recurrent_fwd", shape(gdr), p) == 4
+    p = [fake(i) for i in range(10)]
+    p[3] = fake(3, off=2)  # a (fp32): needs 4 bytes
+    assert call(gdr, "gdr_recurrent_fwd", shape(gdr), p) == 4
+
+
+def test_aliasing(gdr):
+    p = [fake(i) for i in range(10)]
+    p[8] = fake(0)  # o on top of q
+    assert call(gdr, "gdr_recurrent_fwd", shape(gdr), p) == 6
+    p = [fake(i) for i in range(10)]
+    p[9] = fake(7, off=16)  # final_state shifted into initial_state
+    assert call(gdr, "gdr_chunked_fwd", shape(gdr), p) == 6
+
+
+def test_gates_output_alias(gdr):
+    p = [fake(i) for i in range(10)]
+    p[6] = fake(0)  # q_hat over q
+    assert call(gdr, "gdr_gates", shape(gdr), p) == 6
+
+
+def test_binding_refuses_cpu_tensors(gdr):
+    import torch
+    q = torch.zeros(4, 1, 16)
+    v = torch.zeros(4, 2, 16)
+    a = torch.zeros(4, 2)
+    with pytest.raises(ValueError):
+        gdr.recurrent_fwd(q, q, v, a, a, torch.zeros(2), torch.zeros(2))

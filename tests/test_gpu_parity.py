@@ -1,0 +1,309 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Small problems are compared element by element on every (sequence, head);
+the full-size workloads are compared on sampled (sequence, head) pairs that
+the oracle recomputes one by one.  Inputs come from the seeded generators in
+``synth`` and are drawn on the GPU; the oracle receives the same bits.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_68_amd as gdr
+import synth
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdr.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(form, inp, w, chunk=None, initial_state="inp", **kw):
+    s0 = inp["initial_state"] if initial_state == "inp" else initial_state
+    args = (inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], s0)
+    if inp["cu_seqlens"] is not None:
+        kw["cu_seqlens"] = inp["cu_seqlens"]
+    else:
+        kw["num_seqs"] = len(inp["cu_host"]) - 1
+    if form == "chunked":
+        return gdr.chunked_fwd(*args, chunk=chunk or w.chunk, **kw)
+    return gdr.recurrent_fwd(*args, **kw)
+
+
+def check_full(w, seed, form, chunk=None, tol=None):
+    note(f"[parity] {w.name} seed={seed} form={form} chunk={chunk or w.chunk} "
+         f"H={w.H_v}/{w.H_k} d={w.d_k}x{w.d_v} dtype={w.dtype} lens={w.seq_lengths}")
+    inp = synth.make_inputs(w, seed, device=DEV)
+    o, S = run(form, inp, w, chunk)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    o_ref, S_ref = U.oracle_full(inp, cu)
+    eo, es = U.compare_full(o, S, o_ref, S_ref, cu, w.H_v)
+    tol = tol or U.TOL[w.dtype]
+    note(f"  max rel err o={eo:.3e} S={es:.3e} (bar {tol:g})")
+    assert eo <= tol and es <= tol, (eo, es)
+    return eo, es
+
+
+# ------------------------------------------------------------ small, every element
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_tiny_workload(seed, form):
+    check_full(synth.workload("tiny"), seed, form)
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_one_head_workload(form):
+    check_full(synth.workload("one_head"), 0, form)
+
+
+SMALL_SHAPES = [
+    # H_k, H_v, d_k, d_v, lengths
+    (2, 6, 128, 128, [200]),
+    (1, 3, 64, 32, [0, 1, 31, 32, 33, 100]),
+    (2, 2, 16, 64, [17, 64, 5]),
+    (4, 8, 32, 16, [40, 0, 9]),
+    (1, 1, 128, 16, [77]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: f"H{s[1]}/{s[0]}_d{s[2]}x{s[3]}")
+@pytest.mark.parametrize("form,chunk", [("recurrent", None), ("chunked", 16), ("chunked", 32),
+                                        ("chunked", 64)])
+def test_small_shapes(dtype, shape, form, chunk):
+    H_k, H_v, d_k, d_v, lens = shape
+    w = synth.custom(H_k, H_v, d_k, d_v, dtype, lengths=lens, chunk=chunk or 32)
+    check_full(w, 3, form, chunk)
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_dense_batch_without_cu_seqlens(form):
+    w = synth.custom(2, 4, 128, 128, "bf16", seq_len=96, num_seqs=3)
+    check_full(w, 4, form)
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_stress_gates_small(form):
+    """beta -> 1 and g -> 0 on every sequence (the contraction limit)."""
+    w = synth.custom(1, 3, 128, 128, "bf16", lengths=[300, 129], stress_seqs=(0, 1))
+    check_full(w, 5, form)
+
+
+# ------------------------------------------------------------ full-size workloads
+PREFILL_PAIRS = [(0, 0), (0, 1), (0, 2), (0, 23), (0, 47)]
+
+
+@pytest.mark.parametrize("form", ["chunked", "recurrent"])
+def test_prefill_layer_sampled(form):
+    w = synth.workload("prefill")
+    note(f"[parity] prefill T=8192 H=48/16 bf16 form={form}")
+    inp = synth.make_inputs(w, 0, device=DEV)
+    o, S = run(form, inp, w)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    ref = U.oracle_pairs(inp, cu, PREFILL_PAIRS)
+    eo, es, per = U.compare_sampled(o, S, ref, cu)
+    note(f"  max rel err o={eo:.3e} S={es:.3e}")
+    assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], per
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+
+
+def test_decode_workload_sampled():
+    """64 single-token recurrent steps on 256 x 48 states, in place."""
+    w = synth.workload("decode")
+    note("[parity] decode 256 seqs x 48 heads x 64 steps, in place")
+    inp = synth.make_inputs(w, 0, device=DEV)
+    pairs = [(0, 0), (3, 47), (100, 17), (255, 5), (128, 30)]
+    s0_pairs = {p: inp["initial_state"][p[0], p[1]].clone() for p in pairs}
+    state = inp["initial_state"].clone()
+    outs = []
+    for s in range(w.steps):
+        o, st = gdr.recurrent_fwd(inp["q"][s], inp["k"][s], inp["v"][s], inp["a"][s], inp["b"][s],
+                                  inp["A_log"], inp["dt_bias"], state, num_seqs=w.num_seqs,
+                                  inplace=True)
+        assert st.data_ptr() == state.data_ptr()
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_all = torch.stack(outs)  # [steps, N, H, d]
+    d = inp["dense"]
+    s0 = torch.zeros((w.num_seqs, w.H_v, w.d_k, w.d_v))
+    for (n, h), t in s0_pairs.items():
+        s0[n, h] = t.cpu()
+    cu = [i * w.steps for i in range(w.num_seqs + 1)]
+    ref = U.oracle.fwd_sampled(d["q"], d["k"], d["v"], d["a"], d["b"], inp["A_log"],
+                               inp["dt_bias"], pairs, initial_state=s0, cu_seqlens=cu)
+    worst = 0.0
+    for (n, h), (o_r, S_r) in ref.items():
+        eo = U.slice_err(U.to_np(o_all[:, n, h]), o_r)
+        es = U.slice_err(U.to_np(state[n, h]), S_r)
+        worst = max(worst, eo, es)
+    note(f"  max rel err {worst:.3e}")
+    assert worst <= U.TOL["bf16"]
+    # the same 64 tokens as one chunked call agree too
+    o_c, S_c = gdr.chunked_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], inp["A_log"],
+                               inp["dt_bias"], inp["initial_state"], chunk=32,
+                               num_seqs=w.num_seqs)
+    torch.cuda.synchronize()
+    o_c = o_c.view(w.num_seqs, w.steps, w.H_v, w.d_v)
+    worst = 0.0
+    for (n, h), (o_r, S_r) in ref.items():
+        worst = max(worst, U.slice_err(U.to_np(o_c[n, :, h]), o_r),
+                    U.slice_err(U.to_np(S_c[n, h]), S_r))
+    note(f"  chunked form of the same tokens: max rel err {worst:.3e}")
+    assert worst <= U.TOL["bf16"]
+
+
+@pytest.mark.parametrize("form", ["chunked", "recurrent"])
+def test_varlen_workload_sampled(form):
+    w = synth.workload("varlen", seed=0)
+    note(f"[parity] varlen lengths={w.seq_lengths} form={form}")
+    inp = synth.make_inputs(w, 0, device=DEV)
+    o, S = run(form, inp, w)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    pairs = [(n, h) for n in range(w.num_seqs) for h in (0, 29)]
+    ref = U.oracle_pairs(inp, cu, pairs)
+    eo, es, per = U.compare_sampled(o, S, ref, cu)
+    note(f"  max rel err o={eo:.3e} S={es:.3e}; stress seqs "
+         + ", ".join(f"{k}: {v[0]:.2e}/{v[1]:.2e}" for k, v in per.items() if k[0] in (6, 7)))
+    assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], per
+
+
+# ------------------------------------------------------------ properties
+def test_recurrent_equals_chunked_on_gpu():
+    w = synth.custom(2, 6, 128, 128, "bf16", lengths=[333, 64, 1])
+    inp = synth.make_inputs(w, 7, device=DEV)
+    o1, S1 = run("recurrent", inp, w)
+    o2, S2 = run("chunked", inp, w)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        for h in range(w.H_v):
+            worst = max(worst, U.slice_err(U.to_np(o2[cu[n]:cu[n + 1], h]),
+                                           U.to_np(o1[cu[n]:cu[n + 1], h])),
+                        U.slice_err(U.to_np(S2[n, h]), U.to_np(S1[n, h])))
+    assert worst <= U.TOL["bf16"], worst
+
+
+def test_streaming_prefill_then_decode():
+    """Chunked prefill of 100 tokens then 20 recurrent steps equals one call
+    over all 120 tokens (the state is the whole cache)."""
+    w = synth.custom(1, 3, 128, 128, "f32", lengths=[120])
+    inp = synth.make_inputs(w, 8, device=DEV)
+    o_ref, S_ref = U.oracle_full(inp, inp["cu_host"])
+    sl = lambda x, a, b: x[a:b].contiguous()
+    o_p, st = gdr.chunked_fwd(sl(inp["q"], 0, 100), sl(inp["k"], 0, 100), sl(inp["v"], 0, 100),
+                              sl(inp["a"], 0, 100), sl(inp["b"], 0, 100), inp["A_log"],
+                              inp["dt_bias"], inp["initial_state"], chunk=32)
+    outs = [o_p]
+    for t in range(100, 120):
+        o_t, st = gdr.recurrent_fwd(sl(inp["q"], t, t + 1), sl(inp["k"], t, t + 1),
+                                    sl(inp["v"], t, t + 1), sl(inp["a"], t, t + 1),
+                                    sl(inp["b"], t, t + 1), inp["A_log"], inp["dt_bias"], st,
+                                    inplace=True)
+        outs.append(o_t)
+    torch.cuda.synchronize()
+    o = torch.cat(outs)
+    eo, es = U.compare_full(o, st, o_ref, S_ref, inp["cu_host"], w.H_v)
+    assert eo <= U.TOL["f32"] and es <= U.TOL["f32"], (eo, es)
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_deterministic(form):
+    w = synth.custom(2, 4, 128, 128, "bf16", lengths=[257, 31])
+    inp = synth.make_inputs(w, 9, device=DEV)
+    o1, S1 = run(form, inp, w)
+    o2, S2 = run(form, inp, w)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_inplace_equals_out_of_place():
+    w = synth.custom(2, 4, 128, 128, "bf16", seq_len=1, num_seqs=64)
+    inp = synth.make_inputs(w, 10, device=DEV)
+    o1, S1 = run("recurrent", inp, w)
+    st = inp["initial_state"].clone()
+    o2, S2 = run("recurrent", inp, w, initial_state=st, inplace=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked"])
+def test_empty_and_zero_length(form):
+    w = synth.custom(1, 2, 64, 64, "bf16", lengths=[0, 0, 0])
+    inp = synth.make_inputs(w, 11, device=DEV)
+    o, S = run(form, inp, w)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert torch.equal(S, inp["initial_state"])
+    o, S = run(form, inp, w, initial_state=None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0
+
+
+def test_constant_memory_in_sequence_length():
+    """The state does not grow with context: the library allocates nothing,
+    so peak memory is the inputs and outputs alone at every length."""
+    w = synth.custom(1, 1, 128, 128, "bf16", lengths=[32768])
+    inp = synth.make_inputs(w, 12, device=DEV)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    o, S = run("chunked", inp, w)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    assert extra <= o.numel() * o.element_size() + S.numel() * 4 + 4096
+
+
+def test_gates_kernel():
+    for dtype, tol in (("f32", 1e-5), ("bf16", 8e-3)):
+        w = synth.custom(4, 12, 128, 128, dtype, lengths=[77, 3])
+        inp = synth.make_inputs(w, 13, device=DEV)
+        q_hat, k_hat, g, beta = gdr.gates(inp["q"], inp["k"], inp["a"], inp["b"], inp["A_log"],
+                                          inp["dt_bias"])
+        torch.cuda.synchronize()
+        rq, rk, rg, rb = U.oracle.gates(inp["q"], inp["k"], inp["a"], inp["b"], inp["A_log"],
+                                        inp["dt_bias"])
+        assert U.slice_err(U.to_np(q_hat), rq) <= tol
+        assert U.slice_err(U.to_np(k_hat), rk) <= tol
+        assert U.slice_err(U.to_np(g), rg) <= 1e-5
+        assert U.slice_err(U.to_np(beta), rb) <= 1e-5
+    # subsets of the outputs
+    _, _, g2, b2 = gdr.gates(inp["q"], inp["k"], inp["a"], inp["b"], inp["A_log"],
+                             inp["dt_bias"], outputs=("g", "beta"))
+    torch.cuda.synchronize()
+    assert torch.equal(g2, g) and torch.equal(b2, beta)
+
+
+def test_binding_rejects_bad_tensors():
+    w = synth.custom(1, 2, 64, 64, "bf16", lengths=[8])
+    inp = synth.make_inputs(w, 14, device=DEV)
+    with pytest.raises(TypeError):
+        gdr.recurrent_fwd(inp["q"].float(), inp["k"], inp["v"], inp["a"], inp["b"],
+                          inp["A_log"], inp["dt_bias"])
+    with pytest.raises(ValueError):
+        gdr.chunked_fwd(inp["q"], inp["k"], inp["v"][:, :1], inp["a"], inp["b"], inp["A_log"],
+                        inp["dt_bias"])
+    bad = synth.make_inputs(synth.custom(1, 2, 48, 64, "bf16", lengths=[8]), 0, device=DEV)
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.recurrent_fwd(bad["q"], bad["k"], bad["v"], bad["a"], bad["b"], bad["A_log"],
+                          bad["dt_bias"], cu_seqlens=bad["cu_seqlens"])
+    assert e.value.status == 3
