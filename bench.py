@@ -65,6 +65,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters under a profiler)")
     ap.add_argument("--cpu-heads", type=int, default=48,
                     help="value heads of the prefill workload the oracle runs for cpu_baseline")
     args = ap.parse_args()
@@ -140,6 +143,15 @@ def main():
     dbytes = decode_bytes(wd.num_seqs, wd.H_k, wd.H_v, wd.d_k, wd.d_v, 2)
     dgbs = dbytes / (dmean_ms / 1e3) / 1e9
 
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
+
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -196,11 +208,10 @@ def main():
 
 
 def gdr_chunked_dtype(gdr, w):
-    """Arithmetic type of the chunked kernel the library picks for ``w``."""
-    fn = getattr(gdr, "chunked_path", None)
-    if fn is None:
-        return "f32"
-    return "bf16" if fn(w) == "mfma" else "f32"
+    """Arithmetic type of the chunked kernel the library picks for ``w``:
+    bf16 matrix operands (fp32 accumulation and state) or fp32 throughout."""
+    path = gdr.chunked_path(w.H_k, w.H_v, w.d_k, w.d_v, w.dtype, w.chunk)
+    return "bf16" if path == "matrix_bf16" else "f32"
 
 
 if __name__ == "__main__":

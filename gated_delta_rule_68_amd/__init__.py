@@ -31,8 +31,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["gates", "recurrent_fwd", "chunked_fwd", "fwd", "library_path", "lib",
-           "GdrError", "abi_version"]
+__all__ = ["gates", "recurrent_fwd", "chunked_fwd", "fwd", "chunked_path", "library_path",
+           "lib", "GdrError", "abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -76,6 +76,8 @@ def _bind(lib):
     lib.gdr_chunked_fwd.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_chunked_path.argtypes = [sp]
+    lib.gdr_chunked_path.restype = ctypes.c_int
     lib.gdr_abi_version.argtypes = []
     lib.gdr_abi_version.restype = ctypes.c_int
     return lib
@@ -246,6 +248,18 @@ def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_
     if dense_T is not None:
         o = o.view(N, dense_T, H_v, d_v)
     return o, final_state
+
+
+def chunked_path(H_k, H_v, d_k, d_v, dtype, chunk=32) -> str:
+    """Name of the kernel gdr_chunked_fwd runs for this shape: "matrix_bf16"
+    (matrix cores, bf16 operands, fp32 accumulation) or "vector_f32"."""
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else (
+        GDR_F32 if dtype in ("f32", "float32") else GDR_BF16)
+    s = _make_shape(1, H_k, H_v, d_k, d_v, None, 1, code, chunk, None, 1e-6)
+    rc = lib().gdr_chunked_path(ctypes.byref(s))
+    if rc < 0:
+        _raise("gdr_chunked_path", -rc)
+    return {0: "vector_f32", 1: "matrix_bf16"}[rc]
 
 
 def recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, cu_seqlens=None,

@@ -189,4 +189,15 @@ gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
   return launched(launch_chunked_vec(pr, x, stream));
 }
 
+int gdr_chunked_path(const gdr_shape *shape) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return -(int)st;
+  if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return -(int)GDR_ERR_UNSUPPORTED;
+  if (chunked_mfma_supports(pr)) return GDR_PATH_MATRIX_BF16;
+  if (chunked_vec_supports(pr)) return GDR_PATH_VECTOR_F32;
+  return -(int)GDR_ERR_UNSUPPORTED;
+}
+
 }  // extern "C"

@@ -154,6 +154,14 @@ GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const 
                            const float *initial_state, void *o, float *final_state,
                            hipStream_t stream);
 
+/* Which kernel gdr_chunked_fwd runs for `shape`: GDR_PATH_VECTOR_F32 (fp32
+ * on the vector ALUs), GDR_PATH_MATRIX_BF16 (matrix cores, bf16 operands,
+ * fp32 accumulation and state), or the negated gdr_status that
+ * gdr_chunked_fwd would return for this shape (pointers are not checked). */
+#define GDR_PATH_VECTOR_F32 0
+#define GDR_PATH_MATRIX_BF16 1
+GDR_API int gdr_chunked_path(const gdr_shape *shape);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 GDR_API const char *gdr_status_string(gdr_status status);
 

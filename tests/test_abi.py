@@ -30,8 +30,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_gates",
-                                  "gdr_recurrent_fwd", "gdr_status_string"]
+    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_path",
+                                  "gdr_gates", "gdr_recurrent_fwd", "gdr_status_string"]
 
 
 def test_library_exports_every_declared_symbol(gdr):
@@ -176,3 +176,15 @@ def test_binding_refuses_cpu_tensors(gdr):
     a = torch.zeros(4, 2)
     with pytest.raises(ValueError):
         gdr.recurrent_fwd(q, q, v, a, a, torch.zeros(2), torch.zeros(2))
+
+
+def test_chunked_path_selection(gdr):
+    lib = gdr.lib()
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=128, chunk=32))) == 1
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=0, d_k=128, d_v=128, chunk=32))) == 0
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=128, chunk=16))) == 0
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=64, d_v=128, chunk=32))) == 0
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, chunk=48))) == -3
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, H_v=3, H_k=2))) == -2
+    assert gdr.chunked_path(16, 48, 128, 128, "bf16", 32) == "matrix_bf16"
+    assert gdr.chunked_path(1, 1, 128, 128, "f32", 32) == "vector_f32"

@@ -307,3 +307,48 @@ def test_binding_rejects_bad_tensors():
         gdr.recurrent_fwd(bad["q"], bad["k"], bad["v"], bad["a"], bad["b"], bad["A_log"],
                           bad["dt_bias"], cu_seqlens=bad["cu_seqlens"])
     assert e.value.status == 3
+
+
+# ------------------------------------------------------------ matrix-core chunked kernel
+MFMA_CASES = [
+    # H_k, H_v, lengths   (grids of 4 * H_v * N workgroups, with and without a multiple of 8)
+    (1, 1, [1]),
+    (1, 1, [31, 32, 33]),
+    (2, 6, [0, 64, 65, 5]),
+    (1, 3, [300, 129, 0]),
+    (4, 4, [97]),
+    (16, 48, [70]),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=lambda c: f"H{c[1]}/{c[0]}_L{'-'.join(map(str, c[2]))}")
+def test_matrix_core_chunked_kernel(case):
+    H_k, H_v, lens = case
+    assert gdr.chunked_path(H_k, H_v, 128, 128, "bf16", 32) == "matrix_bf16"
+    w = synth.custom(H_k, H_v, 128, 128, "bf16", lengths=lens, chunk=32)
+    check_full(w, 21, "chunked")
+
+
+def test_matrix_core_without_initial_state():
+    w = synth.custom(2, 4, 128, 128, "bf16", lengths=[100, 3], chunk=32, init_state=False)
+    check_full(w, 22, "chunked")
+
+
+def test_matrix_core_agrees_with_vector_kernel():
+    """The same bf16 batch through the matrix-core kernel (chunk 32) and the
+    fp32 vector kernel (chunk 16): both forms of one definition."""
+    w = synth.custom(2, 6, 128, 128, "bf16", lengths=[257, 40])
+    inp = synth.make_inputs(w, 23, device=DEV)
+    assert gdr.chunked_path(2, 6, 128, 128, "bf16", 16) == "vector_f32"
+    o1, S1 = run("chunked", inp, w, chunk=32)
+    o2, S2 = run("chunked", inp, w, chunk=16)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        for h in range(w.H_v):
+            worst = max(worst, U.slice_err(U.to_np(o1[cu[n]:cu[n + 1], h]),
+                                           U.to_np(o2[cu[n]:cu[n + 1], h])),
+                        U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
+    note(f"  matrix-core vs vector kernel: {worst:.3e}")
+    assert worst <= U.TOL["bf16"]
