@@ -188,7 +188,8 @@ def main():
                    "global_batch": 1, "seq_len": T, "H_v": w.H_v, "H_k": w.H_k, "d": w.d_k,
                    "chunk": w.chunk},
         "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
+                     "traffic": profiled_traffic("chunked_mfma_kernel"),
                      "kernel": "chunked prefill", "flop_per_launch": flops,
                      "avg_launch_ms": avg_s * 1e3,
                      "hbm_view": {"bytes_per_launch": pbytes,
@@ -199,12 +200,30 @@ def main():
                    "steps": nsteps, "mean_step_ms": dmean_ms, "median_step_ms": dmed_ms,
                    "tokens_per_s": wd.num_seqs / (dmean_ms / 1e3),
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS, "traffic": None,
+                                "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
+                                "traffic": profiled_traffic("recurrent_kernel"),
                                 "bytes_per_launch": dbytes}},
         "wall_s_prefill_timed": wall,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed hardware-counter
+    profile (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
+    size), or None when that kernel's sources changed after the counters
+    were taken (the recorded sha256 no longer matches)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))["kernels"][kernel]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sha256"] else None
 
 
 def gdr_chunked_dtype(gdr, w):
