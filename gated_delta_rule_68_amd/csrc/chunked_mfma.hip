@@ -15,25 +15,23 @@
 // fp32 to the products.  Only differences gamma_r - gamma_i with i <= r are
 // exponentiated.
 //
-// (I + A)^-1 is applied in 16-row blocks: with A_11, A_22 the diagonal blocks,
-//   Delta_1 = T_11 R_1,  Delta_2 = T_22 (R_2 - A_21 Delta_1),  T_bb = (I + A_bb)^-1.
+// (I + A)^-1 is formed in 16-row blocks and then applied as one 32x32 product:
+//   T = [T_11 0; T_21 T_22],  T_bb = (I + A_bb)^-1,  T_21 = -T_22 A_21 T_11.
 // Each T_bb is formed on the matrix cores from the identity, exact for the
 // strictly lower (nilpotent, N^16 = 0) N = A_bb,
-//   (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8),
-// with the leading products carried in split (hi + lo) bf16 so that the
-// result keeps fp32-level accuracy before its final rounding to bf16.
+//   (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8).
 //
 // Work split.  A workgroup owns (sequence, value head, 32 columns of d_v); the
 // columns of S evolve independently.  Six waves, one workgroup barrier per
 // chunk, three chunks in flight:
 //   * 2 consumer waves each keep a [128 x 16] slice of S in MFMA accumulators
-//     for the whole sequence and run chunk c: K S, Q S, the block solve,
-//     outputs, K^T Delta;
-//   * 2 "prepare" waves form chunk c+1's matrices: P0 the Gram blocks of K,
-//     the row norms of k and the inverses T_11, T_22 and -A_21; P1 the norms of
-//     q and P;
+//     for the whole sequence and run chunk c: K S, Q S, Delta = T R, the
+//     outputs and K^T Delta;
+//   * 2 "prepare" waves form chunk c+1's matrices: P0 the Gram blocks of K
+//     and T; P1 the output mask P;
 //   * 2 staging waves lay out chunk c+2 from registers (rows of k, q and v,
-//     gates and their running sum) and prefetch the raw rows of chunk c+4.
+//     their norms, gates and their running sum) and prefetch the raw rows of
+//     chunks up to c+2+NPF.
 // Operands that need a transposed tile (k^T for the state update, v for R)
 // are read with the transposing LDS read from the row-major tiles.
 // Every stage buffer is written in one step and read in later ones only.
@@ -64,10 +62,12 @@ constexpr int CH = 32;   // tokens per chunk
 constexpr int NC = 2;    // consumer waves (16 columns each)
 constexpr int BV = 16 * NC;
 constexpr int NWAVES = 6;
-constexpr int NSTAGE = 3;
+constexpr int NSTAGE = 4;       // chunk buffers in LDS (three in use, one being filled ahead)
+constexpr int NPF = NSTAGE;     // chunks whose raw rows a staging lane holds in registers
 
-// wave roles (wave w runs on SIMD w % 4: each consumer gets a SIMD of its own)
-constexpr int W_P0 = 0, W_P1 = 1, W_C0 = 2, W_ST0 = 4;
+// wave roles (wave w runs on SIMD w % 4): the matrix-heavy consumers share a
+// SIMD with the vector-heavy staging waves, P0 and P1 have one each
+constexpr int W_C0 = 0, W_P0 = 2, W_P1 = 3, W_ST0 = 4;
 
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -125,6 +125,26 @@ __device__ __forceinline__ float scan32(float x) {
   return x;
 }
 
+// Sum over each row of 16 lanes, result in every lane of the row.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+// Sum of squares of the 8 bf16 values packed in a uint4 (bf16 pair dot products).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sumsq8(const uint4 &x) {
+  const bf16x2 w0 = __builtin_bit_cast(bf16x2, x.x), w1 = __builtin_bit_cast(bf16x2, x.y);
+  const bf16x2 w2 = __builtin_bit_cast(bf16x2, x.z), w3 = __builtin_bit_cast(bf16x2, x.w);
+  float s = __builtin_amdgcn_fdot2_f32_bf16(w0, w0, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(w1, w1, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(w2, w2, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(w3, w3, s, false);
+}
+
 // Order this wave's LDS writes before its later LDS reads of other lanes' data.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -143,13 +163,13 @@ struct Stage {
   alignas(16) bf16 Q[CH][KP];    // raw q rows                        (staging)
   alignas(16) bf16 V[CH][VP];    // raw v rows (this workgroup's columns) (staging)
   alignas(16) bf16 P[CH][TP];    // P, columns in slot order          (P1)
-  alignas(16) bf16 T[2][16][16]; // (I + A_bb)^-1, natural rows       (P0)
-  alignas(16) bf16 nA21[16][16]; // -A_21                             (P0)
+  alignas(16) bf16 TT[CH][TP];   // (I + A)^-1, columns in slot order (P0)
   alignas(16) float gam[CH];     // cumulative log decay              (staging)
   alignas(16) float beta[CH];    //                                   (staging)
   alignas(16) float Gam[CH];     // exp(gam)                          (staging)
   alignas(16) float tail[CH];    // exp(gam_last - gam)               (staging)
-  alignas(16) float ik[CH];      // 1/|k_r| (0 past the end)          (P0)
+  alignas(16) float ik[CH];      // 1/|k_r| (0 past the end)          (staging)
+  float iq[CH];                  // scale/|q_r| (0 past the end); directly after ik (staging)
   alignas(16) float cR[CH];      // beta Gam ik                       (P0)
   alignas(16) float cD[CH];      // tail ik                           (P0)
   alignas(16) float cO[CH];      // Gam iq                            (P1)
@@ -159,8 +179,6 @@ struct Stage {
 
 struct Smem {
   Stage st[NSTAGE];
-  alignas(16) float p1_ik[CH];   // P1's private copy of 1/|k|
-  alignas(16) float p1_iq[CH];   // P1's private copy of scale/|q|
 };
 
 struct MfmaParams {
@@ -216,7 +234,7 @@ __device__ __forceinline__ void load_chunk(const MfmaParams &p, Raw &R, int sl, 
 
 // Staging waves: lay out one chunk from registers (sl = 0..127).
 __device__ __forceinline__ void stage_chunk(const Raw &R, Stage &S, int sl, int cl,
-                                            float neg_exp_A, float dtb) {
+                                            float neg_exp_A, float dtb, float eps, float scale) {
   const int rq = sl >> 4, db = sl & 15;
   const int kb = db >> 2, c0 = 8 * (db & 3);
   const int s0 = 32 * kb + slot_of(c0), s1 = 32 * kb + slot_of(c0 + 4);
@@ -230,6 +248,30 @@ __device__ __forceinline__ void stage_chunk(const Raw &R, Stage &S, int sl, int 
   // v rows: columns 2db, 2db + 1 of rows 4rq..4rq+3
 #pragma unroll
   for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t *>(&S.V[4 * rq + i][2 * db]) = R.v[i];
+  // row norms of k and q: the 16 lanes of row quad rq hold its 128 columns;
+  // afterwards lane db < 4 stores 1/|k| of row 4rq+db, lane 4 <= db < 8
+  // scale/|q| of row 4rq+db-4 (ik and iq are adjacent arrays)
+  {
+    float kk[4], qq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kk[i] = sumsq8(R.k[i]);
+      qq[i] = sumsq8(R.q[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kk[i] = row_sum16(kk[i]);
+      qq[i] = row_sum16(qq[i]);
+    }
+    const int i = db & 3;
+    const bool isq = (db & 4) != 0;
+    const float k01 = (i & 1) ? kk[1] : kk[0], k23 = (i & 1) ? kk[3] : kk[2];
+    const float q01 = (i & 1) ? qq[1] : qq[0], q23 = (i & 1) ? qq[3] : qq[2];
+    const float ks = (i & 2) ? k23 : k01, qs = (i & 2) ? q23 : q01;
+    const int r = 4 * rq + i;
+    const float inv = r < cl ? rsqrtf((isq ? qs : ks) + eps) * (isq ? scale : 1.f) : 0.f;
+    if (db < 8) S.ik[r + (isq ? CH : 0)] = inv;
+  }
   // gates of row r = sl % 32, running sum over the 32 rows (every lane of both
   // staging waves derives the same values and stores them identically)
   {
@@ -246,8 +288,10 @@ __device__ __forceinline__ void stage_chunk(const Raw &R, Stage &S, int sl, int 
     S.beta[r] = bt;
     S.Gam[r] = fast_exp(cum);
     S.tail[r] = fast_exp(last - cum);
-    S.Gc = fast_exp(last);
-    S.cl = cl;
+    if (sl == 0) {
+      S.Gc = fast_exp(last);
+      S.cl = cl;
+    }
   }
 }
 
@@ -274,42 +318,52 @@ __device__ __forceinline__ bf16x8 row_op(const bf16 (*X)[KP], int r, int kb, int
 
 // (I + N)^-1 for one strictly lower 16x16 block N, given in both lane layouts:
 //   na[j] = N[m][4g+j] (A operand layout), nb[j] = N[4g+j][m] (B/accumulator layout).
-// Returns T[m][4g+j] (A operand layout).  Transposes ride along: the
+// The identity (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) is exact since
+// N^16 = 0, and its factors commute.  ta gets T[m][4g+j] (A layout) and, if
+// requested, tb gets T[4g+j][m] (B layout).  Transposes ride along: the
 // accumulator of X Y is the B layout of X Y, that of Y^T X^T its A layout.
-__device__ __forceinline__ f32x4 unit_lower_inverse(f32x4 na, f32x4 nb, int m, int g) {
+template <bool WANT_B>
+__device__ __forceinline__ void unit_lower_inverse(f32x4 na, f32x4 nb, int m, int g, f32x4 &ta,
+                                                   f32x4 &tb) {
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x4 na_h = pack4(na), nb_h = pack4(nb);
-  const bf16x4 na_l = pack4(na - unpack4(na_h)), nb_l = pack4(nb - unpack4(nb_h));
-  // N^2 (split) and (N^2)^T
-  f32x4 n2 = mma16(na_h, nb_h, z);
-  n2 = mma16(na_l, nb_h, n2);
-  n2 = mma16(na_h, nb_l, n2);
-  const f32x4 n2t = mma16(nb_h, na_h, z);
-  const bf16x4 n2b_h = pack4(n2), n2a = pack4(n2t);
-  const bf16x4 n2b_l = pack4(n2 - unpack4(n2b_h));
-  // N^4, (N^4)^T, N^8
-  const f32x4 n4 = mma16(n2a, n2b_h, z);
-  const f32x4 n4t = mma16(n2b_h, n2a, z);
-  const bf16x4 n4b = pack4(n4), n4a = pack4(n4t);
+  const bf16x4 n2b = pack4(mma16(na_h, nb_h, z));  // N^2
+  const bf16x4 n2a = pack4(mma16(nb_h, na_h, z));  // (N^2)^T in B layout = N^2 in A layout
+  const bf16x4 n4b = pack4(mma16(n2a, n2b, z));
+  const bf16x4 n4a = pack4(mma16(n2b, n2a, z));
   const bf16x4 n8b = pack4(mma16(n4a, n4b, z));
-  // pt[j] = P_k[m][4g+j]:  P_1 = I - N,  P_{k+1} = P_k (I + N^(2^k)),
-  // i.e. P_{k+1}^T = P_k^T + (N^(2^k))^T P_k^T.
-  f32x4 pt;
+  f32x4 id;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pt[j] = (m == 4 * g + j ? 1.f : 0.f) - na[j];
-  const bf16x4 ptb = pack4(pt);
-  const f32x4 acc = mma16(n2b_h, ptb, pt);
-  pt = mma16(n2b_l, ptb, acc);
+  for (int j = 0; j < 4; ++j) id[j] = (m == 4 * g + j) ? 1.f : 0.f;
+  // A layout: P_{k+1}^T = P_k^T + (N^(2^k))^T P_k^T, P_1 = I - N
+  f32x4 pt = id - na;
+  pt = mma16(n2b, pack4(pt), pt);
   pt = mma16(n4b, pack4(pt), pt);
-  pt = mma16(n8b, pack4(pt), pt);
-  return pt;
+  ta = mma16(n8b, pack4(pt), pt);
+  if (WANT_B) {
+    // B layout: Q_{k+1} = Q_k + N^(2^k) Q_k, Q_1 = I - N
+    const bf16x4 n8a = pack4(mma16(n4b, n4a, z));
+    f32x4 q = id - nb;
+    q = mma16(n2a, pack4(q), q);
+    q = mma16(n4a, pack4(q), q);
+    tb = mma16(n8a, pack4(q), q);
+  }
 }
 
-// P0: Gram blocks of k, 1/|k|, T_11, T_22, -A_21 of one chunk.
+// P0: Gram blocks of k and T = (I + A)^-1 of one chunk.
+// Lane (m, g) holds the Gram entries (k_i . k_m), i = 4g + j, of each block;
+// exactly one of i < m, i > m holds off the diagonal, so one decay factor
+// exp(-|gam_m - gam_i|) serves both the A-operand (row m) and the B-operand
+// (column m) layout of N.
 __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, int lane) {
   const int m = lane & 15, g = lane >> 4;
-  const int cl = S.cl;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 ik_lo = ld4(&S.ik[4 * g]), ik_hi = ld4(&S.ik[16 + 4 * g]);
+  const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
+  const f32x4 bt_lo = ld4(&S.beta[4 * g]), bt_hi = ld4(&S.beta[16 + 4 * g]);
+  const float ik_m0 = S.ik[m], ik_m1 = S.ik[16 + m];
+  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
+  const float bt_m0 = S.beta[m], bt_m1 = S.beta[16 + m];
   f32x4 t00 = z, t11 = z, t01 = z;  // (K K^T) blocks: rows 4g+j, column m (+16)
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -318,38 +372,36 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, int la
     t11 = mma32(k1, k1, t11);
     t01 = mma32(k0, k1, t01);
   }
-  // 1/|k_r| from the diagonal: lane (m, g = m/4) holds |k_m|^2 in register m%4
-  if (g == (m >> 2)) {
-    const int j = m & 3;
-    S.ik[m] = (m < cl) ? rsqrtf(t00[j] + p.eps) : 0.f;
-    S.ik[16 + m] = (16 + m < cl) ? rsqrtf(t11[j] + p.eps) : 0.f;
-  }
-  wave_lds_sync();
-  const f32x4 ik_lo = ld4(&S.ik[4 * g]), ik_hi = ld4(&S.ik[16 + 4 * g]);
-  const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
-  const f32x4 bt_lo = ld4(&S.beta[4 * g]), bt_hi = ld4(&S.beta[16 + 4 * g]);
-  const float ik_m0 = S.ik[m], ik_m1 = S.ik[16 + m];
-  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
-  const float bt_m0 = S.beta[m], bt_m1 = S.beta[16 + m];
   // A in both layouts for the two diagonal blocks, and -A_21 in A layout.
-  // (K K^T)[4g+j][m] = (K K^T)[m][4g+j]: one accumulator serves both layouts.
   f32x4 na0, nb0, na1, nb1;
   bf16x4 na21;
+  const float bik_m1 = bt_m1 * ik_m1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = 4 * g + j;
-    nb0[j] = (m < r) ? bt_lo[j] * fast_exp(fminf(gm_lo[j] - gm_m0, 0.f)) * ik_lo[j] * ik_m0 * t00[j] : 0.f;
-    na0[j] = (r < m) ? bt_m0 * fast_exp(fminf(gm_m0 - gm_lo[j], 0.f)) * ik_m0 * ik_lo[j] * t00[j] : 0.f;
-    nb1[j] = (m < r) ? bt_hi[j] * fast_exp(fminf(gm_hi[j] - gm_m1, 0.f)) * ik_hi[j] * ik_m1 * t11[j] : 0.f;
-    na1[j] = (r < m) ? bt_m1 * fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * ik_m1 * ik_hi[j] * t11[j] : 0.f;
-    // A_21[m][r] = beta_{16+m} exp(gam_{16+m} - gam_r) ik_{16+m} ik_r (K K^T)[r][16+m]
-    na21[j] = (bf16)(-(bt_m1 * fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * ik_m1 * ik_lo[j] * t01[j]));
+    const int i = 4 * g + j;
+    const float x0 = t00[j] * ik_m0 * ik_lo[j] * fast_exp(-fabsf(gm_m0 - gm_lo[j]));
+    na0[j] = (i < m) ? bt_m0 * x0 : 0.f;
+    nb0[j] = (i > m) ? bt_lo[j] * x0 : 0.f;
+    const float x1 = t11[j] * ik_m1 * ik_hi[j] * fast_exp(-fabsf(gm_m1 - gm_hi[j]));
+    na1[j] = (i < m) ? bt_m1 * x1 : 0.f;
+    nb1[j] = (i > m) ? bt_hi[j] * x1 : 0.f;
+    // A_21[m][i] = beta_{16+m} exp(gam_{16+m} - gam_i) ik_{16+m} ik_i (k_i . k_{16+m})
+    na21[j] = (bf16)(-bik_m1 * ik_lo[j] * fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * t01[j]);
   }
-  *reinterpret_cast<bf16x4 *>(&S.nA21[m][4 * g]) = na21;
-  const f32x4 T0 = unit_lower_inverse(na0, nb0, m, g);
-  const f32x4 T1 = unit_lower_inverse(na1, nb1, m, g);
-  *reinterpret_cast<bf16x4 *>(&S.T[0][m][4 * g]) = pack4(T0);
-  *reinterpret_cast<bf16x4 *>(&S.T[1][m][4 * g]) = pack4(T1);
+  // T = (I + A)^-1 = [T11 0; T21 T22], T_bb = (I + A_bb)^-1, T21 = -T22 A21 T11
+  f32x4 t11a, t11b, t22a, unused;
+  unit_lower_inverse<true>(na0, nb0, m, g, t11a, t11b);
+  unit_lower_inverse<false>(na1, nb1, m, g, t22a, unused);
+  const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Y = -A21 T11 (B layout); its accumulator is the A layout of Y^T, and
+  // Y^T T22^T is the B layout of T21^T, i.e. the A layout of T21.
+  const f32x4 y = mma16(na21, pack4(t11b), z4);
+  const f32x4 t21a = mma16(pack4(y), pack4(t22a), z4);
+  // rows of T with the column index in slot order: row m holds (T11[m][4g..], 0),
+  // row 16 + m holds (T21[m][4g..], T22[m][4g..])
+  const bf16x4 zb = pack4(z4);
+  *reinterpret_cast<bf16x8 *>(&S.TT[m][8 * g]) = cat8(pack4(t11a), zb);
+  *reinterpret_cast<bf16x8 *>(&S.TT[16 + m][8 * g]) = cat8(pack4(t21a), pack4(t22a));
   // per-row factors for the consumers
   if (lane < CH) {
     const int r = lane;
@@ -359,41 +411,23 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, int la
   }
 }
 
-// P1: norms of q (and its own copy of those of k), P and Gam iq.
-__device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, Smem &sm, int lane) {
+// P1: P and Gam iq of one chunk.
+__device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, int lane) {
   const int m = lane & 15, g = lane >> 4;
-  const int cl = S.cl;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 kk0 = z, kk1 = z, qq0 = z, qq1 = z;  // Gram diagonal blocks of k and q
+  const f32x4 ik_lo = ld4(&S.ik[4 * g]), ik_hi = ld4(&S.ik[16 + 4 * g]);
+  const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
+  const float iq_m0 = S.iq[m], iq_m1 = S.iq[16 + m];
+  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
   f32x4 p00 = z, p10 = z, p11 = z;  // (K Q^T) blocks: (q_r . k_i), r = 16 rb + m, i = 16 ib + 4g + j
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const bf16x8 k0 = row_op(S.K, m, kb, g), k1 = row_op(S.K, 16 + m, kb, g);
     const bf16x8 q0 = row_op(S.Q, m, kb, g), q1 = row_op(S.Q, 16 + m, kb, g);
-    kk0 = mma32(k0, k0, kk0);
-    kk1 = mma32(k1, k1, kk1);
-    qq0 = mma32(q0, q0, qq0);
-    qq1 = mma32(q1, q1, qq1);
     p00 = mma32(k0, q0, p00);
     p10 = mma32(k0, q1, p10);
     p11 = mma32(k1, q1, p11);
   }
-  if (g == (m >> 2)) {
-    const int j = m & 3;
-    sm.p1_ik[m] = (m < cl) ? rsqrtf(kk0[j] + p.eps) : 0.f;
-    sm.p1_ik[16 + m] = (16 + m < cl) ? rsqrtf(kk1[j] + p.eps) : 0.f;
-    const float iq0 = (m < cl) ? rsqrtf(qq0[j] + p.eps) * p.scale : 0.f;
-    const float iq1 = (16 + m < cl) ? rsqrtf(qq1[j] + p.eps) * p.scale : 0.f;
-    sm.p1_iq[m] = iq0;
-    sm.p1_iq[16 + m] = iq1;
-    S.cO[m] = S.Gam[m] * iq0;
-    S.cO[16 + m] = S.Gam[16 + m] * iq1;
-  }
-  wave_lds_sync();
-  const f32x4 ik_lo = ld4(&sm.p1_ik[4 * g]), ik_hi = ld4(&sm.p1_ik[16 + 4 * g]);
-  const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
-  const float iq_m0 = sm.p1_iq[m], iq_m1 = sm.p1_iq[16 + m];
-  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
   f32x4 v00, v10, v11;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -407,6 +441,7 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, Smem &
   *reinterpret_cast<bf16x4 *>(&S.P[m][s_hi]) = pack4(z);
   *reinterpret_cast<bf16x4 *>(&S.P[16 + m][s_lo]) = pack4(v10);
   *reinterpret_cast<bf16x4 *>(&S.P[16 + m][s_hi]) = pack4(v11);
+  if (lane < CH) S.cO[lane] = S.Gam[lane] * S.iq[lane];
 }
 
 __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p) {
@@ -432,9 +467,9 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
   const float dtb = p.dt_bias[h];
   const int col0 = vb * BV;
   // step `it` consumes chunk it-2, prepares chunk it-1 and stages chunk it;
-  // the step count is even so that the staging loop below, unrolled by two,
-  // has a straight-line body (an idle step at the end when nch is odd)
-  const int nsteps = (nch + 3) & ~1;
+  // the step count is a multiple of NPF so that the staging loop below,
+  // unrolled by NPF, has a straight-line body (idle steps at the end)
+  const int nsteps = (nch + 2 + NPF - 1) / NPF * NPF;
 
   if (wave >= W_C0 && wave < W_C0 + NC) {
     // ---------------------------------------------------------------- consumers
@@ -453,6 +488,31 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     bf16x8 Sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+    // Operands of the next chunk, read from LDS while this wave would
+    // otherwise wait at the barrier: rows of k and q (A operands of K S and
+    // the B operands of (Q S)^T), k^T (A operand of the state update) and v.
+    // The rows of chunk it-1 are complete once step it-1 has ended.
+    bf16x8 Kr[2][4], Qr[2][4], Kt[8], vv;
+    auto read_operands = [&](const Stage &sn) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          Kr[mt][kb] = row_op(sn.K, 16 * mt + m, kb, g);
+          Qr[mt][kb] = row_op(sn.Q, 16 * mt + m, kb, g);
+        }
+      // k^T[16t + m][slots 8g..8g+7] = k[4g + j][16t + m], k[16 + 4g + j][16t + m]
+      // read transposed from the row-major k tile (d_k in slot order per
+      // 32-block: four consecutive d stay contiguous)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int kc = 32 * (t >> 1) + slot_of(16 * (t & 1) + 4 * (m & 3));
+        Kt[t] = cat8(tr_read(&sn.K[4 * g + (m >> 2)][kc]), tr_read(&sn.K[16 + 4 * g + (m >> 2)][kc]));
+      }
+      // v[4g + j][col] and v[16 + 4g + j][col]
+      const int vc = 16 * cw + 4 * (m & 3);
+      vv = cat8(tr_read(&sn.V[4 * g + (m >> 2)][vc]), tr_read(&sn.V[16 + 4 * g + (m >> 2)][vc]));
+    };
     for (int it = 0; it < nsteps; ++it) {
       const int c = it - 2;
       if (c >= 0 && c < nch) {
@@ -464,15 +524,11 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
-            ks[mt] = mma32(row_op(st.K, 16 * mt + m, kb, g), Sb[kb], ks[mt]);
-            qsT[mt] = mma32(Sb[kb], row_op(st.Q, 16 * mt + m, kb, g), qsT[mt]);
+            ks[mt] = mma32(Kr[mt][kb], Sb[kb], ks[mt]);
+            qsT[mt] = mma32(Sb[kb], Qr[mt][kb], qsT[mt]);
           }
         }
         // R = beta V - (beta Gam ik) K S, rows 4g..4g+3 and 16+4g..16+4g+3
-        // v[4g + j][col] and v[16 + 4g + j][col] (transposing reads of v rows)
-        const int vc = 16 * cw + 4 * (m & 3);
-        const bf16x8 vv = cat8(tr_read(&st.V[4 * g + (m >> 2)][vc]),
-                               tr_read(&st.V[16 + 4 * g + (m >> 2)][vc]));
         const f32x4 bt0 = ld4(&st.beta[4 * g]), bt1 = ld4(&st.beta[16 + 4 * g]);
         const f32x4 cr0 = ld4(&st.cR[4 * g]), cr1 = ld4(&st.cR[16 + 4 * g]);
         f32x4 R0, R1;
@@ -481,13 +537,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           R0[j] = bt0[j] * (float)vv[j] - cr0[j] * ks[0][j];
           R1[j] = bt1[j] * (float)vv[4 + j] - cr1[j] * ks[1][j];
         }
-        // Delta_1 = T11 R1; Delta_2 = T22 (R2 - A21 Delta_1)
-        const bf16x4 t11 = *reinterpret_cast<const bf16x4 *>(&st.T[0][m][4 * g]);
-        const bf16x4 t22 = *reinterpret_cast<const bf16x4 *>(&st.T[1][m][4 * g]);
-        const bf16x4 na21 = *reinterpret_cast<const bf16x4 *>(&st.nA21[m][4 * g]);
-        const f32x4 d1 = mma16(t11, pack4(R0), z);
-        const f32x4 r2 = mma16(na21, pack4(d1), R1);
-        const f32x4 d2 = mma16(t22, pack4(r2), z);
+        // Delta = T R: rows 0..15 and 16..31 of T against R in slot order
+        const bf16x8 Rb = pack8(R0, R1);
+        const bf16x8 ta0 = *reinterpret_cast<const bf16x8 *>(&st.TT[m][8 * g]);
+        const bf16x8 ta1 = *reinterpret_cast<const bf16x8 *>(&st.TT[16 + m][8 * g]);
+        const f32x4 d1 = mma32(ta0, Rb, z);
+        const f32x4 d2 = mma32(ta1, Rb, z);
         const bf16x8 Db = pack8(d1, d2);
         // O^T = Delta^T P^T + (Gam iq Q S)^T: lane (m, g) gets O[16mt + m][4g..4g+3]
 #pragma unroll
@@ -504,19 +559,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         const f32x4 cd0 = ld4(&st.cD[4 * g]), cd1 = ld4(&st.cD[16 + 4 * g]);
         const bf16x8 Dp = pack8(cd0 * d1, cd1 * d2);
         const float gc = st.Gc;
-        // A operand k^T[16t + m][slots 8g..8g+7] = k[4g + j][16t + m], k[16 + 4g + j][16t + m]
-        // read transposed from the row-major k tile (d_k in slot order per 32-block:
-        // four consecutive d stay contiguous)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int kc = 32 * (t >> 1) + slot_of(16 * (t & 1) + 4 * (m & 3));
-          const bf16x8 akt = cat8(tr_read(&st.K[4 * g + (m >> 2)][kc]),
-                                  tr_read(&st.K[16 + 4 * g + (m >> 2)][kc]));
-          S[t] = mma32(akt, Dp, S[t] * gc);
-        }
+        for (int t = 0; t < 8; ++t) S[t] = mma32(Kt[t], Dp, S[t] * gc);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
       }
+      if (it - 1 >= 0 && it - 1 < nch) read_operands(sm.st[(it - 1) % NSTAGE]);
       __syncthreads();
     }
     if (p.sT) {
@@ -533,14 +581,14 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         if (wave == W_P0)
           prepare_p0(p, sm.st[c % NSTAGE], lane);
         else
-          prepare_p1(p, sm.st[c % NSTAGE], sm, lane);
+          prepare_p1(p, sm.st[c % NSTAGE], lane);
       }
       __syncthreads();
     }
   } else {
     // ---------------------------------------------------------------- staging
     const int sl = threadIdx.x - 64 * W_ST0;  // 0..127
-    Raw ra, rb;  // raw rows of even / odd chunks
+    Raw raw[NPF];  // raw rows of chunks it, it+1, ..., it+NPF-1
     auto rows_of = [&](int c, int64_t &row0, int &cl) {
       row0 = t0 + (int64_t)c * CH;
       const int64_t rem = t1 - row0;
@@ -552,36 +600,37 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       rows_of(min(c, nch - 1), row0, cl);
       load_chunk(p, R, sl, row0, cl, hk, h, col0);
     };
-    auto stage = [&](Raw &R, int c) {
+    auto stage = [&](Raw &R, int c, Stage &buf) {
       int64_t row0;
       int cl;
       rows_of(c, row0, cl);
-      stage_chunk(R, sm.st[c % NSTAGE], sl, cl, neg_exp_A, dtb);
+      stage_chunk(R, buf, sl, cl, neg_exp_A, dtb, p.eps, p.scale);
     };
     if (nch == 0) {  // nothing to load; keep the barrier count
       for (int it = 0; it < nsteps; ++it) __syncthreads();
       return;
     }
-    load(ra, 0);
-    // keep the issue order ra-then-rb, as in the loop, so that the loads of
-    // ra are always the older ones where the loop consumes them
-    __builtin_amdgcn_sched_barrier(0);
-    load(rb, 1);
-    // Unrolled by two so that each register set is named statically.  The
+    // Keep the issue order of the register sets as in the loop, so that the
+    // loads of the set staged next are always the oldest in flight.
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      load(raw[u], u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Unrolled by NPF so that each register set is named statically.  The
     // body is straight-line: staging a chunk past the end writes a buffer no
     // one reads again, and loads are clamped to the last chunk.
     // The scheduling barriers keep every read of a register set ahead of the
     // loads that refill it, so that its own loads are always the oldest in
-    // flight and the other set's stay in flight while it is staged.
-    for (int it = 0; it < nsteps; it += 2) {
-      stage(ra, it);
-      __builtin_amdgcn_sched_barrier(0);
-      load(ra, it + 2);
-      __syncthreads();
-      stage(rb, it + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load(rb, it + 3);
-      __syncthreads();
+    // flight and the other sets' stay in flight while it is staged.
+    for (int it = 0; it < nsteps; it += NPF) {
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) {
+        stage(raw[u], it + u, sm.st[u]);  // (it + u) % NSTAGE == u
+        __builtin_amdgcn_sched_barrier(0);
+        load(raw[u], it + u + NPF);
+        __syncthreads();
+      }
     }
   }
 }
