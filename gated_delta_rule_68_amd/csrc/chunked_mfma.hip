@@ -44,9 +44,10 @@
 // covering rows 0..15 and 16..31 gives lane l the rows 4g..4g+3 and
 // 16+4g..16+4g+3 of its column, which is a valid B operand if the contraction
 // index is visited in "slot" order: slot 8g+j is position 4g+j (j < 4) or
-// 16+4g+j-4 (j >= 4) of a 32-block.  Every A operand is read in slot order
-// (two 8-byte reads per lane), so the state and the deltas never leave
-// registers between products.
+// 16+4g+j-4 (j >= 4) of a 32-block.  The chunk-position operands (T, P and
+// k^T) are laid out in slot order; the state tiles hold rows chosen so that
+// the d_k operands (rows of k and q) are plain 16-byte reads (state_row), so
+// the state and the deltas never leave registers between products.
 #include "device_common.h"
 #include "gdr_internal.h"
 
@@ -208,12 +209,19 @@ struct MfmaParams {
   float scale, eps;
 };
 
-// A operand of row r, 32-block kb of d_k, contraction index in slot order:
-// positions 32kb + 4g.. and 32kb + 16 + 4g.. of the row.
+// State rows held in registers.  Accumulator tile t (t = 0..7) of a
+// consumer holds, in lane (m, g) register j, the state row
+//   d(t, g, j) = 32 (t / 2) + 8 g + 4 (t % 2) + j
+// of column m, so that the tile pair (2kb, 2kb+1) gives every lane 8
+// consecutive rows 32kb + 8g .. 32kb + 8g + 7: a B operand whose contraction
+// index runs in natural order, matching one 16-byte read of a k or q row.
+__device__ __forceinline__ int state_row(int t, int g, int j) {
+  return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + j;
+}
+
+// Operand of row r, 32-block kb of d_k: columns 32kb + 8g .. 32kb + 8g + 7.
 __device__ __forceinline__ bf16x8 row_op(const bf16 *X, int r, int kb, int g) {
-  const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(X + kq_off(r, 32 * kb + 4 * g));
-  const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(X + kq_off(r, 32 * kb + 16 + 4 * g));
-  return cat8(lo, hi);
+  return *reinterpret_cast<const bf16x8 *>(X + kq_off(r, 32 * kb + 8 * g));
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
@@ -346,12 +354,31 @@ __device__ __forceinline__ void unit_lower_inverse2(f32x4 na0, f32x4 nb0, f32x4 
   t0b = mma16(a0_8, pk4(q0), q0);
 }
 
+// Row operands of one chunk for the prepare waves: rows m and 16 + m of k
+// (and q), every 32-block of d_k.
+struct RowOps {
+  bf16x8 k0[4], k1[4], q0[4], q1[4];
+};
+template <bool WITH_Q>
+__device__ __forceinline__ void read_row_ops(const Stage &S, RowOps &o, int m, int g) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    o.k0[kb] = row_op(S.K, m, kb, g);
+    o.k1[kb] = row_op(S.K, 16 + m, kb, g);
+    if (WITH_Q) {
+      o.q0[kb] = row_op(S.Q, m, kb, g);
+      o.q1[kb] = row_op(S.Q, 16 + m, kb, g);
+    }
+  }
+}
+
 // P0: Gram blocks of k, 1/|k| and T = (I + A)^-1 of one chunk.
 // Lane (m, g) holds the Gram entries (k_i . k_m), i = 4g + j, of each block;
 // exactly one of i < m, i > m holds off the diagonal, so one decay factor
 // exp(-|gam_m - gam_i|) serves both the A-operand (row m) and the B-operand
 // (column m) layout of N.
-__device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, int lane) {
+__device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const RowOps &o,
+                                           int lane) {
   const int m = lane & 15, g = lane >> 4;
   const int cl = S.cl;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -362,10 +389,9 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, int la
   f32x4 t00 = z, t11 = z, t01 = z;  // (K K^T) blocks: rows 4g+j, column m (+16)
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const bf16x8 k0 = row_op(S.K, m, kb, g), k1 = row_op(S.K, 16 + m, kb, g);
-    t00 = mma32(k0, k0, t00);
-    t11 = mma32(k1, k1, t11);
-    t01 = mma32(k0, k1, t01);
+    t00 = mma32(o.k0[kb], o.k0[kb], t00);
+    t11 = mma32(o.k1[kb], o.k1[kb], t11);
+    t01 = mma32(o.k0[kb], o.k1[kb], t01);
   }
   // 1/|k_r| from the diagonal: lane (m, g = m/4) holds |k_m|^2 in register m%4
   if (g == (m >> 2)) {
@@ -405,7 +431,8 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, int la
 }
 
 // P1: scale/|q|, Gam scale/|q| and P without the factor 1/|k_i| of one chunk.
-__device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, int lane) {
+__device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const RowOps &o,
+                                           int lane) {
   const int m = lane & 15, g = lane >> 4;
   const int cl = S.cl;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -415,13 +442,11 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, int la
   f32x4 p00 = z, p10 = z, p11 = z;  // (K Q^T) blocks: (q_r . k_i), r = 16 rb + m, i = 16 ib + 4g + j
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const bf16x8 k0 = row_op(S.K, m, kb, g), k1 = row_op(S.K, 16 + m, kb, g);
-    const bf16x8 q0 = row_op(S.Q, m, kb, g), q1 = row_op(S.Q, 16 + m, kb, g);
-    qq0 = mma32(q0, q0, qq0);
-    qq1 = mma32(q1, q1, qq1);
-    p00 = mma32(k0, q0, p00);
-    p10 = mma32(k0, q1, p10);
-    p11 = mma32(k1, q1, p11);
+    qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
+    qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
+    p00 = mma32(o.k0[kb], o.q0[kb], p00);
+    p10 = mma32(o.k0[kb], o.q1[kb], p10);
+    p11 = mma32(o.k1[kb], o.q1[kb], p11);
   }
   if (g == (m >> 2)) {
     const int j = m & 3;
@@ -480,7 +505,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) S[t][j] = p.s0[state_off + (size_t)(16 * t + 4 * g + j) * DV + col];
+        for (int j = 0; j < 4; ++j) S[t][j] = p.s0[state_off + (size_t)state_row(t, g, j) * DV + col];
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -488,13 +513,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     bf16x8 Sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
-    // Operands of the next chunk, read from LDS while this wave would
-    // otherwise wait at the barrier: rows of k and q (A operands of K S and
-    // the B operands of (Q S)^T), k^T (A operand of the state update) and v.
-    // The rows of chunk it-1 are in LDS once step it-1 has ended.
+    // Row operands of the next chunk are read from LDS during this one: k and
+    // q rows (A operands of K S, B operands of (Q S)^T) once this chunk's
+    // products with them are issued, k^T (A operand of the state update) and
+    // v after the state update.  The rows of chunk c+1 are in LDS from step
+    // c+1 on (they are published one step ahead of use).
     bf16x8 Kr[2][4], Qr[2][4], Kt[8], vv;
-    block_sync();
-    auto read_operands = [&](const Stage &sn) {
+    auto read_rows = [&](const Stage &sn) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -502,21 +527,39 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           Kr[mt][kb] = row_op(sn.K, 16 * mt + m, kb, g);
           Qr[mt][kb] = row_op(sn.Q, 16 * mt + m, kb, g);
         }
-      // k^T[16t + m][slots 8g..8g+7] = k[4g + j][16t + m], k[16 + 4g + j][16t + m]
+    };
+    auto read_cols = [&](const Stage &sn) {
+      // A operand of tile t: row m is state row state_row(t, m / 4, m % 4),
+      // contraction over chunk positions in slot order, i.e. lane (m, g) gets
+      // k[4g + j][state_row(t, m / 4, m % 4)] and k[16 + 4g + j][...], j = 0..3
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const int r = 4 * g + (m >> 2), d = 16 * t + 4 * (m & 3);
+        const int r = 4 * g + (m >> 2), d = state_row(t, m & 3, 0);
         Kt[t] = cat8(tr_read(sn.K + kq_off(r, d)), tr_read(sn.K + kq_off(16 + r, d)));
       }
       // v[4g + j][col] and v[16 + 4g + j][col]
       const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
       vv = cat8(tr_read(sn.V + vr * BV + vc), tr_read(sn.V + (16 + vr) * BV + vc));
     };
+    block_sync();
     for (int it = 0; it < nsteps; ++it) {
       const int c = it - 2;
       if (c >= 0 && c < nch) {
         const Stage &st = sm.st[c % NSTAGE];
+        const bool more = c + 1 < nch;
+        const Stage &sn = sm.st[(c + 1) % NSTAGE];
         const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+        // this chunk's prepared tiles and row factors
+        const bf16x8 ta0 = *reinterpret_cast<const bf16x8 *>(&st.TT[m][8 * g]);
+        const bf16x8 ta1 = *reinterpret_cast<const bf16x8 *>(&st.TT[16 + m][8 * g]);
+        const bf16x8 pr0 = *reinterpret_cast<const bf16x8 *>(&st.P[m][8 * g]);
+        const bf16x8 pr1 = *reinterpret_cast<const bf16x8 *>(&st.P[16 + m][8 * g]);
+        const f32x4 bt0 = ld4(&st.beta[4 * g]), bt1 = ld4(&st.beta[16 + 4 * g]);
+        const f32x4 gm0 = ld4(&st.Gam[4 * g]), gm1 = ld4(&st.Gam[16 + 4 * g]);
+        const f32x4 ik0 = ld4(&st.ik[4 * g]), ik1 = ld4(&st.ik[16 + 4 * g]);
+        const f32x4 tl0 = ld4(&st.tail[4 * g]), tl1 = ld4(&st.tail[16 + 4 * g]);
+        const float co0 = st.cO[m], co1 = st.cO[16 + m];
+        const float gc = st.Gc;
         // ks[mt]: (K S)[16mt + 4g + j][m];  qsT[mt]: (Q S)[16mt + m][4g + j]
         f32x4 ks[2] = {z, z}, qsT[2] = {z, z};
 #pragma unroll
@@ -527,11 +570,10 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
             qsT[mt] = mma32(Sb[kb], Qr[mt][kb], qsT[mt]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) read_rows(sn);
+        __builtin_amdgcn_sched_barrier(0);
         // R = beta (V - Gam ik K S), rows 4g..4g+3 and 16+4g..16+4g+3
-        const f32x4 bt0 = ld4(&st.beta[4 * g]), bt1 = ld4(&st.beta[16 + 4 * g]);
-        const f32x4 gm0 = ld4(&st.Gam[4 * g]), gm1 = ld4(&st.Gam[16 + 4 * g]);
-        const f32x4 ik0 = ld4(&st.ik[4 * g]), ik1 = ld4(&st.ik[16 + 4 * g]);
-        const f32x4 tl0 = ld4(&st.tail[4 * g]), tl1 = ld4(&st.tail[16 + 4 * g]);
         f32x4 R0, R1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -540,52 +582,61 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         }
         // Delta = T R: rows 0..15 and 16..31 of T against R in slot order
         const bf16x8 Rb = pack8(R0, R1);
-        const bf16x8 ta0 = *reinterpret_cast<const bf16x8 *>(&st.TT[m][8 * g]);
-        const bf16x8 ta1 = *reinterpret_cast<const bf16x8 *>(&st.TT[16 + m][8 * g]);
         const f32x4 d1 = mma32(ta0, Rb, z);
         const f32x4 d2 = mma32(ta1, Rb, z);
         // O^T = (diag(ik) Delta)^T P^T + (Gam iq Q S)^T: lane (m, g) gets O[16mt + m][4g..4g+3]
         const bf16x8 Db = pack8(ik0 * d1, ik1 * d2);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int r = 16 * mt + m;
-          const bf16x8 bp = *reinterpret_cast<const bf16x8 *>(&st.P[r][8 * g]);
-          const f32x4 oc = mma32(Db, bp, qsT[mt] * st.cO[r]);
-          const int64_t row = t0 + (int64_t)c * CH + r;
-          if (row < t1)
-            *reinterpret_cast<bf16x4 *>(p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g) =
-                pack4(oc);
-        }
+        const f32x4 oc0 = mma32(Db, pr0, qsT[0] * co0);
+        const f32x4 oc1 = mma32(Db, pr1, qsT[1] * co1);
+        const int64_t row = t0 + (int64_t)c * CH + m;
+        bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g;
+        if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
+        if (row + 16 < t1) *reinterpret_cast<bf16x4 *>(orow + (int64_t)16 * p.H_v * DV) = pack4(oc1);
         // S <- Gam_last S + K^T diag(tail ik) Delta
         const bf16x8 Dp = pack8(tl0 * ik0 * d1, tl1 * ik1 * d2);
-        const float gc = st.Gc;
 #pragma unroll
         for (int t = 0; t < 8; ++t) S[t] = mma32(Kt[t], Dp, S[t] * gc);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) read_cols(sn);
+      } else if (c == -1 && nch > 0) {
+        read_rows(sm.st[0]);
+        read_cols(sm.st[0]);
       }
-      if (it - 1 >= 0 && it - 1 < nch) read_operands(sm.st[(it - 1) % NSTAGE]);
-      // no wait for these reads: their buffer is refilled only steps later
+      // no wait for the reads in flight: their buffers are refilled only
+      // steps later, and their registers are waited for where they are used
       block_sync<63, false>();
     }
     if (p.sT) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p.sT[state_off + (size_t)(16 * t + 4 * g + j) * DV + col] = S[t][j];
+        for (int j = 0; j < 4; ++j) p.sT[state_off + (size_t)state_row(t, g, j) * DV + col] = S[t][j];
     }
   } else if (wave == W_P0 || wave == W_P1) {
     // ---------------------------------------------------------------- prepare
+    // Each step also reads the row operands of the next chunk (published
+    // one step earlier), after its own LDS writes have completed, so that
+    // the reads overlap the barrier and the next step's wait.
+    RowOps ops;
     block_sync();
     for (int it = 0; it < nsteps; ++it) {
       const int c = it - 1;
       if (c >= 0 && c < nch) {
         if (wave == W_P0)
-          prepare_p0(p, sm.st[c % NSTAGE], lane);
+          prepare_p0(p, sm.st[c % NSTAGE], ops, lane);
         else
-          prepare_p1(p, sm.st[c % NSTAGE], lane);
+          prepare_p1(p, sm.st[c % NSTAGE], ops, lane);
       }
-      block_sync();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS writes are done
+      if (it < nch) {
+        if (wave == W_P0)
+          read_row_ops<false>(sm.st[it % NSTAGE], ops, m, g);
+        else
+          read_row_ops<true>(sm.st[it % NSTAGE], ops, m, g);
+      }
+      block_sync<63, false>();
     }
   } else {
     // ---------------------------------------------------------------- staging
