@@ -6,10 +6,16 @@
 // Decode runs this sequential form, so its cost is one read and one write of S
 // per (sequence, head) per call -- a pure stream of the state through HBM.
 //
-// One workgroup per (sequence, value head) holds the whole [d_k, d_v] state in
-// registers for the whole call.  Thread (rg, cg) owns columns 4cg..4cg+3 of rows
-// rg, rg + RG, rg + 2RG, ...; consecutive threads own consecutive 16-byte
-// column groups, so each wave loads and stores whole rows (fully coalesced).
+// A workgroup holds the whole [d_k, d_v] state of one (sequence, value head)
+// in registers while it runs that unit's tokens.  Thread (rg, cg) owns columns
+// 4cg..4cg+3 of rows rg, rg + RG, rg + 2RG, ...; consecutive threads own
+// consecutive 16-byte column groups, so each wave loads and stores whole rows
+// (fully coalesced).  The grid is persistent (two workgroups per compute unit)
+// and each workgroup walks the units blockIdx.x, + gridDim.x, ...: while it
+// works on one unit the state of its next unit is already streaming into a
+// second register set, and states are loaded and stored non-temporally (each
+// is touched exactly once per call).  On one MI355X this keeps the state
+// stream near the rate of a plain in-place copy.
 //
 // Per token, with the state taken BEFORE the decay (all reassociations of the
 // stated order):
@@ -29,7 +35,7 @@ namespace {
 template <int DK, int DV>
 struct RecGeom {
   static constexpr int CG = DV / 4;                               // column groups
-  static constexpr int RG = (DK < 256 / CG) ? DK : 256 / CG;      // row groups
+  static constexpr int RG = (DK < 512 / CG) ? DK : 512 / CG;      // row groups
   static constexpr int NT = CG * RG;                              // threads
   static constexpr int RPT = DK / RG;                             // rows per thread
   static constexpr int NW = (NT + 63) / 64;                       // waves
@@ -37,6 +43,15 @@ struct RecGeom {
   static constexpr int NRED = 11;  // u[4], w[4], |k|^2, |q|^2, q.k
   static_assert(DV % 4 == 0 && DK % RG == 0, "bad geometry");
 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 nt_load4(const float *p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store4(float *p, float4 v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(p));
+}
 
 template <typename T>
 struct RecParams {
@@ -47,126 +62,154 @@ struct RecParams {
   float *sT;
   const int32_t *cu;
   int seq_len;
+  int units;  // num_seqs * H_v
   int H_k, H_v;
   float scale, eps;
 };
 
 template <int DK, int DV, typename T>
-__global__ __launch_bounds__((RecGeom<DK, DV>::NT)) void recurrent_kernel(RecParams<T> p) {
+// (at most 128 registers per lane: two 8-wave workgroups per compute unit)
+__global__ __launch_bounds__((RecGeom<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4)))
+void recurrent_kernel(RecParams<T> p) {
   using G = RecGeom<DK, DV>;
   constexpr int CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW, NRED = G::NRED;
   __shared__ float red[2][NW > 1 ? NW : 1][CG][NRED];
 
-  const int n = blockIdx.x / p.H_v;
-  const int h = blockIdx.x % p.H_v;
-  const int hk = h / (p.H_v / p.H_k);
   const int tid = threadIdx.x;
   const int cg = tid % CG;
   const int rg = tid / CG;
   const int wave = tid / 64;
 
-  int64_t t0, t1;
-  seq_bounds(p.cu, p.seq_len, n, t0, t1);
-
-  const size_t state_off = ((size_t)n * p.H_v + h) * DK * DV;
-  float4 S[RPT];
-  if (p.s0) {
-    const float *src = p.s0 + state_off + 4 * cg;
+  auto state_at = [&](int u) { return (size_t)u * DK * DV + 4 * cg; };
+  auto load_state = [&](int u, float4 *dst) {
+    if (p.s0) {
+      const float *src = p.s0 + state_at(u);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) S[i] = load4(src + (size_t)(rg + RG * i) * DV);
-  } else {
+      for (int i = 0; i < RPT; ++i) dst[i] = nt_load4(src + (size_t)(rg + RG * i) * DV);
+    } else {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float neg_exp_A = -expf(p.A_log[h]);
-  const float dtb = p.dt_bias[h];
-
-  for (int64_t t = t0; t < t1; ++t) {
-    const T *kr = p.k + (t * p.H_k + hk) * DK;
-    const T *qr = p.q + (t * p.H_k + hk) * DK;
-    float kv[RPT], qv[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      kv[i] = to_f32(kr[rg + RG * i]);
-      qv[i] = to_f32(qr[rg + RG * i]);
+      for (int i = 0; i < RPT; ++i) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const float4 vv = load4(p.v + (t * p.H_v + h) * DV + 4 * cg);
-    const float a_t = to_f32(p.a[t * p.H_v + h]);
-    const float b_t = to_f32(p.b[t * p.H_v + h]);
+  };
 
-    float r[NRED];
+  float4 S[RPT], Sn[RPT];
+  int u = blockIdx.x;
+  if (u < p.units) load_state(u, S);
+  int step = 0;  // tokens processed by this workgroup (selects the reduction buffer)
+  for (; u < p.units; u += gridDim.x) {
+    const int un = u + gridDim.x;
+    if (un < p.units) load_state(un, Sn);
+    const int n = u / p.H_v;
+    const int h = u % p.H_v;
+    const int hk = h / (p.H_v / p.H_k);
+    int64_t t0, t1;
+    seq_bounds(p.cu, p.seq_len, n, t0, t1);
+    const float neg_exp_A = -expf(p.A_log[h]);
+    const float dtb = p.dt_bias[h];
+
+    for (int64_t t = t0; t < t1; ++t, ++step) {
+      const T *kr = p.k + (t * p.H_k + hk) * DK;
+      const T *qr = p.q + (t * p.H_k + hk) * DK;
+      float kv[RPT], qv[RPT];
 #pragma unroll
-    for (int j = 0; j < NRED; ++j) r[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      r[0] += kv[i] * S[i].x;
-      r[1] += kv[i] * S[i].y;
-      r[2] += kv[i] * S[i].z;
-      r[3] += kv[i] * S[i].w;
-      r[4] += qv[i] * S[i].x;
-      r[5] += qv[i] * S[i].y;
-      r[6] += qv[i] * S[i].z;
-      r[7] += qv[i] * S[i].w;
-      r[8] += kv[i] * kv[i];
-      r[9] += qv[i] * qv[i];
-      r[10] += qv[i] * kv[i];
-    }
-    // reduce over the row groups of this wave (lanes that differ by multiples of CG)
-#pragma unroll
-    for (int off = CG; off < CG * G::RG_PER_WAVE; off <<= 1) {
-#pragma unroll
-      for (int j = 0; j < NRED; ++j) r[j] += __shfl_xor(r[j], off, 64);
-    }
-    if constexpr (NW > 1) {
-      const int buf = (int)((t - t0) & 1);
-      if (tid % 64 < CG) {
-#pragma unroll
-        for (int j = 0; j < NRED; ++j) red[buf][wave][cg][j] = r[j];
+      for (int i = 0; i < RPT; ++i) {
+        kv[i] = to_f32(kr[rg + RG * i]);
+        qv[i] = to_f32(qr[rg + RG * i]);
       }
-      __syncthreads();
+      const float4 vv = load4(p.v + (t * p.H_v + h) * DV + 4 * cg);
+      const float a_t = to_f32(p.a[t * p.H_v + h]);
+      const float b_t = to_f32(p.b[t * p.H_v + h]);
+
+      float r[NRED];
 #pragma unroll
-      for (int j = 0; j < NRED; ++j) {
-        float s = 0.f;
+      for (int j = 0; j < NRED; ++j) r[j] = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) s += red[buf][w][cg][j];
-        r[j] = s;
+      for (int i = 0; i < RPT; ++i) {
+        r[0] += kv[i] * S[i].x;
+        r[1] += kv[i] * S[i].y;
+        r[2] += kv[i] * S[i].z;
+        r[3] += kv[i] * S[i].w;
+        r[4] += qv[i] * S[i].x;
+        r[5] += qv[i] * S[i].y;
+        r[6] += qv[i] * S[i].z;
+        r[7] += qv[i] * S[i].w;
+        r[8] += kv[i] * kv[i];
+        r[9] += qv[i] * qv[i];
+        r[10] += qv[i] * kv[i];
+      }
+      // reduce over the row groups of this wave (lanes that differ by multiples of CG)
+#pragma unroll
+      for (int off = CG; off < CG * G::RG_PER_WAVE; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < NRED; ++j) r[j] += __shfl_xor(r[j], off, 64);
+      }
+      if constexpr (NW > 1) {
+        const int buf = step & 1;
+        if (tid % 64 < CG) {
+#pragma unroll
+          for (int j = 0; j < NRED; ++j) red[buf][wave][cg][j] = r[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NRED; ++j) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) sum += red[buf][w][cg][j];
+          r[j] = sum;
+        }
+      }
+      const float ik = rsqrtf(r[8] + p.eps);
+      const float iq = rsqrtf(r[9] + p.eps) * p.scale;
+      const float qk = r[10] * ik * iq;
+      const float g = log_decay(neg_exp_A, a_t, dtb);
+      const float alpha = expf(g);
+      const float beta = sigmoid_f32(b_t);
+      const float au = alpha * ik;
+      float4 d;
+      d.x = beta * (vv.x - au * r[0]);
+      d.y = beta * (vv.y - au * r[1]);
+      d.z = beta * (vv.z - au * r[2]);
+      d.w = beta * (vv.w - au * r[3]);
+      if (rg == 0) {
+        const float aw = alpha * iq;
+        float4 o;
+        o.x = aw * r[4] + qk * d.x;
+        o.y = aw * r[5] + qk * d.y;
+        o.z = aw * r[6] + qk * d.z;
+        o.w = aw * r[7] + qk * d.w;
+        store4(p.o + (t * p.H_v + h) * DV + 4 * cg, o);
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float kh = kv[i] * ik;
+        S[i].x = alpha * S[i].x + kh * d.x;
+        S[i].y = alpha * S[i].y + kh * d.y;
+        S[i].z = alpha * S[i].z + kh * d.z;
+        S[i].w = alpha * S[i].w + kh * d.w;
       }
     }
-    const float ik = rsqrtf(r[8] + p.eps);
-    const float iq = rsqrtf(r[9] + p.eps) * p.scale;
-    const float qk = r[10] * ik * iq;
-    const float g = log_decay(neg_exp_A, a_t, dtb);
-    const float alpha = expf(g);
-    const float beta = sigmoid_f32(b_t);
-    const float au = alpha * ik;
-    float4 d;
-    d.x = beta * (vv.x - au * r[0]);
-    d.y = beta * (vv.y - au * r[1]);
-    d.z = beta * (vv.z - au * r[2]);
-    d.w = beta * (vv.w - au * r[3]);
-    if (rg == 0) {
-      const float aw = alpha * iq;
-      float4 o;
-      o.x = aw * r[4] + qk * d.x;
-      o.y = aw * r[5] + qk * d.y;
-      o.z = aw * r[6] + qk * d.z;
-      o.w = aw * r[7] + qk * d.w;
-      store4(p.o + (t * p.H_v + h) * DV + 4 * cg, o);
+    if (p.sT) {
+      float *dst = p.sT + state_at(u);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) nt_store4(dst + (size_t)(rg + RG * i) * DV, S[i]);
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const float kh = kv[i] * ik;
-      S[i].x = alpha * S[i].x + kh * d.x;
-      S[i].y = alpha * S[i].y + kh * d.y;
-      S[i].z = alpha * S[i].z + kh * d.z;
-      S[i].w = alpha * S[i].w + kh * d.w;
-    }
+    for (int i = 0; i < RPT; ++i) S[i] = Sn[i];
   }
-  if (p.sT) {
-    float *dst = p.sT + state_off + 4 * cg;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) store4(dst + (size_t)(rg + RG * i) * DV, S[i]);
+}
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
   }
+  return cache[dev];
 }
 
 template <int DK, int DV, typename T>
@@ -188,8 +231,13 @@ hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   p.H_v = pr.H_v;
   p.scale = pr.scale;
   p.eps = pr.eps;
-  const int64_t grid = (int64_t)pr.num_seqs * pr.H_v;
-  if (grid == 0) return hipSuccess;
+  const int64_t units = (int64_t)pr.num_seqs * pr.H_v;
+  if (units == 0) return hipSuccess;
+  if (units > INT32_MAX) return hipErrorInvalidValue;
+  p.units = (int)units;
+  // persistent grid: about 16 waves per compute unit
+  const int per_cu = RecGeom<DK, DV>::NW >= 8 ? 2 : 16 / RecGeom<DK, DV>::NW;
+  const int64_t grid = units < (int64_t)cu_count() * per_cu ? units : (int64_t)cu_count() * per_cu;
   hipLaunchKernelGGL((recurrent_kernel<DK, DV, T>), dim3((unsigned)grid),
                      dim3(RecGeom<DK, DV>::NT), 0, s, p);
   return hipGetLastError();
