@@ -513,11 +513,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     bf16x8 Sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
-    // Row operands of the next chunk are read from LDS during this one: k and
-    // q rows (A operands of K S, B operands of (Q S)^T) once this chunk's
-    // products with them are issued, k^T (A operand of the state update) and
-    // v after the state update.  The rows of chunk c+1 are in LDS from step
-    // c+1 on (they are published one step ahead of use).
+    // LDS operands: the k^T tiles of this chunk (A operands of the state
+    // update) are read once the K S and Q S products are issued; the k and q
+    // rows (A operands of K S, B operands of (Q S)^T) and v of the next chunk
+    // are read after the state update, so that they are in registers when
+    // the next step starts.  The rows of chunk c+1 are in LDS from step c+1
+    // on (they are published one step ahead of use).
     bf16x8 Kr[2][4], Qr[2][4], Kt[8], vv;
     auto read_rows = [&](const Stage &sn) {
 #pragma unroll
@@ -528,16 +529,14 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           Qr[mt][kb] = row_op(sn.Q, 16 * mt + m, kb, g);
         }
     };
-    auto read_cols = [&](const Stage &sn) {
-      // A operand of tile t: row m is state row state_row(t, m / 4, m % 4),
-      // contraction over chunk positions in slot order, i.e. lane (m, g) gets
-      // k[4g + j][state_row(t, m / 4, m % 4)] and k[16 + 4g + j][...], j = 0..3
+    auto read_kt = [&](const Stage &sn) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int r = 4 * g + (m >> 2), d = state_row(t, m & 3, 0);
         Kt[t] = cat8(tr_read(sn.K + kq_off(r, d)), tr_read(sn.K + kq_off(16 + r, d)));
       }
-      // v[4g + j][col] and v[16 + 4g + j][col]
+    };
+    auto read_v = [&](const Stage &sn) {
       const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
       vv = cat8(tr_read(sn.V + vr * BV + vc), tr_read(sn.V + (16 + vr) * BV + vc));
     };
@@ -571,7 +570,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (more) read_rows(sn);
+        read_kt(st);
         __builtin_amdgcn_sched_barrier(0);
         // R = beta (V - Gam ik K S), rows 4g..4g+3 and 16+4g..16+4g+3
         f32x4 R0, R1;
@@ -599,10 +598,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
         __builtin_amdgcn_sched_barrier(0);
-        if (more) read_cols(sn);
+        if (more) {
+          read_rows(sn);
+          read_v(sn);
+        }
       } else if (c == -1 && nch > 0) {
         read_rows(sm.st[0]);
-        read_cols(sm.st[0]);
+        read_v(sm.st[0]);
       }
       // no wait for the reads in flight: their buffers are refilled only
       // steps later, and their registers are waited for where they are used
