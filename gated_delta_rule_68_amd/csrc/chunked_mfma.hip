@@ -15,21 +15,25 @@
 // fp32 to the products (the 1/|k_i| of P is applied to the rows of Delta).
 // Only differences gamma_r - gamma_i with i <= r are exponentiated.
 //
-// (I + A)^-1 is formed in 16-row blocks and then applied as one 32x32 product:
-//   T = [T_11 0; T_21 T_22],  T_bb = (I + A_bb)^-1,  T_21 = -T_22 A_21 T_11.
-// Each T_bb is formed on the matrix cores from the identity, exact for the
+// (I + A)^-1 is applied in 16-row blocks,
+//   Delta_1 = T_11 R_1,  Delta_2 = T_22 (R_2 - A_21 Delta_1),  T_bb = (I + A_bb)^-1,
+// each T_bb formed on the matrix cores from the identity, exact for the
 // strictly lower (nilpotent, N^16 = 0) N = A_bb,
 //   (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8).
 //
 // Work split.  A workgroup owns (sequence, value head, 32 columns of d_v); the
-// columns of S evolve independently.  Six waves, one workgroup barrier per
+// columns of S evolve independently.  Eight waves, one workgroup barrier per
 // chunk; chunk c lives in LDS buffer c % NSTAGE from the step its rows are
-// requested until the step it is consumed:
-//   * 2 consumer waves each keep a [128 x 16] slice of S in MFMA accumulators
-//     for the whole sequence and run chunk c: K S, Q S, Delta = T R, the
-//     outputs and K^T Delta;
+// requested until the step its outputs are written:
+//   * 2 state waves each keep a [128 x 16] slice of S in MFMA accumulators for
+//     the whole sequence and run chunk c: K S, R, the block solve for Delta
+//     and S <- Gam_last S + K^T D Delta; they hand the state at chunk entry
+//     and diag(1/|k|) Delta (bf16) to
+//   * 2 output waves, which form Q S of chunk c in the same step and the
+//     outputs O = P Delta + Gam Q S of chunk c one step later;
 //   * 2 "prepare" waves form chunk c+1's matrices: P0 the Gram blocks of K,
-//     the norms of k and T; P1 the norms of q and the output mask P;
+//     the norms of k, T_11, T_22 and -A_21; P1 the norms of q and the output
+//     mask P;
 //   * 2 staging waves request the rows of chunk c+2+AHEAD: the k, q, v rows
 //     and the raw gates go straight from global memory into LDS
 //     (global_load_lds), never through registers; staging wave 1 derives the
@@ -67,14 +71,14 @@ constexpr int DV = 128;
 constexpr int CH = 32;      // tokens per chunk
 constexpr int NC = 2;       // consumer waves (16 columns each)
 constexpr int BV = 16 * NC;
-constexpr int NWAVES = 6;
-constexpr int NSTAGE = 6;   // chunk buffers in LDS
-constexpr int AHEAD = 3;    // chunks whose rows are in flight beyond the one being published
+constexpr int NWAVES = 8;
+constexpr int NSTAGE = 5;   // chunk buffers in LDS
+constexpr int AHEAD = 2;    // chunks whose rows are in flight beyond the one being published
 static_assert(AHEAD <= NSTAGE - 3, "a buffer is refilled only after its chunk was consumed");
 
-// wave roles (wave w runs on SIMD w % 4): the matrix-heavy consumers share a
-// SIMD with the light staging waves, P0 and P1 have one each
-constexpr int W_C0 = 0, W_P0 = 2, W_P1 = 3, W_ST0 = 4;
+// wave roles (wave w runs on SIMD w % 4): the state waves share a SIMD with
+// the light staging waves, the output waves one with P0 and P1
+constexpr int W_C0 = 0, W_P0 = 2, W_P1 = 3, W_ST0 = 4, W_O0 = 6;
 
 // vector-memory operations one staging wave issues per chunk
 constexpr int ST0_OPS = 8 + 1;       // k rows, half of v
@@ -179,7 +183,8 @@ struct Stage {
   alignas(16) bf16 Q[CH * DK];   // q rows, swizzled                     (staging wave 1)
   alignas(16) bf16 V[CH * BV];   // v rows, this workgroup's columns     (both)
   alignas(16) bf16 P[CH][TP];    // P without 1/|k_i|, columns in slot order (P1)
-  alignas(16) bf16 TT[CH][TP];   // (I + A)^-1, columns in slot order    (P0)
+  alignas(16) bf16 T[2][16][16];  // (I + A_bb)^-1 of the two diagonal blocks, A layout (P0)
+  alignas(16) bf16 nA21[16][16];  // -A_21, A layout                      (P0)
   alignas(16) uint32_t ab[2 * CH]; // raw a_r (low half of word r), b_r (word 32 + r) (staging wave 1)
   alignas(16) float gam[CH];     // cumulative log decay                 (staging wave 1, a step early)
   alignas(16) float beta[CH];    //                                      (staging wave 1, a step early)
@@ -194,6 +199,9 @@ struct Stage {
 
 struct Smem {
   Stage st[NSTAGE];
+  // handed from the state waves to the output waves, per state wave and lane:
+  alignas(16) bf16x8 sb[2][NC][4][64];  // state at chunk entry, bf16 B operands (ring by chunk)
+  alignas(16) bf16x8 db[2][NC][64];     // diag(1/|k|) Delta of the chunk, bf16 (ring by chunk)
 };
 
 struct MfmaParams {
@@ -325,6 +333,7 @@ __device__ __forceinline__ void stage_gates(Stage &S, int lane, int cl, float ne
 // t0b gets T0[4g+j][m] (B layout).  Transposes ride along: the accumulator of
 // X Y is the B layout of X Y, that of Y^T X^T its A layout.  The two blocks
 // are interleaved step by step so that each waits on the other's latency.
+template <bool WANT_B>
 __device__ __forceinline__ void unit_lower_inverse2(f32x4 na0, f32x4 nb0, f32x4 na1, f32x4 nb1,
                                                     int m, int g, f32x4 &t0a, f32x4 &t0b,
                                                     f32x4 &t1a) {
@@ -336,7 +345,7 @@ __device__ __forceinline__ void unit_lower_inverse2(f32x4 na0, f32x4 nb0, f32x4 
   const s16x4 b0_4 = pk4(mma16(a0_2, b0_2, z)), b1_4 = pk4(mma16(a1_2, b1_2, z));
   const s16x4 a0_4 = pk4(mma16(b0_2, a0_2, z)), a1_4 = pk4(mma16(b1_2, a1_2, z));
   const s16x4 b0_8 = pk4(mma16(a0_4, b0_4, z)), b1_8 = pk4(mma16(a1_4, b1_4, z));
-  const s16x4 a0_8 = pk4(mma16(b0_4, a0_4, z));
+  const s16x4 a0_8 = WANT_B ? pk4(mma16(b0_4, a0_4, z)) : s16x4{0, 0, 0, 0};
   f32x4 id;
 #pragma unroll
   for (int j = 0; j < 4; ++j) id[j] = (m == 4 * g + j) ? 1.f : 0.f;
@@ -345,13 +354,13 @@ __device__ __forceinline__ void unit_lower_inverse2(f32x4 na0, f32x4 nb0, f32x4 
   f32x4 p0 = id - na0, p1 = id - na1, q0 = id - nb0;
   p0 = mma16(b0_2, pk4(p0), p0);
   p1 = mma16(b1_2, pk4(p1), p1);
-  q0 = mma16(a0_2, pk4(q0), q0);
+  if (WANT_B) q0 = mma16(a0_2, pk4(q0), q0);
   p0 = mma16(b0_4, pk4(p0), p0);
   p1 = mma16(b1_4, pk4(p1), p1);
-  q0 = mma16(a0_4, pk4(q0), q0);
+  if (WANT_B) q0 = mma16(a0_4, pk4(q0), q0);
   t0a = mma16(b0_8, pk4(p0), p0);
   t1a = mma16(b1_8, pk4(p1), p1);
-  t0b = mma16(a0_8, pk4(q0), q0);
+  t0b = WANT_B ? mma16(a0_8, pk4(q0), q0) : q0;
 }
 
 // Row operands of one chunk for the prepare waves: rows m and 16 + m of k
@@ -417,17 +426,12 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const 
     // A_21[m][i] = beta_{16+m} exp(gam_{16+m} - gam_i) ik_{16+m} ik_i (k_i . k_{16+m})
     na21[j] = -bik_m1 * ik_lo[j] * fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * t01[j];
   }
-  // T = (I + A)^-1 = [T11 0; T21 T22]
+  // T11, T22 (the state waves apply T21 = -T22 A21 T11 as a block solve)
   f32x4 t11a, t11b, t22a;
-  unit_lower_inverse2(na0, nb0, na1, nb1, m, g, t11a, t11b, t22a);
-  // Y = -A21 T11 (B layout); its accumulator is the A layout of Y^T, and
-  // Y^T T22^T is the B layout of T21^T, i.e. the A layout of T21.
-  const f32x4 y = mma16(pk4(na21), pk4(t11b), z);
-  const f32x4 t21a = mma16(pk4(y), pk4(t22a), z);
-  // rows of T with the column index in slot order: row m holds (T11[m][4g..], 0),
-  // row 16 + m holds (T21[m][4g..], T22[m][4g..])
-  *reinterpret_cast<bf16x8 *>(&S.TT[m][8 * g]) = pack8(t11a, z);
-  *reinterpret_cast<bf16x8 *>(&S.TT[16 + m][8 * g]) = pack8(t21a, t22a);
+  unit_lower_inverse2<false>(na0, nb0, na1, nb1, m, g, t11a, t11b, t22a);
+  *reinterpret_cast<bf16x4 *>(&S.T[0][m][4 * g]) = pack4(t11a);
+  *reinterpret_cast<bf16x4 *>(&S.T[1][m][4 * g]) = pack4(t22a);
+  *reinterpret_cast<bf16x4 *>(&S.nA21[m][4 * g]) = pack4(na21);
 }
 
 // P1: scale/|q|, Gam scale/|q| and P without the factor 1/|k_i| of one chunk.
@@ -492,15 +496,19 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
   const int nch = (int)((L + CH - 1) / CH);
   const size_t state_off = ((size_t)n * p.H_v + h) * DK * DV;
   const int col0 = vb * BV;
-  // step `it` consumes chunk it-2, prepares chunk it-1 and derives the gates
-  // of chunk it+1; every wave passes nsteps + 1 barriers
-  const int nsteps = nch + 2;
+  // step `it` updates the state with chunk it-2, writes the outputs of chunk
+  // it-3, prepares chunk it-1 and derives the gates of chunk it+1; every wave
+  // passes nsteps + 1 barriers
+  const int nsteps = nch + 3;
 
   if (wave >= W_C0 && wave < W_C0 + NC) {
-    // ---------------------------------------------------------------- consumers
+    // ------------------------------------------------------------ state waves
+    // chunk c in step c + 2: K S, R, Delta = T R, S <- Gam_last S + K^T D Delta;
+    // they hand the state at chunk entry (before step c + 2) and the scaled
+    // Delta (during step c + 2) to the output waves.
     const int cw = wave - W_C0;
     const int col = col0 + 16 * cw + m;
-    f32x4 S[8];  // S[16t + 4g + j][col]
+    f32x4 S[8];  // S[state_row(t, g, j)][col]
     if (p.s0) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
@@ -514,22 +522,21 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
     // LDS operands: the k^T tiles of this chunk (A operands of the state
-    // update) are read once the K S and Q S products are issued; the k and q
-    // rows (A operands of K S, B operands of (Q S)^T) and v of the next chunk
-    // are read after the state update, so that they are in registers when
-    // the next step starts.  The rows of chunk c+1 are in LDS from step c+1
-    // on (they are published one step ahead of use).
-    bf16x8 Kr[2][4], Qr[2][4], Kt[8], vv;
+    // update) are read once the K S products are issued; the k rows (A
+    // operands of K S) and v of the next chunk are read after the state
+    // update, so that they are in registers when the next step starts.  The
+    // rows of chunk c+1 are in LDS from step c+1 on.
+    bf16x8 Kr[2][4], Kt[8], vv;
     auto read_rows = [&](const Stage &sn) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          Kr[mt][kb] = row_op(sn.K, 16 * mt + m, kb, g);
-          Qr[mt][kb] = row_op(sn.Q, 16 * mt + m, kb, g);
-        }
+        for (int mt = 0; mt < 2; ++mt) Kr[mt][kb] = row_op(sn.K, 16 * mt + m, kb, g);
     };
     auto read_kt = [&](const Stage &sn) {
+      // A operand of tile t: row m is state row state_row(t, m / 4, m % 4),
+      // contraction over chunk positions in slot order, i.e. lane (m, g) gets
+      // k[4g + j][state_row(t, m / 4, m % 4)] and k[16 + 4g + j][...], j = 0..3
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int r = 4 * g + (m >> 2), d = state_row(t, m & 3, 0);
@@ -537,8 +544,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       }
     };
     auto read_v = [&](const Stage &sn) {
+      // v[4g + j][col] and v[16 + 4g + j][col]
       const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
       vv = cat8(tr_read(sn.V + vr * BV + vc), tr_read(sn.V + (16 + vr) * BV + vc));
+    };
+    auto hand_state = [&](int c) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sm.sb[c & 1][cw][kb][lane] = Sb[kb];
     };
     block_sync();
     for (int it = 0; it < nsteps; ++it) {
@@ -548,26 +560,21 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         const bool more = c + 1 < nch;
         const Stage &sn = sm.st[(c + 1) % NSTAGE];
         const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-        // this chunk's prepared tiles and row factors
-        const bf16x8 ta0 = *reinterpret_cast<const bf16x8 *>(&st.TT[m][8 * g]);
-        const bf16x8 ta1 = *reinterpret_cast<const bf16x8 *>(&st.TT[16 + m][8 * g]);
-        const bf16x8 pr0 = *reinterpret_cast<const bf16x8 *>(&st.P[m][8 * g]);
-        const bf16x8 pr1 = *reinterpret_cast<const bf16x8 *>(&st.P[16 + m][8 * g]);
+        // this chunk's prepared tile and row factors
+        const s16x4 t11 = *reinterpret_cast<const s16x4 *>(&st.T[0][m][4 * g]);
+        const s16x4 t22 = *reinterpret_cast<const s16x4 *>(&st.T[1][m][4 * g]);
+        const s16x4 na21 = *reinterpret_cast<const s16x4 *>(&st.nA21[m][4 * g]);
         const f32x4 bt0 = ld4(&st.beta[4 * g]), bt1 = ld4(&st.beta[16 + 4 * g]);
         const f32x4 gm0 = ld4(&st.Gam[4 * g]), gm1 = ld4(&st.Gam[16 + 4 * g]);
         const f32x4 ik0 = ld4(&st.ik[4 * g]), ik1 = ld4(&st.ik[16 + 4 * g]);
         const f32x4 tl0 = ld4(&st.tail[4 * g]), tl1 = ld4(&st.tail[16 + 4 * g]);
-        const float co0 = st.cO[m], co1 = st.cO[16 + m];
         const float gc = st.Gc;
-        // ks[mt]: (K S)[16mt + 4g + j][m];  qsT[mt]: (Q S)[16mt + m][4g + j]
-        f32x4 ks[2] = {z, z}, qsT[2] = {z, z};
+        // ks[mt]: (K S)[16mt + 4g + j][m]
+        f32x4 ks[2] = {z, z};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            ks[mt] = mma32(Kr[mt][kb], Sb[kb], ks[mt]);
-            qsT[mt] = mma32(Sb[kb], Qr[mt][kb], qsT[mt]);
-          }
+          for (int mt = 0; mt < 2; ++mt) ks[mt] = mma32(Kr[mt][kb], Sb[kb], ks[mt]);
         }
         __builtin_amdgcn_sched_barrier(0);
         read_kt(st);
@@ -579,30 +586,26 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           R0[j] = bt0[j] * ((float)vv[j] - gm0[j] * ik0[j] * ks[0][j]);
           R1[j] = bt1[j] * ((float)vv[4 + j] - gm1[j] * ik1[j] * ks[1][j]);
         }
-        // Delta = T R: rows 0..15 and 16..31 of T against R in slot order
-        const bf16x8 Rb = pack8(R0, R1);
-        const f32x4 d1 = mma32(ta0, Rb, z);
-        const f32x4 d2 = mma32(ta1, Rb, z);
-        // O^T = (diag(ik) Delta)^T P^T + (Gam iq Q S)^T: lane (m, g) gets O[16mt + m][4g..4g+3]
-        const bf16x8 Db = pack8(ik0 * d1, ik1 * d2);
-        const f32x4 oc0 = mma32(Db, pr0, qsT[0] * co0);
-        const f32x4 oc1 = mma32(Db, pr1, qsT[1] * co1);
-        const int64_t row = t0 + (int64_t)c * CH + m;
-        bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g;
-        if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
-        if (row + 16 < t1) *reinterpret_cast<bf16x4 *>(orow + (int64_t)16 * p.H_v * DV) = pack4(oc1);
+        // Delta_1 = T11 R1, Delta_2 = T22 (R2 - A21 Delta_1)
+        const f32x4 d1 = mma16(t11, pk4(R0), z);
+        const f32x4 d2 = mma16(t22, pk4(mma16(na21, pk4(d1), R1)), z);
+        // diag(ik) Delta for the outputs of this chunk
+        sm.db[c & 1][cw][lane] = pack8(ik0 * d1, ik1 * d2);
         // S <- Gam_last S + K^T diag(tail ik) Delta
         const bf16x8 Dp = pack8(tl0 * ik0 * d1, tl1 * ik1 * d2);
 #pragma unroll
         for (int t = 0; t < 8; ++t) S[t] = mma32(Kt[t], Dp, S[t] * gc);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        if (more) hand_state(c + 1);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the handed-over writes are done
         if (more) {
           read_rows(sn);
           read_v(sn);
         }
       } else if (c == -1 && nch > 0) {
+        hand_state(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
         read_rows(sm.st[0]);
         read_v(sm.st[0]);
       }
@@ -615,6 +618,48 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) p.sT[state_off + (size_t)state_row(t, g, j) * DV + col] = S[t][j];
+    }
+  } else if (wave >= W_O0 && wave < W_O0 + NC) {
+    // ----------------------------------------------------------- output waves
+    // step it: O of chunk it - 3 = (diag(ik) Delta)^T P^T + (Gam iq Q S)^T,
+    // then (Q S)^T of chunk it - 2 from the state handed over at its entry.
+    const int cw = wave - W_O0;
+    f32x4 qsT[2];
+    block_sync();
+    for (int it = 0; it < nsteps; ++it) {
+      const int co = it - 3;
+      if (co >= 0 && co < nch) {
+        const Stage &st = sm.st[co % NSTAGE];
+        const bf16x8 Db = sm.db[co & 1][cw][lane];
+        const bf16x8 pr0 = *reinterpret_cast<const bf16x8 *>(&st.P[m][8 * g]);
+        const bf16x8 pr1 = *reinterpret_cast<const bf16x8 *>(&st.P[16 + m][8 * g]);
+        const float co0 = st.cO[m], co1 = st.cO[16 + m];
+        // lane (m, g) gets O[16mt + m][4g..4g+3]
+        const f32x4 oc0 = mma32(Db, pr0, qsT[0] * co0);
+        const f32x4 oc1 = mma32(Db, pr1, qsT[1] * co1);
+        const int64_t row = t0 + (int64_t)co * CH + m;
+        bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g;
+        if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
+        if (row + 16 < t1) *reinterpret_cast<bf16x4 *>(orow + (int64_t)16 * p.H_v * DV) = pack4(oc1);
+      }
+      const int c = it - 2;
+      if (c >= 0 && c < nch) {
+        const Stage &st = sm.st[c % NSTAGE];
+        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 Sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Sb[kb] = sm.sb[c & 1][cw][kb][lane];
+        // qsT[mt]: (Q S)[16mt + m][4g + j]
+        qsT[0] = z;
+        qsT[1] = z;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            qsT[mt] = mma32(Sb[kb], row_op(st.Q, 16 * mt + m, kb, g), qsT[mt]);
+        }
+      }
+      block_sync<63, false>();
     }
   } else if (wave == W_P0 || wave == W_P1) {
     // ---------------------------------------------------------------- prepare
