@@ -32,12 +32,12 @@
 //   * 2 output waves, which form Q S of chunk c in the same step and the
 //     outputs O = P Delta + Gam Q S of chunk c one step later;
 //   * 2 "prepare" waves form chunk c+1's matrices: P0 the Gram blocks of K,
-//     the norms of k, T_11, T_22 and -A_21; P1 the norms of q and the output
-//     mask P;
+//     T_11, T_22 and -A_21; P1 the norms of q and the output mask P;
 //   * 2 staging waves request the rows of chunk c+2+AHEAD: the k, q, v rows
 //     and the raw gates go straight from global memory into LDS
-//     (global_load_lds), never through registers; staging wave 1 derives the
-//     gates of chunk c+3 as soon as they have landed.
+//     (global_load_lds), never through registers; as soon as chunk c+3 has
+//     landed, staging wave 0 derives the norms of its k rows and staging
+//     wave 1 its gates.
 // The k and q tiles are stored unpadded with their 16-byte pieces XOR-swizzled
 // per row, so that the operand reads (16 rows at one column) and the
 // transposing reads (8 rows at 2 columns) each touch every bank once.
@@ -190,9 +190,8 @@ struct Stage {
   alignas(16) float beta[CH];    //                                      (staging wave 1, a step early)
   alignas(16) float Gam[CH];     // exp(gam)                             (staging wave 1, a step early)
   alignas(16) float tail[CH];    // exp(gam_last - gam)                  (staging wave 1, a step early)
-  alignas(16) float ik[CH];      // 1/|k_r| (0 past the end)             (P0)
+  alignas(16) float ik[CH];      // 1/|k_r| (0 past the end)             (staging wave 0, a step early)
   alignas(16) float iq[CH];      // scale/|q_r| (0 past the end)         (P1)
-  alignas(16) float cO[CH];      // Gam iq                               (P1)
   alignas(16) float Gc;          // exp(gam_last)                        (staging wave 1, a step early)
   int cl;                        // valid rows of the chunk              (staging wave 1, a step early)
 };
@@ -271,6 +270,28 @@ __device__ __forceinline__ void dma_rows(const bf16 *x, int H, int hk, int64_t r
     dma16(x + ((row0 + rr) * H + hk) * DK + 8 * piece, tile + 512 * i);
   }
 }
+// Byte offsets of the 8 loads of dma_rows for a full chunk, relative to the
+// chunk's first row: the same for every chunk of a workgroup, so a full
+// chunk costs one scalar base per tile.
+struct RowOffsets {
+  uint32_t off[8];
+};
+__device__ __forceinline__ RowOffsets row_offsets(int H, int lane) {
+  RowOffsets o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int piece = (lane & 15) ^ swz(r & 15);
+    o.off[i] = (uint32_t)((r * H * DK + 8 * piece) * (int)sizeof(bf16));
+  }
+  return o;
+}
+// dma_rows for a full chunk: `x` points at element (row0, hk, 0).
+__device__ __forceinline__ void dma_rows_full(const bf16 *x, const RowOffsets &o, bf16 *tile) {
+  const char *base = reinterpret_cast<const char *>(x);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma16(reinterpret_cast<const bf16 *>(base + o.off[i]), tile + 512 * i);
+}
 // Half (rows 16 h .. 16 h + 15) of the v tile: lane l takes row 16h + l/4,
 // columns col0 + 8 (l%4) .. + 7.
 __device__ __forceinline__ void dma_v_half(const bf16 *v, int H_v, int hv, int col0, int64_t row0,
@@ -298,6 +319,54 @@ __device__ __forceinline__ uint32_t lds_read_u32_now(const uint32_t *p) {
   const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint32_t *)p;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
   return v;
+}
+
+// The 128 contiguous bytes at p (8 16-byte LDS reads), complete when the
+// statement ends (see lds_read_u32_now).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_read_128B_now(const bf16 *p, u32x4 (&x)[8]) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const bf16 *)p;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:16\n\t"
+      "ds_read_b128 %2, %8 offset:32\n\t"
+      "ds_read_b128 %3, %8 offset:48\n\t"
+      "ds_read_b128 %4, %8 offset:64\n\t"
+      "ds_read_b128 %5, %8 offset:80\n\t"
+      "ds_read_b128 %6, %8 offset:96\n\t"
+      "ds_read_b128 %7, %8 offset:112\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]),
+        "=v"(x[7])
+      : "v"(addr)
+      : "memory");
+}
+// Sum of squares of the bf16 values in 32-bit words w (bf16 pair dot products).
+__device__ __forceinline__ float sumsq_words(const uint32_t *w, int n, float s) {
+  for (int i = 0; i < n; ++i) {
+    const bf16x2 x = __builtin_bit_cast(bf16x2, w[i]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
+  }
+  return s;
+}
+
+// 1/|k_r| of one chunk (staging wave 0, once its k rows have landed): lane l
+// sums the squares of half a row (row l / 2) -- the swizzle only permutes the
+// 16-byte pieces inside each 128-byte half -- and its neighbour the other half.
+__device__ __forceinline__ void stage_k_norms(Stage &S, int lane, int cl, float eps) {
+  const int r = lane >> 1, half = lane & 1;
+  const int pos = half ^ (swz(r & 15) >> 3);  // where the 8 pieces of this half are stored
+  u32x4 x[8];
+  lds_read_128B_now(S.K + r * DK + 64 * pos, x);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};  // independent chains
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w[4] = {x[i][0], x[i][1], x[i][2], x[i][3]};
+    acc[i & 3] = sumsq_words(w, 4, acc[i & 3]);
+  }
+  float ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  ss += dpp<0xB1>(ss);  // quad_perm [1,0,3,2]: add the other half of the row
+  if (half == 0) S.ik[r] = r < cl ? rsqrtf(ss + eps) : 0.f;
 }
 
 // Gates of one chunk (staging wave 1, once its raw a and b have landed):
@@ -381,7 +450,7 @@ __device__ __forceinline__ void read_row_ops(const Stage &S, RowOps &o, int m, i
   }
 }
 
-// P0: Gram blocks of k, 1/|k| and T = (I + A)^-1 of one chunk.
+// P0: Gram blocks of k, T_11, T_22 and -A_21 of one chunk (1/|k| from staging).
 // Lane (m, g) holds the Gram entries (k_i . k_m), i = 4g + j, of each block;
 // exactly one of i < m, i > m holds off the diagonal, so one decay factor
 // exp(-|gam_m - gam_i|) serves both the A-operand (row m) and the B-operand
@@ -395,6 +464,8 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const 
   const f32x4 bt_lo = ld4(&S.beta[4 * g]), bt_hi = ld4(&S.beta[16 + 4 * g]);
   const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
   const float bt_m0 = S.beta[m], bt_m1 = S.beta[16 + m];
+  const f32x4 ik_lo = ld4(&S.ik[4 * g]), ik_hi = ld4(&S.ik[16 + 4 * g]);
+  const float ik_m0 = S.ik[m], ik_m1 = S.ik[16 + m];
   f32x4 t00 = z, t11 = z, t01 = z;  // (K K^T) blocks: rows 4g+j, column m (+16)
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -402,15 +473,6 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const 
     t11 = mma32(o.k1[kb], o.k1[kb], t11);
     t01 = mma32(o.k0[kb], o.k1[kb], t01);
   }
-  // 1/|k_r| from the diagonal: lane (m, g = m/4) holds |k_m|^2 in register m%4
-  if (g == (m >> 2)) {
-    const int j = m & 3;
-    S.ik[m] = (m < cl) ? rsqrtf(t00[j] + p.eps) : 0.f;
-    S.ik[16 + m] = (16 + m < cl) ? rsqrtf(t11[j] + p.eps) : 0.f;
-  }
-  wave_lds_sync();
-  const f32x4 ik_lo = ld4(&S.ik[4 * g]), ik_hi = ld4(&S.ik[16 + 4 * g]);
-  const float ik_m0 = S.ik[m], ik_m1 = S.ik[16 + m];
   // A in both layouts for the two diagonal blocks, and -A_21 in A layout.
   f32x4 na0, nb0, na1, nb1, na21;
   const float bik_m1 = bt_m1 * ik_m1;
@@ -434,42 +496,39 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const 
   *reinterpret_cast<bf16x4 *>(&S.nA21[m][4 * g]) = pack4(na21);
 }
 
-// P1: scale/|q|, Gam scale/|q| and P without the factor 1/|k_i| of one chunk.
+// P1: scale/|q_r| from the Gram diagonal of q, and the output mask without the
+// row norms, P[r][i] = exp(gam_r - gam_i) (q_r . k_i) for i <= r, of one chunk
+// (scale/|q_r| and 1/|k_i| are applied by the output waves).
 __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const RowOps &o,
                                            int lane) {
   const int m = lane & 15, g = lane >> 4;
-  const int cl = S.cl;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
   const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
-  f32x4 qq0 = z, qq1 = z;           // Gram diagonal blocks of q
   f32x4 p00 = z, p10 = z, p11 = z;  // (K Q^T) blocks: (q_r . k_i), r = 16 rb + m, i = 16 ib + 4g + j
+  f32x4 qq0 = z, qq1 = z;           // Gram diagonal blocks of q
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
-    qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
     p00 = mma32(o.k0[kb], o.q0[kb], p00);
     p10 = mma32(o.k0[kb], o.q1[kb], p10);
     p11 = mma32(o.k1[kb], o.q1[kb], p11);
+    qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
+    qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
   }
+  // scale/|q_r| from the diagonal: lane (m, g = m/4) holds |q_m|^2 in register m%4
   if (g == (m >> 2)) {
+    const int cl = S.cl;
     const int j = m & 3;
-    const float iq0 = (m < cl) ? rsqrtf(qq0[j] + p.eps) * p.scale : 0.f;
-    const float iq1 = (16 + m < cl) ? rsqrtf(qq1[j] + p.eps) * p.scale : 0.f;
-    S.iq[m] = iq0;
-    S.iq[16 + m] = iq1;
-    S.cO[m] = S.Gam[m] * iq0;
-    S.cO[16 + m] = S.Gam[16 + m] * iq1;
+    S.iq[m] = (m < cl) ? rsqrtf(qq0[j] + p.eps) * p.scale : 0.f;
+    S.iq[16 + m] = (16 + m < cl) ? rsqrtf(qq1[j] + p.eps) * p.scale : 0.f;
   }
-  wave_lds_sync();
-  const float iq_m0 = S.iq[m], iq_m1 = S.iq[16 + m];
   f32x4 v00, v10, v11;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = 4 * g + j;  // column inside its 16-block
-    v00[j] = (i <= m) ? fast_exp(fminf(gm_m0 - gm_lo[j], 0.f)) * iq_m0 * p00[j] : 0.f;
-    v10[j] = fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * iq_m1 * p10[j];
-    v11[j] = (i <= m) ? fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * iq_m1 * p11[j] : 0.f;
+    v00[j] = (i <= m) ? fast_exp(fminf(gm_m0 - gm_lo[j], 0.f)) * p00[j] : 0.f;
+    v10[j] = fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * p10[j];
+    v11[j] = (i <= m) ? fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * p11[j] : 0.f;
   }
   // row r of P at slots 8g..8g+3 (columns 4g..4g+3) and 8g+4.. (columns 16+4g..)
   *reinterpret_cast<bf16x8 *>(&S.P[m][8 * g]) = pack8(v00, z);
@@ -633,10 +692,11 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         const bf16x8 Db = sm.db[co & 1][cw][lane];
         const bf16x8 pr0 = *reinterpret_cast<const bf16x8 *>(&st.P[m][8 * g]);
         const bf16x8 pr1 = *reinterpret_cast<const bf16x8 *>(&st.P[16 + m][8 * g]);
-        const float co0 = st.cO[m], co1 = st.cO[16 + m];
-        // lane (m, g) gets O[16mt + m][4g..4g+3]
-        const f32x4 oc0 = mma32(Db, pr0, qsT[0] * co0);
-        const f32x4 oc1 = mma32(Db, pr1, qsT[1] * co1);
+        const float gm0 = st.Gam[m], gm1 = st.Gam[16 + m];
+        const float iq0 = st.iq[m], iq1 = st.iq[16 + m];
+        // lane (m, g) gets O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P diag(ik) Delta)
+        const f32x4 oc0 = mma32(Db, pr0, qsT[0] * gm0) * iq0;
+        const f32x4 oc1 = mma32(Db, pr1, qsT[1] * gm1) * iq1;
         const int64_t row = t0 + (int64_t)co * CH + m;
         bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g;
         if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
@@ -694,6 +754,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       for (int it = 0; it <= nsteps; ++it) block_sync();
       return;
     }
+    // per-lane byte offsets of full-chunk loads: k or q rows, and this wave's
+    // half of the v tile (rows 16 half + lane / 4, columns col0 + 8 (lane % 4))
+    const RowOffsets ko = row_offsets(p.H_k, lane);
+    const int vhalf = wave - W_ST0;
+    const uint32_t voff =
+        (uint32_t)(((16 * vhalf + (lane >> 2)) * p.H_v * DV + col0 + 8 * (lane & 3)) * (int)sizeof(bf16));
     // chunk c (clamped to the last one: requests past the end re-read it into
     // a buffer no one reads again) -> first row and valid rows
     auto rows_of = [&](int c, int64_t &row0, int &cl) {
@@ -711,13 +777,27 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         int cl;
         rows_of(c, row0, cl);
         Stage &S = sm.st[c % NSTAGE];
-        dma_rows(p.k, p.H_k, hk, row0, cl, S.K, lane);
-        dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 0, lane);
+        if (cl == CH) {
+          dma_rows_full(p.k + (row0 * p.H_k + hk) * DK, ko, S.K);
+          dma16(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(p.v + (row0 * p.H_v + h) * DV) + voff), S.V);
+        } else {
+          dma_rows(p.k, p.H_k, hk, row0, cl, S.K, lane);
+          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 0, lane);
+        }
+      };
+      // 1/|k| of chunk c once its rows have landed (c < nch)
+      auto norms = [&](int c) {
+        const int64_t rem = L - (int64_t)c * CH;
+        stage_k_norms(sm.st[c % NSTAGE], lane, rem < CH ? (int)rem : CH, p.eps);
       };
       for (int c = 0; c < AHEAD; ++c) request(c);
+      vm_wait<ST0_OPS * (AHEAD - 1)>();  // chunk 0 has landed
+      norms(0);
       block_sync<ST0_OPS * (AHEAD - 1)>();
       for (int it = 0; it < nsteps; ++it) {
         request(it + AHEAD);
+        vm_wait<ST0_OPS * (AHEAD - 1)>();  // chunk it + 1 has landed
+        if (it + 1 < nch) norms(it + 1);
         block_sync<ST0_OPS * (AHEAD - 1)>();
       }
     } else {
@@ -727,8 +807,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         int cl;
         rows_of(c, row0, cl);
         Stage &S = sm.st[c % NSTAGE];
-        dma_rows(p.q, p.H_k, hk, row0, cl, S.Q, lane);
-        dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 1, lane);
+        if (cl == CH) {
+          dma_rows_full(p.q + (row0 * p.H_k + hk) * DK, ko, S.Q);
+          dma16(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(p.v + (row0 * p.H_v + h) * DV) + voff), S.V + 512);
+        } else {
+          dma_rows(p.q, p.H_k, hk, row0, cl, S.Q, lane);
+          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 1, lane);
+        }
         dma_ab(p.a, p.b, p.H_v, h, row0, cl, S.ab, lane);
       };
       const float neg_exp_A = -expf(p.A_log[h]);
