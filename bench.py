@@ -44,6 +44,12 @@ def prefill_flops(T, H_k, H_v, d_k, d_v, C):
     return total
 
 
+def varlen_flops(lengths, H_k, H_v, d_k, d_v, C):
+    """prefill_flops summed over the sequences of a packed batch (chunks
+    restart at every sequence start)."""
+    return sum(prefill_flops(L, H_k, H_v, d_k, d_v, C) for L in lengths)
+
+
 def prefill_bytes(T, N, H_k, H_v, d_k, d_v, elem=2, s0=False):
     """Algorithmic HBM bytes of one fused pass: q, k, v, a, b read once, o
     written once in the input dtype, the fp32 state written (and read if given)."""
@@ -143,6 +149,32 @@ def main():
     dbytes = decode_bytes(wd.num_seqs, wd.H_k, wd.H_v, wd.d_k, wd.d_v, 2)
     dgbs = dbytes / (dmean_ms / 1e3) / 1e9
 
+    # ------------------------------------------------------------ varlen prefill
+    wv = synth.workload("varlen", seed=0)
+    vinp = synth.make_inputs(wv, 0, device=dev)
+    Tv, Nv = wv.total_tokens, wv.num_seqs
+    ov = torch.empty((Tv, wv.H_v, wv.d_v), dtype=wv.torch_dtype, device=dev)
+    Sv = torch.empty((Nv, wv.H_v, wv.d_k, wv.d_v), dtype=torch.float32, device=dev)
+
+    def varlen_step():
+        gdr.chunked_fwd(vinp["q"], vinp["k"], vinp["v"], vinp["a"], vinp["b"], vinp["A_log"],
+                        vinp["dt_bias"], vinp["initial_state"], chunk=wv.chunk,
+                        cu_seqlens=vinp["cu_seqlens"], o=ov, final_state=Sv)
+
+    varlen_step()
+    torch.cuda.synchronize(dev)
+    vsteps = max(1, min(args.steps, 5))
+    ve = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ve[0].record(stream)
+    for _ in range(vsteps):
+        varlen_step()
+    ve[1].record(stream)
+    torch.cuda.synchronize(dev)
+    vms = ve[0].elapsed_time(ve[1]) / vsteps
+    vflops = varlen_flops(wv.seq_lengths, wv.H_k, wv.H_v, wv.d_k, wv.d_v, wv.chunk)
+    vbytes = prefill_bytes(Tv, Nv, wv.H_k, wv.H_v, wv.d_k, wv.d_v, 2, s0=True)
+    del vinp, ov, Sv
+
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20) // 4
         src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -203,6 +235,16 @@ def main():
                                 "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
                                 "traffic": profiled_traffic("recurrent_kernel"),
                                 "bytes_per_launch": dbytes}},
+        "varlen": {"workload": "8 packed sequences, lengths %s (seed 0), 48 value heads sharing "
+                               "16 key heads, d_k=d_v=128, chunk 32, bf16, carried fp32 state"
+                               % wv.seq_lengths,
+                   "tokens": Tv, "steps": vsteps, "ms_per_step": vms,
+                   "tokens_per_s": Tv / (vms / 1e3),
+                   "roofline": {"bound": "mfma", "achieved": vflops / (vms / 1e3) / 1e12,
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": vflops / (vms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                                "flop_per_launch": vflops,
+                                "hbm_GBs": vbytes / (vms / 1e3) / 1e9}},
         "wall_s_prefill_timed": wall,
         "cpu_baseline": cpu,
     }

@@ -249,12 +249,34 @@ __device__ __forceinline__ void dma16(const bf16 *src, bf16 *lds) {
                                    (__attribute__((address_space(3))) void *)(lds), 16, 0, 0);
 }
 
-// Map the launch index so that the workgroups of one (sequence, key head)
-// land on the same XCD (blocks are dealt round-robin to the 8 XCDs), sharing
-// that XCD's L2 for their common k and q rows.
-__device__ __forceinline__ int unit_of_block(int b, int nb) {
-  if ((nb & 7) != 0) return b;
-  return (b & 7) * (nb >> 3) + (b >> 3);
+// Map the launch index to a work unit so that the gs units of one (sequence,
+// key head) group land on the same XCD (blocks are dealt round-robin to the 8
+// XCDs), sharing that XCD's L2 for their common k and q rows, while the groups
+// still start in unit order (the i-th block of every XCD belongs to the
+// groups 8 (i / gs) .. 8 (i / gs) + 7).
+__device__ __forceinline__ int unit_of_block(int b, int nb, int gs) {
+  if (nb % (8 * gs) != 0) return b;
+  const int slot = b >> 3;
+  return ((slot / gs) * 8 + (b & 7)) * gs + slot % gs;
+}
+
+// Sequence that runs in launch rank `rank` of a packed batch: sequences are
+// ranked by length, longest first (ties by index), so that the longest
+// chains start first and the short ones fill in behind them.  Every lane
+// ranks one sequence (num_seqs <= 64); the result is uniform.
+__device__ __forceinline__ int seq_by_length_rank(const int32_t *cu, int num_seqs, int rank,
+                                                  int lane) {
+  int r = num_seqs;  // lanes without a sequence never match
+  if (lane < num_seqs) {
+    const int len = cu[lane + 1] - cu[lane];
+    r = 0;
+    for (int j = 0; j < num_seqs; ++j) {
+      const int lj = cu[j + 1] - cu[j];
+      r += (lj > len) || (lj == len && j < lane);
+    }
+  }
+  const uint64_t hit = __ballot(r == rank);
+  return hit ? (int)__builtin_ctzll(hit) : rank;
 }
 
 // Request the 32 rows of a k or q tile (8 loads of 1 KB; rows past the end
@@ -540,10 +562,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
   Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
   constexpr int NVB = DV / BV;
 
-  const int unit = unit_of_block(blockIdx.x, gridDim.x);
+  const int unit = unit_of_block(blockIdx.x, gridDim.x, (p.H_v / p.H_k) * NVB);
   const int vb = unit % NVB;
   const int h = (unit / NVB) % p.H_v;
-  const int n = unit / (NVB * p.H_v);
+  const int n = (p.cu && p.num_seqs <= 64)
+                    ? seq_by_length_rank(p.cu, p.num_seqs, unit / (NVB * p.H_v), threadIdx.x & 63)
+                    : unit / (NVB * p.H_v);
   const int hk = h / (p.H_v / p.H_k);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
