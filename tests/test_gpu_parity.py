@@ -318,10 +318,20 @@ MFMA_CASES = [
     (1, 3, [300, 129, 0]),
     (4, 4, [97]),
     (16, 48, [70]),
+    # 64 sequences (longest-first ranking over every lane, ties) and 70 (more
+    # than 64: launch order left as is), grids not a multiple of 8 groups
+    (1, 3, [(7 * i) % 61 for i in range(64)]),
+    (1, 1, [(13 * i) % 75 for i in range(70)]),
 ]
 
 
-@pytest.mark.parametrize("case", MFMA_CASES, ids=lambda c: f"H{c[1]}/{c[0]}_L{'-'.join(map(str, c[2]))}")
+def _case_id(c):
+    lens = c[2]
+    tag = "-".join(map(str, lens)) if len(lens) <= 4 else f"{len(lens)}seqs"
+    return f"H{c[1]}/{c[0]}_L{tag}"
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=_case_id)
 def test_matrix_core_chunked_kernel(case):
     H_k, H_v, lens = case
     assert gdr.chunked_path(H_k, H_v, 128, 128, "bf16", 32) == "matrix_bf16"
