@@ -169,22 +169,31 @@ __device__ __forceinline__ void block_sync() {
 
 // ---------------------------------------------------------------- LDS tiles
 // k and q tiles: [32 rows][128 columns] bf16, row pitch 256 bytes; the 16-byte
-// piece p of row r is stored at piece position p ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// piece p of row r is stored at piece position p ^ swz(r), swz a permutation of
+// the bits of r % 16 (bit 0 stays, bit 1 <- r bit 3, bit 2 <- r bit 1,
+// bit 3 <- r bit 2).  LDS serves 256 bytes a cycle: a 16-byte read in four
+// passes of 16 lanes (lane half l / 32 and the parity of lane bits 2..4), an
+// 8-byte read in two passes of 32 lanes, and a pass is free of bank conflicts
+// when its lanes hit distinct 16- (8-) byte slots modulo 256 bytes.  With
+// this swizzle both the row reads (16 rows, one piece each) and the
+// transposing reads (8 rows x 4 pieces, alternating 8-byte halves, see
+// state_row) fill every slot once.
+__device__ __forceinline__ int swz(int r) {
+  return (r & 1) | ((r >> 2) & 2) | ((r << 1) & 12);
+}
 // Element offset of (row r, column d), d a multiple of 4.
 __device__ __forceinline__ int kq_off(int r, int d) {
   return r * DK + ((((d >> 3) ^ swz(r & 15)) << 3) | (d & 7));
 }
 
-constexpr int TP = CH + 8;   // bf16 [32][TP]: rows x chunk slots, 16 bytes of padding
-
 struct Stage {
   alignas(16) bf16 K[CH * DK];   // k rows, swizzled                     (loaded by staging wave 0)
   alignas(16) bf16 Q[CH * DK];   // q rows, swizzled                     (staging wave 1)
   alignas(16) bf16 V[CH * BV];   // v rows, this workgroup's columns     (both)
-  alignas(16) bf16 P[CH][TP];    // P without 1/|k_i|, columns in slot order (P1)
-  alignas(16) bf16 T[2][16][16];  // (I + A_bb)^-1 of the two diagonal blocks, A layout (P0)
-  alignas(16) bf16 nA21[16][16];  // -A_21, A layout                      (P0)
+  // per lane (m, g), written and read by lanes of the same index:
+  alignas(16) bf16x8 P[2][64];   // P without 1/|k_i|: rows m, 16 + m at chunk slots 8g.. (P1)
+  alignas(16) bf16x4 T[2][64];   // (I + A_bb)^-1 of the diagonal blocks: [m][4g..4g+3] (P0)
+  alignas(16) bf16x4 nA21[64];   // -A_21: [m][4g..4g+3]                 (P0)
   alignas(16) uint32_t ab[2 * CH]; // raw a_r (low half of word r), b_r (word 32 + r) (staging wave 1)
   alignas(16) float gam[CH];     // cumulative log decay                 (staging wave 1, a step early)
   alignas(16) float beta[CH];    //                                      (staging wave 1, a step early)
@@ -218,12 +227,21 @@ struct MfmaParams {
 
 // State rows held in registers.  Accumulator tile t (t = 0..7) of a
 // consumer holds, in lane (m, g) register j, the state row
-//   d(t, g, j) = 32 (t / 2) + 8 g + 4 (t % 2) + j
+//   d(t, g, j) = 32 (t / 2) + 8 g + 4 ((t ^ g) % 2) + j
 // of column m, so that the tile pair (2kb, 2kb+1) gives every lane 8
-// consecutive rows 32kb + 8g .. 32kb + 8g + 7: a B operand whose contraction
-// index runs in natural order, matching one 16-byte read of a k or q row.
+// consecutive rows 32kb + 8g .. 32kb + 8g + 7 (tile 2kb + g % 2 holds the
+// lower four): a B operand whose contraction index runs in natural order,
+// matching one 16-byte read of a k or q row.  The transposing reads of tile t
+// then take the lower 8-byte half of a piece in two of their four segments
+// and the upper half in the other two, which keeps them free of bank conflicts.
 __device__ __forceinline__ int state_row(int t, int g, int j) {
-  return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + j;
+  return 32 * (t >> 1) + 8 * g + 4 * ((t ^ g) & 1) + j;
+}
+// Rows 32kb + 8g .. + 7 of the state in natural order, from the tile pair
+// (2kb, 2kb + 1) of lane group g.
+__device__ __forceinline__ bf16x8 state_operand(const f32x4 &t0, const f32x4 &t1, int g) {
+  const bf16x4 a = pack4(t0), b = pack4(t1);
+  return (g & 1) ? cat8(b, a) : cat8(a, b);
 }
 
 // Operand of row r, 32-block kb of d_k: columns 32kb + 8g .. 32kb + 8g + 7.
@@ -314,13 +332,23 @@ __device__ __forceinline__ void dma_rows_full(const bf16 *x, const RowOffsets &o
 #pragma unroll
   for (int i = 0; i < 8; ++i) dma16(reinterpret_cast<const bf16 *>(base + o.off[i]), tile + 512 * i);
 }
-// Half (rows 16 h .. 16 h + 15) of the v tile: lane l takes row 16h + l/4,
-// columns col0 + 8 (l%4) .. + 7.
+// v tile: [32 rows][BV = 32 columns] bf16, row pitch 64 bytes; the 16-byte
+// piece p of row r is stored at piece position p ^ (2 ((r / 4) % 2)), so that
+// the transposing reads of 8 rows x 4 segments fill all 32 8-byte slots of a
+// 256-byte bank cycle once.  Element offset of (row r, column c), c % 4 == 0:
+static_assert(BV == 32, "the v tile swizzle assumes 4 pieces per row");
+__device__ __forceinline__ int v_off(int r, int c) {
+  return r * BV + ((((c >> 3) ^ (2 * ((r >> 2) & 1))) << 3) | (c & 7));
+}
+// Source piece of the 16 bytes lane l stores in a v half tile (row
+// 16 h + l / 4, piece position l % 4).
+__device__ __forceinline__ int v_src_piece(int lane) { return (lane & 3) ^ (2 * ((lane >> 4) & 1)); }
+// Half (rows 16 h .. 16 h + 15) of the v tile: lane l takes row 16h + l/4.
 __device__ __forceinline__ void dma_v_half(const bf16 *v, int H_v, int hv, int col0, int64_t row0,
                                            int cl, bf16 *tile, int half, int lane) {
   const int r = 16 * half + (lane >> 2);
   const int rr = min(r, cl - 1);
-  dma16(v + ((row0 + rr) * H_v + hv) * DV + col0 + 8 * (lane & 3), tile + 512 * half);
+  dma16(v + ((row0 + rr) * H_v + hv) * DV + col0 + 8 * v_src_piece(lane), tile + 512 * half);
 }
 
 // a and b of the 32 rows in one load: lane l < 32 takes a of row l, lane
@@ -343,24 +371,29 @@ __device__ __forceinline__ uint32_t lds_read_u32_now(const uint32_t *p) {
   return v;
 }
 
-// The 128 contiguous bytes at p (8 16-byte LDS reads), complete when the
-// statement ends (see lds_read_u32_now).
+// The 128 bytes at p (8 16-byte LDS reads), piece i read by the i-th read from
+// piece (i + rot) % 8, complete when the statement ends (see lds_read_u32_now).
+// The outputs are early-clobber: a read that returns while later reads of the
+// block are still to issue must not land on their address registers.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void lds_read_128B_now(const bf16 *p, u32x4 (&x)[8]) {
-  const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const bf16 *)p;
+__device__ __forceinline__ void lds_read_128B_now(const bf16 *p, int rot, u32x4 (&x)[8]) {
+  const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const bf16 *)p;
+  uint32_t a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = base + 16u * (uint32_t)((i + rot) & 7);
   asm volatile(
       "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:16\n\t"
-      "ds_read_b128 %2, %8 offset:32\n\t"
-      "ds_read_b128 %3, %8 offset:48\n\t"
-      "ds_read_b128 %4, %8 offset:64\n\t"
-      "ds_read_b128 %5, %8 offset:80\n\t"
-      "ds_read_b128 %6, %8 offset:96\n\t"
-      "ds_read_b128 %7, %8 offset:112\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]),
-        "=v"(x[7])
-      : "v"(addr)
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+        "=&v"(x[6]), "=&v"(x[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
 // Sum of squares of the bf16 values in 32-bit words w (bf16 pair dot products).
@@ -373,13 +406,14 @@ __device__ __forceinline__ float sumsq_words(const uint32_t *w, int n, float s) 
 }
 
 // 1/|k_r| of one chunk (staging wave 0, once its k rows have landed): lane l
-// sums the squares of half a row (row l / 2) -- the swizzle only permutes the
-// 16-byte pieces inside each 128-byte half -- and its neighbour the other half.
+// sums the squares of half a row (row l / 2) -- the swizzle keeps the 8 pieces
+// of a 128-byte half together -- and its neighbour the other half.  Starting
+// each lane at piece r % 8 spreads the lanes of every read over all banks.
 __device__ __forceinline__ void stage_k_norms(Stage &S, int lane, int cl, float eps) {
   const int r = lane >> 1, half = lane & 1;
   const int pos = half ^ (swz(r & 15) >> 3);  // where the 8 pieces of this half are stored
   u32x4 x[8];
-  lds_read_128B_now(S.K + r * DK + 64 * pos, x);
+  lds_read_128B_now(S.K + r * DK + 64 * pos, r & 7, x);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};  // independent chains
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -513,9 +547,9 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const 
   // T11, T22 (the state waves apply T21 = -T22 A21 T11 as a block solve)
   f32x4 t11a, t11b, t22a;
   unit_lower_inverse2<false>(na0, nb0, na1, nb1, m, g, t11a, t11b, t22a);
-  *reinterpret_cast<bf16x4 *>(&S.T[0][m][4 * g]) = pack4(t11a);
-  *reinterpret_cast<bf16x4 *>(&S.T[1][m][4 * g]) = pack4(t22a);
-  *reinterpret_cast<bf16x4 *>(&S.nA21[m][4 * g]) = pack4(na21);
+  S.T[0][lane] = pack4(t11a);
+  S.T[1][lane] = pack4(t22a);
+  S.nA21[lane] = pack4(na21);
 }
 
 // P1: scale/|q_r| from the Gram diagonal of q, and the output mask without the
@@ -553,8 +587,8 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const 
     v11[j] = (i <= m) ? fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * p11[j] : 0.f;
   }
   // row r of P at slots 8g..8g+3 (columns 4g..4g+3) and 8g+4.. (columns 16+4g..)
-  *reinterpret_cast<bf16x8 *>(&S.P[m][8 * g]) = pack8(v00, z);
-  *reinterpret_cast<bf16x8 *>(&S.P[16 + m][8 * g]) = pack8(v10, v11);
+  S.P[0][lane] = pack8(v00, z);
+  S.P[1][lane] = pack8(v10, v11);
 }
 
 __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p) {
@@ -603,7 +637,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     }
     bf16x8 Sb[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+    for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1], g);
     // LDS operands: the k^T tiles of this chunk (A operands of the state
     // update) are read once the K S products are issued; the k rows (A
     // operands of K S) and v of the next chunk are read after the state
@@ -629,7 +663,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     auto read_v = [&](const Stage &sn) {
       // v[4g + j][col] and v[16 + 4g + j][col]
       const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
-      vv = cat8(tr_read(sn.V + vr * BV + vc), tr_read(sn.V + (16 + vr) * BV + vc));
+      vv = cat8(tr_read(sn.V + v_off(vr, vc)), tr_read(sn.V + v_off(16 + vr, vc)));
     };
     auto hand_state = [&](int c) {
 #pragma unroll
@@ -644,9 +678,9 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         const Stage &sn = sm.st[(c + 1) % NSTAGE];
         const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
         // this chunk's prepared tile and row factors
-        const s16x4 t11 = *reinterpret_cast<const s16x4 *>(&st.T[0][m][4 * g]);
-        const s16x4 t22 = *reinterpret_cast<const s16x4 *>(&st.T[1][m][4 * g]);
-        const s16x4 na21 = *reinterpret_cast<const s16x4 *>(&st.nA21[m][4 * g]);
+        const s16x4 t11 = __builtin_bit_cast(s16x4, st.T[0][lane]);
+        const s16x4 t22 = __builtin_bit_cast(s16x4, st.T[1][lane]);
+        const s16x4 na21 = __builtin_bit_cast(s16x4, st.nA21[lane]);
         const f32x4 bt0 = ld4(&st.beta[4 * g]), bt1 = ld4(&st.beta[16 + 4 * g]);
         const f32x4 gm0 = ld4(&st.Gam[4 * g]), gm1 = ld4(&st.Gam[16 + 4 * g]);
         const f32x4 ik0 = ld4(&st.ik[4 * g]), ik1 = ld4(&st.ik[16 + 4 * g]);
@@ -679,7 +713,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
 #pragma unroll
         for (int t = 0; t < 8; ++t) S[t] = mma32(Kt[t], Dp, S[t] * gc);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) Sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1], g);
         if (more) hand_state(c + 1);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the handed-over writes are done
         if (more) {
@@ -714,8 +748,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       if (co >= 0 && co < nch) {
         const Stage &st = sm.st[co % NSTAGE];
         const bf16x8 Db = sm.db[co & 1][cw][lane];
-        const bf16x8 pr0 = *reinterpret_cast<const bf16x8 *>(&st.P[m][8 * g]);
-        const bf16x8 pr1 = *reinterpret_cast<const bf16x8 *>(&st.P[16 + m][8 * g]);
+        const bf16x8 pr0 = st.P[0][lane];
+        const bf16x8 pr1 = st.P[1][lane];
         const float gm0 = st.Gam[m], gm1 = st.Gam[16 + m];
         const float iq0 = st.iq[m], iq1 = st.iq[16 + m];
         // lane (m, g) gets O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P diag(ik) Delta)
@@ -783,7 +817,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     const RowOffsets ko = row_offsets(p.H_k, lane);
     const int vhalf = wave - W_ST0;
     const uint32_t voff =
-        (uint32_t)(((16 * vhalf + (lane >> 2)) * p.H_v * DV + col0 + 8 * (lane & 3)) * (int)sizeof(bf16));
+        (uint32_t)(((16 * vhalf + (lane >> 2)) * p.H_v * DV + col0 + 8 * v_src_piece(lane)) * (int)sizeof(bf16));
     // chunk c (clamped to the last one: requests past the end re-read it into
     // a buffer no one reads again) -> first row and valid rows
     auto rows_of = [&](int c, int64_t &row0, int &cl) {

@@ -228,12 +228,19 @@ def test_streaming_prefill_then_decode():
 
 @pytest.mark.parametrize("form", ["recurrent", "chunked"])
 def test_deterministic(form):
-    w = synth.custom(2, 4, 128, 128, "bf16", lengths=[257, 31])
+    """Repeated launches on the same inputs give the same bits, also with a
+    launch on other inputs in between (a race inside a kernel, or a read of
+    memory the launch did not write, shows up as a difference)."""
+    w = synth.custom(2, 6, 128, 128, "bf16", lengths=[257, 31, 64], chunk=32)
     inp = synth.make_inputs(w, 9, device=DEV)
-    o1, S1 = run(form, inp, w)
-    o2, S2 = run(form, inp, w)
-    torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    other = synth.make_inputs(w, 10, device=DEV)
+    first = run(form, inp, w)
+    for i in range(4):
+        if i == 1:
+            run(form, other, w)
+        again = run(form, inp, w)
+        torch.cuda.synchronize()
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1]), f"launch {i + 1}"
 
 
 def test_inplace_equals_out_of_place():
