@@ -675,7 +675,6 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       if (c >= 0 && c < nch) {
         const Stage &st = sm.st[c % NSTAGE];
         const bool more = c + 1 < nch;
-        const Stage &sn = sm.st[(c + 1) % NSTAGE];
         const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
         // this chunk's prepared tile and row factors
         const s16x4 t11 = __builtin_bit_cast(s16x4, st.T[0][lane]);
@@ -715,16 +714,17 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1], g);
         if (more) hand_state(c + 1);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the handed-over writes are done
-        if (more) {
-          read_rows(sn);
-          read_v(sn);
-        }
       } else if (c == -1 && nch > 0) {
         hand_state(0);
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        read_rows(sm.st[0]);
-        read_v(sm.st[0]);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the handed-over writes are done
+      {
+        // operands of the next step's chunk c + 1, read unconditionally (the
+        // index clamped into the sequence) so that the loads write the loop's
+        // registers directly and stay in flight across the barrier
+        const Stage &sr = sm.st[max(min(c + 1, nch - 1), 0) % NSTAGE];
+        read_rows(sr);
+        read_v(sr);
       }
       // no wait for the reads in flight: their buffers are refilled only
       // steps later, and their registers are waited for where they are used
