@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
             Reference ("Detailed Description") describes the backend doing:
             sequences no longer than one chunk run the recurrence, longer
             ones the chunked form.
+  conv_silu(x, weight, H_k, H_v, d_k, d_v, bias=None, conv_state=None, ...)
+            -> q, k, v, final_conv_state   (the layer's step before the rule)
+  gated_rmsnorm(o, z, weight, eps=1e-6)  -> out   (the layer's step after it)
 
 Layouts: q, k [total, H_k, d_k]; v [total, H_v, d_v]; a, b [total, H_v]
 (all fp32 or all bf16); A_log, dt_bias [H_v] fp32; states
@@ -31,8 +34,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["gates", "recurrent_fwd", "chunked_fwd", "fwd", "chunked_path", "library_path",
-           "lib", "GdrError", "abi_version"]
+__all__ = ["gates", "recurrent_fwd", "chunked_fwd", "fwd", "chunked_path", "conv_silu",
+           "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -80,6 +83,10 @@ def _bind(lib):
     lib.gdr_chunked_path.restype = ctypes.c_int
     lib.gdr_abi_version.argtypes = []
     lib.gdr_abi_version.restype = ctypes.c_int
+    lib.gdr_conv_silu.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdr_conv_silu.restype = ctypes.c_int
+    lib.gdr_gated_rmsnorm.argtypes = [sp, vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.gdr_gated_rmsnorm.restype = ctypes.c_int
     return lib
 
 
@@ -297,3 +304,76 @@ def fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32, cu_seqle
                              num_seqs=num_seqs, **kw)
     return chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state, chunk=chunk,
                        cu_seqlens=cu_seqlens, num_seqs=num_seqs, **kw)
+
+
+def conv_silu(x, weight, H_k, H_v, d_k, d_v, *, bias=None, conv_state=None, cu_seqlens=None,
+              num_seqs=None, final_conv_state=None, output_final_state=True, inplace=False):
+    """Short causal convolution + SiLU over the channels q | k | v of the
+    in_proj output x [total, 2 H_k d_k + H_v d_v] (fp32 or bf16); weight
+    [C, width] fp32, bias [C] fp32 or None; conv_state [N, C, width-1] in x's
+    dtype or None.  Returns q [total, H_k, d_k], k, v [total, H_v, d_v] and
+    the new history (or None); ``inplace=True`` updates conv_state."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError(f"gdr_conv_silu: tensors must be on a GPU (got {dev})")
+    dt = x.dtype
+    code = _dtype_code(dt)
+    total = x.shape[0]
+    C = 2 * H_k * d_k + H_v * d_v
+    _check(x, "x", dev, dt, (total, C))
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError(f"weight has shape {tuple(weight.shape)}, expected ({C}, width)")
+    width = weight.shape[1]
+    _check(weight, "weight", dev, torch.float32, (C, width))
+    if bias is not None:
+        _check(bias, "bias", dev, torch.float32, (C,))
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    shape = _make_shape(total, H_k, H_v, d_k, d_v, cu_seqlens, num_seqs, code, 32, None, 1e-6)
+    N = shape.num_seqs
+    st_shape = (N, C, width - 1)
+    if conv_state is not None:
+        _check(conv_state, "conv_state", dev, dt, st_shape)
+    if inplace:
+        if conv_state is None:
+            raise ValueError("inplace=True needs a conv_state to update")
+        final_conv_state = conv_state
+    elif final_conv_state is None and output_final_state:
+        final_conv_state = torch.empty(st_shape, dtype=dt, device=dev)
+    elif final_conv_state is not None:
+        _check(final_conv_state, "final_conv_state", dev, dt, st_shape)
+    q = torch.empty((total, H_k, d_k), dtype=dt, device=dev)
+    k = torch.empty((total, H_k, d_k), dtype=dt, device=dev)
+    v = torch.empty((total, H_v, d_v), dtype=dt, device=dev)
+    rc = lib().gdr_conv_silu(ctypes.byref(shape), width, _ptr(x), _ptr(weight), _ptr(bias),
+                             _ptr(conv_state), _ptr(q), _ptr(k), _ptr(v), _ptr(final_conv_state),
+                             _stream(dev))
+    _raise("gdr_conv_silu", rc)
+    return q, k, v, final_conv_state
+
+
+def gated_rmsnorm(o, z, weight, eps=1e-6, *, out=None):
+    """out = o / sqrt(mean(o^2) + eps) * weight * SiLU(z) per (token, head)
+    row; o, z [total, H_v, d_v] (or [N, T, H_v, d_v]) fp32 or bf16, weight
+    [d_v] fp32.  ``out`` may be o or z."""
+    shape4 = o.shape if o.dim() == 4 else None
+    o, z = _flatten(o, 2), _flatten(z, 2)
+    dev = o.device
+    if dev.type != "cuda":
+        raise ValueError(f"gdr_gated_rmsnorm: tensors must be on a GPU (got {dev})")
+    dt = o.dtype
+    code = _dtype_code(dt)
+    total, H_v, d_v = o.shape
+    _check(o, "o", dev, dt)
+    _check(z, "z", dev, dt, (total, H_v, d_v))
+    _check(weight, "weight", dev, torch.float32, (d_v,))
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        out = _flatten(out, 2)
+        _check(out, "out", dev, dt, (total, H_v, d_v))
+    shape = _make_shape(total, 1, H_v, d_v, d_v, None, 1, code, 32, None, 1e-6)
+    rc = lib().gdr_gated_rmsnorm(ctypes.byref(shape), _ptr(o), _ptr(z), _ptr(weight),
+                                 float(eps), _ptr(out), _stream(dev))
+    _raise("gdr_gated_rmsnorm", rc)
+    return out.view(shape4) if shape4 is not None else out

@@ -189,6 +189,79 @@ gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
   return launched(launch_chunked_vec(pr, x, stream));
 }
 
+gdr_status gdr_conv_silu(const gdr_shape *shape, int32_t width, const void *x, const float *weight,
+                         const float *bias, const void *conv_state_in, void *q, void *k, void *v,
+                         void *conv_state_out, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (width < 2 || width > 4) return GDR_ERR_UNSUPPORTED;
+  if (!weight) return GDR_ERR_NULL;
+  if (pr.total > 0 && (!x || !q || !k || !v)) return GDR_ERR_NULL;
+  const void *rows[] = {x, q, k, v};
+  for (const void *p : rows)
+    if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+  const size_t es = elem_size(pr.dtype);
+  const void *elems[] = {conv_state_in, conv_state_out};
+  for (const void *p : elems)
+    if (p && !aligned_to(p, es)) return GDR_ERR_ALIGN;
+  const void *words[] = {weight, bias, pr.cu};
+  for (const void *p : words)
+    if (p && !aligned_to(p, 4)) return GDR_ERR_ALIGN;
+  const size_t T = (size_t)pr.total;
+  const size_t Cq = (size_t)pr.H_k * pr.d_k, Cv = (size_t)pr.H_v * pr.d_v, C = 2 * Cq + Cv;
+  const size_t hist = (size_t)pr.num_seqs * C * (width - 1) * es;
+  const Range ins[] = {span(x, T * C * es), span(weight, C * width * 4),
+                       span(bias, bias ? C * 4 : 0), span(conv_state_in, conv_state_in ? hist : 0),
+                       span(pr.cu, pr.cu ? (size_t)(pr.num_seqs + 1) * 4 : 0)};
+  const Range outs[] = {span(q, T * Cq * es), span(k, T * Cq * es), span(v, T * Cv * es),
+                        span(conv_state_out, conv_state_out ? hist : 0)};
+  for (int i = 0; i < 4; ++i) {
+    const Range &o = outs[i];
+    if (o.lo == 0 || o.hi == o.lo) continue;
+    for (int j = 0; j < 5; ++j) {
+      const Range &r = ins[j];
+      if (r.lo == 0 || r.hi == r.lo) continue;
+      // the new history may replace the old one exactly
+      if (i == 3 && j == 3 && conv_state_out == conv_state_in) continue;
+      if (overlap(r, o)) return GDR_ERR_ALIAS;
+    }
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j].lo && outs[j].hi > outs[j].lo && overlap(o, outs[j])) return GDR_ERR_ALIAS;
+  }
+  ConvArgs a{width, x, weight, bias, conv_state_in, conv_state_out, q, k, v};
+  return launched(launch_conv_silu(pr, a, stream));
+}
+
+gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, const void *z,
+                             const float *weight, float eps, void *out, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return GDR_ERR_SHAPE;
+  if (!weight) return GDR_ERR_NULL;
+  if (pr.total > 0 && (!o || !z || !out)) return GDR_ERR_NULL;
+  const void *rows[] = {o, z, out};
+  for (const void *p : rows)
+    if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+  if (!aligned_to(weight, 4)) return GDR_ERR_ALIGN;
+  const size_t es = elem_size(pr.dtype);
+  const size_t bytes = (size_t)pr.total * pr.H_v * pr.d_v * es;
+  const Range ro = span(o, bytes), rz = span(z, bytes), rout = span(out, bytes),
+              rw = span(weight, (size_t)pr.d_v * 4);
+  if (bytes > 0) {
+    // out may be o or z exactly (each element is read before the same
+    // thread writes it), not a shifted overlap of either
+    if (out != o && overlap(rout, ro)) return GDR_ERR_ALIAS;
+    if (out != z && overlap(rout, rz)) return GDR_ERR_ALIAS;
+    if (overlap(rout, rw)) return GDR_ERR_ALIAS;
+  }
+  NormArgs a{o, z, weight, eps, out};
+  return launched(launch_gated_rmsnorm(pr, a, stream));
+}
+
 int gdr_chunked_path(const gdr_shape *shape) {
   using namespace gdr;
   Problem pr;

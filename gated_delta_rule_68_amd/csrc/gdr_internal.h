@@ -38,7 +38,27 @@ struct GatesArgs {
   float *g, *beta;
 };
 
+// Short convolution + SiLU producing q, k, v (channels q | k | v of x).
+struct ConvArgs {
+  int width;
+  const void *x;
+  const float *weight, *bias;  // bias may be nullptr
+  const void *s_in;            // may be nullptr (zero history)
+  void *s_out;                 // may be nullptr (dropped); may equal s_in
+  void *q, *k, *v;
+};
+
+// Gated RMSNorm of the rule's output rows.
+struct NormArgs {
+  const void *o, *z;
+  const float *weight;
+  float eps;
+  void *out;  // may equal o or z
+};
+
 hipError_t launch_gates(const Problem &p, const GatesArgs &x, hipStream_t s);
+hipError_t launch_conv_silu(const Problem &p, const ConvArgs &x, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const Problem &p, const NormArgs &x, hipStream_t s);
 hipError_t launch_recurrent(const Problem &p, const FwdArgs &x, hipStream_t s);
 hipError_t launch_chunked_vec(const Problem &p, const FwdArgs &x, hipStream_t s);
 hipError_t launch_chunked_mfma(const Problem &p, const FwdArgs &x, hipStream_t s);

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -153,6 +153,59 @@ GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const 
                            const void *a, const void *b, const float *A_log, const float *dt_bias,
                            const float *initial_state, void *o, float *final_state,
                            hipStream_t stream);
+
+/*
+ * gdr_conv_silu -- the short causal convolution and SiLU that turn the in_proj
+ * output into q, k, v (flashprove issue "P1: Qwen3.8-27B port, tracking": the
+ * layer runs from the in_proj outputs through a 4-tap conv1d and SiLU to the
+ * q/k L2 norm, the gates and the rule; PLENA_Simulator pull request 113: the
+ * short convolution has per-channel weights, an optional bias and a history
+ * carried between calls).  The pages print no formula; this library reads it
+ * as a depthwise convolution over the C = 2 H_k d_k + H_v d_v channels of x,
+ * tap width-1 on the newest input:
+ *     y[t, c] = SiLU(bias[c] + sum_j weight[c, j] * x[t - (width-1) + j, c]),
+ * SiLU(u) = u * sigmoid(u), inputs before a sequence's first token taken from
+ * its history conv_state_in[n, c, 0 .. width-2] (oldest first; NULL for
+ * zeros).  y is split by channel into q ([0, H_k d_k)), k ([H_k d_k,
+ * 2 H_k d_k)) and v (the rest), each dense in the layouts above, ready for
+ * gdr_chunked_fwd / gdr_recurrent_fwd.  conv_state_out receives the last
+ * width-1 inputs of every sequence (older history moving up when a sequence is
+ * shorter than width-1); a decode step is a call with seq_len = 1.
+ *   x              : dtype [total, C]                      (16-byte aligned)
+ *   weight         : fp32  [C, width], 2 <= width <= 4
+ *   bias           : fp32  [C], or NULL for none
+ *   conv_state_in  : dtype [num_seqs, C, width-1], or NULL for zeros
+ *   q, k           : dtype [total, H_k, d_k]                (16-byte aligned)
+ *   v              : dtype [total, H_v, d_v]                (16-byte aligned)
+ *   conv_state_out : dtype [num_seqs, C, width-1], or NULL to drop it; may be
+ *                    conv_state_in itself (in-place decode)
+ * Uses num_seqs, seq_len, total_tokens, cu_seqlens, H_k, H_v, d_k, d_v and
+ * dtype of `shape` (chunk, scale and l2_eps are checked but unused).
+ * GDR_ERR_UNSUPPORTED for other widths.  No output may overlap an input or
+ * another output, except conv_state_out == conv_state_in.
+ */
+GDR_API gdr_status gdr_conv_silu(const gdr_shape *shape, int32_t width, const void *x,
+                                 const float *weight, const float *bias, const void *conv_state_in,
+                                 void *q, void *k, void *v, void *conv_state_out,
+                                 hipStream_t stream);
+
+/*
+ * gdr_gated_rmsnorm -- the gated RMSNorm that ends the layer after the rule
+ * (flashprove issue "P1: Qwen3.8-27B port, tracking": the layer's output is
+ * the gated RMSNorm of o).  The pages print no formula; this library reads it
+ * per (token, value head) row of o as
+ *     out = o / sqrt(mean(o^2) + eps) * weight * SiLU(z)
+ * with one weight vector shared by all heads.
+ *   o, z, out : dtype [total, H_v, d_v]   (16-byte aligned)
+ *   weight    : fp32  [d_v]
+ *   eps       : >= 0 and finite, else GDR_ERR_SHAPE
+ * out may be o or z itself (every element is read before it is written); no
+ * other overlap with an input is allowed.  Uses total_tokens, H_v, d_v and
+ * dtype of `shape` (the other fields are checked but unused).
+ */
+GDR_API gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, const void *z,
+                                     const float *weight, float eps, void *out,
+                                     hipStream_t stream);
 
 /* Which kernel gdr_chunked_fwd runs for `shape`: GDR_PATH_VECTOR_F32 (fp32
  * on the vector ALUs), GDR_PATH_MATRIX_BF16 (matrix cores, bf16 operands,

@@ -31,7 +31,8 @@ def declared_symbols():
 
 def test_header_declares_the_abi():
     assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_path",
-                                  "gdr_gates", "gdr_recurrent_fwd", "gdr_status_string"]
+                                  "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
+                                  "gdr_recurrent_fwd", "gdr_status_string"]
 
 
 def test_library_exports_every_declared_symbol(gdr):
@@ -188,3 +189,60 @@ def test_chunked_path_selection(gdr):
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, H_v=3, H_k=2))) == -2
     assert gdr.chunked_path(16, 48, 128, 128, "bf16", 32) == "matrix_bf16"
     assert gdr.chunked_path(1, 1, 128, 128, "f32", 32) == "vector_f32"
+
+
+# ------------------------------------------ the layer's steps either side of the rule
+def conv_call(gdr, s, width=4, **over):
+    """gdr_conv_silu with fake pointers; shape(gdr) has C = 2*16 + 2*16 = 64."""
+    names = ["x", "weight", "bias", "s_in", "q", "k", "v", "s_out"]
+    p = {n: fake(i) for i, n in enumerate(names)}
+    p.update(over)
+    return gdr.lib().gdr_conv_silu(ctypes.byref(s) if s is not None else None, width,
+                                   *[p[n] for n in names], None)
+
+
+def norm_call(gdr, s, eps=1e-6, **over):
+    names = ["o", "z", "weight", "out"]
+    p = {n: fake(i) for i, n in enumerate(names)}
+    p.update(over)
+    return gdr.lib().gdr_gated_rmsnorm(ctypes.byref(s) if s is not None else None, p["o"], p["z"],
+                                       p["weight"], eps, p["out"], None)
+
+
+def test_conv_silu_validation(gdr):
+    assert conv_call(gdr, None) == 1                                  # no shape
+    assert conv_call(gdr, shape(gdr, H_v=3, H_k=2)) == 2
+    assert conv_call(gdr, shape(gdr), width=1) == 3                   # widths 2..4 only
+    assert conv_call(gdr, shape(gdr), width=5) == 3
+    assert conv_call(gdr, shape(gdr), weight=None) == 1
+    assert conv_call(gdr, shape(gdr), x=None) == 1
+    assert conv_call(gdr, shape(gdr), v=None) == 1
+    assert conv_call(gdr, shape(gdr), x=fake(0, off=8)) == 4          # rows need 16 bytes
+    assert conv_call(gdr, shape(gdr), weight=fake(1, off=2)) == 4     # fp32 needs 4 bytes
+    assert conv_call(gdr, shape(gdr, dtype=1), s_in=fake(3, off=1)) == 4
+    assert conv_call(gdr, shape(gdr), q=fake(0)) == 6                 # q over x
+    assert conv_call(gdr, shape(gdr), k=fake(4, off=64)) == 6         # k inside q
+    assert conv_call(gdr, shape(gdr), s_out=fake(3, off=16)) == 6     # shifted over the history
+
+
+def test_gated_rmsnorm_validation(gdr):
+    assert norm_call(gdr, None) == 1
+    assert norm_call(gdr, shape(gdr), eps=-1.0) == 2
+    assert norm_call(gdr, shape(gdr), eps=float("nan")) == 2
+    assert norm_call(gdr, shape(gdr), eps=float("inf")) == 2
+    assert norm_call(gdr, shape(gdr), weight=None) == 1
+    assert norm_call(gdr, shape(gdr), o=None) == 1
+    assert norm_call(gdr, shape(gdr), z=fake(1, off=4)) == 4
+    assert norm_call(gdr, shape(gdr), out=fake(0, off=16)) == 6       # shifted over o
+    assert norm_call(gdr, shape(gdr), out=fake(2)) == 6               # over the weight
+    assert norm_call(gdr, shape(gdr, d_v=24)) == 3
+
+
+def test_layer_binding_refuses_cpu_tensors(gdr):
+    import torch
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        gdr.conv_silu(x, torch.zeros(64, 4), 1, 2, 16, 16)
+    o = torch.zeros(4, 2, 16)
+    with pytest.raises(ValueError):
+        gdr.gated_rmsnorm(o, o, torch.zeros(16))
