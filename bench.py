@@ -184,6 +184,9 @@ def main():
         torch.cuda.synchronize(dev)
         del src, dst
 
+    # ------------------------------------ the layer's steps either side of the rule
+    layer_line = layer_legs(gdr, dev, stream, max(1, min(args.steps, 10)))
+
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -245,10 +248,68 @@ def main():
                                 "frac": vflops / (vms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                                 "flop_per_launch": vflops,
                                 "hbm_GBs": vbytes / (vms / 1e3) / 1e9}},
+        "layer": layer_line,
         "wall_s_prefill_timed": wall,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def layer_legs(gdr, dev, stream, steps):
+    """gdr_conv_silu and gdr_gated_rmsnorm at the prefill layer's shapes
+    (8192 tokens; C = 2*16*128 + 48*128 = 10240 conv channels; o, z
+    [8192, 48, 128]), bf16, synthetic N(0, 1) inputs resident in HBM.  Both
+    are bound by HBM; the bytes are the algorithmic ones (every input read
+    once, every output written once)."""
+    import torch
+    T, H_k, H_v, d = 8192, 16, 48, 128
+    C, W = 2 * H_k * d + H_v * d, 4
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn((T, C), generator=g, device=dev).to(torch.bfloat16)
+    w = torch.randn((C, W), generator=g, device=dev) / 2.0
+    b = 0.1 * torch.randn((C,), generator=g, device=dev)
+    hist = torch.randn((1, C, W - 1), generator=g, device=dev).to(torch.bfloat16)
+    hist_out = torch.empty_like(hist)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    o = torch.randn((T, H_v, d), generator=g, device=dev).to(torch.bfloat16)
+    z = torch.randn((T, H_v, d), generator=g, device=dev).to(torch.bfloat16)
+    nw = 1.0 + 0.1 * torch.randn((d,), generator=g, device=dev)
+    out = torch.empty_like(o)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize(dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(steps):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize(dev)
+        return e[0].elapsed_time(e[1]) / steps
+
+    conv_ms = timed(lambda: gdr.conv_silu(x, w, H_k, H_v, d, d, bias=b, conv_state=hist,
+                                          cu_seqlens=cu, final_conv_state=hist_out))
+    norm_ms = timed(lambda: gdr.gated_rmsnorm(o, z, nw, 1e-6, out=out))
+    conv_bytes = 2 * T * C * 2 + C * W * 4 + C * 4 + 2 * C * (W - 1) * 2
+    norm_bytes = 3 * T * H_v * d * 2 + d * 4
+
+    def leg(workload, ms, nbytes, kernel):
+        gbs = nbytes / (ms / 1e3) / 1e9
+        return {"workload": workload, "steps": steps, "ms_per_launch": ms,
+                "tokens_per_s": T / (ms / 1e3),
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                             "traffic": profiled_traffic(kernel), "bytes_per_launch": nbytes}}
+
+    res = {
+        "conv_silu": leg("short causal conv (width 4, bias, carried history) + SiLU over the "
+                         "q|k|v channels of the in_proj output: 8192 tokens x 10240 channels, "
+                         "bf16, split into q, k, v", conv_ms, conv_bytes, "conv_silu_kernel"),
+        "gated_rmsnorm": leg("gated RMSNorm of o: 8192 tokens x 48 value heads x 128, bf16",
+                             norm_ms, norm_bytes, "gated_rmsnorm_kernel"),
+    }
+    del x, w, b, hist, hist_out, o, z, out
+    return res
 
 
 def profiled_traffic(kernel):

@@ -199,14 +199,15 @@ gdr_status gdr_conv_silu(const gdr_shape *shape, int32_t width, const void *x, c
   if (width < 2 || width > 4) return GDR_ERR_UNSUPPORTED;
   if (!weight) return GDR_ERR_NULL;
   if (pr.total > 0 && (!x || !q || !k || !v)) return GDR_ERR_NULL;
-  const void *rows[] = {x, q, k, v};
+  // rows, weights and biases move in 16-byte vectors
+  const void *rows[] = {x, q, k, v, weight, bias};
   for (const void *p : rows)
     if (p && !aligned16(p)) return GDR_ERR_ALIGN;
   const size_t es = elem_size(pr.dtype);
   const void *elems[] = {conv_state_in, conv_state_out};
   for (const void *p : elems)
     if (p && !aligned_to(p, es)) return GDR_ERR_ALIGN;
-  const void *words[] = {weight, bias, pr.cu};
+  const void *words[] = {pr.cu};
   for (const void *p : words)
     if (p && !aligned_to(p, 4)) return GDR_ERR_ALIGN;
   const size_t T = (size_t)pr.total;

@@ -34,7 +34,12 @@ __device__ __forceinline__ void store_vec(T *p, const float (&v)[Vec16<T>::N]) {
   *reinterpret_cast<tv *>(p) = x;
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+// SiLU(x) = x / (1 + e^-x) from the hardware exp2 and reciprocal (each about
+// 1 ulp): e^-x = 2^(-x log2 e).  Large negative x gives x * rcp(inf) = -0,
+// large positive x gives x.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
 
 // Sequence holding token t: the last n with cu[n] <= t (cu nondecreasing,
 // t < cu[N]); empty sequences before it are skipped.
@@ -77,12 +82,24 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(ConvParams p) {
   const T *x = static_cast<const T *>(p.x);
   const T *s_in = static_cast<const T *>(p.s_in);
 
+  // the V x W weights and V biases of these channels are contiguous: read
+  // them as 16-byte vectors (c0 is a multiple of 4, so are V * W and V)
   float w[W][V], b[V];
+  {
+    const float4 *wp = reinterpret_cast<const float4 *>(p.w + (int64_t)c0 * W);
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
+    for (int q = 0; q < V * W / 4; ++q) {
+      const float4 f = wp[q];
+      const float e[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-    for (int j = 0; j < W; ++j) w[j][i] = p.w[(int64_t)(c0 + i) * W + j];
-    b[i] = p.bias ? p.bias[c0 + i] : 0.0f;
+      for (int r = 0; r < 4; ++r) w[(4 * q + r) % W][(4 * q + r) / W] = e[r];
+    }
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      const float4 f = p.bias ? reinterpret_cast<const float4 *>(p.bias + c0)[q]
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      b[4 * q] = f.x; b[4 * q + 1] = f.y; b[4 * q + 2] = f.z; b[4 * q + 3] = f.w;
+    }
   }
   // destination: the q, k or v part holding these channels
   T *dst;
@@ -113,20 +130,9 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(ConvParams p) {
         win[j][i] = s_in ? to_f32(s_in[((int64_t)n * p.C + c0 + i) * (W - 1) + h]) : 0.0f;
     }
   }
-  for (int64_t t = tb; t < te; ++t) {
-    if (t >= t1) {  // a new sequence starts here (skipping empty ones)
-      do {
-        ++n;
-        seq_bounds(p.cu, p.seq_len, n, t0, t1);
-      } while (t >= t1);
-#pragma unroll
-      for (int j = 0; j < W - 1; ++j)
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-          win[j][i] = s_in ? to_f32(s_in[((int64_t)n * p.C + c0 + i) * (W - 1) + (W - 2 - j)]) : 0.0f;
-    }
-    float xt[V], y[V];
-    load_vec(x + t * p.C + c0, xt);
+  // one output row from the input row xt; the window moves on by one
+  auto row = [&](int64_t t, const float (&xt)[V]) {
+    float y[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       float acc = b[i] + w[W - 1][i] * xt[i];
@@ -141,6 +147,36 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(ConvParams p) {
       for (int i = 0; i < V; ++i) win[j][i] = win[j - 1][i];
 #pragma unroll
     for (int i = 0; i < V; ++i) win[0][i] = xt[i];
+  };
+  // the tile in pieces that stay inside one sequence; within a piece the
+  // rows go in groups of U whose loads are all issued before any is used
+  constexpr int U = 4;
+  int64_t t = tb;
+  while (t < te) {
+    if (t >= t1) {  // a new sequence starts here (skipping empty ones)
+      do {
+        ++n;
+        seq_bounds(p.cu, p.seq_len, n, t0, t1);
+      } while (t >= t1);
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          win[j][i] = s_in ? to_f32(s_in[((int64_t)n * p.C + c0 + i) * (W - 1) + (W - 2 - j)]) : 0.0f;
+    }
+    const int64_t pe = te < t1 ? te : t1;  // end of this piece
+    for (; t + U <= pe; t += U) {
+      float xs[U][V];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_vec(x + (t + u) * p.C + c0, xs[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) row(t + u, xs[u]);
+    }
+    for (; t < pe; ++t) {
+      float xt[V];
+      load_vec(x + t * p.C + c0, xt);
+      row(t, xt);
+    }
   }
 }
 
@@ -209,32 +245,68 @@ struct NormParams {
 
 constexpr int NORM_THREADS = 256;
 
-// Each row of d elements is held by d / V consecutive lanes (a power of two
-// dividing the wave); their sums of squares meet by xor shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the tpr consecutive lanes holding one row (tpr a power of two, 2..32):
+// swaps inside quads, then the mirror of each half row and of each row of 16
+// lanes (every lane of the group already holds its group's sum), then the
+// other row of 16 for 32.
+__device__ __forceinline__ float row_sum(float s, int tpr) {
+  if (tpr >= 2) s = dpp_add<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+  if (tpr >= 4) s = dpp_add<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+  if (tpr >= 8) s = dpp_add<0x141>(s);  // row_half_mirror
+  if (tpr >= 16) s = dpp_add<0x140>(s); // row_mirror
+  if (tpr >= 32) s += __shfl_xor(s, 16);
+  return s;
+}
+
+// Each row of d elements is held by tpr = d / V consecutive lanes; a thread
+// holds its part of two rows, NORM_ROWS apart in the grid, so that four
+// 16-byte loads are in flight before the first use.
+constexpr int NORM_ROWS = 2;
 template <typename T>
 __global__ __launch_bounds__(NORM_THREADS) void gated_rmsnorm_kernel(NormParams p) {
   constexpr int V = Vec16<T>::N;
   const int tpr = p.d / V;
   const int64_t gid = (int64_t)blockIdx.x * NORM_THREADS + threadIdx.x;
-  const int64_t row = gid / tpr;
+  const int64_t half = (int64_t)gridDim.x * NORM_THREADS / tpr;  // rows per pass
   const int part = (int)(gid % tpr);
-  const bool live = row < p.rows;
-  const int64_t off = row * p.d + (int64_t)part * V;
-  float o[V], z[V];
-  float ss = 0.0f;
-  if (live) {
-    load_vec(static_cast<const T *>(p.o) + off, o);
-    load_vec(static_cast<const T *>(p.z) + off, z);
+  float wv[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) ss += o[i] * o[i];
+  for (int i = 0; i < V; ++i) wv[i] = p.w[part * V + i];
+  float o[NORM_ROWS][V], z[NORM_ROWS][V], ss[NORM_ROWS];
+  int64_t off[NORM_ROWS];
+  bool live[NORM_ROWS];
+#pragma unroll
+  for (int k = 0; k < NORM_ROWS; ++k) {
+    const int64_t row = gid / tpr + k * half;
+    live[k] = row < p.rows;
+    off[k] = row * p.d + (int64_t)part * V;
+    ss[k] = 0.0f;
+    if (live[k]) {
+      load_vec(static_cast<const T *>(p.o) + off[k], o[k]);
+      load_vec(static_cast<const T *>(p.z) + off[k], z[k]);
+    }
   }
-  for (int m = 1; m < tpr; m <<= 1) ss += __shfl_xor(ss, m);
-  if (!live) return;
-  const float r = rsqrtf(ss / (float)p.d + p.eps);
-  float y[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) y[i] = o[i] * r * p.w[part * V + i] * silu(z[i]);
-  store_vec(static_cast<T *>(p.out) + off, y);
+  for (int k = 0; k < NORM_ROWS; ++k) {
+    if (live[k]) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) ss[k] += o[k][i] * o[k][i];
+    }
+    ss[k] = row_sum(ss[k], tpr);
+  }
+#pragma unroll
+  for (int k = 0; k < NORM_ROWS; ++k) {
+    if (!live[k]) continue;
+    const float r = rsqrtf(ss[k] / (float)p.d + p.eps);
+    float y[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = o[k][i] * r * wv[i] * silu(z[k][i]);
+    store_vec(static_cast<T *>(p.out) + off[k], y);
+  }
 }
 
 }  // namespace
@@ -272,7 +344,8 @@ hipError_t launch_gated_rmsnorm(const Problem &pr, const NormArgs &a, hipStream_
   p.eps = a.eps;
   if (p.rows == 0) return hipSuccess;
   const int V = pr.dtype == GDR_F32 ? 4 : 8;
-  const int64_t threads = p.rows * (p.d / V);
+  // NORM_ROWS passes over the rows: each thread takes one row part per pass
+  const int64_t threads = (p.rows + NORM_ROWS - 1) / NORM_ROWS * (p.d / V);
   const dim3 grid((unsigned)((threads + NORM_THREADS - 1) / NORM_THREADS));
   if (pr.dtype == GDR_F32)
     hipLaunchKernelGGL(gated_rmsnorm_kernel<float>, grid, dim3(NORM_THREADS), 0, s, p);

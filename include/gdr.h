@@ -172,8 +172,8 @@ GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const 
  * width-1 inputs of every sequence (older history moving up when a sequence is
  * shorter than width-1); a decode step is a call with seq_len = 1.
  *   x              : dtype [total, C]                      (16-byte aligned)
- *   weight         : fp32  [C, width], 2 <= width <= 4
- *   bias           : fp32  [C], or NULL for none
+ *   weight         : fp32  [C, width], 2 <= width <= 4      (16-byte aligned)
+ *   bias           : fp32  [C], or NULL for none            (16-byte aligned)
  *   conv_state_in  : dtype [num_seqs, C, width-1], or NULL for zeros
  *   q, k           : dtype [total, H_k, d_k]                (16-byte aligned)
  *   v              : dtype [total, H_v, d_v]                (16-byte aligned)

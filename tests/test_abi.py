@@ -218,7 +218,8 @@ def test_conv_silu_validation(gdr):
     assert conv_call(gdr, shape(gdr), x=None) == 1
     assert conv_call(gdr, shape(gdr), v=None) == 1
     assert conv_call(gdr, shape(gdr), x=fake(0, off=8)) == 4          # rows need 16 bytes
-    assert conv_call(gdr, shape(gdr), weight=fake(1, off=2)) == 4     # fp32 needs 4 bytes
+    assert conv_call(gdr, shape(gdr), weight=fake(1, off=4)) == 4     # weights move in 16 bytes
+    assert conv_call(gdr, shape(gdr), bias=fake(2, off=8)) == 4
     assert conv_call(gdr, shape(gdr, dtype=1), s_in=fake(3, off=1)) == 4
     assert conv_call(gdr, shape(gdr), q=fake(0)) == 6                 # q over x
     assert conv_call(gdr, shape(gdr), k=fake(4, off=64)) == 6         # k inside q

@@ -3,10 +3,12 @@ gdr_gated_rmsnorm, through the C ABI) against the fp64 oracle in
 ``oracle.layer``.
 
 Tolerances: the oracle receives the inputs exactly and the kernels compute in
-fp32, so the error is the fp32 arithmetic (a few ulp) plus the rounding of the
-output to its dtype, at most 2^-9 of |y| for bf16.  Bars, as max |x - y| over
-max |y| per sequence (conv) or over the whole output (norm): 1e-5 for fp32,
-4e-3 for bf16.  The returned conv history is a copy of input values, so it
+fp32 (SiLU from the hardware exp2 and reciprocal, about 1 ulp each), so the
+error is the fp32 arithmetic (a few ulp, under 1e-6 relative) plus the
+rounding of the output to its dtype: bf16 keeps 8 significant bits, so
+round-to-nearest is off by at most 2^-8 = 3.9e-3 of |y|.  Bars, as
+max |x - y| over max |y| per sequence (conv) or over the whole output
+(norm): 1e-5 for fp32, 4.5e-3 for bf16.  The returned conv history is a copy of input values, so it
 must match bit for bit.
 
 Inputs: seeded numpy draws -- in_proj outputs and histories ~ N(0, 1),
@@ -24,7 +26,7 @@ from oracle import layer
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-TOL = {"f32": 1e-5, "bf16": 4e-3}
+TOL = {"f32": 1e-5, "bf16": 4.5e-3}
 TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
