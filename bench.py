@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s (T=8192, 48 heads) + decode HBM GB/s, % of roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
 
 
 def prefill_flops(T, H_k, H_v, d_k, d_v, C):
@@ -186,6 +187,7 @@ def main():
 
     # ------------------------------------ the layer's steps either side of the rule
     layer_line = layer_legs(gdr, dev, stream, max(1, min(args.steps, 10)))
+    split_line = split_legs(gdr, dev, stream, max(1, min(args.steps, 5)))
 
     # ------------------------------------------------------------ CPU baseline
     cpu = None
@@ -249,6 +251,7 @@ def main():
                                 "flop_per_launch": vflops,
                                 "hbm_GBs": vbytes / (vms / 1e3) / 1e9}},
         "layer": layer_line,
+        "split": split_line,
         "wall_s_prefill_timed": wall,
         "cpu_baseline": cpu,
     }
@@ -309,6 +312,53 @@ def layer_legs(gdr, dev, stream, steps):
                              norm_ms, norm_bytes, "gated_rmsnorm_kernel"),
     }
     del x, w, b, hist, hist_out, o, z, out
+    return res
+
+
+def split_legs(gdr, dev, stream, steps):
+    """The segmented chunked form (two-level scan) against the direct form on
+    long single-head prefill, where the direct form has one chain of chunks
+    per (head, 32 columns): the one-head workload (4096 tokens, d = 128,
+    fp32) and one bf16 head of 65536 tokens.  Work is counted as the direct
+    form's algorithmic matrix flops; the split form does about three times
+    that arithmetic."""
+    import torch
+    import synth
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize(dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(steps):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize(dev)
+        return e[0].elapsed_time(e[1]) / steps
+
+    res = {}
+    cases = [("one_head", synth.workload("one_head"), 256),
+             ("single_head_65536_bf16", synth.custom(1, 1, 128, 128, "bf16", seq_len=65536,
+                                                     num_seqs=1, chunk=32), 2048)]
+    for name, w, seg in cases:
+        inp = synth.make_inputs(w, 0, device=dev)
+        args = (inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                inp["initial_state"])
+        T = w.total_tokens
+        direct_ms = timed(lambda: gdr.chunked_fwd(*args, chunk=w.chunk, num_seqs=w.num_seqs))
+        split_ms = timed(lambda: gdr.chunked_fwd_split(*args, segment_len=seg, chunk=w.chunk,
+                                                       num_seqs=w.num_seqs))
+        flops = prefill_flops(T, w.H_k, w.H_v, w.d_k, w.d_v, w.chunk)
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        tf = flops / (split_ms / 1e3) / 1e12
+        res[name] = {"workload": f"1 sequence x {T} tokens, {w.H_v} head, d_k=d_v={w.d_k}, "
+                                 f"{w.dtype}, chunk {w.chunk}, {T // seg} segments of {seg}",
+                     "direct_ms": direct_ms, "split_ms": split_ms, "speedup": direct_ms / split_ms,
+                     "tokens_per_s": T / (split_ms / 1e3),
+                     "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": tf,
+                                  "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
+                                  "flop_per_launch": flops}}
+        del inp, args
     return res
 
 

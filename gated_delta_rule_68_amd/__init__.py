@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
   conv_silu(x, weight, H_k, H_v, d_k, d_v, bias=None, conv_state=None, ...)
             -> q, k, v, final_conv_state   (the layer's step before the rule)
   gated_rmsnorm(o, z, weight, eps=1e-6)  -> out   (the layer's step after it)
+  chunked_fwd_split(..., segment_len)    -> o, final_state   (segments of each
+            sequence in parallel: a two-level scan for long, few-head prefill)
 
 Layouts: q, k [total, H_k, d_k]; v [total, H_v, d_v]; a, b [total, H_v]
 (all fp32 or all bf16); A_log, dt_bias [H_v] fp32; states
@@ -34,7 +36,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["gates", "recurrent_fwd", "chunked_fwd", "fwd", "chunked_path", "conv_silu",
+__all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", "chunked_path", "conv_silu",
            "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +89,10 @@ def _bind(lib):
     lib.gdr_conv_silu.restype = ctypes.c_int
     lib.gdr_gated_rmsnorm.argtypes = [sp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.gdr_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdr_chunked_fwd_split.argtypes = [sp, ctypes.c_int32] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
+    lib.gdr_chunked_fwd_split.restype = ctypes.c_int
+    lib.gdr_chunked_split_workspace.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunked_split_workspace.restype = ctypes.c_int
     return lib
 
 
@@ -377,3 +383,59 @@ def gated_rmsnorm(o, z, weight, eps=1e-6, *, out=None):
                                  float(eps), _ptr(out), _stream(dev))
     _raise("gdr_gated_rmsnorm", rc)
     return out.view(shape4) if shape4 is not None else out
+
+
+def chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segment_len,
+                      chunk=32, num_seqs=None, scale=None, l2_eps=1e-6, o=None,
+                      final_state=None, output_final_state=True, inplace=False):
+    """Chunked form with every sequence cut into segments of ``segment_len``
+    tokens run in parallel (two-level scan).  Dense batches, d_k == d_v; the
+    workspace is allocated here with torch."""
+    dense_T = q.shape[1] if q.dim() == 4 else None
+    q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
+    a, b = _flatten(a, 1), _flatten(b, 1)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"gdr_chunked_fwd_split: tensors must be on a GPU (got {dev})")
+    dt = q.dtype
+    code = _dtype_code(dt)
+    total, H_k, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    _check(q, "q", dev, dt)
+    _check(k, "k", dev, dt, (total, H_k, d_k))
+    _check(v, "v", dev, dt, (total, H_v, d_v))
+    _check(a, "a", dev, dt, (total, H_v))
+    _check(b, "b", dev, dt, (total, H_v))
+    _check(A_log, "A_log", dev, torch.float32, (H_v,))
+    _check(dt_bias, "dt_bias", dev, torch.float32, (H_v,))
+    shape = _make_shape(total, H_k, H_v, d_k, d_v, None, num_seqs, code, chunk, scale, l2_eps,
+                        dense_T)
+    N = shape.num_seqs
+    st_shape = (N, H_v, d_k, d_v)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, st_shape)
+    if o is None:
+        o = torch.empty((total, H_v, d_v), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dev, dt, (total, H_v, d_v))
+    if inplace:
+        if initial_state is None:
+            raise ValueError("inplace=True needs an initial_state to update")
+        final_state = initial_state
+    elif final_state is None and output_final_state:
+        final_state = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", dev, torch.float32, st_shape)
+    nbytes = ctypes.c_size_t(0)
+    _raise("gdr_chunked_split_workspace",
+           lib().gdr_chunked_split_workspace(ctypes.byref(shape), int(segment_len), ctypes.byref(nbytes)))
+    ws = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
+    rc = lib().gdr_chunked_fwd_split(ctypes.byref(shape), int(segment_len), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                     _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                     _ptr(ws) if nbytes.value else None, int(nbytes.value),
+                                     _stream(dev))
+    _raise("gdr_chunked_fwd_split", rc)
+    if dense_T is not None:
+        o = o.view(N, dense_T, H_v, d_v)
+    return o, final_state

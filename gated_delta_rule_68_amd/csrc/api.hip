@@ -263,6 +263,73 @@ gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, const void *
   return launched(launch_gated_rmsnorm(pr, a, stream));
 }
 
+namespace gdr {
+namespace {
+// Segmented chunked form: shape rules, then the workspace layout.
+gdr_status split_problem(const gdr_shape *shape, int32_t segment_len, Problem &pr) {
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
+  if (pr.cu != nullptr || pr.d_k != pr.d_v) return GDR_ERR_UNSUPPORTED;
+  if (segment_len <= 0 || segment_len % pr.chunk != 0) return GDR_ERR_SHAPE;
+  if (pr.seq_len % segment_len != 0) return GDR_ERR_SHAPE;
+  if (!chunked_mfma_supports(pr) && !chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  if ((int64_t)pr.num_seqs * (pr.seq_len / segment_len) > 0x7fffffffLL / pr.H_v)
+    return GDR_ERR_UNSUPPORTED;
+  return GDR_OK;
+}
+}  // namespace
+}  // namespace gdr
+
+gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
+                                       size_t *bytes) {
+  using namespace gdr;
+  if (!bytes) return GDR_ERR_NULL;
+  Problem pr;
+  const gdr_status st = split_problem(shape, segment_len, pr);
+  if (st != GDR_OK) return st;
+  *bytes = pr.seq_len / segment_len > 1 ? split_layout(pr, segment_len).bytes : 0;
+  return GDR_OK;
+}
+
+gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, const void *q,
+                                 const void *k, const void *v, const void *a, const void *b,
+                                 const float *A_log, const float *dt_bias,
+                                 const float *initial_state, void *o, float *final_state,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = split_problem(shape, segment_len, pr);
+  if (st != GDR_OK) return st;
+  FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
+  st = check_fwd(pr, x);
+  if (st != GDR_OK) return st;
+  if (pr.seq_len / segment_len <= 1) {  // one segment: the direct form
+    if (chunked_mfma_supports(pr)) return launched(launch_chunked_mfma(pr, x, stream));
+    return launched(launch_chunked_vec(pr, x, stream));
+  }
+  const SplitLayout L = split_layout(pr, segment_len);
+  if (!workspace) return GDR_ERR_NULL;
+  if (workspace_bytes < L.bytes) return GDR_ERR_SHAPE;
+  if (!aligned_to(workspace, 256)) return GDR_ERR_ALIGN;
+  // the workspace may overlap nothing the call reads or writes
+  const size_t es = elem_size(pr.dtype);
+  const size_t T = (size_t)pr.total;
+  const size_t state_bytes = (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4;
+  const Range ws = span(workspace, L.bytes);
+  const Range others[] = {
+      span(q, T * pr.H_k * pr.d_k * es), span(k, T * pr.H_k * pr.d_k * es),
+      span(v, T * pr.H_v * pr.d_v * es), span(a, T * pr.H_v * es), span(b, T * pr.H_v * es),
+      span(A_log, (size_t)pr.H_v * 4), span(dt_bias, (size_t)pr.H_v * 4),
+      span(initial_state, initial_state ? state_bytes : 0), span(o, T * pr.H_v * pr.d_v * es),
+      span(final_state, final_state ? state_bytes : 0)};
+  for (const Range &r : others)
+    if (r.lo != 0 && r.hi > r.lo && overlap(r, ws)) return GDR_ERR_ALIAS;
+  // final_state == initial_state is fine: the initial state is read by the
+  // combine pass, before the last launch writes the final state
+  return launched(launch_chunked_split(pr, x, segment_len, workspace, stream));
+}
+
 int gdr_chunked_path(const gdr_shape *shape) {
   using namespace gdr;
   Problem pr;

@@ -56,6 +56,15 @@ struct NormArgs {
   void *out;  // may equal o or z
 };
 
+// Workspace of the segmented chunked form (byte offsets, 256-byte aligned).
+struct SplitLayout {
+  int P;  // segments per sequence
+  size_t zero_v, ident, M, Sloc, Sin, bytes;
+};
+SplitLayout split_layout(const Problem &p, int segment_len);
+hipError_t launch_chunked_split(const Problem &p, const FwdArgs &x, int segment_len,
+                                void *workspace, hipStream_t s);
+
 hipError_t launch_gates(const Problem &p, const GatesArgs &x, hipStream_t s);
 hipError_t launch_conv_silu(const Problem &p, const ConvArgs &x, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const Problem &p, const NormArgs &x, hipStream_t s);

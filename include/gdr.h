@@ -207,6 +207,42 @@ GDR_API gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, cons
                                      const float *weight, float eps, void *out,
                                      hipStream_t stream);
 
+/*
+ * gdr_chunked_fwd_split -- the chunked form with every sequence cut into
+ * segments of segment_len tokens that run in parallel: a two-level scan for
+ * long sequences with few heads, where one chain of chunks per (sequence,
+ * value head) would leave most of the GPU idle (Track L pull request, L2, the
+ * cooperative-parallel chunk kernel it lists as not yet built).  The state
+ * update is affine in the state, so over a segment S_out = M S_in + S_loc,
+ * with M the segment run from S_in = I on v = 0 and S_loc the run from
+ * S_in = 0.  The library computes every segment's M and S_loc with two
+ * chunked launches, the entry states S_in(p+1) = M_p S_in(p) + S_loc,p in a
+ * short sequential pass (fp32), and the outputs with a third chunked launch
+ * from those entry states: about three times the arithmetic of
+ * gdr_chunked_fwd in exchange for segments-per-sequence times the parallelism.
+ * Results agree with gdr_chunked_fwd up to float reassociation.
+ *   segment_len : a positive multiple of chunk that divides seq_len, else
+ *                 GDR_ERR_SHAPE; segment_len == seq_len runs gdr_chunked_fwd
+ *   workspace   : device scratch of at least the bytes gdr_chunked_split_workspace
+ *                 reports (256-byte aligned; may be NULL when that is 0); it
+ *                 may overlap no other argument; contents are not kept
+ * Dense batches (cu_seqlens == NULL) with d_k == d_v only, else
+ * GDR_ERR_UNSUPPORTED.  Other arguments as gdr_chunked_fwd (final_state may
+ * be initial_state).  Several kernels are launched; a launch failure after
+ * the first leaves o and final_state unspecified.
+ */
+GDR_API gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len,
+                                         const void *q, const void *k, const void *v,
+                                         const void *a, const void *b, const float *A_log,
+                                         const float *dt_bias, const float *initial_state,
+                                         void *o, float *final_state, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace gdr_chunked_fwd_split needs for `shape` and segment_len
+ * (0 when there is a single segment); the same shape errors as that call. */
+GDR_API gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
+                                               size_t *bytes);
+
 /* Which kernel gdr_chunked_fwd runs for `shape`: GDR_PATH_VECTOR_F32 (fp32
  * on the vector ALUs), GDR_PATH_MATRIX_BF16 (matrix cores, bf16 operands,
  * fp32 accumulation and state), or the negated gdr_status that

@@ -329,6 +329,31 @@ def pin_streaming_equals_recompute():
     assert np.array_equal(state, S), "C9: token-by-token final state differs"
 
 
+def pin_segment_transition_map(seeds=range(3)):
+    """The two-level scan's premise: over a segment the final state is affine
+    in the entry state, S_out = M S_in + S_loc, where M is the segment run
+    from S_in = I with v = 0 (d_k = d_v) and S_loc the run from S_in = 0
+    (each step is alpha (I - beta k k^T) S + beta k v^T).  Chaining the maps
+    of consecutive segments reproduces the one long run."""
+    for s in seeds:
+        p = rand_problem(800 + s, T=36, H_k=1, H_v=2, d_k=5, d_v=5)
+        _, S_full = run_oracle(p)
+        I = np.broadcast_to(np.eye(5), (1, 2, 5, 5)).copy()
+        state = p["initial_state"]
+        for t0, t1 in ((0, 12), (12, 24), (24, 36)):
+            seg = {k: (p[k][t0:t1] if k in ("q", "k", "v", "a", "b") else p[k]) for k in p}
+            _, M = oracle.fwd(seg["q"], seg["k"], np.zeros_like(seg["v"]), seg["a"], seg["b"],
+                              p["A_log"], p["dt_bias"], initial_state=I)
+            _, S_loc = oracle.fwd(seg["q"], seg["k"], seg["v"], seg["a"], seg["b"], p["A_log"],
+                                  p["dt_bias"], initial_state=None)
+            _, S_ref = oracle.fwd(seg["q"], seg["k"], seg["v"], seg["a"], seg["b"], p["A_log"],
+                                  p["dt_bias"], initial_state=state)
+            nxt = np.einsum("nhij,nhjk->nhik", M, state) + S_loc
+            close(nxt, S_ref, rtol=1e-10, atol=1e-12, what=f"segment map, seed {s}, [{t0},{t1})")
+            state = nxt
+        close(state, S_full, rtol=1e-10, atol=1e-12, what=f"chained segment maps, seed {s}")
+
+
 def pin_constant_state():
     """C10: the state does not grow with context (GatedDeltaRule.ixx File
     Reference): final-state shape is independent of T."""
@@ -351,5 +376,6 @@ ALL_PINS = [
     pin_wy_transition,
     pin_linearity_and_structure,
     pin_streaming_equals_recompute,
+    pin_segment_transition_map,
     pin_constant_state,
 ]

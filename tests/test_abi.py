@@ -30,7 +30,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_path",
+    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_split",
+                                  "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
                                   "gdr_recurrent_fwd", "gdr_status_string"]
 
@@ -247,3 +248,46 @@ def test_layer_binding_refuses_cpu_tensors(gdr):
     o = torch.zeros(4, 2, 16)
     with pytest.raises(ValueError):
         gdr.gated_rmsnorm(o, o, torch.zeros(16))
+
+
+# ------------------------------------------------------- segmented chunked form
+def split_call(gdr, s, seg, ws=None, ws_bytes=1 << 30, **over):
+    names = ["q", "k", "v", "a", "b", "A_log", "dt_bias", "s0", "o", "sT"]
+    p = {n: fake(i) for i, n in enumerate(names)}
+    p.update(over)
+    return gdr.lib().gdr_chunked_fwd_split(ctypes.byref(s), seg, *[p[n] for n in names],
+                                           fake(20) if ws is None else ws, ws_bytes, None)
+
+
+def workspace_bytes(gdr, s, seg):
+    n = ctypes.c_size_t(0)
+    rc = gdr.lib().gdr_chunked_split_workspace(ctypes.byref(s), seg, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_split_workspace_size(gdr):
+    # N = 2 sequences of 64 tokens, H_v = 2, d = 16, fp32, chunk 16, segments of 16: P = 4
+    s = shape(gdr, num_seqs=2, seq_len=64, total_tokens=128, chunk=16)
+    rc, n = workspace_bytes(gdr, s, 16)
+    assert rc == 0
+    r256 = lambda b: (b + 255) // 256 * 256
+    st = 2 * 4 * 2 * 16 * 16 * 4  # N * P * H_v * d_k * d_v * fp32
+    assert n == r256(128 * 2 * 16 * 4) + 4 * r256(st)  # zero v, then four state buffers
+    assert workspace_bytes(gdr, s, 64) == (0, 0)  # one segment: no workspace
+
+
+def test_split_validation(gdr):
+    s = shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16)
+    assert split_call(gdr, shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16, d_v=32), 16) == 3
+    cu = shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16)
+    cu.cu_seqlens = fake(30).value
+    assert split_call(gdr, cu, 16) == 3                      # packed batches: no
+    assert split_call(gdr, s, 0) == 2
+    assert split_call(gdr, s, 24) == 2                       # not a multiple of the chunk
+    assert split_call(gdr, s, 48) == 2                       # does not divide seq_len
+    assert split_call(gdr, s, 16, ws=ctypes.c_void_p(0)) == 1
+    _, need = workspace_bytes(gdr, s, 16)
+    assert split_call(gdr, s, 16, ws_bytes=need - 1) == 2
+    assert split_call(gdr, s, 16, ws=fake(20, off=128)) == 4
+    assert split_call(gdr, s, 16, ws=fake(8)) == 6           # over o
+    assert split_call(gdr, s, 16, o=fake(0)) == 6            # o over q, as gdr_chunked_fwd
