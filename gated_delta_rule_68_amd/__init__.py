@@ -37,7 +37,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", "chunked_path", "conv_silu",
-           "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version"]
+           "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version",
+           "ssd_recurrent_fwd", "ssd_chunked_fwd"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -93,6 +94,9 @@ def _bind(lib):
     lib.gdr_chunked_fwd_split.restype = ctypes.c_int
     lib.gdr_chunked_split_workspace.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunked_split_workspace.restype = ctypes.c_int
+    for name in ("gdr_ssd_recurrent_fwd", "gdr_ssd_chunked_fwd"):
+        getattr(lib, name).argtypes = [sp] + [vp] * 10
+        getattr(lib, name).restype = ctypes.c_int
     return lib
 
 
@@ -439,3 +443,69 @@ def chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segm
     if dense_T is not None:
         o = o.view(N, dense_T, H_v, d_v)
     return o, final_state
+
+
+def _ssd(fn_name, x, delta, A, B, C, initial_state, z, cu_seqlens, num_seqs, chunk, y,
+         final_state, output_final_state, inplace):
+    dense_T = x.shape[1] if x.dim() == 4 else None
+    x, B, C = _flatten(x, 2), _flatten(B, 2), _flatten(C, 2)
+    delta = _flatten(delta, 1)
+    z = None if z is None else _flatten(z, 2)
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError(f"{fn_name}: tensors must be on a GPU (got {dev})")
+    dt = x.dtype
+    code = _dtype_code(dt)
+    total, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    _check(x, "x", dev, dt)
+    _check(delta, "delta", dev, dt, (total, H))
+    _check(A, "A", dev, torch.float32, (H,))
+    _check(B, "B", dev, dt, (total, G, N))
+    _check(C, "C", dev, dt, (total, G, N))
+    if z is not None:
+        _check(z, "z", dev, dt, (total, H, P))
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    shape = _make_shape(total, G, H, N, P, cu_seqlens, num_seqs, code, chunk, 1.0, 0.0, dense_T)
+    S = shape.num_seqs
+    st_shape = (S, H, N, P)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, st_shape)
+    if y is None:
+        y = torch.empty((total, H, P), dtype=dt, device=dev)
+    else:
+        _check(y, "y", dev, dt, (total, H, P))
+    if inplace:
+        if initial_state is None:
+            raise ValueError("inplace=True needs an initial_state to update")
+        final_state = initial_state
+    elif final_state is None and output_final_state:
+        final_state = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", dev, torch.float32, st_shape)
+    rc = getattr(lib(), fn_name)(ctypes.byref(shape), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(initial_state), _ptr(z), _ptr(y),
+                                 _ptr(final_state), _stream(dev))
+    _raise(fn_name, rc)
+    if dense_T is not None:
+        y = y.view(S, dense_T, H, P)
+    return y, final_state
+
+
+def ssd_recurrent_fwd(x, delta, A, B, C, initial_state=None, *, z=None, cu_seqlens=None,
+                      num_seqs=None, y=None, final_state=None, output_final_state=True,
+                      inplace=False):
+    """Mamba-2 SSD recurrence, sequential form: x [total, H, P], delta
+    [total, H], A fp32 [H], B and C [total, G, N], states fp32 [S, H, N, P];
+    ``z`` gates y by SiLU(z)."""
+    return _ssd("gdr_ssd_recurrent_fwd", x, delta, A, B, C, initial_state, z, cu_seqlens,
+                num_seqs, 32, y, final_state, output_final_state, inplace)
+
+
+def ssd_chunked_fwd(x, delta, A, B, C, initial_state=None, *, z=None, chunk=32,
+                    cu_seqlens=None, num_seqs=None, y=None, final_state=None,
+                    output_final_state=True, inplace=False):
+    """Mamba-2 SSD recurrence, chunked form (same arguments plus ``chunk``)."""
+    return _ssd("gdr_ssd_chunked_fwd", x, delta, A, B, C, initial_state, z, cu_seqlens,
+                num_seqs, chunk, y, final_state, output_final_state, inplace)

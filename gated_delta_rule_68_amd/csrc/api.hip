@@ -330,6 +330,75 @@ gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, co
   return launched(launch_chunked_split(pr, x, segment_len, workspace, stream));
 }
 
+namespace gdr {
+namespace {
+// SSD: the rule's kernels in mode 1 (q = C, k = B, v = x, a = delta, A_log
+// holds A, no b and no dt_bias); z gates the output afterwards.
+gdr_status ssd_call(const gdr_shape *shape, bool chunked, const void *x, const void *delta,
+                    const float *A, const void *B, const void *C, const float *initial_state,
+                    const void *z, void *y, float *final_state, hipStream_t stream) {
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  pr.mode = 1;
+  pr.scale = 1.0f;
+  if (chunked && pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
+  if (!A) return GDR_ERR_NULL;
+  if (pr.total > 0 && (!x || !delta || !B || !C || !y)) return GDR_ERR_NULL;
+  const void *rows[] = {x, B, C, z, y, initial_state, final_state};
+  for (const void *p : rows)
+    if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+  const size_t es = elem_size(pr.dtype);
+  if (delta && !aligned_to(delta, es)) return GDR_ERR_ALIGN;
+  if (!aligned_to(A, 4) || (pr.cu && !aligned_to(pr.cu, 4))) return GDR_ERR_ALIGN;
+  const size_t T = (size_t)pr.total;
+  const size_t state_bytes = (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4;
+  const Range ins[] = {span(x, T * pr.H_v * pr.d_v * es), span(delta, T * pr.H_v * es),
+                       span(A, (size_t)pr.H_v * 4), span(B, T * pr.H_k * pr.d_k * es),
+                       span(C, T * pr.H_k * pr.d_k * es), span(z, z ? T * pr.H_v * pr.d_v * es : 0),
+                       span(pr.cu, pr.cu ? (size_t)(pr.num_seqs + 1) * 4 : 0)};
+  const Range ry = span(y, T * pr.H_v * pr.d_v * es);
+  const Range rT = span(final_state, final_state ? state_bytes : 0);
+  const Range r0 = span(initial_state, initial_state ? state_bytes : 0);
+  for (const Range &r : ins) {
+    if (r.lo == 0 || r.hi == r.lo) continue;
+    if (ry.hi > ry.lo && overlap(r, ry)) return GDR_ERR_ALIAS;
+    if (rT.hi > rT.lo && overlap(r, rT)) return GDR_ERR_ALIAS;
+  }
+  if (ry.hi > ry.lo && rT.hi > rT.lo && overlap(ry, rT)) return GDR_ERR_ALIAS;
+  if (ry.hi > ry.lo && r0.hi > r0.lo && overlap(ry, r0)) return GDR_ERR_ALIAS;
+  if (initial_state && final_state && initial_state != final_state && overlap(r0, rT))
+    return GDR_ERR_ALIAS;
+  FwdArgs a{C, B, x, delta, nullptr, A, nullptr, initial_state, y, final_state};
+  hipError_t e;
+  if (chunked) {
+    if (chunked_mfma_supports(pr)) e = launch_chunked_mfma(pr, a, stream);
+    else if (chunked_vec_supports(pr)) e = launch_chunked_vec(pr, a, stream);
+    else return GDR_ERR_UNSUPPORTED;
+  } else {
+    if (!recurrent_supports(pr)) return GDR_ERR_UNSUPPORTED;
+    e = launch_recurrent(pr, a, stream);
+  }
+  if (e == hipSuccess && z) e = launch_silu_gate(pr, y, z, stream);
+  return launched(e);
+}
+}  // namespace
+}  // namespace gdr
+
+gdr_status gdr_ssd_recurrent_fwd(const gdr_shape *shape, const void *x, const void *delta,
+                                 const float *A, const void *B, const void *C,
+                                 const float *initial_state, const void *z, void *y,
+                                 float *final_state, hipStream_t stream) {
+  return gdr::ssd_call(shape, false, x, delta, A, B, C, initial_state, z, y, final_state, stream);
+}
+
+gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, const void *delta,
+                               const float *A, const void *B, const void *C,
+                               const float *initial_state, const void *z, void *y,
+                               float *final_state, hipStream_t stream) {
+  return gdr::ssd_call(shape, true, x, delta, A, B, C, initial_state, z, y, final_state, stream);
+}
+
 int gdr_chunked_path(const gdr_shape *shape) {
   using namespace gdr;
   Problem pr;

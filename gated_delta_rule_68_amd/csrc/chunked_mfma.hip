@@ -67,7 +67,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
-constexpr int DV = 128;
+// d_v is a template parameter of the kernel (64 or 128)
 constexpr int CH = 32;      // tokens per chunk
 constexpr int NC = 2;       // consumer waves (16 columns each)
 constexpr int BV = 16 * NC;
@@ -345,7 +345,7 @@ __device__ __forceinline__ int v_off(int r, int c) {
 __device__ __forceinline__ int v_src_piece(int lane) { return (lane & 3) ^ (2 * ((lane >> 4) & 1)); }
 // Half (rows 16 h .. 16 h + 15) of the v tile: lane l takes row 16h + l/4.
 __device__ __forceinline__ void dma_v_half(const bf16 *v, int H_v, int hv, int col0, int64_t row0,
-                                           int cl, bf16 *tile, int half, int lane) {
+                                           int cl, bf16 *tile, int half, int lane, int DV) {
   const int r = 16 * half + (lane >> 2);
   const int rr = min(r, cl - 1);
   dma16(v + ((row0 + rr) * H_v + hv) * DV + col0 + 8 * v_src_piece(lane), tile + 512 * half);
@@ -427,15 +427,25 @@ __device__ __forceinline__ void stage_k_norms(Stage &S, int lane, int cl, float 
 
 // Gates of one chunk (staging wave 1, once its raw a and b have landed):
 // row r = lane % 32.
+// SSD (the Mamba-2 SSD recurrence on the same scan): a is delta, neg_exp_A is
+// A itself, g = A delta and beta = delta.
+template <bool SSD>
 __device__ __forceinline__ void stage_gates(Stage &S, int lane, int cl, float neg_exp_A,
                                             float dtb) {
   const int r = lane & 31;
   const bool valid = r < cl;
-  const float a_r = __uint_as_float(lds_read_u32_now(&S.ab[r]) << 16) + dtb;
-  const float b_r = __uint_as_float(lds_read_u32_now(&S.ab[CH + r]) << 16);
-  const float sp = fmaxf(a_r, 0.f) + fast_log(1.f + fast_exp(-fabsf(a_r)));
-  const float g = valid ? neg_exp_A * sp : 0.f;
-  const float bt = valid ? __builtin_amdgcn_rcpf(1.f + fast_exp(-b_r)) : 0.f;
+  float g, bt;
+  if constexpr (SSD) {
+    const float dl = __uint_as_float(lds_read_u32_now(&S.ab[r]) << 16);
+    g = valid ? neg_exp_A * dl : 0.f;
+    bt = valid ? dl : 0.f;
+  } else {
+    const float a_r = __uint_as_float(lds_read_u32_now(&S.ab[r]) << 16) + dtb;
+    const float b_r = __uint_as_float(lds_read_u32_now(&S.ab[CH + r]) << 16);
+    const float sp = fmaxf(a_r, 0.f) + fast_log(1.f + fast_exp(-fabsf(a_r)));
+    g = valid ? neg_exp_A * sp : 0.f;
+    bt = valid ? __builtin_amdgcn_rcpf(1.f + fast_exp(-b_r)) : 0.f;
+  }
   const float cum = scan32(g);
   const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 31));
   if (lane < 32) {
@@ -555,6 +565,7 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const 
 // P1: scale/|q_r| from the Gram diagonal of q, and the output mask without the
 // row norms, P[r][i] = exp(gam_r - gam_i) (q_r . k_i) for i <= r, of one chunk
 // (scale/|q_r| and 1/|k_i| are applied by the output waves).
+template <bool SSD>
 __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const RowOps &o,
                                            int lane) {
   const int m = lane & 15, g = lane >> 4;
@@ -568,15 +579,18 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const 
     p00 = mma32(o.k0[kb], o.q0[kb], p00);
     p10 = mma32(o.k0[kb], o.q1[kb], p10);
     p11 = mma32(o.k1[kb], o.q1[kb], p11);
-    qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
-    qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
+    if constexpr (!SSD) {
+      qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
+      qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
+    }
   }
   // scale/|q_r| from the diagonal: lane (m, g = m/4) holds |q_m|^2 in register m%4
+  // (SSD: q is not normalised, the scale is 1)
   if (g == (m >> 2)) {
     const int cl = S.cl;
     const int j = m & 3;
-    S.iq[m] = (m < cl) ? rsqrtf(qq0[j] + p.eps) * p.scale : 0.f;
-    S.iq[16 + m] = (16 + m < cl) ? rsqrtf(qq1[j] + p.eps) * p.scale : 0.f;
+    S.iq[m] = (m < cl) ? (SSD ? 1.0f : rsqrtf(qq0[j] + p.eps) * p.scale) : 0.f;
+    S.iq[16 + m] = (16 + m < cl) ? (SSD ? 1.0f : rsqrtf(qq1[j] + p.eps) * p.scale) : 0.f;
   }
   f32x4 v00, v10, v11;
 #pragma unroll
@@ -591,7 +605,12 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const 
   S.P[1][lane] = pack8(v10, v11);
 }
 
+// DVT: d_v (64 or 128; d_k is 128).  SSD: the Mamba-2 SSD recurrence on the
+// same scan -- no norms, no erase (T = I, Delta = diag(beta) V with no K S),
+// g = A delta, beta = delta; the prepare wave P0 is idle.
+template <int DVT, bool SSD>
 __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p) {
+  constexpr int DV = DVT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
   constexpr int NVB = DV / BV;
@@ -687,10 +706,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         const float gc = st.Gc;
         // ks[mt]: (K S)[16mt + 4g + j][m]
         f32x4 ks[2] = {z, z};
+        if constexpr (!SSD) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+          for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) ks[mt] = mma32(Kr[mt][kb], Sb[kb], ks[mt]);
+            for (int mt = 0; mt < 2; ++mt) ks[mt] = mma32(Kr[mt][kb], Sb[kb], ks[mt]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         read_kt(st);
@@ -702,9 +723,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           R0[j] = bt0[j] * ((float)vv[j] - gm0[j] * ik0[j] * ks[0][j]);
           R1[j] = bt1[j] * ((float)vv[4 + j] - gm1[j] * ik1[j] * ks[1][j]);
         }
-        // Delta_1 = T11 R1, Delta_2 = T22 (R2 - A21 Delta_1)
-        const f32x4 d1 = mma16(t11, pk4(R0), z);
-        const f32x4 d2 = mma16(t22, pk4(mma16(na21, pk4(d1), R1)), z);
+        // Delta_1 = T11 R1, Delta_2 = T22 (R2 - A21 Delta_1); SSD: no erase, Delta = R
+        f32x4 d1 = R0, d2 = R1;
+        if constexpr (!SSD) {
+          d1 = mma16(t11, pk4(R0), z);
+          d2 = mma16(t22, pk4(mma16(na21, pk4(d1), R1)), z);
+        }
         // diag(ik) Delta for the outputs of this chunk
         sm.db[c & 1][cw][lane] = pack8(ik0 * d1, ik1 * d2);
         // S <- Gam_last S + K^T diag(tail ik) Delta
@@ -723,7 +747,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         // index clamped into the sequence) so that the loads write the loop's
         // registers directly and stay in flight across the barrier
         const Stage &sr = sm.st[max(min(c + 1, nch - 1), 0) % NSTAGE];
-        read_rows(sr);
+        if constexpr (!SSD) read_rows(sr);
         read_v(sr);
       }
       // no wait for the reads in flight: their buffers are refilled only
@@ -788,18 +812,21 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     block_sync();
     for (int it = 0; it < nsteps; ++it) {
       const int c = it - 1;
+      // (SSD: no erase, so P0 has nothing to prepare and only keeps the barriers)
       if (c >= 0 && c < nch) {
-        if (wave == W_P0)
-          prepare_p0(p, sm.st[c % NSTAGE], ops, lane);
-        else
-          prepare_p1(p, sm.st[c % NSTAGE], ops, lane);
+        if (wave == W_P0) {
+          if constexpr (!SSD) prepare_p0(p, sm.st[c % NSTAGE], ops, lane);
+        } else {
+          prepare_p1<SSD>(p, sm.st[c % NSTAGE], ops, lane);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS writes are done
       if (it < nch) {
-        if (wave == W_P0)
-          read_row_ops<false>(sm.st[it % NSTAGE], ops, m, g);
-        else
+        if (wave == W_P0) {
+          if constexpr (!SSD) read_row_ops<false>(sm.st[it % NSTAGE], ops, m, g);
+        } else {
           read_row_ops<true>(sm.st[it % NSTAGE], ops, m, g);
+        }
       }
       block_sync<63, false>();
     }
@@ -840,13 +867,18 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           dma16(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(p.v + (row0 * p.H_v + h) * DV) + voff), S.V);
         } else {
           dma_rows(p.k, p.H_k, hk, row0, cl, S.K, lane);
-          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 0, lane);
+          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 0, lane, DV);
         }
       };
       // 1/|k| of chunk c once its rows have landed (c < nch)
       auto norms = [&](int c) {
         const int64_t rem = L - (int64_t)c * CH;
-        stage_k_norms(sm.st[c % NSTAGE], lane, rem < CH ? (int)rem : CH, p.eps);
+        const int cl = rem < CH ? (int)rem : CH;
+        if constexpr (SSD) {  // keys are not normalised
+          if (lane < CH) sm.st[c % NSTAGE].ik[lane] = lane < cl ? 1.0f : 0.0f;
+        } else {
+          stage_k_norms(sm.st[c % NSTAGE], lane, cl, p.eps);
+        }
       };
       for (int c = 0; c < AHEAD; ++c) request(c);
       vm_wait<ST0_OPS * (AHEAD - 1)>();  // chunk 0 has landed
@@ -870,16 +902,16 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           dma16(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(p.v + (row0 * p.H_v + h) * DV) + voff), S.V + 512);
         } else {
           dma_rows(p.q, p.H_k, hk, row0, cl, S.Q, lane);
-          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 1, lane);
+          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 1, lane, DV);
         }
-        dma_ab(p.a, p.b, p.H_v, h, row0, cl, S.ab, lane);
+        dma_ab(p.a, SSD ? p.a : p.b, p.H_v, h, row0, cl, S.ab, lane);  // SSD: no b
       };
-      const float neg_exp_A = -expf(p.A_log[h]);
-      const float dtb = p.dt_bias[h];
+      const float neg_exp_A = SSD ? p.A_log[h] : -expf(p.A_log[h]);  // SSD: A itself
+      const float dtb = SSD ? 0.0f : p.dt_bias[h];
       // gates of chunk c once its raw a, b have landed (c < nch)
       auto gates = [&](int c) {
         const int64_t rem = L - (int64_t)c * CH;
-        stage_gates(sm.st[c % NSTAGE], lane, rem < CH ? (int)rem : CH, neg_exp_A, dtb);
+        stage_gates<SSD>(sm.st[c % NSTAGE], lane, rem < CH ? (int)rem : CH, neg_exp_A, dtb);
       };
       for (int c = 0; c < AHEAD; ++c) request(c);
       vm_wait<ST1_OPS * (AHEAD - 1)>();  // chunk 0 has landed
@@ -896,6 +928,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
   }
 }
 
+template <int DVT, bool SSD>
 hipError_t launch_kernel(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   MfmaParams p;
   p.q = static_cast<const bf16 *>(x.q);
@@ -915,24 +948,27 @@ hipError_t launch_kernel(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   p.H_v = pr.H_v;
   p.scale = pr.scale;
   p.eps = pr.eps;
-  const int64_t grid = (int64_t)pr.num_seqs * pr.H_v * (DV / BV);
+  const int64_t grid = (int64_t)pr.num_seqs * pr.H_v * (DVT / BV);
   if (grid == 0) return hipSuccess;
   const size_t smem = sizeof(Smem);
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(chunked_mfma_kernel),
+  auto kern = chunked_mfma_kernel<DVT, SSD>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(chunked_mfma_kernel, dim3((unsigned)grid), dim3(64 * NWAVES), smem, s, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWAVES), smem, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool chunked_mfma_supports(const Problem &p) {
-  return p.dtype == GDR_BF16 && p.d_k == DK && p.d_v == DV && p.chunk == CH;
+  return p.dtype == GDR_BF16 && p.d_k == DK && (p.d_v == 64 || p.d_v == 128) && p.chunk == CH;
 }
 
 hipError_t launch_chunked_mfma(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  return launch_kernel(pr, x, s);
+  if (pr.mode == 1)
+    return pr.d_v == 64 ? launch_kernel<64, true>(pr, x, s) : launch_kernel<128, true>(pr, x, s);
+  return pr.d_v == 64 ? launch_kernel<64, false>(pr, x, s) : launch_kernel<128, false>(pr, x, s);
 }
 
 }  // namespace gdr

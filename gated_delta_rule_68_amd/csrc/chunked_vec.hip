@@ -69,7 +69,10 @@ struct VecSmem {
   float tail[C];  // exp(gamma_{c-1} - gamma_r)
 };
 
-template <int DK, int C, typename T>
+// SSD: the Mamba-2 SSD recurrence on the same chunk scan (Problem::mode 1):
+// no norms, no erase (A = 0, so T = I and Delta = diag(beta) V without K S),
+// g = A delta with delta in `a` and A in `A_log`, beta = delta.
+template <int DK, int C, typename T, bool SSD>
 __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   VecSmem<DK, C> &sm = *reinterpret_cast<VecSmem<DK, C> *>(smem_raw);
@@ -90,8 +93,8 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
     const int d = e / kBV, j = e % kBV;
     sm.S[d][j] = p.s0 ? p.s0[state_off + (size_t)d * DV + j] : 0.0f;
   }
-  const float neg_exp_A = -expf(p.A_log[h]);
-  const float dtb = p.dt_bias[h];
+  const float neg_exp_A = SSD ? p.A_log[h] : -expf(p.A_log[h]);  // SSD: A itself
+  const float dtb = SSD ? 0.0f : p.dt_bias[h];
 
   for (int64_t c0 = t0; c0 < t1; c0 += C) {
     const int cl = (int)((t1 - c0) < C ? (t1 - c0) : C);
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
         ss += x[e] * x[e];
       }
       ss = wave_sum(ss);
-      const float inv = (r < cl) ? rsqrtf(ss + p.eps) * (is_q ? p.scale : 1.0f) : 0.f;
+      const float inv = (r < cl) ? (SSD ? 1.0f : rsqrtf(ss + p.eps) * (is_q ? p.scale : 1.0f)) : 0.f;
       float *dst = is_q ? sm.Q[r] : sm.K[r];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -125,8 +128,14 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
       const int r = tid;
       float g = 0.f, bt = 0.f;
       if (r < cl) {
-        g = log_decay(neg_exp_A, to_f32(p.a[(c0 + r) * p.H_v + h]), dtb);
-        bt = sigmoid_f32(to_f32(p.b[(c0 + r) * p.H_v + h]));
+        const float a_r = to_f32(p.a[(c0 + r) * p.H_v + h]);
+        if constexpr (SSD) {
+          g = neg_exp_A * a_r;
+          bt = a_r;
+        } else {
+          g = log_decay(neg_exp_A, a_r, dtb);
+          bt = sigmoid_f32(to_f32(p.b[(c0 + r) * p.H_v + h]));
+        }
       }
       sm.gam[r] = g;
       sm.beta[r] = bt;
@@ -152,12 +161,12 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
         float kk = 0.f, qk = 0.f;
 #pragma unroll 8
         for (int d = 0; d < DK; ++d) {
-          kk += sm.K[r][d] * sm.K[i][d];
+          if constexpr (!SSD) kk += sm.K[r][d] * sm.K[i][d];
           qk += sm.Q[r][d] * sm.K[i][d];
         }
         const float dec = expf(sm.gam[r] - sm.gam[i]);
         p_ri = dec * qk;
-        if (i < r) a_ri = sm.beta[r] * dec * kk;
+        if (!SSD && i < r) a_ri = sm.beta[r] * dec * kk;
       }
       sm.A[r][i] = a_ri;
       sm.P[r][i] = p_ri;
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
       float ks = 0.f, qs = 0.f;
 #pragma unroll 8
       for (int d = 0; d < DK; ++d) {
-        ks += sm.K[r][d] * sm.S[d][j];
+        if constexpr (!SSD) ks += sm.K[r][d] * sm.S[d][j];
         qs += sm.Q[r][d] * sm.S[d][j];
       }
       sm.KS[r][j] = ks;
@@ -175,7 +184,15 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
     }
     __syncthreads();
     // -- stage 3: T = (I + A)^-1, one column per thread; R = beta (V - Gamma K S)
-    if (tid < C) {
+    //    (SSD: no erase, Delta = beta V straight away)
+    if constexpr (SSD) {
+      for (int e = tid; e < C * kBV; e += kVecThreads) {
+        const int r = e / kBV, j = e % kBV;
+        sm.D[r][j] = sm.beta[r] * sm.V[r][j];
+      }
+      __syncthreads();
+    }
+    if (!SSD && tid < C) {
       const int j = tid;
       float x[C];
 #pragma unroll
@@ -188,19 +205,21 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
 #pragma unroll
       for (int r = 0; r < C; ++r) sm.Tm[r][j] = x[r];
     }
-    for (int e = tid; e < C * kBV; e += kVecThreads) {
-      const int r = e / kBV, j = e % kBV;
-      sm.R[r][j] = sm.beta[r] * (sm.V[r][j] - sm.eg[r] * sm.KS[r][j]);
+    if constexpr (!SSD) {
+      for (int e = tid; e < C * kBV; e += kVecThreads) {
+        const int r = e / kBV, j = e % kBV;
+        sm.R[r][j] = sm.beta[r] * (sm.V[r][j] - sm.eg[r] * sm.KS[r][j]);
+      }
+      __syncthreads();
+      // -- stage 4: Delta = T R
+      for (int e = tid; e < C * kBV; e += kVecThreads) {
+        const int r = e / kBV, j = e % kBV;
+        float s = 0.f;
+        for (int i = 0; i <= r; ++i) s += sm.Tm[r][i] * sm.R[i][j];
+        sm.D[r][j] = s;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    // -- stage 4: Delta = T R
-    for (int e = tid; e < C * kBV; e += kVecThreads) {
-      const int r = e / kBV, j = e % kBV;
-      float s = 0.f;
-      for (int i = 0; i <= r; ++i) s += sm.Tm[r][i] * sm.R[i][j];
-      sm.D[r][j] = s;
-    }
-    __syncthreads();
     // -- stage 5: O = Gamma Q S + P Delta; S' = Gamma_c S + (tail K)^T Delta
     for (int e = tid; e < C * kBV; e += kVecThreads) {
       const int r = e / kBV, j = e % kBV;
@@ -228,7 +247,7 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
   }
 }
 
-template <int DK, int C, typename T>
+template <int DK, int C, typename T, bool SSD>
 hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   VecParams<T> p;
   p.q = static_cast<const T *>(x.q);
@@ -251,7 +270,7 @@ hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   const int64_t grid = (int64_t)pr.num_seqs * pr.H_v * (pr.d_v / kBV);
   if (grid == 0) return hipSuccess;
   const size_t smem = sizeof(VecSmem<DK, C>);
-  auto kern = chunked_vec_kernel<DK, C, T>;
+  auto kern = chunked_vec_kernel<DK, C, T, SSD>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
@@ -259,23 +278,23 @@ hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DK, typename T>
+template <int DK, typename T, bool SSD>
 hipError_t launch_c(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.chunk) {
-    case 16: return launch_typed<DK, 16, T>(pr, x, s);
-    case 32: return launch_typed<DK, 32, T>(pr, x, s);
-    case 64: return launch_typed<DK, 64, T>(pr, x, s);
+    case 16: return launch_typed<DK, 16, T, SSD>(pr, x, s);
+    case 32: return launch_typed<DK, 32, T, SSD>(pr, x, s);
+    case 64: return launch_typed<DK, 64, T, SSD>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, bool SSD>
 hipError_t launch_dk(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.d_k) {
-    case 16: return launch_c<16, T>(pr, x, s);
-    case 32: return launch_c<32, T>(pr, x, s);
-    case 64: return launch_c<64, T>(pr, x, s);
-    case 128: return launch_c<128, T>(pr, x, s);
+    case 16: return launch_c<16, T, SSD>(pr, x, s);
+    case 32: return launch_c<32, T, SSD>(pr, x, s);
+    case 64: return launch_c<64, T, SSD>(pr, x, s);
+    case 128: return launch_c<128, T, SSD>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -288,7 +307,9 @@ bool chunked_vec_supports(const Problem &p) {
 }
 
 hipError_t launch_chunked_vec(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  return pr.dtype == GDR_F32 ? launch_dk<float>(pr, x, s) : launch_dk<bf16>(pr, x, s);
+  if (pr.mode == 1)
+    return pr.dtype == GDR_F32 ? launch_dk<float, true>(pr, x, s) : launch_dk<bf16, true>(pr, x, s);
+  return pr.dtype == GDR_F32 ? launch_dk<float, false>(pr, x, s) : launch_dk<bf16, false>(pr, x, s);
 }
 
 }  // namespace gdr

@@ -20,6 +20,10 @@ struct Problem {
   int chunk;
   float scale;             // resolved: never <= 0
   float eps;
+  // 0: the gated delta rule.  1: the Mamba-2 SSD recurrence on the same
+  // kernels: no L2 norm (scale 1), no erase, g = A delta and beta = delta,
+  // with `a` carrying delta, `A_log` carrying A itself and b, dt_bias unused.
+  int mode = 0;
 };
 
 // Pointers of one forward call (types erased; dtype in Problem).
@@ -68,6 +72,8 @@ hipError_t launch_chunked_split(const Problem &p, const FwdArgs &x, int segment_
 hipError_t launch_gates(const Problem &p, const GatesArgs &x, hipStream_t s);
 hipError_t launch_conv_silu(const Problem &p, const ConvArgs &x, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const Problem &p, const NormArgs &x, hipStream_t s);
+// y <- y * SiLU(z) over [total, H_v, d_v] (the SSD's optional gate).
+hipError_t launch_silu_gate(const Problem &p, void *y, const void *z, hipStream_t s);
 hipError_t launch_recurrent(const Problem &p, const FwdArgs &x, hipStream_t s);
 hipError_t launch_chunked_vec(const Problem &p, const FwdArgs &x, hipStream_t s);
 hipError_t launch_chunked_mfma(const Problem &p, const FwdArgs &x, hipStream_t s);

@@ -309,7 +309,37 @@ __global__ __launch_bounds__(NORM_THREADS) void gated_rmsnorm_kernel(NormParams 
   }
 }
 
+// y <- y * SiLU(z), elementwise over n 16-byte vectors.
+template <typename T>
+__global__ __launch_bounds__(NORM_THREADS) void silu_gate_kernel(T *y, const T *z, int64_t nvec) {
+  constexpr int V = Vec16<T>::N;
+  for (int64_t i = (int64_t)blockIdx.x * NORM_THREADS + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * NORM_THREADS) {
+    float a[V], g[V];
+    load_vec(y + i * V, a);
+    load_vec(z + i * V, g);
+#pragma unroll
+    for (int k = 0; k < V; ++k) a[k] *= silu(g[k]);
+    store_vec(y + i * V, a);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_silu_gate(const Problem &pr, void *y, const void *z, hipStream_t s) {
+  const int V = pr.dtype == GDR_F32 ? 4 : 8;
+  const int64_t nvec = pr.total * pr.H_v * pr.d_v / V;
+  if (nvec == 0) return hipSuccess;
+  int64_t blocks = (nvec + NORM_THREADS - 1) / NORM_THREADS;
+  if (blocks > 8192) blocks = 8192;
+  if (pr.dtype == GDR_F32)
+    hipLaunchKernelGGL(silu_gate_kernel<float>, dim3((unsigned)blocks), dim3(NORM_THREADS), 0, s,
+                       static_cast<float *>(y), static_cast<const float *>(z), nvec);
+  else
+    hipLaunchKernelGGL(silu_gate_kernel<bf16>, dim3((unsigned)blocks), dim3(NORM_THREADS), 0, s,
+                       static_cast<bf16 *>(y), static_cast<const bf16 *>(z), nvec);
+  return hipGetLastError();
+}
 
 hipError_t launch_conv_silu(const Problem &pr, const ConvArgs &a, hipStream_t s) {
   ConvParams p;

@@ -67,7 +67,9 @@ struct RecParams {
   float scale, eps;
 };
 
-template <int DK, int DV, typename T>
+// SSD: the Mamba-2 SSD recurrence on the same scan (Problem::mode 1): no
+// norms, no erase, g = A delta with delta in `a` and A in `A_log`, beta = delta.
+template <int DK, int DV, typename T, bool SSD>
 // (at most 128 registers per lane: two 8-wave workgroups per compute unit)
 __global__ __launch_bounds__((RecGeom<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4)))
 void recurrent_kernel(RecParams<T> p) {
@@ -104,8 +106,8 @@ void recurrent_kernel(RecParams<T> p) {
     const int hk = h / (p.H_v / p.H_k);
     int64_t t0, t1;
     seq_bounds(p.cu, p.seq_len, n, t0, t1);
-    const float neg_exp_A = -expf(p.A_log[h]);
-    const float dtb = p.dt_bias[h];
+    const float neg_exp_A = SSD ? p.A_log[h] : -expf(p.A_log[h]);  // SSD: A itself
+    const float dtb = SSD ? 0.0f : p.dt_bias[h];
 
     for (int64_t t = t0; t < t1; ++t, ++step) {
       const T *kr = p.k + (t * p.H_k + hk) * DK;
@@ -118,7 +120,7 @@ void recurrent_kernel(RecParams<T> p) {
       }
       const float4 vv = load4(p.v + (t * p.H_v + h) * DV + 4 * cg);
       const float a_t = to_f32(p.a[t * p.H_v + h]);
-      const float b_t = to_f32(p.b[t * p.H_v + h]);
+      const float b_t = SSD ? 0.0f : to_f32(p.b[t * p.H_v + h]);
 
       float r[NRED];
 #pragma unroll
@@ -158,13 +160,13 @@ void recurrent_kernel(RecParams<T> p) {
           r[j] = sum;
         }
       }
-      const float ik = rsqrtf(r[8] + p.eps);
-      const float iq = rsqrtf(r[9] + p.eps) * p.scale;
+      const float ik = SSD ? 1.0f : rsqrtf(r[8] + p.eps);
+      const float iq = SSD ? 1.0f : rsqrtf(r[9] + p.eps) * p.scale;
       const float qk = r[10] * ik * iq;
-      const float g = log_decay(neg_exp_A, a_t, dtb);
+      const float g = SSD ? neg_exp_A * a_t : log_decay(neg_exp_A, a_t, dtb);
       const float alpha = expf(g);
-      const float beta = sigmoid_f32(b_t);
-      const float au = alpha * ik;
+      const float beta = SSD ? a_t : sigmoid_f32(b_t);
+      const float au = SSD ? 0.0f : alpha * ik;  // SSD: no erase
       float4 d;
       d.x = beta * (vv.x - au * r[0]);
       d.y = beta * (vv.y - au * r[1]);
@@ -212,7 +214,7 @@ int cu_count() {
   return cache[dev];
 }
 
-template <int DK, int DV, typename T>
+template <int DK, int DV, typename T, bool SSD>
 hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   RecParams<T> p;
   p.q = static_cast<const T *>(x.q);
@@ -238,29 +240,29 @@ hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   // persistent grid: about 16 waves per compute unit
   const int per_cu = RecGeom<DK, DV>::NW >= 8 ? 2 : 16 / RecGeom<DK, DV>::NW;
   const int64_t grid = units < (int64_t)cu_count() * per_cu ? units : (int64_t)cu_count() * per_cu;
-  hipLaunchKernelGGL((recurrent_kernel<DK, DV, T>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((recurrent_kernel<DK, DV, T, SSD>), dim3((unsigned)grid),
                      dim3(RecGeom<DK, DV>::NT), 0, s, p);
   return hipGetLastError();
 }
 
-template <int DK, typename T>
+template <int DK, typename T, bool SSD>
 hipError_t launch_dv(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.d_v) {
-    case 16: return launch_typed<DK, 16, T>(pr, x, s);
-    case 32: return launch_typed<DK, 32, T>(pr, x, s);
-    case 64: return launch_typed<DK, 64, T>(pr, x, s);
-    case 128: return launch_typed<DK, 128, T>(pr, x, s);
+    case 16: return launch_typed<DK, 16, T, SSD>(pr, x, s);
+    case 32: return launch_typed<DK, 32, T, SSD>(pr, x, s);
+    case 64: return launch_typed<DK, 64, T, SSD>(pr, x, s);
+    case 128: return launch_typed<DK, 128, T, SSD>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, bool SSD>
 hipError_t launch_dk(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.d_k) {
-    case 16: return launch_dv<16, T>(pr, x, s);
-    case 32: return launch_dv<32, T>(pr, x, s);
-    case 64: return launch_dv<64, T>(pr, x, s);
-    case 128: return launch_dv<128, T>(pr, x, s);
+    case 16: return launch_dv<16, T, SSD>(pr, x, s);
+    case 32: return launch_dv<32, T, SSD>(pr, x, s);
+    case 64: return launch_dv<64, T, SSD>(pr, x, s);
+    case 128: return launch_dv<128, T, SSD>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -273,7 +275,9 @@ bool recurrent_supports(const Problem &p) {
 }
 
 hipError_t launch_recurrent(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  return pr.dtype == GDR_F32 ? launch_dk<float>(pr, x, s) : launch_dk<bf16>(pr, x, s);
+  if (pr.mode == 1)
+    return pr.dtype == GDR_F32 ? launch_dk<float, true>(pr, x, s) : launch_dk<bf16, true>(pr, x, s);
+  return pr.dtype == GDR_F32 ? launch_dk<float, false>(pr, x, s) : launch_dk<bf16, false>(pr, x, s);
 }
 
 }  // namespace gdr

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -242,6 +242,44 @@ GDR_API gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment
  * (0 when there is a single segment); the same shape errors as that call. */
 GDR_API gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
                                                size_t *bytes);
+
+/*
+ * gdr_ssd_recurrent_fwd / gdr_ssd_chunked_fwd -- the Mamba-2 SSD recurrence
+ * (selective SSM) on the same two forms as the rule: a sequential scan for
+ * decode and the chunked scan for prefill.  The Track L pull request ("What
+ * landed", L4 and L4.1) names the op's inputs x, A, B, C and delta, an
+ * optional gate and an optional initial state, and a carried state for
+ * streaming decode, but prints no formula; this library takes the plain
+ * reading, per (sequence, head h) with an fp32 state h_t of shape [N, P]:
+ *     h_t <- exp(delta_t A_h) h_{t-1} + B_t (delta_t x_t)^T
+ *     y_t <- h_t^T C_t,      then y_t <- y_t * SiLU(z_t) when z is given
+ * i.e. the rule with a scalar decay and no erase term: no normalisation, no
+ * 1/sqrt scale, C in the place of q, B of k, x of v, g_t = delta_t A_h and
+ * beta_t = delta_t.  delta and A are used as given (delta > 0, A < 0 for a
+ * decaying state: no softplus, no exp).  Heads are grouped as in the rule:
+ * head h reads group h / (H / G) of B and C.
+ *   shape      : H_k = G groups, H_v = H heads, d_k = N (state size),
+ *                d_v = P (head size); scale and l2_eps are checked but unused
+ *   x, z, y    : dtype [total, H, P]   (16-byte aligned; z may be NULL)
+ *   delta      : dtype [total, H]
+ *   A          : fp32  [H]
+ *   B, C       : dtype [total, G, N]   (16-byte aligned)
+ *   states     : fp32  [num_seqs, H, N, P]   (the page's h[P, N], stored
+ *                transposed so that a state row is one N index)
+ * initial_state may be NULL (zero state); final_state may be NULL (dropped)
+ * or initial_state itself.  The chunked form needs chunk 16, 32 or 64 and
+ * runs on the matrix cores for bf16 with N = 128, P = 64 or 128 and
+ * chunk 32 (gdr_chunked_path tells which, as for the rule), else on the
+ * vector ALUs in fp32.  The gate is a second launch over y.
+ */
+GDR_API gdr_status gdr_ssd_recurrent_fwd(const gdr_shape *shape, const void *x, const void *delta,
+                                         const float *A, const void *B, const void *C,
+                                         const float *initial_state, const void *z, void *y,
+                                         float *final_state, hipStream_t stream);
+GDR_API gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, const void *delta,
+                                       const float *A, const void *B, const void *C,
+                                       const float *initial_state, const void *z, void *y,
+                                       float *final_state, hipStream_t stream);
 
 /* Which kernel gdr_chunked_fwd runs for `shape`: GDR_PATH_VECTOR_F32 (fp32
  * on the vector ALUs), GDR_PATH_MATRIX_BF16 (matrix cores, bf16 operands,

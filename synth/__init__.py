@@ -156,3 +156,39 @@ def custom(H_k, H_v, d_k, d_v, dtype, lengths=None, seq_len=0, num_seqs=1, chunk
     return Workload("custom", H_k=H_k, H_v=H_v, d_k=d_k, d_v=d_v, dtype=dtype, chunk=chunk,
                     num_seqs=num_seqs if lengths is None else len(lengths), seq_len=seq_len,
                     lengths=lengths, init_state=init_state, stress_seqs=tuple(stress_seqs))
+
+
+def ssd_inputs(G, H, N, P, dtype, lengths=None, seq_len=0, num_seqs=1, seed=0, device="cpu",
+               init_state=True, gate=False, delta_range=(1e-3, 1e-1)):
+    """Inputs of the Mamba-2 SSD recurrence: x [total, H, P], delta [total, H],
+    B, C [total, G, N], z [total, H, P] (when ``gate``) in ``dtype``; A [H]
+    fp32; initial_state [S, H, N, P] fp32 or None.
+
+    Distributions: x, B, C, z ~ N(0, 1); delta log-uniform on
+    ``delta_range`` (the usual time-step range of Mamba-2 initialisation,
+    1e-3 to 1e-1); A = -exp(U(0, ln 16)) (decay rates 1 to 16); initial
+    state ~ N(0, 0.01).  Sequences are dense (``num_seqs`` x ``seq_len``)
+    or packed with ``lengths`` (then cu_seqlens is on ``device``).
+    """
+    gen = torch.Generator(device=device).manual_seed(seed)
+    lens = list(lengths) if lengths is not None else [seq_len] * num_seqs
+    S = len(lens)
+    total = sum(lens)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    x = _normal((total, H, P), gen, device)
+    B = _normal((total, G, N), gen, device)
+    C = _normal((total, G, N), gen, device)
+    lo, hi = math.log(delta_range[0]), math.log(delta_range[1])
+    delta = torch.empty((total, H), dtype=torch.float32, device=device).uniform_(
+        lo, hi, generator=gen).exp()
+    A = -torch.empty(H, dtype=torch.float32, device=device).uniform_(
+        0.0, math.log(16.0), generator=gen).exp()
+    z = _normal((total, H, P), gen, device) if gate else None
+    s0 = _normal((S, H, N, P), gen, device, std=0.01) if init_state else None
+    cu_host = [0]
+    for L in lens:
+        cu_host.append(cu_host[-1] + L)
+    return dict(x=x.to(dt), delta=delta.to(dt), A=A, B=B.to(dt), C=C.to(dt),
+                z=None if z is None else z.to(dt), initial_state=s0, cu_host=cu_host,
+                cu_seqlens=(torch.tensor(cu_host, dtype=torch.int32, device=device)
+                            if lengths is not None else None))

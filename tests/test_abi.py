@@ -33,7 +33,8 @@ def test_header_declares_the_abi():
     assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_split",
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
-                                  "gdr_recurrent_fwd", "gdr_status_string"]
+                                  "gdr_recurrent_fwd", "gdr_ssd_chunked_fwd",
+                                  "gdr_ssd_recurrent_fwd", "gdr_status_string"]
 
 
 def test_library_exports_every_declared_symbol(gdr):
@@ -186,6 +187,8 @@ def test_chunked_path_selection(gdr):
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=0, d_k=128, d_v=128, chunk=32))) == 0
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=128, chunk=16))) == 0
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=64, d_v=128, chunk=32))) == 0
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=64, chunk=32))) == 1
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=32, chunk=32))) == 0
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, chunk=48))) == -3
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, H_v=3, H_k=2))) == -2
     assert gdr.chunked_path(16, 48, 128, 128, "bf16", 32) == "matrix_bf16"
@@ -291,3 +294,41 @@ def test_split_validation(gdr):
     assert split_call(gdr, s, 16, ws=fake(20, off=128)) == 4
     assert split_call(gdr, s, 16, ws=fake(8)) == 6           # over o
     assert split_call(gdr, s, 16, o=fake(0)) == 6            # o over q, as gdr_chunked_fwd
+
+
+# ------------------------------------------------------------- the SSD recurrence
+SSD_ARGS = ["x", "delta", "A", "B", "C", "s0", "z", "y", "sT"]
+
+
+def ssd_call(gdr, fn, s, **over):
+    p = {n: fake(i) for i, n in enumerate(SSD_ARGS)}
+    p.update(over)
+    return getattr(gdr.lib(), fn)(ctypes.byref(s) if s is not None else None,
+                                  *[p[n] for n in SSD_ARGS], None)
+
+
+@pytest.mark.parametrize("fn", ["gdr_ssd_recurrent_fwd", "gdr_ssd_chunked_fwd"])
+def test_ssd_validation(gdr, fn):
+    assert ssd_call(gdr, fn, None) == 1                                  # no shape
+    assert ssd_call(gdr, fn, shape(gdr, H_v=3, H_k=2)) == 2              # heads not grouped
+    assert ssd_call(gdr, fn, shape(gdr, d_k=24)) == 3                    # state size
+    assert ssd_call(gdr, fn, shape(gdr), A=None) == 1
+    assert ssd_call(gdr, fn, shape(gdr), C=None) == 1
+    assert ssd_call(gdr, fn, shape(gdr), B=fake(3, off=8)) == 4          # rows need 16 bytes
+    assert ssd_call(gdr, fn, shape(gdr), A=fake(2, off=2)) == 4
+    assert ssd_call(gdr, fn, shape(gdr), y=fake(0)) == 6                 # y over x
+    assert ssd_call(gdr, fn, shape(gdr), sT=fake(7)) == 6                # state over y
+    assert ssd_call(gdr, fn, shape(gdr), sT=fake(5, off=16)) == 6        # shifted in place
+
+
+def test_ssd_chunk_checked(gdr):
+    assert ssd_call(gdr, "gdr_ssd_chunked_fwd", shape(gdr, chunk=48)) == 3
+    assert ssd_call(gdr, "gdr_ssd_chunked_fwd", shape(gdr, chunk=0)) == 3
+
+
+def test_ssd_binding_refuses_cpu_tensors(gdr):
+    import torch
+    x = torch.zeros(4, 2, 16)
+    with pytest.raises(ValueError):
+        gdr.ssd_chunked_fwd(x, torch.zeros(4, 2), torch.zeros(2), torch.zeros(4, 1, 16),
+                            torch.zeros(4, 1, 16))

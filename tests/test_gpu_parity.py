@@ -369,3 +369,12 @@ def test_matrix_core_agrees_with_vector_kernel():
                         U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
     note(f"  matrix-core vs vector kernel: {worst:.3e}")
     assert worst <= U.TOL["bf16"]
+
+
+@pytest.mark.parametrize("lens", [[300, 1, 64, 0, 97], [2048]], ids=["ragged", "T2048"])
+def test_matrix_core_value_head_64(lens):
+    """d_v = 64 on the matrix cores: two workgroups of 32 value columns per
+    head instead of four."""
+    assert gdr.chunked_path(2, 6, 128, 64, "bf16", 32) == "matrix_bf16"
+    w = synth.custom(2, 6, 128, 64, "bf16", lengths=lens, chunk=32)
+    check_full(w, 24, "chunked")

@@ -1,0 +1,224 @@
+"""GPU parity of the Mamba-2 SSD recurrence (gdr_ssd_recurrent_fwd,
+gdr_ssd_chunked_fwd, through the C ABI) against the fp64 oracle in
+``oracle.ssd``.
+
+Same metric and bars as the rule: per (sequence, head) slice of y and of the
+final state, max |x - y| / max |y|; 1e-4 for fp32 inputs, 2e-2 for bf16
+inputs (fp32 state).  The chunked form runs on the matrix cores for bf16 with
+N = 128, P = 64 or 128 and chunk 32, else on the vector ALUs in fp32.
+
+Inputs (synth.ssd_inputs): x, B, C, z ~ N(0, 1); delta log-uniform on
+[1e-3, 1e-1]; A = -exp(U(0, ln 16)); initial state ~ N(0, 0.01); stress
+cases move delta to [0.5, 2] (fast decay) and to [1e-4, 1e-3] (long memory).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_68_amd as gdr
+import synth
+from oracle import ssd
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdr.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(form, inp, chunk=32, num_seqs=None, **kw):
+    fn = gdr.ssd_recurrent_fwd if form == "recurrent" else gdr.ssd_chunked_fwd
+    extra = {} if form == "recurrent" else {"chunk": chunk}
+    return fn(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["initial_state"],
+              z=inp["z"], cu_seqlens=inp["cu_seqlens"], num_seqs=num_seqs, **extra, **kw)
+
+
+def oracle_of(inp, heads=None):
+    """The oracle over every head, or over ``heads`` only (inputs sliced to
+    those heads and their groups; returns arrays over the chosen heads)."""
+    x, delta, A, B, C = inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"]
+    z, s0 = inp["z"], inp["initial_state"]
+    if heads is None:
+        return ssd.ssd(x.cpu(), delta.cpu(), A.cpu(), B.cpu(), C.cpu(),
+                       None if s0 is None else s0.cpu(), None if z is None else z.cpu(),
+                       cu_seqlens=inp["cu_host"])
+    H, G = x.shape[1], B.shape[1]
+    ys, ss = [], []
+    for h in heads:
+        g = h // (H // G)
+        y, S = ssd.ssd(x[:, h:h + 1].cpu(), delta[:, h:h + 1].cpu(), A[h:h + 1].cpu(),
+                       B[:, g:g + 1].cpu(), C[:, g:g + 1].cpu(),
+                       None if s0 is None else s0[:, h:h + 1].cpu(),
+                       None if z is None else z[:, h:h + 1].cpu(), cu_seqlens=inp["cu_host"])
+        ys.append(y)
+        ss.append(S)
+    return np.concatenate(ys, axis=1), np.concatenate(ss, axis=1)
+
+
+def check(inp, dtype, form, chunk=32, heads=None, tag=""):
+    G, N = inp["B"].shape[1], inp["B"].shape[2]
+    H, P = inp["x"].shape[1], inp["x"].shape[2]
+    note(f"[ssd] {tag} {form} chunk={chunk} {dtype} G={G} H={H} N={N} P={P} "
+         f"lens={inp['cu_host'][-1] if len(inp['cu_host']) > 6 else inp['cu_host']}")
+    y, S = run(form, inp, chunk)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle_of(inp, heads)
+    if heads is not None:
+        y, S = y[:, heads], S[:, heads]
+    eo, es = U.compare_full(y, S, y_ref, S_ref, inp["cu_host"], y_ref.shape[1])
+    tol = U.TOL[dtype]
+    note(f"  max rel err y={eo:.3e} state={es:.3e} (bar {tol:g})")
+    assert eo <= tol and es <= tol, (eo, es)
+    return y, S
+
+
+SHAPES = [
+    # G, H, N, P, lengths
+    (1, 2, 128, 64, [200, 0, 33]),
+    (2, 4, 128, 128, [97, 64, 1]),
+    (1, 3, 64, 32, [0, 1, 31, 32, 33, 100]),
+    (4, 8, 16, 64, [40, 9]),
+    (2, 2, 32, 16, [77]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"G{s[0]}H{s[1]}_N{s[2]}P{s[3]}")
+@pytest.mark.parametrize("form,chunk", [("recurrent", None), ("chunked", 16), ("chunked", 32),
+                                        ("chunked", 64)])
+def test_ssd_small_shapes(dtype, shape, form, chunk):
+    G, H, N, P, lens = shape
+    inp = synth.ssd_inputs(G, H, N, P, dtype, lengths=lens, seed=41, device=DEV, gate=True)
+    check(inp, dtype, form, chunk or 32)
+
+
+@pytest.mark.parametrize("P", [64, 128])
+@pytest.mark.parametrize("gate,init", [(True, True), (False, False)])
+def test_ssd_matrix_core(P, gate, init):
+    assert gdr.chunked_path(2, 6, 128, P, "bf16", 32) == "matrix_bf16"
+    lens = [300, 129, 0, 64, 1, 2]
+    inp = synth.ssd_inputs(2, 6, 128, P, "bf16", lengths=lens, seed=42, device=DEV, gate=gate,
+                           init_state=init)
+    check(inp, "bf16", "chunked", 32)
+
+
+@pytest.mark.parametrize("form", ["chunked", "recurrent"])
+@pytest.mark.parametrize("rng", [(0.5, 2.0), (1e-4, 1e-3)], ids=["fast_decay", "long_memory"])
+def test_ssd_stress_delta(form, rng):
+    inp = synth.ssd_inputs(2, 4, 128, 64, "bf16", lengths=[513, 40], seed=43, device=DEV,
+                           delta_range=rng)
+    check(inp, "bf16", form, 32, tag=str(rng))
+
+
+def test_ssd_dense_batch():
+    inp = synth.ssd_inputs(1, 4, 128, 64, "bf16", seq_len=96, num_seqs=3, seed=44, device=DEV)
+    y, S = run("chunked", inp, 32, num_seqs=3)
+    y1, S1 = run("recurrent", inp, num_seqs=3)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle_of(inp)
+    for yy, SS in ((y, S), (y1, S1)):
+        eo, es = U.compare_full(yy.reshape(-1, 4, 64), SS, y_ref, S_ref, inp["cu_host"], 4)
+        assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], (eo, es)
+
+
+def test_ssd_chunked_equals_recurrent_and_vector():
+    """One bf16 batch through the matrix-core kernel (chunk 32), the vector
+    kernel (chunk 16) and the recurrence: three forms of one definition."""
+    inp = synth.ssd_inputs(2, 6, 128, 64, "bf16", lengths=[257, 40], seed=45, device=DEV,
+                           gate=True)
+    assert gdr.chunked_path(2, 6, 128, 64, "bf16", 16) == "vector_f32"
+    outs = [run("chunked", inp, 32), run("chunked", inp, 16), run("recurrent", inp)]
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    worst = 0.0
+    for y, S in outs[1:]:
+        for n in range(len(cu) - 1):
+            for h in range(6):
+                worst = max(worst, U.slice_err(U.to_np(outs[0][0][cu[n]:cu[n + 1], h]),
+                                               U.to_np(y[cu[n]:cu[n + 1], h])),
+                            U.slice_err(U.to_np(outs[0][1][n, h]), U.to_np(S[n, h])))
+    note(f"  matrix-core vs vector vs recurrent: {worst:.3e}")
+    assert worst <= U.TOL["bf16"]
+
+
+def test_ssd_streaming_prefill_then_decode():
+    """Prefill 96 tokens with the chunked form, then decode 24 single tokens
+    in place with the recurrence: the same outputs and state as the oracle
+    over all 120 tokens (the carried state h[N, P] is exact)."""
+    inp = synth.ssd_inputs(1, 3, 128, 64, "f32", lengths=[120], seed=46, device=DEV, gate=True)
+    y_ref, S_ref = oracle_of(inp)
+    pre = {k: (v[:96] if isinstance(v, torch.Tensor) and v.dim() >= 2 and k != "initial_state"
+               else v) for k, v in inp.items()}
+    pre.update(cu_seqlens=None, cu_host=[0, 96])
+    y0, state = run("chunked", pre, 32)
+    state = state.clone()
+    ys = [y0]
+    for t in range(96, 120):
+        step = {k: (v[t:t + 1] if isinstance(v, torch.Tensor) and v.dim() >= 2
+                    and k != "initial_state" else v) for k, v in inp.items()}
+        step.update(cu_seqlens=None, cu_host=[0, 1], initial_state=state)
+        yt, _ = run("recurrent", step, inplace=True)
+        ys.append(yt)
+    torch.cuda.synchronize()
+    y = torch.cat(ys, dim=0)
+    eo, es = U.compare_full(y, state.view(1, 3, 128, 64), y_ref, S_ref, [0, 120], 3)
+    note(f"  streamed: y={eo:.3e} state={es:.3e}")
+    assert eo <= U.TOL["f32"] and es <= U.TOL["f32"], (eo, es)
+
+
+def test_ssd_without_final_state_and_empty():
+    inp = synth.ssd_inputs(1, 2, 128, 64, "bf16", lengths=[50], seed=47, device=DEV)
+    y, S = run("chunked", inp, 32, output_final_state=False)
+    torch.cuda.synchronize()
+    assert S is None
+    y_ref, _ = oracle_of(inp)
+    eo, _ = U.compare_full(y, None, y_ref, None, inp["cu_host"], 2)
+    assert eo <= U.TOL["bf16"]
+    for form in ("chunked", "recurrent"):
+        e = synth.ssd_inputs(1, 2, 128, 64, "bf16", lengths=[0, 0], seed=48, device=DEV)
+        y, S = run(form, e, 32)
+        torch.cuda.synchronize()
+        assert y.numel() == 0
+        assert torch.equal(S, e["initial_state"]), "empty sequences must pass the state through"
+
+
+def test_ssd_deterministic():
+    inp = synth.ssd_inputs(2, 6, 128, 128, "bf16", lengths=[257, 31], seed=49, device=DEV,
+                           gate=True)
+    a = run("chunked", inp, 32)
+    b = run("chunked", inp, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("P,H,G", [(64, 128, 8), (128, 48, 16)], ids=["P64_H128", "P128_H48"])
+def test_ssd_prefill_sampled(P, H, G):
+    """The prefill workload, 8192 tokens in one sequence, bf16, N = 128,
+    chunk 32, in the launch configuration the benchmark times; the oracle
+    checks three heads."""
+    inp = synth.ssd_inputs(G, H, 128, P, "bf16", seq_len=8192, num_seqs=1, seed=50, device=DEV,
+                           gate=True)
+    check(inp, "bf16", "chunked", 32, heads=[0, H // 2 + 1, H - 1], tag="prefill")
+
+
+def test_ssd_rejects_bad_arguments():
+    inp = synth.ssd_inputs(1, 2, 128, 64, "bf16", lengths=[8], seed=51, device=DEV)
+    with pytest.raises(gdr.GdrError, match="UNSUPPORTED"):
+        run("chunked", inp, 48)
+    with pytest.raises(TypeError):
+        gdr.ssd_chunked_fwd(inp["x"], inp["delta"], inp["A"].double(), inp["B"], inp["C"])
+    with pytest.raises(ValueError):
+        gdr.ssd_chunked_fwd(inp["x"], inp["delta"], inp["A"], inp["B"][:, :, :64].contiguous(),
+                            inp["C"])
