@@ -188,6 +188,7 @@ def main():
     # ------------------------------------ the layer's steps either side of the rule
     layer_line = layer_legs(gdr, dev, stream, max(1, min(args.steps, 10)))
     split_line = split_legs(gdr, dev, stream, max(1, min(args.steps, 5)))
+    ssd_line = ssd_legs(gdr, dev, stream, max(1, min(args.steps, 10)))
 
     # ------------------------------------------------------------ CPU baseline
     cpu = None
@@ -252,6 +253,7 @@ def main():
                                 "hbm_GBs": vbytes / (vms / 1e3) / 1e9}},
         "layer": layer_line,
         "split": split_line,
+        "ssd": ssd_line,
         "wall_s_prefill_timed": wall,
         "cpu_baseline": cpu,
     }
@@ -360,6 +362,106 @@ def split_legs(gdr, dev, stream, steps):
                                   "flop_per_launch": flops}}
         del inp, args
     return res
+
+
+def ssd_flops(T, G, H, N, P, C):
+    """Algorithmic matrix flops of the chunked SSD scan (lower triangles
+    counted half): per chunk of c tokens G c(c+1) N for the C B^T products of
+    each group and H [c(c+1) P + 4 c N P] per head (the masked outputs, C S
+    and the state update B^T Delta)."""
+    total = 0
+    t = 0
+    while t < T:
+        c = min(C, T - t)
+        total += G * c * (c + 1) * N + H * (c * (c + 1) * P + 4 * c * N * P)
+        t += c
+    return total
+
+
+def ssd_bytes(T, S, G, H, N, P, elem=2, s0=False, gate=False):
+    """Algorithmic HBM bytes of one SSD pass: x, delta, B, C (and z) read
+    once, y written once in the input dtype, the fp32 state written (and
+    read when given)."""
+    per_tok = (H * P + H + 2 * G * N + H * P + (H * P if gate else 0)) * elem
+    return T * per_tok + S * H * N * P * 4 * (2 if s0 else 1) + 4 * H
+
+
+def ssd_legs(gdr, dev, stream, steps):
+    """The Mamba-2 SSD recurrence on the same chunk scan: prefill of 8192
+    tokens with 128 heads of P = 64 in 8 groups of B and C, state N = 128,
+    chunk 32, bf16 (the chunked kernel, and the SiLU gate as its own launch),
+    and decode of 256 sequences x 128 heads with the fp32 state carried in
+    place (the recurrent kernel, 64 single-token steps).  Inputs from
+    synth.ssd_inputs, resident in HBM."""
+    import torch
+    import synth
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize(dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(n):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize(dev)
+        return e[0].elapsed_time(e[1]) / n
+
+    T, G, H, N, P = 8192, 8, 128, 128, 64
+    inp = synth.ssd_inputs(G, H, N, P, "bf16", seq_len=T, num_seqs=1, seed=0, device=dev,
+                           init_state=False, gate=True)
+    y = torch.empty((T, H, P), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((1, H, N, P), dtype=torch.float32, device=dev)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], None)
+    scan_ms = timed(lambda: gdr.ssd_chunked_fwd(*args, chunk=32, num_seqs=1, y=y, final_state=S),
+                    steps)
+    gated_ms = timed(lambda: gdr.ssd_chunked_fwd(*args, z=inp["z"], chunk=32, num_seqs=1, y=y,
+                                                 final_state=S), steps)
+    flops = ssd_flops(T, G, H, N, P, 32)
+    pbytes = ssd_bytes(T, 1, G, H, N, P)
+    del inp, args, y, S
+
+    Nd, steps_d = 256, 64
+    dinp = synth.ssd_inputs(G, H, N, P, "bf16", seq_len=steps_d, num_seqs=Nd, seed=1,
+                            device=dev, init_state=True)
+    # step-major copies: step s of every sequence is one contiguous batch
+    xs = dinp["x"].view(Nd, steps_d, H, P).transpose(0, 1).contiguous()
+    ds = dinp["delta"].view(Nd, steps_d, H).transpose(0, 1).contiguous()
+    Bs = dinp["B"].view(Nd, steps_d, G, N).transpose(0, 1).contiguous()
+    Cs = dinp["C"].view(Nd, steps_d, G, N).transpose(0, 1).contiguous()
+    state = dinp["initial_state"].clone()
+    yd = torch.empty((Nd, H, P), dtype=torch.bfloat16, device=dev)
+    box = [0]
+
+    def dstep():
+        s = box[0] % steps_d
+        box[0] += 1
+        gdr.ssd_recurrent_fwd(xs[s], ds[s], dinp["A"], Bs[s], Cs[s], state, num_seqs=Nd, y=yd,
+                              inplace=True)
+
+    dec_ms = timed(dstep, steps_d)
+    dbytes = Nd * H * N * P * 4 * 2 + Nd * (2 * H * P + H + 2 * G * N) * 2 + 4 * H
+    del dinp, xs, ds, Bs, Cs, state, yd
+    tf = flops / (scan_ms / 1e3) / 1e12
+    gbs = pbytes / (scan_ms / 1e3) / 1e9
+    dgbs = dbytes / (dec_ms / 1e3) / 1e9
+    return {
+        "prefill": {"workload": f"1 sequence x {T} tokens, {H} heads of P={P} in {G} groups "
+                                f"of B and C, N={N}, chunk 32, bf16 inputs, fp32 state",
+                    "steps": steps, "ms_per_launch": scan_ms, "tokens_per_s": T / (scan_ms / 1e3),
+                    "with_gate_ms": gated_ms,
+                    "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                 "bytes_per_launch": pbytes,
+                                 "mfma_view": {"flop_per_launch": flops, "achieved_TFs": tf,
+                                               "frac": tf / PEAK_BF16_TFLOPS}}},
+        "decode": {"workload": f"{Nd} sequences x {H} heads of P={P} ({G} groups), N={N}, "
+                               "fp32 state in place, bf16 inputs, single-token steps",
+                   "steps": steps_d, "mean_step_ms": dec_ms, "tokens_per_s": Nd / (dec_ms / 1e3),
+                   "roofline": {"bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
+                                "bytes_per_launch": dbytes}},
+    }
 
 
 def profiled_traffic(kernel):
