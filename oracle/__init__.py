@@ -10,6 +10,9 @@ package never imports the GPU library: the two share no code.
 ``chunked`` (module ``oracle.chunked``) is an fp64 numpy regrouping of the same
 arithmetic into chunks (the UT-transform form of the Track L pull request,
 "What landed"), pinned against ``fwd`` by the tests.
+``oracle.ssd`` (the Mamba-2 SSD recurrence) and ``oracle.kda`` (the rule with
+one decay per key channel) are the fp64 oracles of the two neighbouring
+mixers, each pinned by its own tests.
 
 Every function takes numpy arrays or CPU torch tensors of any float dtype and
 widens them exactly to fp64; results are fp64 numpy arrays.
