@@ -189,6 +189,7 @@ def main():
     layer_line = layer_legs(gdr, dev, stream, max(1, min(args.steps, 10)))
     split_line = split_legs(gdr, dev, stream, max(1, min(args.steps, 5)))
     ssd_line = ssd_legs(gdr, dev, stream, max(1, min(args.steps, 10)))
+    kda_line = kda_legs(gdr, dev, stream, max(1, min(args.steps, 5)))
 
     # ------------------------------------------------------------ CPU baseline
     cpu = None
@@ -254,6 +255,7 @@ def main():
         "layer": layer_line,
         "split": split_line,
         "ssd": ssd_line,
+        "kda": kda_line,
         "wall_s_prefill_timed": wall,
         "cpu_baseline": cpu,
     }
@@ -461,6 +463,89 @@ def ssd_legs(gdr, dev, stream, steps):
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
                                 "bytes_per_launch": dbytes}},
+    }
+
+
+def kda_prefill_flops(T, H_k, H_v, d_k, d_v, C):
+    """Algorithmic fp32 flops of the chunked KDA form: the rule's contractions
+    (prefill_flops) plus, for the channel-weighted Gram matrices, one more
+    multiply per channel of every (row, earlier row) pair, per value head:
+    H_v c(c+1)/2 d_k x 2 (the A and P sums share the weight).  The
+    exponentials of the weights are not counted."""
+    extra = 0
+    t = 0
+    while t < T:
+        c = min(C, T - t)
+        extra += H_v * c * (c + 1) // 2 * d_k * 2
+        t += c
+    return prefill_flops(T, H_k, H_v, d_k, d_v, C) + extra
+
+
+def kda_legs(gdr, dev, stream, steps):
+    """The per-channel-decay variant (KDA) at the rule's shapes: decode of
+    256 sequences x 48 value heads (16 key heads), d = 128, fp32 state in
+    place, 64 single-token steps (recurrent kernel, HBM-bound), and the
+    prefill layer (8192 tokens, chunk 32) on the fp32 vector chunked kernel.
+    Inputs from synth.kda_inputs, resident in HBM."""
+    import torch
+    import synth
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize(dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(n):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize(dev)
+        return e[0].elapsed_time(e[1]) / n
+
+    wd = synth.workload("decode")
+    d = synth.kda_inputs(wd, 0, device=dev)
+    state = d["initial_state"].clone()
+    od = torch.empty((wd.num_seqs, wd.H_v, wd.d_v), dtype=wd.torch_dtype, device=dev)
+    box = [0]
+
+    def dstep():
+        s = box[0] % wd.steps
+        box[0] += 1
+        gdr.kda_recurrent_fwd(d["q"][s], d["k"][s], d["v"][s], d["a"][s], d["b"][s], d["A_log"],
+                              d["dt_bias"], state, num_seqs=wd.num_seqs, o=od, inplace=True)
+
+    dec_ms = timed(dstep, wd.steps)
+    N, H_k, H_v, dk, dv = wd.num_seqs, wd.H_k, wd.H_v, wd.d_k, wd.d_v
+    dbytes = (N * H_v * dk * dv * 4 * 2 + N * (2 * H_k * dk + H_v * dv) * 2
+              + N * H_v * (dk + 1) * 2 + N * H_v * dv * 2 + 4 * H_v * (dk + 1))
+    del d, state, od
+
+    w = synth.workload("prefill")
+    inp = synth.kda_inputs(w, 0, device=dev)
+    o = torch.empty((w.total_tokens, w.H_v, w.d_v), dtype=w.torch_dtype, device=dev)
+    S = torch.empty((1, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    pre_ms = timed(lambda: gdr.kda_chunked_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"],
+                                               inp["A_log"], inp["dt_bias"], None, chunk=32,
+                                               num_seqs=1, o=o, final_state=S), steps)
+    T = w.total_tokens
+    flops = kda_prefill_flops(T, w.H_k, w.H_v, w.d_k, w.d_v, 32)
+    del inp, o, S
+    dgbs = dbytes / (dec_ms / 1e3) / 1e9
+    tf = flops / (pre_ms / 1e3) / 1e12
+    return {
+        "decode": {"workload": "256 sequences x 48 value heads (16 key heads), d_k=d_v=128, "
+                               "per-channel gates a [256, 48, 128], fp32 state in place, bf16 "
+                               "inputs, single-token steps",
+                   "steps": wd.steps, "mean_step_ms": dec_ms, "tokens_per_s": N / (dec_ms / 1e3),
+                   "roofline": {"bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
+                                "bytes_per_launch": dbytes}},
+        "prefill": {"workload": "prefill layer: 1 sequence x 8192 tokens, 48 value heads sharing "
+                                "16 key heads, d_k=d_v=128, chunk 32, bf16 inputs, fp32 vector "
+                                "kernel",
+                    "steps": steps, "ms_per_launch": pre_ms, "tokens_per_s": T / (pre_ms / 1e3),
+                    "roofline": {"bound": "alu", "achieved": tf, "peak": PEAK_F32_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": tf / PEAK_F32_TFLOPS,
+                                 "flop_per_launch": flops}},
     }
 
 

@@ -38,7 +38,7 @@ import torch
 
 __all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", "chunked_path", "conv_silu",
            "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version",
-           "ssd_recurrent_fwd", "ssd_chunked_fwd"]
+           "ssd_recurrent_fwd", "ssd_chunked_fwd", "kda_recurrent_fwd", "kda_chunked_fwd"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -94,6 +94,9 @@ def _bind(lib):
     lib.gdr_chunked_fwd_split.restype = ctypes.c_int
     lib.gdr_chunked_split_workspace.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunked_split_workspace.restype = ctypes.c_int
+    for name in ("gdr_kda_recurrent_fwd", "gdr_kda_chunked_fwd"):
+        getattr(lib, name).argtypes = [sp] + [vp] * 11
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("gdr_ssd_recurrent_fwd", "gdr_ssd_chunked_fwd"):
         getattr(lib, name).argtypes = [sp] + [vp] * 10
         getattr(lib, name).restype = ctypes.c_int
@@ -220,10 +223,10 @@ def gates(q, k, a, b, A_log, dt_bias, *, scale=None, l2_eps=1e-6, num_seqs=None,
 
 
 def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_seqs, chunk,
-         scale, l2_eps, o, final_state, output_final_state, inplace):
+         scale, l2_eps, o, final_state, output_final_state, inplace, kda=False):
     dense_T = q.shape[1] if q.dim() == 4 else None
     q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
-    a, b = _flatten(a, 1), _flatten(b, 1)
+    a, b = _flatten(a, 2 if kda else 1), _flatten(b, 1)
     dev = q.device
     if dev.type != "cuda":
         raise ValueError(f"{fn_name}: tensors must be on a GPU (got {dev})")
@@ -234,10 +237,11 @@ def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_
     _check(q, "q", dev, dt)
     _check(k, "k", dev, dt, (total, H_k, d_k))
     _check(v, "v", dev, dt, (total, H_v, d_v))
-    _check(a, "a", dev, dt, (total, H_v))
+    # KDA: one gate value per key channel
+    _check(a, "a", dev, dt, (total, H_v, d_k) if kda else (total, H_v))
     _check(b, "b", dev, dt, (total, H_v))
     _check(A_log, "A_log", dev, torch.float32, (H_v,))
-    _check(dt_bias, "dt_bias", dev, torch.float32, (H_v,))
+    _check(dt_bias, "dt_bias", dev, torch.float32, (H_v, d_k) if kda else (H_v,))
     if cu_seqlens is not None:
         _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
     shape = _make_shape(total, H_k, H_v, d_k, d_v, cu_seqlens, num_seqs, code, chunk, scale,
@@ -509,3 +513,22 @@ def ssd_chunked_fwd(x, delta, A, B, C, initial_state=None, *, z=None, chunk=32,
     """Mamba-2 SSD recurrence, chunked form (same arguments plus ``chunk``)."""
     return _ssd("gdr_ssd_chunked_fwd", x, delta, A, B, C, initial_state, z, cu_seqlens,
                 num_seqs, chunk, y, final_state, output_final_state, inplace)
+
+
+def kda_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, cu_seqlens=None,
+                      num_seqs=None, scale=None, l2_eps=1e-6, o=None, final_state=None,
+                      output_final_state=True, inplace=False):
+    """The rule with one decay per key channel (KDA), sequential form:
+    a [total, H_v, d_k] and dt_bias fp32 [H_v, d_k]; the rest as recurrent_fwd."""
+    return _fwd("gdr_kda_recurrent_fwd", q, k, v, a, b, A_log, dt_bias, initial_state,
+                cu_seqlens, num_seqs, 32, scale, l2_eps, o, final_state, output_final_state,
+                inplace, kda=True)
+
+
+def kda_chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32,
+                    cu_seqlens=None, num_seqs=None, scale=None, l2_eps=1e-6, o=None,
+                    final_state=None, output_final_state=True, inplace=False):
+    """KDA, chunked form (chunk 16 or 32)."""
+    return _fwd("gdr_kda_chunked_fwd", q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens,
+                num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state, inplace,
+                kda=True)

@@ -73,11 +73,14 @@ gdr_status check_fwd(const Problem &pr, const FwdArgs &x) {
     if (p && !aligned_to(p, 4)) return GDR_ERR_ALIGN;
   const size_t T = (size_t)pr.total;
   const size_t state_bytes = (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4;
+  // KDA: a and dt_bias carry one value per key channel
+  const size_t ga = pr.mode == kModeKDA ? (size_t)pr.d_k : 1;
   const Range ins[] = {
       span(x.q, T * pr.H_k * pr.d_k * es), span(x.k, T * pr.H_k * pr.d_k * es),
-      span(x.v, T * pr.H_v * pr.d_v * es), span(x.a, T * pr.H_v * es),
+      span(x.v, T * pr.H_v * pr.d_v * es), span(x.a, T * pr.H_v * ga * es),
       span(x.b, T * pr.H_v * es),          span(x.A_log, (size_t)pr.H_v * 4),
-      span(x.dt_bias, (size_t)pr.H_v * 4), span(pr.cu, pr.cu ? (size_t)(pr.num_seqs + 1) * 4 : 0)};
+      span(x.dt_bias, (size_t)pr.H_v * ga * 4),
+      span(pr.cu, pr.cu ? (size_t)(pr.num_seqs + 1) * 4 : 0)};
   const Range o = span(x.o, T * pr.H_v * pr.d_v * es);
   const Range sT = span(x.sT, x.sT ? state_bytes : 0);
   const Range s0 = span(x.s0, x.s0 ? state_bytes : 0);
@@ -340,7 +343,7 @@ gdr_status ssd_call(const gdr_shape *shape, bool chunked, const void *x, const v
   Problem pr;
   gdr_status st = resolve(shape, pr);
   if (st != GDR_OK) return st;
-  pr.mode = 1;
+  pr.mode = kModeSSD;
   pr.scale = 1.0f;
   if (chunked && pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
   if (!A) return GDR_ERR_NULL;
@@ -397,6 +400,38 @@ gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, const void
                                const float *initial_state, const void *z, void *y,
                                float *final_state, hipStream_t stream) {
   return gdr::ssd_call(shape, true, x, delta, A, B, C, initial_state, z, y, final_state, stream);
+}
+
+gdr_status gdr_kda_recurrent_fwd(const gdr_shape *shape, const void *q, const void *k,
+                                 const void *v, const void *a, const void *b, const float *A_log,
+                                 const float *dt_bias, const float *initial_state, void *o,
+                                 float *final_state, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  pr.mode = kModeKDA;
+  if (!recurrent_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
+  st = check_fwd(pr, x);
+  if (st != GDR_OK) return st;
+  return launched(launch_recurrent(pr, x, stream));
+}
+
+gdr_status gdr_kda_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
+                               const void *v, const void *a, const void *b, const float *A_log,
+                               const float *dt_bias, const float *initial_state, void *o,
+                               float *final_state, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  pr.mode = kModeKDA;
+  if (!chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
+  st = check_fwd(pr, x);
+  if (st != GDR_OK) return st;
+  return launched(launch_chunked_vec(pr, x, stream));
 }
 
 int gdr_chunked_path(const gdr_shape *shape) {

@@ -962,7 +962,8 @@ hipError_t launch_kernel(const Problem &pr, const FwdArgs &x, hipStream_t s) {
 }  // namespace
 
 bool chunked_mfma_supports(const Problem &p) {
-  return p.dtype == GDR_BF16 && p.d_k == DK && (p.d_v == 64 || p.d_v == 128) && p.chunk == CH;
+  return p.mode != kModeKDA && p.dtype == GDR_BF16 && p.d_k == DK && (p.d_v == 64 || p.d_v == 128) &&
+         p.chunk == CH;
 }
 
 hipError_t launch_chunked_mfma(const Problem &pr, const FwdArgs &x, hipStream_t s) {

@@ -50,7 +50,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int DK, int C>
+template <int DK, int C, bool KDA>
 struct VecSmem {
   float K[C][DK + 1];
   float Q[C][DK + 1];
@@ -67,15 +67,27 @@ struct VecSmem {
   float beta[C];
   float eg[C];    // exp(gamma_r)
   float tail[C];  // exp(gamma_{c-1} - gamma_r)
+  // KDA: per-channel cumulative log decays, and exp of them (after the Gram
+  // stage, the rows of K weighted by exp(gamma_{c-1} - gamma_r) per channel)
+  float G[KDA ? C : 1][DK + 1];
+  float EG[KDA ? C : 1][DK + 1];
 };
 
-// SSD: the Mamba-2 SSD recurrence on the same chunk scan (Problem::mode 1):
-// no norms, no erase (A = 0, so T = I and Delta = diag(beta) V without K S),
+// MODE kModeSSD: the Mamba-2 SSD recurrence on the same chunk scan: no
+// norms, no erase (A = 0, so T = I and Delta = diag(beta) V without K S),
 // g = A delta with delta in `a` and A in `A_log`, beta = delta.
-template <int DK, int C, typename T, bool SSD>
+// MODE kModeKDA: one decay per key channel.  gamma becomes gamma[r][c] and
+// every exp(gamma_r - gamma_i) moves inside the channel sums:
+//   A[r][i] = beta_r sum_c k_r[c] k_i[c] exp(gamma_r[c] - gamma_i[c])   (i < r)
+//   P[r][i] = sum_c q_r[c] k_i[c] exp(gamma_r[c] - gamma_i[c])          (i <= r)
+//   K S and Q S take the rows weighted by exp(gamma_r[c]);
+//   S'[c] = exp(gamma_{c-1}[c]) S[c] + sum_r k_r[c] exp(gamma_{c-1}[c] - gamma_r[c]) Delta_r
+// and again only differences with i <= r are exponentiated.
+template <int DK, int C, typename T, int MODE>
 __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p) {
+  constexpr bool SSD = MODE == kModeSSD, KDA = MODE == kModeKDA;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  VecSmem<DK, C> &sm = *reinterpret_cast<VecSmem<DK, C> *>(smem_raw);
+  VecSmem<DK, C, KDA> &sm = *reinterpret_cast<VecSmem<DK, C, KDA> *>(smem_raw);
   constexpr int E = (DK + 63) / 64;
   const int nvb = p.d_v / kBV;
   const int vb = blockIdx.x % nvb;
@@ -94,7 +106,7 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
     sm.S[d][j] = p.s0 ? p.s0[state_off + (size_t)d * DV + j] : 0.0f;
   }
   const float neg_exp_A = SSD ? p.A_log[h] : -expf(p.A_log[h]);  // SSD: A itself
-  const float dtb = SSD ? 0.0f : p.dt_bias[h];
+  const float dtb = (SSD || KDA) ? 0.0f : p.dt_bias[h];
 
   for (int64_t c0 = t0; c0 < t1; c0 += C) {
     const int cl = (int)((t1 - c0) < C ? (t1 - c0) : C);
@@ -128,8 +140,10 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
       const int r = tid;
       float g = 0.f, bt = 0.f;
       if (r < cl) {
-        const float a_r = to_f32(p.a[(c0 + r) * p.H_v + h]);
-        if constexpr (SSD) {
+        const float a_r = KDA ? 0.0f : to_f32(p.a[(c0 + r) * p.H_v + h]);
+        if constexpr (KDA) {  // the decays are per channel, below
+          bt = sigmoid_f32(to_f32(p.b[(c0 + r) * p.H_v + h]));
+        } else if constexpr (SSD) {
           g = neg_exp_A * a_r;
           bt = a_r;
         } else {
@@ -140,7 +154,26 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
       sm.gam[r] = g;
       sm.beta[r] = bt;
     }
+    if constexpr (KDA) {
+      for (int e = tid; e < C * DK; e += kVecThreads) {
+        const int r = e / DK, c = e % DK;
+        sm.G[r][c] = (r < cl) ? log_decay(neg_exp_A,
+                                          to_f32(p.a[((c0 + r) * p.H_v + h) * DK + c]),
+                                          p.dt_bias[h * DK + c])
+                              : 0.f;
+      }
+    }
     __syncthreads();
+    if constexpr (KDA) {  // cumulative over the chunk, one channel per thread
+      for (int c = tid; c < DK; c += kVecThreads) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+          acc += sm.G[r][c];
+          sm.G[r][c] = acc;
+          sm.EG[r][c] = expf(acc);
+        }
+      }
+    }
     if (tid == 0) {
       float acc = 0.f;
       for (int r = 0; r < C; ++r) {
@@ -161,8 +194,10 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
         float kk = 0.f, qk = 0.f;
 #pragma unroll 8
         for (int d = 0; d < DK; ++d) {
-          if constexpr (!SSD) kk += sm.K[r][d] * sm.K[i][d];
-          qk += sm.Q[r][d] * sm.K[i][d];
+          // KDA: the decay of each channel inside the sum
+          const float w = KDA ? expf(sm.G[r][d] - sm.G[i][d]) : 1.0f;
+          if constexpr (!SSD) kk += sm.K[r][d] * sm.K[i][d] * w;
+          qk += sm.Q[r][d] * sm.K[i][d] * w;
         }
         const float dec = expf(sm.gam[r] - sm.gam[i]);
         p_ri = dec * qk;
@@ -176,8 +211,9 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
       float ks = 0.f, qs = 0.f;
 #pragma unroll 8
       for (int d = 0; d < DK; ++d) {
-        if constexpr (!SSD) ks += sm.K[r][d] * sm.S[d][j];
-        qs += sm.Q[r][d] * sm.S[d][j];
+        const float w = KDA ? sm.EG[r][d] : 1.0f;
+        if constexpr (!SSD) ks += sm.K[r][d] * w * sm.S[d][j];
+        qs += sm.Q[r][d] * w * sm.S[d][j];
       }
       sm.KS[r][j] = ks;
       sm.QS[r][j] = qs;
@@ -204,6 +240,12 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
       }
 #pragma unroll
       for (int r = 0; r < C; ++r) sm.Tm[r][j] = x[r];
+    }
+    if constexpr (KDA) {  // EG is free now: K weighted for the state update
+      for (int e = tid; e < C * DK; e += kVecThreads) {
+        const int r = e / DK, c = e % DK;
+        sm.EG[r][c] = sm.K[r][c] * expf(sm.G[C - 1][c] - sm.G[r][c]);
+      }
     }
     if constexpr (!SSD) {
       for (int e = tid; e < C * kBV; e += kVecThreads) {
@@ -232,10 +274,17 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
     const float gc = sm.eg[C - 1];
     for (int e = tid; e < DK * kBV; e += kVecThreads) {
       const int d = e / kBV, j = e % kBV;
-      float s = gc * sm.S[d][j];
+      if constexpr (KDA) {
+        float s = expf(sm.G[C - 1][d]) * sm.S[d][j];
 #pragma unroll 8
-      for (int r = 0; r < C; ++r) s += sm.tail[r] * sm.K[r][d] * sm.D[r][j];
-      sm.S[d][j] = s;
+        for (int r = 0; r < C; ++r) s += sm.EG[r][d] * sm.D[r][j];
+        sm.S[d][j] = s;
+      } else {
+        float s = gc * sm.S[d][j];
+#pragma unroll 8
+        for (int r = 0; r < C; ++r) s += sm.tail[r] * sm.K[r][d] * sm.D[r][j];
+        sm.S[d][j] = s;
+      }
     }
     __syncthreads();
   }
@@ -247,7 +296,7 @@ __global__ __launch_bounds__(kVecThreads) void chunked_vec_kernel(VecParams<T> p
   }
 }
 
-template <int DK, int C, typename T, bool SSD>
+template <int DK, int C, typename T, int MODE>
 hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   VecParams<T> p;
   p.q = static_cast<const T *>(x.q);
@@ -269,8 +318,8 @@ hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   p.eps = pr.eps;
   const int64_t grid = (int64_t)pr.num_seqs * pr.H_v * (pr.d_v / kBV);
   if (grid == 0) return hipSuccess;
-  const size_t smem = sizeof(VecSmem<DK, C>);
-  auto kern = chunked_vec_kernel<DK, C, T, SSD>;
+  const size_t smem = sizeof(VecSmem<DK, C, MODE == kModeKDA>);
+  auto kern = chunked_vec_kernel<DK, C, T, MODE>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
@@ -278,23 +327,25 @@ hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DK, typename T, bool SSD>
+template <int DK, typename T, int MODE>
 hipError_t launch_c(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.chunk) {
-    case 16: return launch_typed<DK, 16, T, SSD>(pr, x, s);
-    case 32: return launch_typed<DK, 32, T, SSD>(pr, x, s);
-    case 64: return launch_typed<DK, 64, T, SSD>(pr, x, s);
+    case 16: return launch_typed<DK, 16, T, MODE>(pr, x, s);
+    case 32: return launch_typed<DK, 32, T, MODE>(pr, x, s);
+    case 64:
+      if constexpr (MODE == kModeKDA) return hipErrorInvalidValue;  // LDS: see chunked_vec_supports
+      else return launch_typed<DK, 64, T, MODE>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, bool SSD>
+template <typename T, int MODE>
 hipError_t launch_dk(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.d_k) {
-    case 16: return launch_c<16, T, SSD>(pr, x, s);
-    case 32: return launch_c<32, T, SSD>(pr, x, s);
-    case 64: return launch_c<64, T, SSD>(pr, x, s);
-    case 128: return launch_c<128, T, SSD>(pr, x, s);
+    case 16: return launch_c<16, T, MODE>(pr, x, s);
+    case 32: return launch_c<32, T, MODE>(pr, x, s);
+    case 64: return launch_c<64, T, MODE>(pr, x, s);
+    case 128: return launch_c<128, T, MODE>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -303,13 +354,16 @@ hipError_t launch_dk(const Problem &pr, const FwdArgs &x, hipStream_t s) {
 
 bool chunked_vec_supports(const Problem &p) {
   auto ok = [](int d) { return d == 16 || d == 32 || d == 64 || d == 128; };
-  return ok(p.d_k) && ok(p.d_v) && (p.chunk == 16 || p.chunk == 32 || p.chunk == 64);
+  // KDA keeps two more [chunk, d_k] tiles in LDS: chunk 64 would not fit
+  return ok(p.d_k) && ok(p.d_v) &&
+         (p.chunk == 16 || p.chunk == 32 || (p.chunk == 64 && p.mode != kModeKDA));
 }
 
 hipError_t launch_chunked_vec(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  if (pr.mode == 1)
-    return pr.dtype == GDR_F32 ? launch_dk<float, true>(pr, x, s) : launch_dk<bf16, true>(pr, x, s);
-  return pr.dtype == GDR_F32 ? launch_dk<float, false>(pr, x, s) : launch_dk<bf16, false>(pr, x, s);
+  const bool f = pr.dtype == GDR_F32;
+  if (pr.mode == kModeSSD) return f ? launch_dk<float, kModeSSD>(pr, x, s) : launch_dk<bf16, kModeSSD>(pr, x, s);
+  if (pr.mode == kModeKDA) return f ? launch_dk<float, kModeKDA>(pr, x, s) : launch_dk<bf16, kModeKDA>(pr, x, s);
+  return f ? launch_dk<float, kModeRule>(pr, x, s) : launch_dk<bf16, kModeRule>(pr, x, s);
 }
 
 }  // namespace gdr

@@ -20,11 +20,18 @@ struct Problem {
   int chunk;
   float scale;             // resolved: never <= 0
   float eps;
-  // 0: the gated delta rule.  1: the Mamba-2 SSD recurrence on the same
-  // kernels: no L2 norm (scale 1), no erase, g = A delta and beta = delta,
-  // with `a` carrying delta, `A_log` carrying A itself and b, dt_bias unused.
+  // kModeRule: the gated delta rule.  kModeSSD: the Mamba-2 SSD recurrence
+  // on the same kernels: no L2 norm (scale 1), no erase, g = A delta and
+  // beta = delta, with `a` carrying delta, `A_log` carrying A itself and b,
+  // dt_bias unused.  kModeKDA: the rule with one decay per key channel,
+  // g[i] = -exp(A_log) softplus(a[i] + dt_bias[i]) with a [total, H_v, d_k]
+  // and dt_bias [H_v, d_k].
   int mode = 0;
 };
+
+constexpr int kModeRule = 0;
+constexpr int kModeSSD = 1;
+constexpr int kModeKDA = 2;
 
 // Pointers of one forward call (types erased; dtype in Problem).
 struct FwdArgs {

@@ -67,13 +67,17 @@ struct RecParams {
   float scale, eps;
 };
 
-// SSD: the Mamba-2 SSD recurrence on the same scan (Problem::mode 1): no
-// norms, no erase, g = A delta with delta in `a` and A in `A_log`, beta = delta.
-template <int DK, int DV, typename T, bool SSD>
+// MODE kModeSSD: the Mamba-2 SSD recurrence on the same scan: no norms, no
+// erase, g = A delta with delta in `a` and A in `A_log`, beta = delta.
+// MODE kModeKDA: one decay per key channel, so row i of S decays by its own
+// alpha_i = exp(g[i]); the rows are decayed in place before the reductions and
+// the rest is the rule's step with alpha = 1.
+template <int DK, int DV, typename T, int MODE>
 // (at most 128 registers per lane: two 8-wave workgroups per compute unit)
 __global__ __launch_bounds__((RecGeom<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4)))
 void recurrent_kernel(RecParams<T> p) {
   using G = RecGeom<DK, DV>;
+  constexpr bool SSD = MODE == kModeSSD, KDA = MODE == kModeKDA;
   constexpr int CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW, NRED = G::NRED;
   __shared__ float red[2][NW > 1 ? NW : 1][CG][NRED];
 
@@ -107,7 +111,7 @@ void recurrent_kernel(RecParams<T> p) {
     int64_t t0, t1;
     seq_bounds(p.cu, p.seq_len, n, t0, t1);
     const float neg_exp_A = SSD ? p.A_log[h] : -expf(p.A_log[h]);  // SSD: A itself
-    const float dtb = SSD ? 0.0f : p.dt_bias[h];
+    const float dtb = (SSD || KDA) ? 0.0f : p.dt_bias[h];
 
     for (int64_t t = t0; t < t1; ++t, ++step) {
       const T *kr = p.k + (t * p.H_k + hk) * DK;
@@ -119,8 +123,22 @@ void recurrent_kernel(RecParams<T> p) {
         qv[i] = to_f32(qr[rg + RG * i]);
       }
       const float4 vv = load4(p.v + (t * p.H_v + h) * DV + 4 * cg);
-      const float a_t = to_f32(p.a[t * p.H_v + h]);
+      const float a_t = KDA ? 0.0f : to_f32(p.a[t * p.H_v + h]);
       const float b_t = SSD ? 0.0f : to_f32(p.b[t * p.H_v + h]);
+      // KDA: decay this thread's rows in place first (each by its own
+      // alpha), then run the rule's step with alpha = 1
+      if constexpr (KDA) {
+        const T *ar = p.a + (t * p.H_v + h) * DK;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const float al = expf(log_decay(neg_exp_A, to_f32(ar[rg + RG * i]),
+                                          p.dt_bias[h * DK + rg + RG * i]));
+          S[i].x *= al;
+          S[i].y *= al;
+          S[i].z *= al;
+          S[i].w *= al;
+        }
+      }
 
       float r[NRED];
 #pragma unroll
@@ -163,8 +181,8 @@ void recurrent_kernel(RecParams<T> p) {
       const float ik = SSD ? 1.0f : rsqrtf(r[8] + p.eps);
       const float iq = SSD ? 1.0f : rsqrtf(r[9] + p.eps) * p.scale;
       const float qk = r[10] * ik * iq;
-      const float g = SSD ? neg_exp_A * a_t : log_decay(neg_exp_A, a_t, dtb);
-      const float alpha = expf(g);
+      const float g = SSD ? neg_exp_A * a_t : (KDA ? 0.0f : log_decay(neg_exp_A, a_t, dtb));
+      const float alpha = KDA ? 1.0f : expf(g);  // KDA: rows already decayed
       const float beta = SSD ? a_t : sigmoid_f32(b_t);
       const float au = SSD ? 0.0f : alpha * ik;  // SSD: no erase
       float4 d;
@@ -214,7 +232,7 @@ int cu_count() {
   return cache[dev];
 }
 
-template <int DK, int DV, typename T, bool SSD>
+template <int DK, int DV, typename T, int MODE>
 hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   RecParams<T> p;
   p.q = static_cast<const T *>(x.q);
@@ -240,29 +258,29 @@ hipError_t launch_typed(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   // persistent grid: about 16 waves per compute unit
   const int per_cu = RecGeom<DK, DV>::NW >= 8 ? 2 : 16 / RecGeom<DK, DV>::NW;
   const int64_t grid = units < (int64_t)cu_count() * per_cu ? units : (int64_t)cu_count() * per_cu;
-  hipLaunchKernelGGL((recurrent_kernel<DK, DV, T, SSD>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((recurrent_kernel<DK, DV, T, MODE>), dim3((unsigned)grid),
                      dim3(RecGeom<DK, DV>::NT), 0, s, p);
   return hipGetLastError();
 }
 
-template <int DK, typename T, bool SSD>
+template <int DK, typename T, int MODE>
 hipError_t launch_dv(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.d_v) {
-    case 16: return launch_typed<DK, 16, T, SSD>(pr, x, s);
-    case 32: return launch_typed<DK, 32, T, SSD>(pr, x, s);
-    case 64: return launch_typed<DK, 64, T, SSD>(pr, x, s);
-    case 128: return launch_typed<DK, 128, T, SSD>(pr, x, s);
+    case 16: return launch_typed<DK, 16, T, MODE>(pr, x, s);
+    case 32: return launch_typed<DK, 32, T, MODE>(pr, x, s);
+    case 64: return launch_typed<DK, 64, T, MODE>(pr, x, s);
+    case 128: return launch_typed<DK, 128, T, MODE>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, bool SSD>
+template <typename T, int MODE>
 hipError_t launch_dk(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   switch (pr.d_k) {
-    case 16: return launch_dv<16, T, SSD>(pr, x, s);
-    case 32: return launch_dv<32, T, SSD>(pr, x, s);
-    case 64: return launch_dv<64, T, SSD>(pr, x, s);
-    case 128: return launch_dv<128, T, SSD>(pr, x, s);
+    case 16: return launch_dv<16, T, MODE>(pr, x, s);
+    case 32: return launch_dv<32, T, MODE>(pr, x, s);
+    case 64: return launch_dv<64, T, MODE>(pr, x, s);
+    case 128: return launch_dv<128, T, MODE>(pr, x, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -275,9 +293,10 @@ bool recurrent_supports(const Problem &p) {
 }
 
 hipError_t launch_recurrent(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  if (pr.mode == 1)
-    return pr.dtype == GDR_F32 ? launch_dk<float, true>(pr, x, s) : launch_dk<bf16, true>(pr, x, s);
-  return pr.dtype == GDR_F32 ? launch_dk<float, false>(pr, x, s) : launch_dk<bf16, false>(pr, x, s);
+  const bool f = pr.dtype == GDR_F32;
+  if (pr.mode == kModeSSD) return f ? launch_dk<float, kModeSSD>(pr, x, s) : launch_dk<bf16, kModeSSD>(pr, x, s);
+  if (pr.mode == kModeKDA) return f ? launch_dk<float, kModeKDA>(pr, x, s) : launch_dk<bf16, kModeKDA>(pr, x, s);
+  return f ? launch_dk<float, kModeRule>(pr, x, s) : launch_dk<bf16, kModeRule>(pr, x, s);
 }
 
 }  // namespace gdr

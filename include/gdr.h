@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -280,6 +280,36 @@ GDR_API gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, co
                                        const float *A, const void *B, const void *C,
                                        const float *initial_state, const void *z, void *y,
                                        float *final_state, hipStream_t stream);
+
+/*
+ * gdr_kda_recurrent_fwd / gdr_kda_chunked_fwd -- the rule with one decay per
+ * key channel (KDA): the Mamba + KDA pull requests of the PLENA compiler and
+ * simulator name a KDA recurrent-state core beside the Mamba-2 one, with an
+ * fp32 state, but print no formula.  This library reads it as the rule of
+ * gdr_recurrent_fwd with the scalar decay exp(g_t) replaced by a diagonal
+ * one on the state's rows, and the gate of the rule applied per channel:
+ *     g_t[i] = -exp(A_log[h]) * softplus(a_t[i] + dt_bias[h, i])   (i < d_k)
+ *     S <- diag(exp(g_t)) S;  delta <- (v_t - k_t^T S) * beta_t;
+ *     S <- S + k_t (outer) delta;  o_t <- q_t^T S
+ * with q, k normalised and q scaled as in the rule, beta_t = sigmoid(b_t).
+ *   a        : dtype [total, H_v, d_k]   (per-channel raw gate projections)
+ *   dt_bias  : fp32  [H_v, d_k]
+ * All other arguments, layouts and rules as gdr_recurrent_fwd /
+ * gdr_chunked_fwd.  The chunked form runs on the vector ALUs in fp32 for both
+ * dtypes (the channel-weighted Gram matrices exponentiate every channel of
+ * every pair, so they are not plain matrix products) and takes chunk 16 or
+ * 32 (64 returns GDR_ERR_UNSUPPORTED).
+ */
+GDR_API gdr_status gdr_kda_recurrent_fwd(const gdr_shape *shape, const void *q, const void *k,
+                                         const void *v, const void *a, const void *b,
+                                         const float *A_log, const float *dt_bias,
+                                         const float *initial_state, void *o, float *final_state,
+                                         hipStream_t stream);
+GDR_API gdr_status gdr_kda_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
+                                       const void *v, const void *a, const void *b,
+                                       const float *A_log, const float *dt_bias,
+                                       const float *initial_state, void *o, float *final_state,
+                                       hipStream_t stream);
 
 /* Which kernel gdr_chunked_fwd runs for `shape`: GDR_PATH_VECTOR_F32 (fp32
  * on the vector ALUs), GDR_PATH_MATRIX_BF16 (matrix cores, bf16 operands,

@@ -192,3 +192,20 @@ def ssd_inputs(G, H, N, P, dtype, lengths=None, seq_len=0, num_seqs=1, seed=0, d
                 z=None if z is None else z.to(dt), initial_state=s0, cu_host=cu_host,
                 cu_seqlens=(torch.tensor(cu_host, dtype=torch.int32, device=device)
                             if lengths is not None else None))
+
+
+def kda_inputs(w: Workload, seed: int = 0, device="cpu", a_mean=0.0):
+    """Inputs of the per-channel-decay variant for workload ``w``: those of
+    ``make_inputs`` with a replaced by [..., H_v, d_k] ~ N(a_mean, 1) (in
+    w.dtype) and dt_bias by [H_v, d_k] ~ N(0, 0.1) fp32, drawn from a second
+    generator seeded seed + 7919 (so the other tensors equal make_inputs')."""
+    out = make_inputs(w, seed, device=device)
+    gen = torch.Generator(device=device).manual_seed(seed + 7919)
+    lead = tuple(out["b"].shape)
+    a = _normal(lead + (w.d_k,), gen, device, mean=a_mean)
+    out["a"] = a.to(w.torch_dtype)
+    out["dt_bias"] = _normal((w.H_v, w.d_k), gen, device, std=0.1)
+    if w.steps:
+        N = lead[1]
+        out["dense"]["a"] = out["a"].transpose(0, 1).reshape((N * w.steps, w.H_v, w.d_k)).contiguous()
+    return out

@@ -33,6 +33,7 @@ def test_header_declares_the_abi():
     assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_split",
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
+                                  "gdr_kda_chunked_fwd", "gdr_kda_recurrent_fwd",
                                   "gdr_recurrent_fwd", "gdr_ssd_chunked_fwd",
                                   "gdr_ssd_recurrent_fwd", "gdr_status_string"]
 
@@ -332,3 +333,31 @@ def test_ssd_binding_refuses_cpu_tensors(gdr):
     with pytest.raises(ValueError):
         gdr.ssd_chunked_fwd(x, torch.zeros(4, 2), torch.zeros(2), torch.zeros(4, 1, 16),
                             torch.zeros(4, 1, 16))
+
+
+# ------------------------------------------------------- the per-channel decay (KDA)
+@pytest.mark.parametrize("fn", ["gdr_kda_recurrent_fwd", "gdr_kda_chunked_fwd"])
+def test_kda_validation(gdr, fn):
+    assert call(gdr, fn, None) == 1
+    assert call(gdr, fn, shape(gdr, H_v=3, H_k=2)) == 2
+    assert call(gdr, fn, shape(gdr, d_k=24)) == 3
+    p = [fake(i) for i in range(10)]
+    p[5] = None  # A_log
+    assert call(gdr, fn, shape(gdr), p) == 1
+    p = [fake(i) for i in range(10)]
+    p[6] = fake(6, off=2)  # dt_bias (fp32)
+    assert call(gdr, fn, shape(gdr), p) == 4
+    # a holds total x H_v x d_k values here (4 x 2 x 16 fp32 = 512 bytes): an
+    # output 64 bytes past its start overlaps it
+    p = [fake(i) for i in range(10)]
+    p[8] = fake(3, off=64)
+    assert call(gdr, fn, shape(gdr), p) == 6
+    # ... and so does a final state 64 bytes past the start of dt_bias (2 x 16 fp32)
+    p = [fake(i) for i in range(10)]
+    p[9] = fake(6, off=64)
+    assert call(gdr, fn, shape(gdr), p) == 6
+
+
+def test_kda_chunk_sizes(gdr):
+    assert call(gdr, "gdr_kda_chunked_fwd", shape(gdr, chunk=64)) == 3
+    assert call(gdr, "gdr_kda_chunked_fwd", shape(gdr, chunk=48)) == 3
