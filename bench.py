@@ -467,7 +467,7 @@ def ssd_legs(gdr, dev, stream, steps):
 
 
 def kda_prefill_flops(T, H_k, H_v, d_k, d_v, C):
-    """Algorithmic fp32 flops of the chunked KDA form: the rule's contractions
+    """Algorithmic flops of the chunked KDA form: the rule's contractions
     (prefill_flops) plus, for the channel-weighted Gram matrices, one more
     multiply per channel of every (row, earlier row) pair, per value head:
     H_v c(c+1)/2 d_k x 2 (the A and P sums share the weight).  The
@@ -485,8 +485,8 @@ def kda_legs(gdr, dev, stream, steps):
     """The per-channel-decay variant (KDA) at the rule's shapes: decode of
     256 sequences x 48 value heads (16 key heads), d = 128, fp32 state in
     place, 64 single-token steps (recurrent kernel, HBM-bound), and the
-    prefill layer (8192 tokens, chunk 32) on the fp32 vector chunked kernel.
-    Inputs from synth.kda_inputs, resident in HBM."""
+    prefill layer (8192 tokens, chunk 32, bf16) on the matrix-core chunked
+    KDA kernel.  Inputs from synth.kda_inputs, resident in HBM."""
     import torch
     import synth
 
@@ -540,11 +540,10 @@ def kda_legs(gdr, dev, stream, steps):
                                 "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
                                 "bytes_per_launch": dbytes}},
         "prefill": {"workload": "prefill layer: 1 sequence x 8192 tokens, 48 value heads sharing "
-                                "16 key heads, d_k=d_v=128, chunk 32, bf16 inputs, fp32 vector "
-                                "kernel",
+                                "16 key heads, d_k=d_v=128, chunk 32, bf16 inputs, fp32 state",
                     "steps": steps, "ms_per_launch": pre_ms, "tokens_per_s": T / (pre_ms / 1e3),
-                    "roofline": {"bound": "alu", "achieved": tf, "peak": PEAK_F32_TFLOPS,
-                                 "unit": "TFLOP/s", "frac": tf / PEAK_F32_TFLOPS,
+                    "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                                  "flop_per_launch": flops}},
     }
 

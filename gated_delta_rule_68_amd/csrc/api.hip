@@ -427,10 +427,11 @@ gdr_status gdr_kda_chunked_fwd(const gdr_shape *shape, const void *q, const void
   gdr_status st = resolve(shape, pr);
   if (st != GDR_OK) return st;
   pr.mode = kModeKDA;
-  if (!chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  if (!chunked_kda_supports(pr) && !chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
   FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
   st = check_fwd(pr, x);
   if (st != GDR_OK) return st;
+  if (chunked_kda_supports(pr)) return launched(launch_chunked_kda(pr, x, stream));
   return launched(launch_chunked_vec(pr, x, stream));
 }
 

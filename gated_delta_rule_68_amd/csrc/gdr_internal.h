@@ -88,6 +88,9 @@ hipError_t launch_chunked_mfma(const Problem &p, const FwdArgs &x, hipStream_t s
 // Shapes each kernel family is instantiated for.
 bool recurrent_supports(const Problem &p);
 bool chunked_vec_supports(const Problem &p);
+// KDA chunked form on the matrix cores (bf16, d_k = 128, d_v = 64 or 128, chunk 32).
+bool chunked_kda_supports(const Problem &p);
+hipError_t launch_chunked_kda(const Problem &p, const FwdArgs &x, hipStream_t s);
 bool chunked_mfma_supports(const Problem &p);
 
 }  // namespace gdr

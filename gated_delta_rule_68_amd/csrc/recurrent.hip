@@ -128,11 +128,15 @@ void recurrent_kernel(RecParams<T> p) {
       // KDA: decay this thread's rows in place first (each by its own
       // alpha), then run the rule's step with alpha = 1
       if constexpr (KDA) {
+        // per-row gates through the hardware base-2 units (eight per token
+        // per thread: the library expf / log1pf would dominate the step)
         const T *ar = p.a + (t * p.H_v + h) * DK;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          const float al = expf(log_decay(neg_exp_A, to_f32(ar[rg + RG * i]),
-                                          p.dt_bias[h * DK + rg + RG * i]));
+          const float x = to_f32(ar[rg + RG * i]) + p.dt_bias[h * DK + rg + RG * i];
+          const float sp = fmaxf(x, 0.f) + 0.6931471805599453f *
+                                               __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f));
+          const float al = __builtin_amdgcn_exp2f(neg_exp_A * 1.4426950408889634f * sp);
           S[i].x *= al;
           S[i].y *= al;
           S[i].z *= al;

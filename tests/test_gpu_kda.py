@@ -84,6 +84,7 @@ def check(w, seed, form, chunk=32, heads=None, a_mean=0.0, tag=""):
 SHAPES = [
     # H_k, H_v, d_k, d_v, lengths
     (2, 6, 128, 128, [100, 0, 37]),
+    (2, 4, 128, 64, [300, 1, 0, 64]),
     (1, 3, 64, 32, [0, 1, 31, 32, 33, 70]),
     (2, 2, 16, 64, [17, 64, 5]),
     (4, 8, 32, 16, [40, 9]),
@@ -102,6 +103,9 @@ def test_kda_small_shapes(dtype, shape, form, chunk):
 @pytest.mark.parametrize("form", ["chunked", "recurrent"])
 @pytest.mark.parametrize("a_mean", [4.0, -6.0], ids=["strong_decay", "long_memory"])
 def test_kda_gate_extremes(form, a_mean):
+    """Strong decay: factors through a row inside a 16-row block would
+    overflow, so this checks the exact diagonal blocks of the matrix-core
+    kernel; long memory: the state carries across many chunks."""
     w = synth.custom(1, 2, 128, 128, "bf16", lengths=[200, 65], chunk=32)
     check(w, 62, form, 32, a_mean=a_mean, tag=f"a~N({a_mean},1)")
 
@@ -200,3 +204,23 @@ def test_kda_rejects_bad_arguments():
     with pytest.raises(ValueError):  # a with one value per head is the rule's, not KDA's
         gdr.kda_recurrent_fwd(inp["q"], inp["k"], inp["v"], inp["a"][..., 0].contiguous(),
                               inp["b"], inp["A_log"], inp["dt_bias"])
+
+
+@pytest.mark.parametrize("lens", [[2048], [31, 32, 33, 95, 1]], ids=["T2048", "ragged"])
+def test_kda_matrix_core_vs_vector_kernel(lens):
+    """The bf16 matrix-core kernel (chunk 32) against the fp32 vector kernel
+    (chunk 16) on the same inputs, over a long sequence and ragged tails."""
+    w = synth.custom(2, 6, 128, 128, "bf16", lengths=lens, chunk=32)
+    inp = synth.kda_inputs(w, 70, device=DEV)
+    o1, S1 = run("chunked", inp, w, 32)
+    o2, S2 = run("chunked", inp, w, 16)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        for h in range(w.H_v):
+            worst = max(worst, U.slice_err(U.to_np(o1[cu[n]:cu[n + 1], h]),
+                                           U.to_np(o2[cu[n]:cu[n + 1], h])),
+                        U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
+    note(f"  matrix-core vs vector kernel: {worst:.3e}")
+    assert worst <= U.TOL["bf16"]
