@@ -33,12 +33,12 @@
 //    T22 = (I + A22)^-1 from forward substitution in fp32.
 // The decays are kept in base 2 (log2 e folded into gamma) for exp2.
 //
-// Launch: 512 threads (8 waves) per (sequence, value head).  Wave w < d_v/16
-// owns value columns 16w..16w+15 and its [128 x 16] slice of S as 8
-// accumulator tiles for the whole sequence; all waves share the per-chunk
-// work that does not touch the state.  Chunks run one after the other; the
-// rows of the next chunk are loaded into registers while the current one is
-// computed.
+// Launch: 512 threads (8 waves) per (sequence, value head, 32 value
+// columns).  Waves 0 and 1 own 16 of the columns each and their [128 x 16]
+// slice of S as 8 accumulator tiles for the whole sequence; all waves share
+// the per-chunk work that does not touch the state.  Chunks run one after
+// the other; the rows of the next chunk are loaded into registers while the
+// current one is computed.
 //
 // Operand lane orders (v_mfma_f32_16x16x16_bf16 and ..._16x16x32_bf16, lane
 // l = 16 g + m): A operand row m at k = 4g..4g+3 (8g..8g+7 for x32), B operand
@@ -65,6 +65,11 @@ constexpr int CH = 32;
 constexpr int NT = 512;          // threads (8 waves)
 constexpr int FP = DK + 4;       // fp32 row pitch: rows 16 bytes apart modulo 256
 constexpr int MP = 36;           // pitch of the 32 x 32 matrices
+// value columns per workgroup: 32 (4 workgroups per head at d_v = 128) beat
+// 64 and 128 on the prefill layer (1.80 / 1.86 / 2.12 ms): the chunk work that
+// does not touch the state is repeated per workgroup, but the state phases
+// shrink and more compute units take part
+constexpr int KDA_BW = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -89,7 +94,7 @@ constexpr int TP = CH + 8;
 __device__ __forceinline__ int sw8(int r, int c) { return r * KP + c; }
 __device__ __forceinline__ int swT(int r, int c) { return r * TP + c; }
 
-template <int DV>
+template <int BW>
 struct KdaSmem {
   alignas(16) float Gm[CH][FP];   // cumulative decay, log2 units
   alignas(16) bf16 Ke[CH * KP];   // k * exp(gamma)                              (sw8)
@@ -101,7 +106,7 @@ struct KdaSmem {
   alignas(16) bf16 QU[5][16 * KP];  // q, upper rows
   alignas(16) bf16 KL[5][16 * KP];  // k, lower rows
   alignas(16) bf16 KtT[DK * TP];  // (k * exp(gamma_31 - gamma))^T: [channel][row] (swT)
-  alignas(16) bf16 VT[DV * TP];   // v^T: [column][row]                            (swT)
+  alignas(16) bf16 VT[BW * TP];   // v^T of the block's columns: [column][row]    (swT)
   alignas(16) float Am[CH][MP];   // A (strictly lower; upper blocks stay 0)
   alignas(16) float Pm[CH][MP];   // P (lower)
   alignas(16) float Tm[CH][MP];   // T11 in [0,16)^2, T22 in [16,32)^2
@@ -152,24 +157,26 @@ __device__ __forceinline__ f32x4 gram16(const bf16 *X, const bf16 *Y, int m, int
   return acc;
 }
 
-template <int DV>
+template <int DV, int BW>
 __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
-  constexpr int NSW = DV / 16;  // state waves: wave w < NSW owns columns 16w..16w+15
+  constexpr int NSW = BW / 16;  // state waves: wave w < NSW owns block columns 16w..16w+15
+  constexpr int NVB = DV / BW;  // workgroups per (sequence, head)
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  KdaSmem<DV> &sm = *reinterpret_cast<KdaSmem<DV> *>(smem_raw);
+  KdaSmem<BW> &sm = *reinterpret_cast<KdaSmem<BW> *>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int h = blockIdx.x % p.H_v;
-  const int n = blockIdx.x / p.H_v;
+  const int vb = blockIdx.x % NVB;
+  const int h = (blockIdx.x / NVB) % p.H_v;
+  const int n = blockIdx.x / (NVB * p.H_v);
   const int hk = h / (p.H_v / p.H_k);
-  const int col0 = 16 * wave;  // this wave's first value column (state waves)
+  const int col0 = vb * BW + 16 * wave;  // this wave's first value column (state waves)
   int64_t t0, t1;
   seq_bounds(p.cu, p.seq_len, n, t0, t1);
 
   // row-phase mapping: thread t holds row t / 16, channels 8 (t % 16) .. +7
   const int pr = tid >> 4, pc = 8 * (tid & 15);
-  constexpr int VC = DV / 16;  // value columns per thread in the row phase
+  constexpr int VC = BW / 16;  // value columns per thread in the row phase
   const float neg_exp_A = -expf(p.A_log[h]) * LOG2E;
   if (tid < DK) sm.dtb[tid] = p.dt_bias[h * DK + tid];
 
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
     pk = *reinterpret_cast<const bf16x8 *>(p.k + (row * p.H_k + hk) * DK + pc);
     pq = *reinterpret_cast<const bf16x8 *>(p.q + (row * p.H_k + hk) * DK + pc);
     pa = *reinterpret_cast<const bf16x8 *>(p.a + (row * p.H_v + h) * DK + pc);
-    pv = *reinterpret_cast<const bf16xv *>(p.v + (row * p.H_v + h) * DV + VC * (tid & 15));
+    pv = *reinterpret_cast<const bf16xv *>(p.v + (row * p.H_v + h) * DV + vb * BW + VC * (tid & 15));
     if (tid < CH) pb = p.b[(t0 + (int64_t)c * CH + min(tid, last)) * p.H_v + h];
   };
   if (nch > 0) prefetch(0);
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
       f32x4 R[2];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const bf16x4 vb4 = __builtin_bit_cast(bf16x4, ld_op4(&sm.VT[swT(col0 + m, 16 * rt + 4 * g)]));
+        const bf16x4 vb4 = __builtin_bit_cast(bf16x4, ld_op4(&sm.VT[swT(16 * wave + m, 16 * rt + 4 * g)]));
         const f32x4 bt = ld4(&sm.beta[16 * rt + 4 * g]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) R[rt][j] = bt[j] * (static_cast<float>(vb4[j]) - ks[rt][j]);
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
   }
 }
 
-template <int DV>
+template <int DV, int BW>
 hipError_t launch_dv(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   KdaParams p;
   p.q = static_cast<const bf16 *>(x.q);
@@ -439,10 +446,10 @@ hipError_t launch_dv(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   p.H_v = pr.H_v;
   p.scale = pr.scale;
   p.eps = pr.eps;
-  const int64_t grid = (int64_t)pr.num_seqs * pr.H_v;
+  const int64_t grid = (int64_t)pr.num_seqs * pr.H_v * (DV / BW);
   if (grid == 0) return hipSuccess;
-  const size_t smem = sizeof(KdaSmem<DV>);
-  auto kern = chunked_kda_kernel<DV>;
+  const size_t smem = sizeof(KdaSmem<BW>);
+  auto kern = chunked_kda_kernel<DV, BW>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
@@ -458,7 +465,7 @@ bool chunked_kda_supports(const Problem &p) {
 }
 
 hipError_t launch_chunked_kda(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  return pr.d_v == 64 ? launch_dv<64>(pr, x, s) : launch_dv<128>(pr, x, s);
+  return pr.d_v == 64 ? launch_dv<64, KDA_BW>(pr, x, s) : launch_dv<128, KDA_BW>(pr, x, s);
 }
 
 }  // namespace gdr
