@@ -3,7 +3,7 @@
  *
  * The plain, slow, fp64 CPU definition of the gated delta rule, used by the
  * tests, by the smoke check and by the CPU-baseline leg of the benchmark to
- * judge the GPU library.  Nothing in the product path may link, load or call
+ * check the GPU library.  Nothing in the product path may link, load or call
  * this file; it shares no code, header or table with the GPU library.
  *
  * What it computes (one sequential pass per (sequence, value head), exactly in
@@ -26,7 +26,7 @@
  *   switch below exists only so that the tests can pin that reduction; the
  *   GPU library has no such switch.
  *
- * Readings of points the pages leave open (each also listed in the design doc):
+ * Readings of points the pages leave open:
  *   - value head h reads key head h / (H_v / H_k) (contiguous groups);
  *   - q has the key heads' layout [tokens, H_k, d_k];
  *   - L2 normalisation is x / sqrt(sum x^2 + l2_eps), l2_eps given by caller;
