@@ -214,6 +214,22 @@ __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
   };
   if (nch > 0) prefetch(0);
   __syncthreads();
+  // outputs of the previous chunk, stored one chunk late: after the next
+  // chunk's rows have been waited for and before its prefetch is issued, so
+  // that no wait for a prefetch also waits for these stores
+  f32x4 o_prev0 = {0.f, 0.f, 0.f, 0.f}, o_prev1 = {0.f, 0.f, 0.f, 0.f};
+  int64_t c0_prev = 0;
+  int cl_prev = 0;
+  auto store_outputs = [&]() {
+    if (wave < NSW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = 4 * g + j, r1 = 16 + 4 * g + j;
+        if (r0 < cl_prev) p.o[((c0_prev + r0) * p.H_v + h) * DV + col0 + m] = static_cast<bf16>(o_prev0[j]);
+        if (r1 < cl_prev) p.o[((c0_prev + r1) * p.H_v + h) * DV + col0 + m] = static_cast<bf16>(o_prev1[j]);
+      }
+    }
+  };
 
   for (int c = 0; c < nch; ++c) {
     const int64_t c0 = t0 + (int64_t)c * CH;
@@ -259,6 +275,7 @@ __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
       if (tid < CH) sm.beta[tid] = tid < cl ? sigmoid_f32(static_cast<float>(pb)) : 0.f;
     }
     __syncthreads();
+    if (c > 0) store_outputs();
     if (c + 1 < nch) prefetch(c + 1);
     // ---- 2: cumulative decay per channel (two threads per channel, 16 rows
     //         each, in adjacent lanes); exp(gamma_31)
@@ -401,12 +418,10 @@ __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
       const f32x4 o0 = mma16(pk4(ld4(&sm.Pm[m][4 * g])), d1b, qs[0]);
       const f32x4 o1 = mma16(pk4(ld4(&sm.Pm[16 + m][16 + 4 * g])), d2b,
                              mma16(pk4(ld4(&sm.Pm[16 + m][4 * g])), d1b, qs[1]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r0 = 4 * g + j, r1 = 16 + 4 * g + j;
-        if (r0 < cl) p.o[((c0 + r0) * p.H_v + h) * DV + col0 + m] = static_cast<bf16>(o0[j]);
-        if (r1 < cl) p.o[((c0 + r1) * p.H_v + h) * DV + col0 + m] = static_cast<bf16>(o1[j]);
-      }
+      o_prev0 = o0;
+      o_prev1 = o1;
+      c0_prev = c0;
+      cl_prev = cl;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const f32x4 dc = ld4(&sm.decay[16 * t + 4 * g]);
@@ -418,6 +433,7 @@ __global__ __launch_bounds__(NT) void chunked_kda_kernel(KdaParams p) {
     }
     __syncthreads();
   }
+  if (nch > 0) store_outputs();
   if (wave < NSW && p.sT) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
