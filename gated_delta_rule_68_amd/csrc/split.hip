@@ -35,16 +35,16 @@ __global__ __launch_bounds__(FILL_THREADS) void identity_kernel(float *dst, int6
   }
 }
 
-// Entry states of the segments of one (sequence, value head), 16 columns per
+// Entry states of the segments of one (sequence, value head), 4 columns per
 // workgroup:  S_in(0) = S0 (or 0),  S_in(p+1) = M_p S_in(p) + S_loc,p.
-// The current 16 columns of S_in stay in LDS; each M_p is staged into LDS
-// transposed (rows padded to D + 4 floats), and thread (rg, cg) accumulates
-// rows RPT rg .. RPT rg + RPT-1 and columns 2cg, 2cg+1.  The loads of the next
-// segment's M and S_loc are issued, all at once, before this segment's
-// contraction, so the pass waits for memory once per launch rather than once
-// per load.
-constexpr int COMB_THREADS = 256;
-constexpr int COMB_COLS = 16;
+// The workgroup keeps its 4 columns of S_in in LDS.  Thread (r, half) holds
+// half of row r of M_p in registers, columns 64 half .. (D/2 of them), and the
+// same half of M_{p+1} is loaded while segment p is contracted; each thread
+// sums its half over the 4 columns, and the two halves of a row (adjacent
+// lanes) add up by a lane exchange.  M never passes through LDS, so a step is
+// one register-resident contraction of D/2 x 4 and a barrier, and D/4 * (N H)
+// workgroups share the work.
+constexpr int COMB_COLS = 4;
 
 struct CombParams {
   const float *s0;    // [N, H, D, D] or nullptr
@@ -55,93 +55,66 @@ struct CombParams {
 };
 
 template <int D>
-__global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombParams p) {
-  extern __shared__ __align__(16) float lds[];
-  constexpr int PITCH = D + 4;
-  constexpr int RPT = D >= 32 ? D / 32 : 1;            // rows per thread
-  constexpr int NF4 = (D * D / 4 + COMB_THREADS - 1) / COMB_THREADS;  // M float4 per thread
-  float *Mt = lds;                                     // [D][PITCH]: Mt[j][r] = M[r][j]
-  float *Sb = lds + D * PITCH;                         // [D][COMB_COLS]
-  const int nh = blockIdx.x;                           // n * H + h
+__global__ __launch_bounds__(2 * D) void combine_kernel(CombParams p) {
+  constexpr int HALF = D / 2;        // contraction columns per thread
+  constexpr int NF4 = HALF / 4;      // float4 of M per thread
+  __shared__ __align__(16) float Sb[2][D][COMB_COLS];  // S_in columns, double-buffered
+  const int nh = blockIdx.x;                          // n * H + h
   const int n = nh / p.H, h = nh % p.H;
   const int c0 = blockIdx.y * COMB_COLS;
   const int tid = threadIdx.x;
-  const int rg = tid / (COMB_COLS / 2), cg = tid % (COMB_COLS / 2);  // rg < 32
-  const bool rows = rg * RPT < D;
+  const int r = tid >> 1, half = tid & 1;
+  const int j0 = HALF * half;
   constexpr size_t MAT = (size_t)D * D;
   auto at = [&](int seg) { return ((size_t)(n * p.P + seg) * p.H + h) * MAT; };
 
-  float4 mr[NF4];
-  float lr[RPT][2], ln[RPT][2];
-  auto fetch = [&](int seg, float (&l)[RPT][2]) {
-    const float4 *M4 = reinterpret_cast<const float4 *>(p.M + at(seg));
+  float4 mc[NF4], mn[NF4];
+  float lc[2] = {0.f, 0.f}, ln[2] = {0.f, 0.f};  // S_loc[r][c0 + 2 half + 0..1]
+  auto fetch = [&](int seg, float4 (&m)[NF4], float (&l)[2]) {
+    const float4 *M4 = reinterpret_cast<const float4 *>(p.M + at(seg) + (size_t)r * D + j0);
 #pragma unroll
-    for (int f = 0; f < NF4; ++f) {
-      const int i = tid + f * COMB_THREADS;
-      if (i < D * D / 4) mr[f] = M4[i];
-    }
-    if (rows) {
-      const float *L = p.Sloc + at(seg);
-#pragma unroll
-      for (int a = 0; a < RPT; ++a) {
-        const int r = RPT * rg + a;
-        l[a][0] = L[(size_t)r * D + c0 + 2 * cg];
-        l[a][1] = L[(size_t)r * D + c0 + 2 * cg + 1];
-      }
-    }
+    for (int f = 0; f < NF4; ++f) m[f] = M4[f];
+    const float *L = p.Sloc + at(seg) + (size_t)r * D + c0 + 2 * half;
+    l[0] = L[0];
+    l[1] = L[1];
   };
 
-  for (int i = tid; i < D * COMB_COLS; i += COMB_THREADS) {
-    const int r = i / COMB_COLS, c = i % COMB_COLS;
-    Sb[i] = p.s0 ? p.s0[((size_t)n * p.H + h) * MAT + (size_t)r * D + c0 + c] : 0.0f;
-  }
-  if (p.P > 1) fetch(0, lr);
+  // S_in(0): thread (r, half) owns columns c0 + 2 half, +1 of row r
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    Sb[0][r][2 * half + c] =
+        p.s0 ? p.s0[((size_t)n * p.H + h) * MAT + (size_t)r * D + c0 + 2 * half + c] : 0.0f;
+  if (p.P > 1) fetch(0, mc, lc);
   __syncthreads();
   for (int seg = 0;; ++seg) {
-    for (int i = tid; i < D * COMB_COLS; i += COMB_THREADS) {
-      const int r = i / COMB_COLS, c = i % COMB_COLS;
-      p.Sin[at(seg) + (size_t)r * D + c0 + c] = Sb[i];
-    }
+    const int cur = seg & 1;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      p.Sin[at(seg) + (size_t)r * D + c0 + 2 * half + c] = Sb[cur][r][2 * half + c];
     if (seg + 1 == p.P) break;
+    if (seg + 2 < p.P) fetch(seg + 1, mn, ln);  // in flight during this contraction
+    float acc[COMB_COLS] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int f = 0; f < NF4; ++f) {
-      const int i = tid + f * COMB_THREADS;
-      if (i < D * D / 4) {
-        const int r = (4 * i) / D, j = (4 * i) % D;
-        Mt[(j + 0) * PITCH + r] = mr[f].x;
-        Mt[(j + 1) * PITCH + r] = mr[f].y;
-        Mt[(j + 2) * PITCH + r] = mr[f].z;
-        Mt[(j + 3) * PITCH + r] = mr[f].w;
+      const float mv[4] = {mc[f].x, mc[f].y, mc[f].z, mc[f].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 sv = *reinterpret_cast<const float4 *>(&Sb[cur][j0 + 4 * f + e][0]);
+        acc[0] += mv[e] * sv.x;
+        acc[1] += mv[e] * sv.y;
+        acc[2] += mv[e] * sv.z;
+        acc[3] += mv[e] * sv.w;
       }
     }
-    if (seg + 2 < p.P) fetch(seg + 1, ln);  // next segment's operands, in flight meanwhile
-    __syncthreads();
-    float acc[RPT][2];
 #pragma unroll
-    for (int a = 0; a < RPT; ++a) acc[a][0] = acc[a][1] = 0.0f;
-    if (rows) {
-#pragma unroll 8
-      for (int j = 0; j < D; ++j) {
-        const float2 sv = *reinterpret_cast<const float2 *>(Sb + j * COMB_COLS + 2 * cg);
+    for (int c = 0; c < COMB_COLS; ++c) acc[c] += __shfl_xor(acc[c], 1, 64);
+    // the other buffer was last read a step ago, behind the previous barrier
+    Sb[cur ^ 1][r][2 * half] = acc[2 * half] + lc[0];
+    Sb[cur ^ 1][r][2 * half + 1] = acc[2 * half + 1] + lc[1];
 #pragma unroll
-        for (int a = 0; a < RPT; ++a) {
-          const float m = Mt[j * PITCH + RPT * rg + a];
-          acc[a][0] += m * sv.x;
-          acc[a][1] += m * sv.y;
-        }
-      }
-    }
-    __syncthreads();  // every thread is done with Sb and Mt
-    if (rows) {
-#pragma unroll
-      for (int a = 0; a < RPT; ++a) {
-        const int r = RPT * rg + a;
-        Sb[r * COMB_COLS + 2 * cg] = acc[a][0] + lr[a][0];
-        Sb[r * COMB_COLS + 2 * cg + 1] = acc[a][1] + lr[a][1];
-        lr[a][0] = ln[a][0];
-        lr[a][1] = ln[a][1];
-      }
-    }
+    for (int f = 0; f < NF4; ++f) mc[f] = mn[f];
+    lc[0] = ln[0];
+    lc[1] = ln[1];
     __syncthreads();
   }
 }
@@ -167,12 +140,7 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 template <int D>
 hipError_t launch_combine(const CombParams &cp, hipStream_t s) {
-  const size_t lds = ((size_t)D * (D + 4) + (size_t)D * COMB_COLS) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(combine_kernel<D>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel<D>, dim3(cp.N * cp.H, D / COMB_COLS), dim3(COMB_THREADS), lds,
-                     s, cp);
+  hipLaunchKernelGGL(combine_kernel<D>, dim3(cp.N * cp.H, D / COMB_COLS), dim3(2 * D), 0, s, cp);
   return hipGetLastError();
 }
 
