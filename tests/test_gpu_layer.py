@@ -199,3 +199,44 @@ def test_gated_rmsnorm_prefill_layer():
     err = np.max(np.abs(to_np(out) - ref)) / np.max(np.abs(ref))
     note(f"  norm prefill layer max rel err {err:.2e}")
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_layer_end_to_end(dtype):
+    """conv + SiLU -> the rule (chunked) -> gated RMSNorm through the library,
+    against the same chain of fp64 oracles (the conv oracle's outputs feed the
+    rule's oracle directly, unrounded).  The chain's error is dominated by the
+    rule's bar, so that is the bar here: per sequence and head, max |x - y| /
+    max |y| of the normalised output within 2e-2 (bf16) or 1e-4 (fp32)."""
+    import oracle
+    H_k, H_v, d = 2, 6, 128
+    lens = [130, 1, 64]
+    note(f"[layer e2e] {dtype} H={H_v}/{H_k} d={d} lens={lens}")
+    c = conv_case(21, H_k, H_v, d, d, lens, 4, dtype, True, True)
+    rng = np.random.default_rng(22)
+    total, N = int(sum(lens)), len(lens)
+    dt = TDT[dtype]
+    a = to_dev(rng.standard_normal((total, H_v)), dt)
+    b = to_dev(rng.standard_normal((total, H_v)), dt)
+    A_log = to_dev(rng.uniform(0.0, np.log(16.0), H_v), torch.float32)
+    dt_bias = to_dev(0.1 * rng.standard_normal(H_v), torch.float32)
+    s0 = to_dev(0.01 * rng.standard_normal((N, H_v, d, d)), torch.float32)
+    z = to_dev(rng.standard_normal((total, H_v, d)), dt)
+    nw = to_dev(1.0 + 0.1 * rng.standard_normal(d), torch.float32)
+    q, k, v, _ = gdr.conv_silu(c["x"], c["w"], H_k, H_v, d, d, bias=c["b"], conv_state=c["s0"],
+                               cu_seqlens=c["cu"])
+    o, S = gdr.chunked_fwd(q, k, v, a, b, A_log, dt_bias, s0, chunk=32, cu_seqlens=c["cu"])
+    out = gdr.gated_rmsnorm(o, z, nw, 1e-6)
+    torch.cuda.synchronize()
+    cu = c["cu"].cpu().numpy()
+    y_ref, _ = layer.short_conv_silu(c["x"], c["w"], c["b"], c["s0"], cu_seqlens=cu)
+    qr = y_ref[:, :H_k * d].reshape(total, H_k, d)
+    kr = y_ref[:, H_k * d:2 * H_k * d].reshape(total, H_k, d)
+    vr = y_ref[:, 2 * H_k * d:].reshape(total, H_v, d)
+    o_ref, S_ref = oracle.fwd(qr, kr, vr, a, b, A_log, dt_bias, initial_state=s0, cu_seqlens=cu)
+    out_ref = layer.gated_rmsnorm(o_ref, z, nw, 1e-6)
+    from tests import gpu_util as U
+    eo, es = U.compare_full(out, S, out_ref, S_ref, [int(x) for x in cu], H_v)
+    bar = 2e-2 if dtype == "bf16" else 1e-4
+    note(f"  end to end: out {eo:.3e}, state {es:.3e} (bar {bar:g})")
+    assert eo <= bar and es <= bar, (eo, es)
