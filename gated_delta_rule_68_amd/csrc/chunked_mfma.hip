@@ -605,6 +605,51 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const 
   S.P[1][lane] = pack8(v10, v11);
 }
 
+// SSD mode: the output mask of one chunk split over both prepare waves (P0
+// has no erase work to do there): PART 0 takes rows 0..15 (one diagonal
+// block), PART 1 rows 16..31 (the block below it and the second diagonal
+// block), each writing its own P slot.  Otherwise as prepare_p1 with q
+// unnormalised.
+template <int PART>
+__device__ __forceinline__ void prepare_p_ssd(Stage &S, const RowOps &o, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
+  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
+  if constexpr (PART == 0) {
+    f32x4 p00 = z;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) p00 = mma32(o.k0[kb], o.q0[kb], p00);
+    f32x4 v00;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * g + j;
+      v00[j] = (i <= m) ? fast_exp(fminf(gm_m0 - gm_lo[j], 0.f)) * p00[j] : 0.f;
+    }
+    S.P[0][lane] = pack8(v00, z);
+    if (g == 0) {
+      const int cl = S.cl;
+      S.iq[m] = (m < cl) ? 1.0f : 0.f;
+      S.iq[16 + m] = (16 + m < cl) ? 1.0f : 0.f;
+    }
+  } else {
+    f32x4 p10 = z, p11 = z;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      p10 = mma32(o.k0[kb], o.q1[kb], p10);
+      p11 = mma32(o.k1[kb], o.q1[kb], p11);
+    }
+    f32x4 v10, v11;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * g + j;
+      v10[j] = fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * p10[j];
+      v11[j] = (i <= m) ? fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * p11[j] : 0.f;
+    }
+    S.P[1][lane] = pack8(v10, v11);
+  }
+}
+
 // DVT: d_v (64 or 128; d_k is 128).  SSD: the Mamba-2 SSD recurrence on the
 // same scan -- no norms, no erase (T = I, Delta = diag(beta) V with no K S),
 // g = A delta, beta = delta; the prepare wave P0 is idle.
@@ -814,19 +859,23 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       const int c = it - 1;
       // (SSD: no erase, so P0 has nothing to prepare and only keeps the barriers)
       if (c >= 0 && c < nch) {
-        if (wave == W_P0) {
-          if constexpr (!SSD) prepare_p0(p, sm.st[c % NSTAGE], ops, lane);
+        if constexpr (SSD) {
+          if (wave == W_P0)
+            prepare_p_ssd<0>(sm.st[c % NSTAGE], ops, lane);
+          else
+            prepare_p_ssd<1>(sm.st[c % NSTAGE], ops, lane);
+        } else if (wave == W_P0) {
+          prepare_p0(p, sm.st[c % NSTAGE], ops, lane);
         } else {
           prepare_p1<SSD>(p, sm.st[c % NSTAGE], ops, lane);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS writes are done
       if (it < nch) {
-        if (wave == W_P0) {
-          if constexpr (!SSD) read_row_ops<false>(sm.st[it % NSTAGE], ops, m, g);
-        } else {
+        if (wave == W_P0 && !SSD)
+          read_row_ops<false>(sm.st[it % NSTAGE], ops, m, g);
+        else
           read_row_ops<true>(sm.st[it % NSTAGE], ops, m, g);
-        }
       }
       block_sync<63, false>();
     }
