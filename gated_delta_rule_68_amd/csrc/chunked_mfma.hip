@@ -565,7 +565,6 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const 
 // P1: scale/|q_r| from the Gram diagonal of q, and the output mask without the
 // row norms, P[r][i] = exp(gam_r - gam_i) (q_r . k_i) for i <= r, of one chunk
 // (scale/|q_r| and 1/|k_i| are applied by the output waves).
-template <bool SSD>
 __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const RowOps &o,
                                            int lane) {
   const int m = lane & 15, g = lane >> 4;
@@ -579,18 +578,15 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const 
     p00 = mma32(o.k0[kb], o.q0[kb], p00);
     p10 = mma32(o.k0[kb], o.q1[kb], p10);
     p11 = mma32(o.k1[kb], o.q1[kb], p11);
-    if constexpr (!SSD) {
-      qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
-      qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
-    }
+    qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
+    qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
   }
   // scale/|q_r| from the diagonal: lane (m, g = m/4) holds |q_m|^2 in register m%4
-  // (SSD: q is not normalised, the scale is 1)
   if (g == (m >> 2)) {
     const int cl = S.cl;
     const int j = m & 3;
-    S.iq[m] = (m < cl) ? (SSD ? 1.0f : rsqrtf(qq0[j] + p.eps) * p.scale) : 0.f;
-    S.iq[16 + m] = (16 + m < cl) ? (SSD ? 1.0f : rsqrtf(qq1[j] + p.eps) * p.scale) : 0.f;
+    S.iq[m] = (m < cl) ? rsqrtf(qq0[j] + p.eps) * p.scale : 0.f;
+    S.iq[16 + m] = (16 + m < cl) ? rsqrtf(qq1[j] + p.eps) * p.scale : 0.f;
   }
   f32x4 v00, v10, v11;
 #pragma unroll
@@ -867,7 +863,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         } else if (wave == W_P0) {
           prepare_p0(p, sm.st[c % NSTAGE], ops, lane);
         } else {
-          prepare_p1<SSD>(p, sm.st[c % NSTAGE], ops, lane);
+          prepare_p1(p, sm.st[c % NSTAGE], ops, lane);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS writes are done
