@@ -363,6 +363,27 @@ def split_legs(gdr, dev, stream, steps):
                                   "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
                                   "flop_per_launch": flops}}
         del inp, args
+    # the per-channel-decay variant on one long head (its chunk step is slower
+    # than the rule's, so the chain of chunks weighs more)
+    w = synth.custom(1, 1, 128, 128, "bf16", seq_len=16384, num_seqs=1, chunk=32)
+    seg = 1024
+    inp = synth.kda_inputs(w, 0, device=dev)
+    args = (inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+            inp["initial_state"])
+    T = w.total_tokens
+    direct_ms = timed(lambda: gdr.kda_chunked_fwd(*args, chunk=32, num_seqs=1))
+    split_ms = timed(lambda: gdr.kda_chunked_fwd_split(*args, segment_len=seg, chunk=32,
+                                                       num_seqs=1))
+    flops = kda_prefill_flops(T, 1, 1, 128, 128, 32)
+    tf = flops / (split_ms / 1e3) / 1e12
+    res["kda_single_head_16384_bf16"] = {
+        "workload": f"KDA, 1 sequence x {T} tokens, 1 head, d_k=d_v=128, bf16, chunk 32, "
+                    f"{T // seg} segments of {seg}",
+        "direct_ms": direct_ms, "split_ms": split_ms, "speedup": direct_ms / split_ms,
+        "tokens_per_s": T / (split_ms / 1e3),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "flop_per_launch": flops}}
+    del inp, args
     return res
 
 

@@ -38,7 +38,8 @@ import torch
 
 __all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", "chunked_path", "conv_silu",
            "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version",
-           "ssd_recurrent_fwd", "ssd_chunked_fwd", "kda_recurrent_fwd", "kda_chunked_fwd"]
+           "ssd_recurrent_fwd", "ssd_chunked_fwd", "kda_recurrent_fwd", "kda_chunked_fwd",
+           "kda_chunked_fwd_split"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -90,8 +91,9 @@ def _bind(lib):
     lib.gdr_conv_silu.restype = ctypes.c_int
     lib.gdr_gated_rmsnorm.argtypes = [sp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.gdr_gated_rmsnorm.restype = ctypes.c_int
-    lib.gdr_chunked_fwd_split.argtypes = [sp, ctypes.c_int32] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
-    lib.gdr_chunked_fwd_split.restype = ctypes.c_int
+    for name in ("gdr_chunked_fwd_split", "gdr_kda_chunked_fwd_split"):
+        getattr(lib, name).argtypes = [sp, ctypes.c_int32] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
+        getattr(lib, name).restype = ctypes.c_int
     lib.gdr_chunked_split_workspace.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunked_split_workspace.restype = ctypes.c_int
     for name in ("gdr_kda_recurrent_fwd", "gdr_kda_chunked_fwd"):
@@ -399,12 +401,28 @@ def chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segm
     """Chunked form with every sequence cut into segments of ``segment_len``
     tokens run in parallel (two-level scan).  Dense batches, d_k == d_v; the
     workspace is allocated here with torch."""
+    return _split("gdr_chunked_fwd_split", q, k, v, a, b, A_log, dt_bias, initial_state,
+                  segment_len, chunk, num_seqs, scale, l2_eps, o, final_state,
+                  output_final_state, inplace, kda=False)
+
+
+def kda_chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segment_len,
+                          chunk=32, num_seqs=None, scale=None, l2_eps=1e-6, o=None,
+                          final_state=None, output_final_state=True, inplace=False):
+    """The segmented chunked form for KDA (a [.., H_v, d_k], dt_bias [H_v, d_k])."""
+    return _split("gdr_kda_chunked_fwd_split", q, k, v, a, b, A_log, dt_bias, initial_state,
+                  segment_len, chunk, num_seqs, scale, l2_eps, o, final_state,
+                  output_final_state, inplace, kda=True)
+
+
+def _split(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, segment_len, chunk, num_seqs,
+           scale, l2_eps, o, final_state, output_final_state, inplace, kda):
     dense_T = q.shape[1] if q.dim() == 4 else None
     q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
-    a, b = _flatten(a, 1), _flatten(b, 1)
+    a, b = _flatten(a, 2 if kda else 1), _flatten(b, 1)
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError(f"gdr_chunked_fwd_split: tensors must be on a GPU (got {dev})")
+        raise ValueError(f"{fn_name}: tensors must be on a GPU (got {dev})")
     dt = q.dtype
     code = _dtype_code(dt)
     total, H_k, d_k = q.shape
@@ -412,10 +430,10 @@ def chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segm
     _check(q, "q", dev, dt)
     _check(k, "k", dev, dt, (total, H_k, d_k))
     _check(v, "v", dev, dt, (total, H_v, d_v))
-    _check(a, "a", dev, dt, (total, H_v))
+    _check(a, "a", dev, dt, (total, H_v, d_k) if kda else (total, H_v))
     _check(b, "b", dev, dt, (total, H_v))
     _check(A_log, "A_log", dev, torch.float32, (H_v,))
-    _check(dt_bias, "dt_bias", dev, torch.float32, (H_v,))
+    _check(dt_bias, "dt_bias", dev, torch.float32, (H_v, d_k) if kda else (H_v,))
     shape = _make_shape(total, H_k, H_v, d_k, d_v, None, num_seqs, code, chunk, scale, l2_eps,
                         dense_T)
     N = shape.num_seqs
@@ -438,12 +456,12 @@ def chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segm
     _raise("gdr_chunked_split_workspace",
            lib().gdr_chunked_split_workspace(ctypes.byref(shape), int(segment_len), ctypes.byref(nbytes)))
     ws = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
-    rc = lib().gdr_chunked_fwd_split(ctypes.byref(shape), int(segment_len), _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
-                                     _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                     _ptr(ws) if nbytes.value else None, int(nbytes.value),
-                                     _stream(dev))
-    _raise("gdr_chunked_fwd_split", rc)
+    rc = getattr(lib(), fn_name)(ctypes.byref(shape), int(segment_len), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                 _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                 _ptr(ws) if nbytes.value else None, int(nbytes.value),
+                                 _stream(dev))
+    _raise(fn_name, rc)
     if dense_T is not None:
         o = o.view(N, dense_T, H_v, d_v)
     return o, final_state

@@ -269,14 +269,20 @@ gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, const void *
 namespace gdr {
 namespace {
 // Segmented chunked form: shape rules, then the workspace layout.
-gdr_status split_problem(const gdr_shape *shape, int32_t segment_len, Problem &pr) {
+bool chunked_any_supports(const Problem &pr) {
+  if (pr.mode == kModeKDA) return chunked_kda_supports(pr) || chunked_vec_supports(pr);
+  return chunked_mfma_supports(pr) || chunked_vec_supports(pr);
+}
+gdr_status split_problem(const gdr_shape *shape, int32_t segment_len, Problem &pr,
+                         int mode = kModeRule) {
   gdr_status st = resolve(shape, pr);
   if (st != GDR_OK) return st;
+  pr.mode = mode;
   if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
   if (pr.cu != nullptr || pr.d_k != pr.d_v) return GDR_ERR_UNSUPPORTED;
   if (segment_len <= 0 || segment_len % pr.chunk != 0) return GDR_ERR_SHAPE;
   if (pr.seq_len % segment_len != 0) return GDR_ERR_SHAPE;
-  if (!chunked_mfma_supports(pr) && !chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  if (!chunked_any_supports(pr)) return GDR_ERR_UNSUPPORTED;
   if ((int64_t)pr.num_seqs * (pr.seq_len / segment_len) > 0x7fffffffLL / pr.H_v)
     return GDR_ERR_UNSUPPORTED;
   return GDR_OK;
@@ -295,19 +301,23 @@ gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t segment_l
   return GDR_OK;
 }
 
-gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, const void *q,
-                                 const void *k, const void *v, const void *a, const void *b,
-                                 const float *A_log, const float *dt_bias,
-                                 const float *initial_state, void *o, float *final_state,
-                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  using namespace gdr;
+namespace gdr {
+namespace {
+gdr_status split_call(int mode, const gdr_shape *shape, int32_t segment_len, const void *q,
+                      const void *k, const void *v, const void *a, const void *b,
+                      const float *A_log, const float *dt_bias, const float *initial_state,
+                      void *o, float *final_state, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   Problem pr;
-  gdr_status st = split_problem(shape, segment_len, pr);
+  gdr_status st = split_problem(shape, segment_len, pr, mode);
   if (st != GDR_OK) return st;
   FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
   st = check_fwd(pr, x);
   if (st != GDR_OK) return st;
   if (pr.seq_len / segment_len <= 1) {  // one segment: the direct form
+    if (mode == kModeKDA)
+      return launched(chunked_kda_supports(pr) ? launch_chunked_kda(pr, x, stream)
+                                               : launch_chunked_vec(pr, x, stream));
     if (chunked_mfma_supports(pr)) return launched(launch_chunked_mfma(pr, x, stream));
     return launched(launch_chunked_vec(pr, x, stream));
   }
@@ -319,11 +329,12 @@ gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, co
   const size_t es = elem_size(pr.dtype);
   const size_t T = (size_t)pr.total;
   const size_t state_bytes = (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4;
+  const size_t ga = mode == kModeKDA ? (size_t)pr.d_k : 1;  // KDA: per-channel gates
   const Range ws = span(workspace, L.bytes);
   const Range others[] = {
       span(q, T * pr.H_k * pr.d_k * es), span(k, T * pr.H_k * pr.d_k * es),
-      span(v, T * pr.H_v * pr.d_v * es), span(a, T * pr.H_v * es), span(b, T * pr.H_v * es),
-      span(A_log, (size_t)pr.H_v * 4), span(dt_bias, (size_t)pr.H_v * 4),
+      span(v, T * pr.H_v * pr.d_v * es), span(a, T * pr.H_v * ga * es), span(b, T * pr.H_v * es),
+      span(A_log, (size_t)pr.H_v * 4), span(dt_bias, (size_t)pr.H_v * ga * 4),
       span(initial_state, initial_state ? state_bytes : 0), span(o, T * pr.H_v * pr.d_v * es),
       span(final_state, final_state ? state_bytes : 0)};
   for (const Range &r : others)
@@ -331,6 +342,27 @@ gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, co
   // final_state == initial_state is fine: the initial state is read by the
   // combine pass, before the last launch writes the final state
   return launched(launch_chunked_split(pr, x, segment_len, workspace, stream));
+}
+}  // namespace
+}  // namespace gdr
+
+gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, const void *q,
+                                 const void *k, const void *v, const void *a, const void *b,
+                                 const float *A_log, const float *dt_bias,
+                                 const float *initial_state, void *o, float *final_state,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return gdr::split_call(gdr::kModeRule, shape, segment_len, q, k, v, a, b, A_log, dt_bias,
+                         initial_state, o, final_state, workspace, workspace_bytes, stream);
+}
+
+gdr_status gdr_kda_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, const void *q,
+                                     const void *k, const void *v, const void *a, const void *b,
+                                     const float *A_log, const float *dt_bias,
+                                     const float *initial_state, void *o, float *final_state,
+                                     void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  return gdr::split_call(gdr::kModeKDA, shape, segment_len, q, k, v, a, b, A_log, dt_bias,
+                         initial_state, o, final_state, workspace, workspace_bytes, stream);
 }
 
 namespace gdr {

@@ -132,6 +132,8 @@ __global__ __launch_bounds__(FILL_THREADS) void last_state_kernel(const float *S
 }
 
 hipError_t chunked_any(const Problem &pr, const FwdArgs &x, hipStream_t s) {
+  if (pr.mode == kModeKDA)
+    return chunked_kda_supports(pr) ? launch_chunked_kda(pr, x, s) : launch_chunked_vec(pr, x, s);
   if (chunked_mfma_supports(pr)) return launch_chunked_mfma(pr, x, s);
   return launch_chunked_vec(pr, x, s);
 }

@@ -33,7 +33,8 @@ def test_header_declares_the_abi():
     assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_split",
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
-                                  "gdr_kda_chunked_fwd", "gdr_kda_recurrent_fwd",
+                                  "gdr_kda_chunked_fwd", "gdr_kda_chunked_fwd_split",
+                                  "gdr_kda_recurrent_fwd",
                                   "gdr_recurrent_fwd", "gdr_ssd_chunked_fwd",
                                   "gdr_ssd_recurrent_fwd", "gdr_status_string"]
 

@@ -107,3 +107,38 @@ def test_split_long_memory_stress():
     check(w, 37, 256)
     wf = synth.custom(1, 2, 64, 64, "f32", seq_len=1024, num_seqs=1, chunk=32, stress_seqs=(0,))
     check(wf, 38, 128)
+
+
+# ---------------------------------------------------------------- KDA segments
+def check_kda(w, seed, seg, a_mean=0.0):
+    from oracle import kda
+    note(f"[kda split] H={w.H_v}/{w.H_k} d={w.d_k} {w.dtype} N={w.num_seqs} T={w.seq_len} "
+         f"chunk={w.chunk} segment={seg} seed={seed}")
+    inp = synth.kda_inputs(w, seed, device=DEV, a_mean=a_mean)
+    args = (inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+            inp["initial_state"])
+    o, S = gdr.kda_chunked_fwd_split(*args, segment_len=seg, chunk=w.chunk, num_seqs=w.num_seqs)
+    torch.cuda.synchronize()
+    o_ref, S_ref = kda.kda(*[t.cpu() if t is not None else None for t in args],
+                           cu_seqlens=inp["cu_host"])
+    eo, es = U.compare_full(o, S, o_ref, S_ref, inp["cu_host"], w.H_v)
+    tol = U.TOL[w.dtype]
+    note(f"  max rel err o={eo:.3e} S={es:.3e} (bar {tol:g})")
+    assert eo <= tol and es <= tol, (eo, es)
+    return inp, args, o, S
+
+
+@pytest.mark.parametrize("dtype,chunk,seg", [("bf16", 32, 256), ("f32", 16, 64), ("bf16", 16, 128)])
+def test_kda_split(dtype, chunk, seg):
+    w = synth.custom(1, 2, 128, 128, dtype, seq_len=1024, num_seqs=2, chunk=chunk)
+    check_kda(w, 40, seg)
+
+
+def test_kda_split_one_segment_is_the_direct_form_and_long_memory():
+    w = synth.custom(1, 2, 128, 128, "bf16", seq_len=512, num_seqs=1, chunk=32)
+    inp, args, o1, S1 = check_kda(w, 41, 512)
+    o2, S2 = gdr.kda_chunked_fwd(*args, chunk=32, num_seqs=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    wl = synth.custom(1, 1, 64, 64, "f32", seq_len=2048, num_seqs=1, chunk=32)
+    check_kda(wl, 42, 256, a_mean=-6.0)  # long memory: the segment maps carry the state
