@@ -96,9 +96,12 @@ def _bind(lib):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdr_chunked_split_workspace.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunked_split_workspace.restype = ctypes.c_int
-    for name in ("gdr_kda_recurrent_fwd", "gdr_kda_chunked_fwd"):
-        getattr(lib, name).argtypes = [sp] + [vp] * 11
-        getattr(lib, name).restype = ctypes.c_int
+    lib.gdr_kda_recurrent_fwd.argtypes = [sp] + [vp] * 11
+    lib.gdr_kda_recurrent_fwd.restype = ctypes.c_int
+    lib.gdr_kda_chunked_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
+    lib.gdr_kda_chunked_fwd.restype = ctypes.c_int
+    lib.gdr_kda_chunked_workspace.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_kda_chunked_workspace.restype = ctypes.c_int
     for name in ("gdr_ssd_recurrent_fwd", "gdr_ssd_chunked_fwd"):
         getattr(lib, name).argtypes = [sp] + [vp] * 10
         getattr(lib, name).restype = ctypes.c_int
@@ -225,7 +228,7 @@ def gates(q, k, a, b, A_log, dt_bias, *, scale=None, l2_eps=1e-6, num_seqs=None,
 
 
 def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_seqs, chunk,
-         scale, l2_eps, o, final_state, output_final_state, inplace, kda=False):
+         scale, l2_eps, o, final_state, output_final_state, inplace, kda=False, fused=None):
     dense_T = q.shape[1] if q.dim() == 4 else None
     q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
     a, b = _flatten(a, 2 if kda else 1), _flatten(b, 1)
@@ -265,8 +268,17 @@ def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_
     elif final_state is not None:
         _check(final_state, "final_state", dev, torch.float32, st_shape)
     fn = getattr(lib(), fn_name)
-    rc = fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
-            _ptr(dt_bias), _ptr(initial_state), _ptr(o), _ptr(final_state), _stream(dev))
+    args = [ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+            _ptr(dt_bias), _ptr(initial_state), _ptr(o), _ptr(final_state)]
+    if fused is not None:
+        # gdr_kda_chunked_fwd: a workspace from torch selects the two-launch form
+        nbytes = ctypes.c_size_t(0)
+        if not fused:
+            _raise("gdr_kda_chunked_workspace",
+                   lib().gdr_kda_chunked_workspace(ctypes.byref(shape), ctypes.byref(nbytes)))
+        ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev) if nbytes.value else None
+        args += [_ptr(ws), ctypes.c_size_t(nbytes.value)]
+    rc = fn(*args, _stream(dev))
     _raise(fn_name, rc)
     if dense_T is not None:
         o = o.view(N, dense_T, H_v, d_v)
@@ -545,8 +557,10 @@ def kda_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, cu_s
 
 def kda_chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32,
                     cu_seqlens=None, num_seqs=None, scale=None, l2_eps=1e-6, o=None,
-                    final_state=None, output_final_state=True, inplace=False):
-    """KDA, chunked form (chunk 16 or 32)."""
+                    final_state=None, output_final_state=True, inplace=False, fused=False):
+    """KDA, chunked form (chunk 16 or 32).  By default the workspace the
+    library asks for is allocated here, which selects its two-launch form;
+    ``fused=True`` passes none and runs the one-launch form."""
     return _fwd("gdr_kda_chunked_fwd", q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens,
                 num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state, inplace,
-                kda=True)
+                kda=True, fused=bool(fused))

@@ -98,6 +98,30 @@ gdr_status check_fwd(const Problem &pr, const FwdArgs &x) {
 
 gdr_status launched(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH; }
 
+// A caller's workspace of `need` bytes: present, large enough, 256-byte
+// aligned, and overlapping nothing the call reads or writes.
+gdr_status check_workspace(const Problem &pr, const FwdArgs &x, const void *workspace,
+                           size_t workspace_bytes, size_t need) {
+  if (!workspace) return GDR_ERR_NULL;
+  if (workspace_bytes < need) return GDR_ERR_SHAPE;
+  if (!aligned_to(workspace, 256)) return GDR_ERR_ALIGN;
+  const size_t es = elem_size(pr.dtype);
+  const size_t T = (size_t)pr.total;
+  const size_t state_bytes = (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4;
+  const size_t ga = pr.mode == kModeKDA ? (size_t)pr.d_k : 1;  // KDA: per-channel gates
+  const Range ws = span(workspace, need);
+  const Range others[] = {
+      span(x.q, T * pr.H_k * pr.d_k * es), span(x.k, T * pr.H_k * pr.d_k * es),
+      span(x.v, T * pr.H_v * pr.d_v * es), span(x.a, T * pr.H_v * ga * es),
+      span(x.b, T * pr.H_v * es), span(x.A_log, (size_t)pr.H_v * 4),
+      span(x.dt_bias, (size_t)pr.H_v * ga * 4), span(x.s0, x.s0 ? state_bytes : 0),
+      span(x.o, T * pr.H_v * pr.d_v * es), span(x.sT, x.sT ? state_bytes : 0),
+      span(pr.cu, pr.cu ? (size_t)(pr.num_seqs + 1) * 4 : 0)};
+  for (const Range &r : others)
+    if (r.lo != 0 && r.hi > r.lo && overlap(r, ws)) return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
 }  // namespace
 }  // namespace gdr
 
@@ -322,23 +346,8 @@ gdr_status split_call(int mode, const gdr_shape *shape, int32_t segment_len, con
     return launched(launch_chunked_vec(pr, x, stream));
   }
   const SplitLayout L = split_layout(pr, segment_len);
-  if (!workspace) return GDR_ERR_NULL;
-  if (workspace_bytes < L.bytes) return GDR_ERR_SHAPE;
-  if (!aligned_to(workspace, 256)) return GDR_ERR_ALIGN;
-  // the workspace may overlap nothing the call reads or writes
-  const size_t es = elem_size(pr.dtype);
-  const size_t T = (size_t)pr.total;
-  const size_t state_bytes = (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4;
-  const size_t ga = mode == kModeKDA ? (size_t)pr.d_k : 1;  // KDA: per-channel gates
-  const Range ws = span(workspace, L.bytes);
-  const Range others[] = {
-      span(q, T * pr.H_k * pr.d_k * es), span(k, T * pr.H_k * pr.d_k * es),
-      span(v, T * pr.H_v * pr.d_v * es), span(a, T * pr.H_v * ga * es), span(b, T * pr.H_v * es),
-      span(A_log, (size_t)pr.H_v * 4), span(dt_bias, (size_t)pr.H_v * ga * 4),
-      span(initial_state, initial_state ? state_bytes : 0), span(o, T * pr.H_v * pr.d_v * es),
-      span(final_state, final_state ? state_bytes : 0)};
-  for (const Range &r : others)
-    if (r.lo != 0 && r.hi > r.lo && overlap(r, ws)) return GDR_ERR_ALIAS;
+  st = check_workspace(pr, x, workspace, workspace_bytes, L.bytes);
+  if (st != GDR_OK) return st;
   // final_state == initial_state is fine: the initial state is read by the
   // combine pass, before the last launch writes the final state
   return launched(launch_chunked_split(pr, x, segment_len, workspace, stream));
@@ -450,21 +459,42 @@ gdr_status gdr_kda_recurrent_fwd(const gdr_shape *shape, const void *q, const vo
   return launched(launch_recurrent(pr, x, stream));
 }
 
+gdr_status gdr_kda_chunked_workspace(const gdr_shape *shape, size_t *bytes) {
+  using namespace gdr;
+  if (!bytes) return GDR_ERR_NULL;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  pr.mode = kModeKDA;
+  if (!kda_two_pass_supports(pr) && !chunked_kda_supports(pr) && !chunked_vec_supports(pr))
+    return GDR_ERR_UNSUPPORTED;
+  *bytes = kda_two_pass_bytes(pr);
+  return GDR_OK;
+}
+
 gdr_status gdr_kda_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
                                const void *v, const void *a, const void *b, const float *A_log,
                                const float *dt_bias, const float *initial_state, void *o,
-                               float *final_state, hipStream_t stream) {
+                               float *final_state, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   using namespace gdr;
   Problem pr;
   gdr_status st = resolve(shape, pr);
   if (st != GDR_OK) return st;
   pr.mode = kModeKDA;
-  if (!chunked_kda_supports(pr) && !chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  const bool two = kda_two_pass_supports(pr);
+  if (!two && !chunked_kda_supports(pr) && !chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
   FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
   st = check_fwd(pr, x);
   if (st != GDR_OK) return st;
+  if (workspace && two) {
+    st = check_workspace(pr, x, workspace, workspace_bytes, kda_two_pass_bytes(pr));
+    if (st != GDR_OK) return st;
+    return launched(launch_kda_two_pass(pr, x, workspace, stream));
+  }
   if (chunked_kda_supports(pr)) return launched(launch_chunked_kda(pr, x, stream));
-  return launched(launch_chunked_vec(pr, x, stream));
+  if (chunked_vec_supports(pr)) return launched(launch_chunked_vec(pr, x, stream));
+  return GDR_ERR_UNSUPPORTED;
 }
 
 int gdr_chunked_path(const gdr_shape *shape) {

@@ -92,5 +92,12 @@ bool chunked_vec_supports(const Problem &p);
 bool chunked_kda_supports(const Problem &p);
 hipError_t launch_chunked_kda(const Problem &p, const FwdArgs &x, hipStream_t s);
 bool chunked_mfma_supports(const Problem &p);
+// KDA chunked form in two launches (per-chunk operands for every chunk of the
+// batch into a workspace, then the chains): bf16, d_k = 128, d_v a multiple
+// of 16, chunk 32.  kda_two_pass_bytes is 0 for other shapes.
+bool kda_two_pass_supports(const Problem &p);
+size_t kda_two_pass_bytes(const Problem &p);
+hipError_t launch_kda_two_pass(const Problem &p, const FwdArgs &x, void *workspace,
+                               hipStream_t s);
 
 }  // namespace gdr

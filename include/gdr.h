@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 5
+#define GDR_ABI_VERSION 6
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -296,10 +296,19 @@ GDR_API gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, co
  *   a        : dtype [total, H_v, d_k]   (per-channel raw gate projections)
  *   dt_bias  : fp32  [H_v, d_k]
  * All other arguments, layouts and rules as gdr_recurrent_fwd /
- * gdr_chunked_fwd.  The chunked form runs on the vector ALUs in fp32 for both
- * dtypes (the channel-weighted Gram matrices exponentiate every channel of
- * every pair, so they are not plain matrix products) and takes chunk 16 or
- * 32 (64 returns GDR_ERR_UNSUPPORTED).
+ * gdr_chunked_fwd.  The chunked form takes chunk 16 or 32 (64 returns
+ * GDR_ERR_UNSUPPORTED).  For bf16 with d_k = 128 and chunk 32 it runs on the
+ * matrix cores, in one of two ways:
+ *  - with a workspace (gdr_kda_chunked_workspace bytes, 256-byte aligned,
+ *    overlapping no other argument, contents not kept): two launches, first
+ *    the state-free part of every chunk of the batch in parallel (gates,
+ *    cumulative decays, the channel-weighted Gram matrices, (I + A)^-1 and
+ *    the decay-scaled rows, written to the workspace), then the chains of
+ *    chunks, which do only the state-dependent products (any d_v);
+ *  - with workspace == NULL: one launch that does both per chunk on the
+ *    chain (d_v = 64 or 128).
+ * Other shapes and fp32 inputs run on the vector ALUs in fp32 and ignore the
+ * workspace.  workspace_bytes below the reported size returns GDR_ERR_SHAPE.
  */
 GDR_API gdr_status gdr_kda_recurrent_fwd(const gdr_shape *shape, const void *q, const void *k,
                                          const void *v, const void *a, const void *b,
@@ -310,7 +319,14 @@ GDR_API gdr_status gdr_kda_chunked_fwd(const gdr_shape *shape, const void *q, co
                                        const void *v, const void *a, const void *b,
                                        const float *A_log, const float *dt_bias,
                                        const float *initial_state, void *o, float *final_state,
+                                       void *workspace, size_t workspace_bytes,
                                        hipStream_t stream);
+
+/* Bytes of workspace gdr_kda_chunked_fwd uses for `shape` (0 when that shape
+ * does not run the two-launch form): one 29,696-byte record per (chunk slot,
+ * value head), floor(total_tokens / 32) + num_seqs slots.  The same shape
+ * errors as gdr_kda_chunked_fwd. */
+GDR_API gdr_status gdr_kda_chunked_workspace(const gdr_shape *shape, size_t *bytes);
 
 /*
  * gdr_kda_chunked_fwd_split -- the segmented form of gdr_chunked_fwd_split

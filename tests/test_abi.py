@@ -34,6 +34,7 @@ def test_header_declares_the_abi():
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
                                   "gdr_kda_chunked_fwd", "gdr_kda_chunked_fwd_split",
+                                  "gdr_kda_chunked_workspace",
                                   "gdr_kda_recurrent_fwd",
                                   "gdr_recurrent_fwd", "gdr_ssd_chunked_fwd",
                                   "gdr_ssd_recurrent_fwd", "gdr_status_string"]
@@ -111,8 +112,8 @@ def call(gdr, fn, s, ptrs=None):
     p = [fake(i) for i in range(10)] if ptrs is None else ptrs
     f = getattr(gdr.lib(), fn)
     arg = ctypes.byref(s) if s is not None else None
-    if fn == "gdr_gates":
-        return f(arg, *p[:10], None)
+    if fn == "gdr_kda_chunked_fwd":  # no workspace: the one-launch form
+        return f(arg, *p[:10], None, 0, None)
     return f(arg, *p[:10], None)
 
 
@@ -362,3 +363,29 @@ def test_kda_validation(gdr, fn):
 def test_kda_chunk_sizes(gdr):
     assert call(gdr, "gdr_kda_chunked_fwd", shape(gdr, chunk=64)) == 3
     assert call(gdr, "gdr_kda_chunked_fwd", shape(gdr, chunk=48)) == 3
+
+
+def test_kda_workspace_size(gdr):
+    lib = gdr.lib()
+    n = ctypes.c_size_t(123)
+    # bf16, d_k = 128, chunk 32: one 29,696-byte record per (slot, value head),
+    # floor(total / 32) + num_seqs slots
+    s = shape(gdr, dtype=1, d_k=128, d_v=64, chunk=32, total_tokens=100, num_seqs=2, seq_len=50)
+    assert lib.gdr_kda_chunked_workspace(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == (100 // 32 + 2) * 2 * 29696
+    s = shape(gdr, dtype=0, d_k=128, d_v=64, chunk=32)  # fp32: the vector kernel, no workspace
+    assert lib.gdr_kda_chunked_workspace(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.gdr_kda_chunked_workspace(ctypes.byref(shape(gdr, chunk=64)), ctypes.byref(n)) == 3
+    assert lib.gdr_kda_chunked_workspace(ctypes.byref(s), None) == 1
+
+
+def test_kda_workspace_checked(gdr):
+    f = gdr.lib().gdr_kda_chunked_fwd
+    s = shape(gdr, dtype=1, d_k=128, d_v=64, chunk=32)
+    need = (4 // 32 + 1) * 2 * 29696
+    p = [fake(i) for i in range(10)]
+    assert f(ctypes.byref(s), *p, fake(10), need - 1, None) == 2        # too small
+    assert f(ctypes.byref(s), *p, fake(10, off=16), need, None) == 4    # not 256-byte aligned
+    assert f(ctypes.byref(s), *p, fake(0, off=256), need, None) == 6    # over q
+    assert f(ctypes.byref(s), *p, fake(8, off=-4096), need, None) == 6  # runs into o

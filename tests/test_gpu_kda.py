@@ -41,8 +41,10 @@ def run(form, inp, w, chunk=32, **kw):
     if form == "recurrent":
         return gdr.kda_recurrent_fwd(*args, cu_seqlens=inp["cu_seqlens"], num_seqs=w.num_seqs,
                                      **kw)
+    # "chunked": the two-launch form (a workspace); "chunked_fused": the
+    # one-launch form (none); both reach the vector kernel off their shapes
     return gdr.kda_chunked_fwd(*args, chunk=chunk, cu_seqlens=inp["cu_seqlens"],
-                               num_seqs=w.num_seqs, **kw)
+                               num_seqs=w.num_seqs, fused=form == "chunked_fused", **kw)
 
 
 def oracle_of(inp, heads=None):
@@ -93,14 +95,15 @@ SHAPES = [
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"H{s[1]}/{s[0]}_d{s[2]}x{s[3]}")
-@pytest.mark.parametrize("form,chunk", [("recurrent", None), ("chunked", 16), ("chunked", 32)])
+@pytest.mark.parametrize("form,chunk", [("recurrent", None), ("chunked", 16), ("chunked", 32),
+                                        ("chunked_fused", 32)])
 def test_kda_small_shapes(dtype, shape, form, chunk):
     H_k, H_v, d_k, d_v, lens = shape
     w = synth.custom(H_k, H_v, d_k, d_v, dtype, lengths=lens, chunk=chunk or 32)
     check(w, 61, form, chunk or 32)
 
 
-@pytest.mark.parametrize("form", ["chunked", "recurrent"])
+@pytest.mark.parametrize("form", ["chunked", "chunked_fused", "recurrent"])
 @pytest.mark.parametrize("a_mean", [4.0, -6.0], ids=["strong_decay", "long_memory"])
 def test_kda_gate_extremes(form, a_mean):
     """Strong decay: factors through a row inside a 16-row block would
@@ -167,12 +170,49 @@ def test_kda_deterministic_and_inplace():
     assert torch.equal(c[0], a[0]) and torch.equal(st, a[1])
 
 
-def test_kda_prefill_layer_sampled():
+@pytest.mark.parametrize("form", ["chunked", "chunked_fused"])
+def test_kda_prefill_layer_sampled(form):
     """The prefill layer (8192 tokens, 48/16 heads, d = 128, bf16, chunk 32)
     in the launch configuration the benchmark times; the oracle checks three
     value heads."""
     w = synth.workload("prefill")
-    check(w, 67, "chunked", 32, heads=[0, 25, 47], tag="prefill")
+    check(w, 67, form, 32, heads=[0, 25, 47], tag="prefill")
+
+
+@pytest.mark.parametrize("lens,d_v,with_state", [
+    ([31, 0, 32, 33, 95, 1, 64], 128, True),
+    ([31, 0, 32, 33, 95, 1, 64], 64, False),
+    ([700, 5], 128, True),
+], ids=["ragged_dv128", "ragged_dv64_nostate", "long_dv128"])
+def test_kda_two_launch_vs_one_launch(lens, d_v, with_state):
+    """The two-launch form against the one-launch form on the same inputs:
+    ragged tails, empty and one-token sequences, with and without a carried
+    state."""
+    w = synth.custom(2, 6, 128, d_v, "bf16", lengths=lens, chunk=32)
+    inp = synth.kda_inputs(w, 71, device=DEV)
+    if not with_state:
+        inp = dict(inp, initial_state=None)
+    o1, S1 = run("chunked", inp, w, 32)
+    o2, S2 = run("chunked_fused", inp, w, 32)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        for h in range(w.H_v):
+            if cu[n + 1] > cu[n]:
+                worst = max(worst, U.slice_err(U.to_np(o1[cu[n]:cu[n + 1], h]),
+                                               U.to_np(o2[cu[n]:cu[n + 1], h])))
+            worst = max(worst, U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
+    note(f"  two-launch vs one-launch: {worst:.3e}")
+    assert worst <= U.TOL["bf16"]
+
+
+@pytest.mark.parametrize("d_v", [16, 32])
+def test_kda_two_launch_other_widths(d_v):
+    """Value widths that only the two-launch form runs on the matrix cores
+    (the one-launch form takes 64 and 128)."""
+    w = synth.custom(1, 2, 128, d_v, "bf16", lengths=[77, 32], chunk=32)
+    check(w, 72, "chunked", 32, tag=f"d_v={d_v}")
 
 
 def test_kda_decode_step_sampled():
