@@ -544,9 +544,14 @@ def kda_legs(gdr, dev, stream, steps):
     inp = synth.kda_inputs(w, 0, device=dev)
     o = torch.empty((w.total_tokens, w.H_v, w.d_v), dtype=w.torch_dtype, device=dev)
     S = torch.empty((1, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
-    pre_ms = timed(lambda: gdr.kda_chunked_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"],
-                                               inp["A_log"], inp["dt_bias"], None, chunk=32,
-                                               num_seqs=1, o=o, final_state=S), steps)
+
+    def pre(fused):
+        return lambda: gdr.kda_chunked_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"],
+                                           inp["A_log"], inp["dt_bias"], None, chunk=32,
+                                           num_seqs=1, o=o, final_state=S, fused=fused)
+
+    pre_ms = timed(pre(False), steps)  # prep + chains (the library's workspace form)
+    one_ms = timed(pre(True), steps)   # the one-launch form, for comparison
     T = w.total_tokens
     flops = kda_prefill_flops(T, w.H_k, w.H_v, w.d_k, w.d_v, 32)
     del inp, o, S
@@ -561,8 +566,10 @@ def kda_legs(gdr, dev, stream, steps):
                                 "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
                                 "bytes_per_launch": dbytes}},
         "prefill": {"workload": "prefill layer: 1 sequence x 8192 tokens, 48 value heads sharing "
-                                "16 key heads, d_k=d_v=128, chunk 32, bf16 inputs, fp32 state",
+                                "16 key heads, d_k=d_v=128, chunk 32, bf16 inputs, fp32 state; "
+                                "two launches (per-chunk prep over the batch, then the chains)",
                     "steps": steps, "ms_per_launch": pre_ms, "tokens_per_s": T / (pre_ms / 1e3),
+                    "one_launch_ms": one_ms,
                     "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                  "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                                  "flop_per_launch": flops}},

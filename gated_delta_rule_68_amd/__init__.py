@@ -94,8 +94,9 @@ def _bind(lib):
     for name in ("gdr_chunked_fwd_split", "gdr_kda_chunked_fwd_split"):
         getattr(lib, name).argtypes = [sp, ctypes.c_int32] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
         getattr(lib, name).restype = ctypes.c_int
-    lib.gdr_chunked_split_workspace.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
-    lib.gdr_chunked_split_workspace.restype = ctypes.c_int
+    for name in ("gdr_chunked_split_workspace", "gdr_kda_chunked_split_workspace"):
+        getattr(lib, name).argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        getattr(lib, name).restype = ctypes.c_int
     lib.gdr_kda_recurrent_fwd.argtypes = [sp] + [vp] * 11
     lib.gdr_kda_recurrent_fwd.restype = ctypes.c_int
     lib.gdr_kda_chunked_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
@@ -465,8 +466,8 @@ def _split(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, segment_len, c
     elif final_state is not None:
         _check(final_state, "final_state", dev, torch.float32, st_shape)
     nbytes = ctypes.c_size_t(0)
-    _raise("gdr_chunked_split_workspace",
-           lib().gdr_chunked_split_workspace(ctypes.byref(shape), int(segment_len), ctypes.byref(nbytes)))
+    wsq = "gdr_kda_chunked_split_workspace" if fn_name.startswith("gdr_kda") else "gdr_chunked_split_workspace"
+    _raise(wsq, getattr(lib(), wsq)(ctypes.byref(shape), int(segment_len), ctypes.byref(nbytes)))
     ws = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
     rc = getattr(lib(), fn_name)(ctypes.byref(shape), int(segment_len), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),

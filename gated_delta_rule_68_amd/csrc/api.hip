@@ -325,6 +325,17 @@ gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t segment_l
   return GDR_OK;
 }
 
+gdr_status gdr_kda_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
+                                           size_t *bytes) {
+  using namespace gdr;
+  if (!bytes) return GDR_ERR_NULL;
+  Problem pr;
+  const gdr_status st = split_problem(shape, segment_len, pr, kModeKDA);
+  if (st != GDR_OK) return st;
+  *bytes = pr.seq_len / segment_len > 1 ? split_layout(pr, segment_len).bytes : 0;
+  return GDR_OK;
+}
+
 namespace gdr {
 namespace {
 gdr_status split_call(int mode, const gdr_shape *shape, int32_t segment_len, const void *q,

@@ -70,7 +70,9 @@ struct NormArgs {
 // Workspace of the segmented chunked form (byte offsets, 256-byte aligned).
 struct SplitLayout {
   int P;  // segments per sequence
-  size_t zero_v, ident, M, Sloc, Sin, bytes;
+  size_t zero_v, ident, M, Sloc, Sin;
+  size_t prep;  // KDA on the two-launch form: the prep records (else == bytes)
+  size_t bytes;
 };
 SplitLayout split_layout(const Problem &p, int segment_len);
 hipError_t launch_chunked_split(const Problem &p, const FwdArgs &x, int segment_len,
@@ -99,5 +101,11 @@ bool kda_two_pass_supports(const Problem &p);
 size_t kda_two_pass_bytes(const Problem &p);
 hipError_t launch_kda_two_pass(const Problem &p, const FwdArgs &x, void *workspace,
                                hipStream_t s);
+// The two launches on their own: the prep reads q, k, a, b, A_log, dt_bias
+// and writes the workspace; the chains read it with v and the states.  One
+// prep serves any number of chain launches on the same q, k, a, b.
+hipError_t launch_kda_prep(const Problem &p, const FwdArgs &x, void *workspace, hipStream_t s);
+hipError_t launch_kda_chain(const Problem &p, const FwdArgs &x, const void *workspace,
+                            hipStream_t s);
 
 }  // namespace gdr

@@ -658,17 +658,11 @@ size_t kda_two_pass_bytes(const Problem &p) {
   return (size_t)kda_slots(p) * p.H_v * REC_BYTES;
 }
 
-hipError_t launch_kda_two_pass(const Problem &pr, const FwdArgs &x, void *workspace,
-                               hipStream_t s) {
+hipError_t launch_kda_prep(const Problem &pr, const FwdArgs &x, void *workspace, hipStream_t s) {
   const int64_t nslots = kda_slots(pr);
   const int64_t prep_grid = nslots * pr.H_v;
-  const int nb = (pr.d_v + 31) / 32;
-  const int64_t units = (int64_t)pr.num_seqs * pr.H_v;
-  const int64_t chain_grid = (units + 7) / 8 * 8 * nb;
-  // no tokens: every prep workgroup finds an unused slot and the chains copy
-  // the initial state (or zeros) to the final one
-  if (units == 0) return hipSuccess;
-  if (prep_grid > 0x7fffffffLL || chain_grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if ((int64_t)pr.num_seqs * pr.H_v == 0) return hipSuccess;
+  if (prep_grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   PrepParams pp;
   pp.q = static_cast<const bf16 *>(x.q);
   pp.k = static_cast<const bf16 *>(x.k);
@@ -684,9 +678,18 @@ hipError_t launch_kda_two_pass(const Problem &pr, const FwdArgs &x, void *worksp
   pp.H_v = pr.H_v;
   pp.scale = pr.scale;
   pp.eps = pr.eps;
+  // no tokens: every prep workgroup finds an unused slot
   hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)prep_grid), dim3(PREP_NT), 0, s, pp);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+hipError_t launch_kda_chain(const Problem &pr, const FwdArgs &x, const void *workspace,
+                            hipStream_t s) {
+  const int nb = (pr.d_v + 31) / 32;
+  const int64_t units = (int64_t)pr.num_seqs * pr.H_v;
+  const int64_t chain_grid = (units + 7) / 8 * 8 * nb;
+  if (units == 0) return hipSuccess;
+  if (chain_grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   ChainParams cp;
   cp.v = static_cast<const bf16 *>(x.v);
   cp.ws = static_cast<const unsigned char *>(workspace);
@@ -699,13 +702,21 @@ hipError_t launch_kda_two_pass(const Problem &pr, const FwdArgs &x, void *worksp
   cp.d_v = pr.d_v;
   cp.nb = nb;
   cp.units = (int)units;
-  cp.nslots = nslots;
+  cp.nslots = kda_slots(pr);
   const size_t smem = (size_t)NST * STAGE;
-  err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_chain_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_chain_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
+  // with no tokens the chains copy the initial state (or zeros) to the final one
   hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)chain_grid), dim3(256), smem, s, cp);
   return hipGetLastError();
+}
+
+hipError_t launch_kda_two_pass(const Problem &pr, const FwdArgs &x, void *workspace,
+                               hipStream_t s) {
+  const hipError_t e = launch_kda_prep(pr, x, workspace, s);
+  if (e != hipSuccess) return e;
+  return launch_kda_chain(pr, x, workspace, s);
 }
 
 }  // namespace gdr

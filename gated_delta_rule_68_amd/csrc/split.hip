@@ -153,6 +153,15 @@ unsigned fill_blocks(int64_t n) {
 
 }  // namespace
 
+// The segments of a dense batch as a dense batch of num_seqs * P sequences.
+Problem segments(const Problem &pr, int segment_len) {
+  Problem seg = pr;
+  seg.num_seqs = pr.num_seqs * (pr.seq_len / segment_len);
+  seg.seq_len = segment_len;
+  seg.cu = nullptr;
+  return seg;
+}
+
 SplitLayout split_layout(const Problem &pr, int segment_len) {
   SplitLayout L;
   const size_t es = pr.dtype == GDR_F32 ? 4 : 2;
@@ -164,7 +173,8 @@ SplitLayout split_layout(const Problem &pr, int segment_len) {
   L.M = L.ident + round256(st);
   L.Sloc = L.M + round256(st);
   L.Sin = L.Sloc + round256(st);
-  L.bytes = L.Sin + round256(st);
+  L.prep = L.Sin + round256(st);
+  L.bytes = L.prep + round256(kda_two_pass_bytes(segments(pr, segment_len)));
   return L;
 }
 
@@ -189,21 +199,26 @@ hipError_t launch_chunked_split(const Problem &pr, const FwdArgs &x, int segment
   if (e != hipSuccess) return e;
 
   // the segments as a dense batch of NP sequences
-  Problem seg = pr;
-  seg.num_seqs = NP;
-  seg.seq_len = segment_len;
-  seg.cu = nullptr;
+  const Problem seg = segments(pr, segment_len);
+  // KDA on the two-launch form: the per-chunk prep depends on q, k, a, b only,
+  // so one prep serves the three chain launches below
+  void *prep = ws + L.prep;
+  const bool two = L.bytes > L.prep;
+  if (two && (e = launch_kda_prep(seg, x, prep, s)) != hipSuccess) return e;
+  auto chunked = [&](const FwdArgs &y) {
+    return two ? launch_kda_chain(seg, y, prep, s) : chunked_any(seg, y, s);
+  };
   // S_loc: from zero on the real v;  M: from I on v = 0  (outputs land in o and
   // are overwritten by the last launch)
   FwdArgs a = x;
   a.s0 = nullptr;
   a.sT = Sloc;
-  if ((e = chunked_any(seg, a, s)) != hipSuccess) return e;
+  if ((e = chunked(a)) != hipSuccess) return e;
   FwdArgs b = x;
   b.v = zero_v;
   b.s0 = ident;
   b.sT = M;
-  if ((e = chunked_any(seg, b, s)) != hipSuccess) return e;
+  if ((e = chunked(b)) != hipSuccess) return e;
 
   CombParams cp{x.s0, M, Sloc, Sin, pr.num_seqs, L.P, pr.H_v};
   switch (pr.d_k) {
@@ -219,7 +234,7 @@ hipError_t launch_chunked_split(const Problem &pr, const FwdArgs &x, int segment
   FwdArgs c = x;
   c.s0 = Sin;
   c.sT = x.sT ? ident : nullptr;
-  if ((e = chunked_any(seg, c, s)) != hipSuccess) return e;
+  if ((e = chunked(c)) != hipSuccess) return e;
   if (x.sT) {
     const int64_t per_seq = (int64_t)pr.H_v * pr.d_k * pr.d_v;
     hipLaunchKernelGGL(last_state_kernel, dim3(fill_blocks((int64_t)pr.num_seqs * per_seq / 4)),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 6
+#define GDR_ABI_VERSION 7
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -239,8 +239,7 @@ GDR_API gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment
                                          size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace gdr_chunked_fwd_split needs for `shape` and segment_len
- * (0 when there is a single segment); the same shape errors as that call.
- * gdr_kda_chunked_fwd_split needs the same number of bytes. */
+ * (0 when there is a single segment); the same shape errors as that call. */
 GDR_API gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
                                                size_t *bytes);
 
@@ -334,7 +333,10 @@ GDR_API gdr_status gdr_kda_chunked_workspace(const gdr_shape *shape, size_t *byt
  * gdr_kda_chunked_fwd, segments, workspace and rules as
  * gdr_chunked_fwd_split).  The state update stays affine in the state, so
  * the same decomposition S_out = M S_in + S_loc holds per segment.  chunk 16
- * or 32; the workspace size is gdr_chunked_split_workspace's.
+ * or 32; the workspace size is gdr_kda_chunked_split_workspace's.  Where
+ * gdr_kda_chunked_fwd takes its two-launch form (bf16, d_k = 128, chunk 32),
+ * the three chunked passes share one per-chunk prep over all segments, which
+ * the workspace also holds.
  */
 GDR_API gdr_status gdr_kda_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len,
                                              const void *q, const void *k, const void *v,
@@ -342,6 +344,12 @@ GDR_API gdr_status gdr_kda_chunked_fwd_split(const gdr_shape *shape, int32_t seg
                                              const float *dt_bias, const float *initial_state,
                                              void *o, float *final_state, void *workspace,
                                              size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace gdr_kda_chunked_fwd_split needs for `shape` and
+ * segment_len (0 when there is a single segment); the same shape errors as
+ * that call. */
+GDR_API gdr_status gdr_kda_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
+                                                   size_t *bytes);
 
 /* Which kernel gdr_chunked_fwd runs for `shape`: GDR_PATH_VECTOR_F32 (fp32
  * on the vector ALUs), GDR_PATH_MATRIX_BF16 (matrix cores, bf16 operands,

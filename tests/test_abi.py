@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
                                   "gdr_kda_chunked_fwd", "gdr_kda_chunked_fwd_split",
-                                  "gdr_kda_chunked_workspace",
+                                  "gdr_kda_chunked_split_workspace", "gdr_kda_chunked_workspace",
                                   "gdr_kda_recurrent_fwd",
                                   "gdr_recurrent_fwd", "gdr_ssd_chunked_fwd",
                                   "gdr_ssd_recurrent_fwd", "gdr_status_string"]
@@ -389,3 +389,23 @@ def test_kda_workspace_checked(gdr):
     assert f(ctypes.byref(s), *p, fake(10, off=16), need, None) == 4    # not 256-byte aligned
     assert f(ctypes.byref(s), *p, fake(0, off=256), need, None) == 6    # over q
     assert f(ctypes.byref(s), *p, fake(8, off=-4096), need, None) == 6  # runs into o
+
+
+def test_kda_split_workspace_holds_the_prep(gdr):
+    """The KDA split's workspace is the rule's plus, on the two-launch form,
+    one prep record per (segment chunk slot, value head)."""
+    lib = gdr.lib()
+    rule, kda_ = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    s = shape(gdr, dtype=1, d_k=128, d_v=128, chunk=32, num_seqs=2, seq_len=1024,
+              total_tokens=2048)
+    assert lib.gdr_chunked_split_workspace(ctypes.byref(s), 256, ctypes.byref(rule)) == 0
+    assert lib.gdr_kda_chunked_split_workspace(ctypes.byref(s), 256, ctypes.byref(kda_)) == 0
+    slots = 2048 // 32 + 2 * 4  # 8 segments as sequences
+    assert kda_.value - rule.value >= slots * 2 * 29696
+    s = shape(gdr, dtype=0, d_k=128, d_v=128, chunk=32, num_seqs=2, seq_len=1024,
+              total_tokens=2048)  # fp32: the vector kernel, no prep
+    assert lib.gdr_chunked_split_workspace(ctypes.byref(s), 256, ctypes.byref(rule)) == 0
+    assert lib.gdr_kda_chunked_split_workspace(ctypes.byref(s), 256, ctypes.byref(kda_)) == 0
+    assert kda_.value == rule.value
+    assert lib.gdr_kda_chunked_split_workspace(ctypes.byref(s), 1024, ctypes.byref(kda_)) == 0
+    assert kda_.value == 0  # one segment

@@ -91,9 +91,11 @@ def test_kda_random(seed):
                            cu_seqlens=inp["cu_host"])
     o1, S1 = gdr.kda_recurrent_fwd(*args, cu_seqlens=inp["cu_seqlens"])
     o2, S2 = gdr.kda_chunked_fwd(*args, chunk=chunk, cu_seqlens=inp["cu_seqlens"])
+    o3, S3 = gdr.kda_chunked_fwd(*args, chunk=chunk, cu_seqlens=inp["cu_seqlens"], fused=True)
     torch.cuda.synchronize()
     check(o1, S1, o_ref, S_ref, inp["cu_host"], w.H_v, c["dtype"], "kda recurrent")
     check(o2, S2, o_ref, S_ref, inp["cu_host"], w.H_v, c["dtype"], "kda chunked")
+    check(o3, S3, o_ref, S_ref, inp["cu_host"], w.H_v, c["dtype"], "kda chunked, one launch")
 
 
 @pytest.mark.parametrize("seed", range(12))

@@ -137,7 +137,8 @@ def test_kda_split(dtype, chunk, seg):
 def test_kda_split_one_segment_is_the_direct_form_and_long_memory():
     w = synth.custom(1, 2, 128, 128, "bf16", seq_len=512, num_seqs=1, chunk=32)
     inp, args, o1, S1 = check_kda(w, 41, 512)
-    o2, S2 = gdr.kda_chunked_fwd(*args, chunk=32, num_seqs=1)
+    # one segment runs the one-launch chunked kernel (no workspace)
+    o2, S2 = gdr.kda_chunked_fwd(*args, chunk=32, num_seqs=1, fused=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
     wl = synth.custom(1, 1, 64, 64, "f32", seq_len=2048, num_seqs=1, chunk=32)
