@@ -508,19 +508,24 @@ __device__ __forceinline__ bf16x8 lds8(const unsigned char *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-// One workgroup of four waves per (sequence, value head, 32 value columns).
-// Waves 0 and 1 each keep a [128 x 16] slice of the state in 8 accumulator
-// tiles for the whole sequence: tile t = 2 tt + u holds, in lane (m, g) and
-// element j, state row 32 tt + 8 g + 4 u + j of column m, so the tiles 2tt
-// and 2tt+1 of a lane together are state rows 32 tt + 8 g .. + 7, the B
-// operand of k = 32 that K S and Q S take without leaving registers.  Waves
-// 2 and 3 copy each chunk's record and its v tile into a ring of 4 LDS
-// stages three chunks ahead (global_load_lds, never through registers), and
-// wait for chunk c + 1 before the barrier that ends step c; the compute waves
-// read every operand as one conflict-free 16-byte LDS read per lane.  The
-// workgroups of one (sequence, head) are dealt to one XCD, where they share
-// the records through its L2.
-__global__ __launch_bounds__(256) void kda_chain_kernel(ChainParams p) {
+// One workgroup of six waves per (sequence, value head, 32 value columns);
+// each 16-column block has a state wave and an output wave.
+//  - State wave b (wave b): keeps a [128 x 16] slice of the state in 8
+//    accumulator tiles for the whole sequence.  Tile t = 2 tt + u holds, in
+//    lane (m, g) and element j, state row 32 tt + 8 g + 4 u + j of column m,
+//    so the tiles 2tt and 2tt+1 of a lane are state rows 32 tt + 8 g .. + 7:
+//    the B operand of k = 32 that K S takes without leaving registers.  Per
+//    chunk: K S, Delta = T' (V - K S), S <- diag(e^gamma_31) S + K_D Delta.
+//  - Output wave b (wave 2 + b): O = Q S + P Delta from the state (bf16
+//    operands) and Delta that the state wave leaves in LDS.
+//  - Waves 4 and 5 copy each chunk's record and v tile into a ring of 4 LDS
+//    stages three chunks ahead (global_load_lds, never through registers).
+// Two barriers per chunk c: B1 publishes the state's operands (and frees
+// the stage of chunk c - 1 for the loaders), B2 publishes Delta and the data
+// of chunk c + 1.  The barriers wait for LDS traffic and the loaders' copies
+// only.  The workgroups of one (sequence, head) are dealt to one XCD, where
+// they share the records through its L2.
+__global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
   extern __shared__ __align__(16) unsigned char ring[];
   const int bid = blockIdx.x;
   const int vb = (bid >> 3) % p.nb;
@@ -536,10 +541,13 @@ __global__ __launch_bounds__(256) void kda_chain_kernel(ChainParams p) {
   const int nch = (int)max((int64_t)0, min((L + CH - 1) / CH, p.nslots - base));
   const int64_t vstride = (int64_t)p.H_v * p.d_v;
   const int c32 = 32 * vb;  // first column of the workgroup
+  // hand-off of block b: the state's 4 B operands, then Delta (16 B per lane each)
+  unsigned char *xch = ring + NST * STAGE;
+  const size_t pl = (size_t)lane * 16;
 
-  if (wave >= 2) {
+  if (wave >= 4) {
     // ---- loaders
-    const int ld = wave - 2;
+    const int ld = wave - 4;
     auto issue = [&](int c) {
       c = min(c, nch - 1);
       unsigned char *st = ring + (c % NST) * STAGE;
@@ -568,64 +576,130 @@ __global__ __launch_bounds__(256) void kda_chain_kernel(ChainParams p) {
       else vm_wait<2 * L1_COPIES>();
       lds_barrier();
       for (int c = 0; c < nch; ++c) {
+        lds_barrier();  // B1(c): chunk c - 1 is no longer read
         issue(c + NST - 1);
         if (ld == 0) vm_wait<2 * L0_COPIES>();
         else vm_wait<2 * L1_COPIES>();
-        lds_barrier();
+        lds_barrier();  // B2(c): chunk c + 1 has landed
       }
     }
     return;
   }
-  // ---- compute waves
-  const int col = c32 + 16 * wave + m;
-  const bool live = c32 + 16 * wave < p.d_v;  // d_v = 16: wave 1 has no columns
-  const size_t st_off = ((size_t)n * p.H_v + h) * DK * p.d_v + col;
-  f32x4 S[8];
+  const int blk = wave & 1;
+  const int col = c32 + 16 * blk + m;
+  const bool live = c32 + 16 * blk < p.d_v;  // d_v = 16: block 1 has no columns
+  unsigned char *sx = xch + blk * 5 * 1024;  // [4 state operands][Delta]
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  if (wave < 2) {
+    // ---- state wave
+    const size_t st_off = ((size_t)n * p.H_v + h) * DK * p.d_v + col;
+    f32x4 S[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      S[t][j] = (live && p.s0) ? p.s0[st_off + (size_t)(32 * (t >> 1) + 8 * g + 4 * (t & 1) + j) * p.d_v]
-                               : 0.f;
-  if (nch > 0) {
-    lds_barrier();
-    bf16 *oh = p.o + (int64_t)h * p.d_v + col;
-    const size_t pl = (size_t)lane * 16;
-    for (int c = 0; c < nch; ++c) {
-      const unsigned char *st = ring + (c % NST) * STAGE;
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 ks0 = z, ks1 = z, qs0 = z, qs1 = z;
+      for (int j = 0; j < 4; ++j)
+        S[t][j] = (live && p.s0)
+                      ? p.s0[st_off + (size_t)(32 * (t >> 1) + 8 * g + 4 * (t & 1) + j) * p.d_v]
+                      : 0.f;
+    if (nch > 0) {
+      lds_barrier();
+      for (int c = 0; c < nch; ++c) {
+        const unsigned char *st = ring + (c % NST) * STAGE;
+        // this chunk's operands are in LDS since B2(c - 1): read them ahead
+        // of the barriers of this step, which they do not depend on
+        bf16x8 ke[8], tb[2];
+        float vv[8];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const bf16x8 sb = pack8(S[2 * tt], S[2 * tt + 1]);
-        ks0 = mma32(lds8(st + REC_KE + tt * 1024 + pl), sb, ks0);
-        ks1 = mma32(lds8(st + REC_KE + (4 + tt) * 1024 + pl), sb, ks1);
-        qs0 = mma32(lds8(st + REC_QE + tt * 1024 + pl), sb, qs0);
-        qs1 = mma32(lds8(st + REC_QE + (4 + tt) * 1024 + pl), sb, qs1);
+        for (int i = 0; i < 8; ++i) ke[i] = lds8(st + REC_KE + i * 1024 + pl);
+        tb[0] = lds8(st + REC_TB + pl);
+        tb[1] = lds8(st + REC_TB + 1024 + pl);
+        {
+          const bf16 *vt = reinterpret_cast<const bf16 *>(st + REC_BYTES);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            vv[j] = static_cast<float>(vt[(4 * g + j) * 32 + 16 * blk + m]);
+            vv[4 + j] = static_cast<float>(vt[(16 + 4 * g + j) * 32 + 16 * blk + m]);
+          }
+        }
+        bf16x8 sb[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          sb[tt] = pack8(S[2 * tt], S[2 * tt + 1]);
+          *reinterpret_cast<bf16x8 *>(sx + tt * 1024 + pl) = sb[tt];
+        }
+        lds_barrier();  // B1(c)
+        bf16x8 kd[8];
+        f32x4 dc[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          kd[t] = lds8(st + REC_KD + t * 1024 + pl);
+          dc[t] = *reinterpret_cast<const f32x4 *>(st + REC_DEC + 4 * (32 * (t >> 1) + 8 * g + 4 * (t & 1)));
+        }
+        f32x4 ks0 = z, ks1 = z;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          ks0 = mma32(ke[tt], sb[tt], ks0);
+          ks1 = mma32(ke[4 + tt], sb[tt], ks1);
+        }
+        f32x4 u0, u1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u0[j] = vv[j] - ks0[j];
+          u1[j] = vv[4 + j] - ks1[j];
+        }
+        const bf16x8 ub = pack8(u0, u1);
+        const f32x4 d0 = mma32(tb[0], ub, z);
+        const f32x4 d1 = mma32(tb[1], ub, z);
+        const bf16x8 db = pack8(d0, d1);
+        *reinterpret_cast<bf16x8 *>(sx + 4 * 1024 + pl) = db;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] *= dc[t];
+        lds_barrier();  // B2(c)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = mma32(kd[t], db, S[t]);
       }
-      const bf16 *vt = reinterpret_cast<const bf16 *>(st + REC_BYTES);
-      f32x4 u0, u1;
+    }
+    if (live && p.sT) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u0[j] = static_cast<float>(vt[(4 * g + j) * 32 + 16 * wave + m]) - ks0[j];
-        u1[j] = static_cast<float>(vt[(16 + 4 * g + j) * 32 + 16 * wave + m]) - ks1[j];
-      }
-      const bf16x8 ub = pack8(u0, u1);
-      const f32x4 d0 = mma32(lds8(st + REC_TB + pl), ub, z);
-      const f32x4 d1 = mma32(lds8(st + REC_TB + 1024 + pl), ub, z);
-      const bf16x8 db = pack8(d0, d1);
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const f32x4 dc = *reinterpret_cast<const f32x4 *>(
-            st + REC_DEC + 4 * (32 * (t >> 1) + 8 * g + 4 * (t & 1)));
-        S[t] = mma32(lds8(st + REC_KD + t * 1024 + pl), db, S[t] * dc);
-      }
-      const f32x4 o0 = mma32(lds8(st + REC_PB + pl), db, qs0);
-      const f32x4 o1 = mma32(lds8(st + REC_PB + 1024 + pl), db, qs1);
-      lds_barrier();  // this stage is read: the loaders may refill it
-      if (live) {
-        const int64_t c0 = t0 + (int64_t)c * CH;
-        const int cl = (int)min((int64_t)CH, t1 - c0);
+        for (int j = 0; j < 4; ++j)
+          p.sT[st_off + (size_t)(32 * (t >> 1) + 8 * g + 4 * (t & 1) + j) * p.d_v] = S[t][j];
+    }
+    return;
+  }
+  // ---- output wave
+  if (nch == 0) return;
+  bf16 *oh = p.o + (int64_t)h * p.d_v + col;
+  lds_barrier();
+  for (int c = 0; c < nch; ++c) {
+    const unsigned char *st = ring + (c % NST) * STAGE;
+    bf16x8 qe[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qe[i] = lds8(st + REC_QE + i * 1024 + pl);
+    lds_barrier();  // B1(c)
+    const bf16x8 pb0 = lds8(st + REC_PB + pl), pb1 = lds8(st + REC_PB + 1024 + pl);
+    f32x4 qs0 = z, qs1 = z;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 sb = lds8(sx + tt * 1024 + pl);
+      qs0 = mma32(qe[tt], sb, qs0);
+      qs1 = mma32(qe[4 + tt], sb, qs1);
+    }
+    lds_barrier();  // B2(c)
+    const bf16x8 db = lds8(sx + 4 * 1024 + pl);
+    const f32x4 o0 = mma32(pb0, db, qs0);
+    const f32x4 o1 = mma32(pb1, db, qs1);
+    if (live) {
+      const int64_t c0 = t0 + (int64_t)c * CH;
+      const int cl = (int)min((int64_t)CH, t1 - c0);
+      if (cl == CH) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          oh[(c0 + 4 * g + j) * vstride] = static_cast<bf16>(o0[j]);
+          oh[(c0 + 16 + 4 * g + j) * vstride] = static_cast<bf16>(o1[j]);
+        }
+      } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r0 = 4 * g + j, r1 = 16 + 4 * g + j;
@@ -634,13 +708,6 @@ __global__ __launch_bounds__(256) void kda_chain_kernel(ChainParams p) {
         }
       }
     }
-  }
-  if (live && p.sT) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        p.sT[st_off + (size_t)(32 * (t >> 1) + 8 * g + 4 * (t & 1) + j) * p.d_v] = S[t][j];
   }
 }
 
@@ -703,12 +770,12 @@ hipError_t launch_kda_chain(const Problem &pr, const FwdArgs &x, const void *wor
   cp.nb = nb;
   cp.units = (int)units;
   cp.nslots = kda_slots(pr);
-  const size_t smem = (size_t)NST * STAGE;
+  const size_t smem = (size_t)NST * STAGE + 2 * 5 * 1024;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_chain_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
   // with no tokens the chains copy the initial state (or zeros) to the final one
-  hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)chain_grid), dim3(256), smem, s, cp);
+  hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)chain_grid), dim3(384), smem, s, cp);
   return hipGetLastError();
 }
 
