@@ -6,10 +6,10 @@
 //     Gram matrices A and P, (I + A)^-1, and the decay-scaled k and q rows.
 //     It writes them to a workspace record, each matrix already in the lane
 //     order of the matrix-core operand that reads it.
-//  2. kda_chain_kernel, one wave per (sequence, value head, 16 value
+//  2. kda_chain_kernel, one workgroup per (sequence, value head, 32 value
 //     columns), which walks the chunks of its sequence in order and does only
-//     the state-dependent products, reading its operands straight from the
-//     records into registers one chunk ahead.
+//     the state-dependent products; loader waves stage the records through
+//     LDS three chunks ahead.
 //
 // The map is the one the single-kernel form computes (the rule of
 // GatedDeltaRule.ixx File Reference, "Detailed Description", with one decay
@@ -25,13 +25,14 @@
 //   S'      = diag(exp(gamma_31)) S + (K * exp(gamma_31 - gamma))^T Delta
 // The prep side splits every pair (r, i) at the highest bit in which r and i
 // differ, so that each exponential it takes is of a non-positive number (see
-// the level products below); (I + A)^-1 is a forward substitution in fp32.
+// the level products below); (I + A)^-1 is formed by blocks in fp32.
 //
 // Why two launches: the state-free work is most of the arithmetic and all of
 // the exponentials (7 per key element), and in one kernel it sits on the
 // serial chain of chunks.  Here it runs at full occupancy over every (chunk,
 // head) of the batch, and the chain keeps only 28 16x16x32 products per
-// chunk and wave.
+// chunk and 16 columns.  One prep also serves several chain launches on the
+// same q, k, a, b (the segmented form's three passes).
 #include "device_common.h"
 #include "gdr_internal.h"
 
