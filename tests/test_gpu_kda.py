@@ -264,3 +264,26 @@ def test_kda_matrix_core_vs_vector_kernel(lens):
                         U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
     note(f"  matrix-core vs vector kernel: {worst:.3e}")
     assert worst <= U.TOL["bf16"]
+
+
+def test_kda_two_launch_on_the_varlen_batch():
+    """The varlen workload (8 packed sequences, about 94k tokens, 48/16
+    heads, carried state) through both matrix-core forms: the two-launch
+    form's slot numbering and per-slot sequence lookup at full scale.  The
+    fp64 oracle checks both forms on the smaller cases above; here they are
+    compared with each other per (sequence, head)."""
+    w = synth.workload("varlen")
+    inp = synth.kda_inputs(w, 73, device=DEV)
+    note(f"[kda] varlen two-launch vs one-launch lens={w.seq_lengths}")
+    o1, S1 = run("chunked", inp, w, 32)
+    o2, S2 = run("chunked_fused", inp, w, 32)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        for h in range(w.H_v):
+            worst = max(worst, U.slice_err(U.to_np(o1[cu[n]:cu[n + 1], h]),
+                                           U.to_np(o2[cu[n]:cu[n + 1], h])),
+                        U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
+    note(f"  two-launch vs one-launch on the varlen batch: {worst:.3e}")
+    assert worst <= U.TOL["bf16"]
