@@ -287,3 +287,18 @@ def test_kda_two_launch_on_the_varlen_batch():
                         U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
     note(f"  two-launch vs one-launch on the varlen batch: {worst:.3e}")
     assert worst <= U.TOL["bf16"]
+
+
+@pytest.mark.parametrize("form", ["recurrent", "chunked", "chunked_fused"])
+def test_kda_empty_batch(form):
+    """Only empty sequences: the two-launch form's prep finds no chunk in any
+    slot and its chains copy the initial state (or zeros) to the final one."""
+    w = synth.custom(1, 2, 128, 64, "bf16", lengths=[0, 0, 0], chunk=32)
+    inp = synth.kda_inputs(w, 74, device=DEV)
+    o, S = run(form, inp, w)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert torch.equal(S, inp["initial_state"])
+    o, S = run(form, dict(inp, initial_state=None), w)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0
