@@ -507,9 +507,11 @@ def kda_prefill_flops(T, H_k, H_v, d_k, d_v, C):
 def kda_legs(gdr, dev, stream, steps):
     """The per-channel-decay variant (KDA) at the rule's shapes: decode of
     256 sequences x 48 value heads (16 key heads), d = 128, fp32 state in
-    place, 64 single-token steps (recurrent kernel, HBM-bound), and the
-    prefill layer (8192 tokens, chunk 32, bf16) on the matrix-core chunked
-    KDA kernel.  Inputs from synth.kda_inputs, resident in HBM."""
+    place, 64 single-token steps (recurrent kernel, HBM-bound); the prefill
+    layer (8192 tokens, chunk 32, bf16) on the two-launch chunked form, with
+    the one-launch form timed beside it; and the varlen workload (8 packed
+    sequences, carried state) on the two-launch form.  Inputs from
+    synth.kda_inputs, resident in HBM."""
     import torch
     import synth
 
@@ -557,6 +559,20 @@ def kda_legs(gdr, dev, stream, steps):
     T = w.total_tokens
     flops = kda_prefill_flops(T, w.H_k, w.H_v, w.d_k, w.d_v, 32)
     del inp, o, S
+
+    # the varlen workload (8 packed sequences, carried state) on the same form
+    wv = synth.workload("varlen")
+    vin = synth.kda_inputs(wv, 0, device=dev)
+    vo = torch.empty((wv.total_tokens, wv.H_v, wv.d_v), dtype=wv.torch_dtype, device=dev)
+    vS = torch.empty_like(vin["initial_state"])
+    var_ms = timed(lambda: gdr.kda_chunked_fwd(vin["q"], vin["k"], vin["v"], vin["a"], vin["b"],
+                                               vin["A_log"], vin["dt_bias"], vin["initial_state"],
+                                               chunk=32, cu_seqlens=vin["cu_seqlens"], o=vo,
+                                               final_state=vS), steps)
+    var_flops = sum(kda_prefill_flops(L, wv.H_k, wv.H_v, wv.d_k, wv.d_v, 32) for L in wv.seq_lengths)
+    var_tokens = wv.total_tokens
+    var_lens = list(wv.seq_lengths)
+    del vin, vo, vS
     dgbs = dbytes / (dec_ms / 1e3) / 1e9
     tf = flops / (pre_ms / 1e3) / 1e12
     return {
@@ -575,6 +591,15 @@ def kda_legs(gdr, dev, stream, steps):
                     "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                  "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                                  "flop_per_launch": flops}},
+        "varlen": {"workload": f"{len(var_lens)} packed sequences, lengths {var_lens} (seed 0), "
+                               "48 value heads sharing 16 key heads, d_k=d_v=128, per-channel "
+                               "gates, chunk 32, bf16, carried fp32 state; two launches",
+                   "tokens": var_tokens, "steps": steps, "ms_per_launch": var_ms,
+                   "tokens_per_s": var_tokens / (var_ms / 1e3),
+                   "roofline": {"bound": "mfma", "achieved": var_flops / (var_ms / 1e3) / 1e12,
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": var_flops / (var_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                                "flop_per_launch": var_flops}},
     }
 
 
