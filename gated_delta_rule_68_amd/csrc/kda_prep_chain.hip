@@ -137,6 +137,22 @@ struct PrepParams {
   float scale, eps;
 };
 
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
+}
+
+// Workgroup barrier that waits only for this wave's LDS accesses
+// (lgkmcnt(0)), not for its global accesses in flight; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Orders LDS accesses of one wave around a point (its LDS operations run in
 // order; this keeps the compiler from moving them).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -244,20 +260,24 @@ __global__ __launch_bounds__(PREP_NT) void kda_prep_kernel(PrepParams p) {
           make_float4(gl[4 * e4], gl[4 * e4 + 1], gl[4 * e4 + 2], gl[4 * e4 + 3]);
   }
   if (tid < CH) sm.beta[tid] = tid < cl ? sigmoid_f32(braw) : 0.f;
-  __syncthreads();
-  // carry of the earlier waves; exp(gamma_31) per channel
-  float glast[16];
+  lds_barrier();
+  // carry of the earlier waves (a loop uniform per wave)
+  {
+    float carry[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float carry = 0.f, tot = 0.f;
+    for (int e = 0; e < 16; ++e) carry[e] = 0.f;
+    for (int w = 0; w < wave; ++w) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float x = sm.wt[w][cc + e];
-      carry += w < wave ? x : 0.f;
-      tot += x;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const float4 x = *reinterpret_cast<const float4 *>(&sm.wt[w][cc + 4 * e4]);
+        carry[4 * e4] += x.x;
+        carry[4 * e4 + 1] += x.y;
+        carry[4 * e4 + 2] += x.z;
+        carry[4 * e4 + 3] += x.w;
+      }
     }
-    gl[e] += carry;
-    glast[e] = tot;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gl[e] += carry[e];
   }
 #pragma unroll
   for (int e4 = 0; e4 < 4; ++e4)
@@ -283,15 +303,17 @@ __global__ __launch_bounds__(PREP_NT) void kda_prep_kernel(PrepParams p) {
       *reinterpret_cast<bf16x8 *>(rec + REC_KE + piece) = pack8(ke0, ke1);
       *reinterpret_cast<bf16x8 *>(rec + REC_QE + piece) = pack8(qe0, qe1);
     }
-    if (r == 0) {
+    if (r == 0) {  // exp(gamma_31) per channel: the sum of the four waves' totals
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        *reinterpret_cast<float4 *>(rec + REC_DEC + 4 * (cc + 4 * e4)) =
-            make_float4(xexp2(glast[4 * e4]), xexp2(glast[4 * e4 + 1]), xexp2(glast[4 * e4 + 2]),
-                        xexp2(glast[4 * e4 + 3]));
+      for (int e = 0; e < 16; ++e) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) tot += sm.wt[w][cc + e];
+        reinterpret_cast<float *>(rec + REC_DEC)[cc + e] = xexp2(tot);
+      }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- level products.  Level b (h = 2^b) holds the pairs (r, i), i < r,
   // whose highest differing bit is b: r in the upper half and i in the lower
   // half of a common block of 2h rows.  With ref the last row of the lower
@@ -355,7 +377,7 @@ __global__ __launch_bounds__(PREP_NT) void kda_prep_kernel(PrepParams p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- T11 = (I + A11)^-1 and T22 = (I + A22)^-1 by forward substitution
   // (wave 0, lanes 0..15 and 16..31: one column each); the other waves add
   // up level 4 (A21 and P's lower-left block) and write the KD operands
@@ -403,7 +425,7 @@ __global__ __launch_bounds__(PREP_NT) void kda_prep_kernel(PrepParams p) {
       *reinterpret_cast<bf16x8 *>(rec + REC_KD + (size_t)q * 16) = pack8(lo, hi);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- T21 = -T22 (A21 T11) (wave 0: lane l computes 4 entries of row
   // l / 4); P's operands (the other waves)
   if (wave == 0) {
@@ -446,7 +468,7 @@ __global__ __launch_bounds__(PREP_NT) void kda_prep_kernel(PrepParams p) {
       *reinterpret_cast<bf16x8 *>(rec + REC_PB + (size_t)q * 16) = pack8(lo, hi);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- T' = T diag(beta), as the TB operands
   if (tid < 2 * 64) {
     const int a = tid >> 6, m = lane & 15, g = lane >> 4, rw = 16 * a + m;
@@ -482,22 +504,6 @@ struct ChainParams {
   int seq_len, H_v, d_v, nb, units;
   int64_t nslots;
 };
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 15));
-}
-
-// Workgroup barrier that waits only for this wave's LDS accesses
-// (lgkmcnt(0)), not for its global accesses in flight; the empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes
 // land at lds + 16 l (`lds` the same for the whole wave).
