@@ -162,6 +162,8 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
+// The barriers wait for LDS traffic only: no wave of the workgroup reads the
+// record stores, which the kernel's end makes visible to the chains.
 __global__ __launch_bounds__(PREP_NT) void kda_prep_kernel(PrepParams p) {
   __shared__ PrepSmem sm;
   const int h = (int)(blockIdx.x % (unsigned)p.H_v);
