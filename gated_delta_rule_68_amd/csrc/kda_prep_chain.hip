@@ -523,17 +523,21 @@ __device__ __forceinline__ bf16x8 lds8(const unsigned char *p) {
 //    accumulator tiles for the whole sequence.  Tile t = 2 tt + u holds, in
 //    lane (m, g) and element j, state row 32 tt + 8 g + 4 u + j of column m,
 //    so the tiles 2tt and 2tt+1 of a lane are state rows 32 tt + 8 g .. + 7:
-//    the B operand of k = 32 that K S takes without leaving registers.  Per
-//    chunk: K S, Delta = T' (V - K S), S <- diag(e^gamma_31) S + K_D Delta.
-//  - Output wave b (wave 2 + b): O = Q S + P Delta from the state (bf16
-//    operands) and Delta that the state wave leaves in LDS.
+//    the B operand of k = 32 that K S takes without leaving registers.  Step
+//    c: K S, Delta = T' (V - K S), S <- diag(e^gamma_31) S + K_D Delta, then
+//    the bf16 operands of the new state and Delta go to LDS for the output
+//    wave.
+//  - Output wave b (wave 2 + b) trails by half a step: in step c it forms
+//    O(c - 1) = Q S(c - 1) + P Delta(c - 1) and then Q S(c), from the
+//    operands the state wave left in LDS.
 //  - Waves 4 and 5 copy each chunk's record and v tile into a ring of 4 LDS
 //    stages three chunks ahead (global_load_lds, never through registers).
-// Two barriers per chunk c: B1 publishes the state's operands (and frees
-// the stage of chunk c - 1 for the loaders), B2 publishes Delta and the data
-// of chunk c + 1.  The barriers wait for LDS traffic and the loaders' copies
-// only.  The workgroups of one (sequence, head) are dealt to one XCD, where
-// they share the records through its L2.
+// One barrier B(c) ends step c.  It publishes Delta(c), the state operands of
+// chunk c + 1 and the data of chunk c + 1, and it frees the stage of chunk
+// c - 1 (the output wave keeps that chunk's P in registers).  It waits for
+// LDS traffic and the loaders' copies only.  The workgroups of one
+// (sequence, head) are dealt to one XCD, where they share the records
+// through its L2.
 __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
   extern __shared__ __align__(16) unsigned char ring[];
   const int bid = blockIdx.x;
@@ -550,8 +554,6 @@ __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
   const int nch = (int)max((int64_t)0, min((L + CH - 1) / CH, p.nslots - base));
   const int64_t vstride = (int64_t)p.H_v * p.d_v;
   const int c32 = 32 * vb;  // first column of the workgroup
-  // hand-off of block b: the state's 4 B operands, then Delta (16 B per lane each)
-  unsigned char *xch = ring + NST * STAGE;
   const size_t pl = (size_t)lane * 16;
 
   if (wave >= 4) {
@@ -583,13 +585,12 @@ __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
       issue(2);
       if (ld == 0) vm_wait<2 * L0_COPIES>();
       else vm_wait<2 * L1_COPIES>();
-      lds_barrier();
+      lds_barrier();  // chunk 0 has landed
       for (int c = 0; c < nch; ++c) {
-        lds_barrier();  // B1(c): chunk c - 1 is no longer read
-        issue(c + NST - 1);
+        issue(c + NST - 1);  // into the stage of chunk c - 1, free since B(c - 1)
         if (ld == 0) vm_wait<2 * L0_COPIES>();
         else vm_wait<2 * L1_COPIES>();
-        lds_barrier();  // B2(c): chunk c + 1 has landed
+        lds_barrier();  // B(c): chunk c + 1 has landed
       }
     }
     return;
@@ -597,7 +598,10 @@ __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
   const int blk = wave & 1;
   const int col = c32 + 16 * blk + m;
   const bool live = c32 + 16 * blk < p.d_v;  // d_v = 16: block 1 has no columns
-  unsigned char *sx = xch + blk * 5 * 1024;  // [4 state operands][Delta]
+  // hand-off of block b, two parities: the state's 4 B operands (4 KB), then Delta (1 KB)
+  unsigned char *xb = ring + NST * STAGE + blk * 2 * 5 * 1024;
+  auto sop = [&](int c, int tt) { return xb + (c & 1) * 5 * 1024 + tt * 1024 + pl; };
+  auto dop = [&](int c) { return xb + (c & 1) * 5 * 1024 + 4 * 1024 + pl; };
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   if (wave < 2) {
     // ---- state wave
@@ -611,12 +615,17 @@ __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
                       ? p.s0[st_off + (size_t)(32 * (t >> 1) + 8 * g + 4 * (t & 1) + j) * p.d_v]
                       : 0.f;
     if (nch > 0) {
-      lds_barrier();
+      bf16x8 sb[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        sb[tt] = pack8(S[2 * tt], S[2 * tt + 1]);
+        *reinterpret_cast<bf16x8 *>(sop(0, tt)) = sb[tt];
+      }
+      lds_barrier();  // chunk 0 and the state operands of chunk 0
       for (int c = 0; c < nch; ++c) {
         const unsigned char *st = ring + (c % NST) * STAGE;
-        // this chunk's operands are in LDS since B2(c - 1): read them ahead
-        // of the barriers of this step, which they do not depend on
-        bf16x8 ke[8], tb[2];
+        bf16x8 ke[8], tb[2], kd[8];
+        f32x4 dc[8];
         float vv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) ke[i] = lds8(st + REC_KE + i * 1024 + pl);
@@ -630,15 +639,6 @@ __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
             vv[4 + j] = static_cast<float>(vt[(16 + 4 * g + j) * 32 + 16 * blk + m]);
           }
         }
-        bf16x8 sb[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          sb[tt] = pack8(S[2 * tt], S[2 * tt + 1]);
-          *reinterpret_cast<bf16x8 *>(sx + tt * 1024 + pl) = sb[tt];
-        }
-        lds_barrier();  // B1(c)
-        bf16x8 kd[8];
-        f32x4 dc[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           kd[t] = lds8(st + REC_KD + t * 1024 + pl);
@@ -660,12 +660,15 @@ __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
         const f32x4 d0 = mma32(tb[0], ub, z);
         const f32x4 d1 = mma32(tb[1], ub, z);
         const bf16x8 db = pack8(d0, d1);
-        *reinterpret_cast<bf16x8 *>(sx + 4 * 1024 + pl) = db;
+        *reinterpret_cast<bf16x8 *>(dop(c)) = db;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] *= dc[t];
-        lds_barrier();  // B2(c)
+        for (int t = 0; t < 8; ++t) S[t] = mma32(kd[t], db, S[t] * dc[t]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = mma32(kd[t], db, S[t]);
+        for (int tt = 0; tt < 4; ++tt) {
+          sb[tt] = pack8(S[2 * tt], S[2 * tt + 1]);
+          *reinterpret_cast<bf16x8 *>(sop(c + 1, tt)) = sb[tt];
+        }
+        lds_barrier();  // B(c)
       }
     }
     if (live && p.sT) {
@@ -680,44 +683,48 @@ __global__ __launch_bounds__(384) void kda_chain_kernel(ChainParams p) {
   // ---- output wave
   if (nch == 0) return;
   bf16 *oh = p.o + (int64_t)h * p.d_v + col;
-  lds_barrier();
-  for (int c = 0; c < nch; ++c) {
-    const unsigned char *st = ring + (c % NST) * STAGE;
-    bf16x8 qe[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qe[i] = lds8(st + REC_QE + i * 1024 + pl);
-    lds_barrier();  // B1(c)
-    const bf16x8 pb0 = lds8(st + REC_PB + pl), pb1 = lds8(st + REC_PB + 1024 + pl);
-    f32x4 qs0 = z, qs1 = z;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const bf16x8 sb = lds8(sx + tt * 1024 + pl);
-      qs0 = mma32(qe[tt], sb, qs0);
-      qs1 = mma32(qe[4 + tt], sb, qs1);
-    }
-    lds_barrier();  // B2(c)
-    const bf16x8 db = lds8(sx + 4 * 1024 + pl);
+  f32x4 qs0 = z, qs1 = z;
+  bf16x8 pb0 = {}, pb1 = {};
+  // O(c) = Q S(c) + P Delta(c), stored as bf16 rows of chunk c
+  auto out = [&](int c) {
+    const bf16x8 db = lds8(dop(c));
     const f32x4 o0 = mma32(pb0, db, qs0);
     const f32x4 o1 = mma32(pb1, db, qs1);
-    if (live) {
-      const int64_t c0 = t0 + (int64_t)c * CH;
-      const int cl = (int)min((int64_t)CH, t1 - c0);
-      if (cl == CH) {
+    if (!live) return;
+    const int64_t c0 = t0 + (int64_t)c * CH;
+    const int cl = (int)min((int64_t)CH, t1 - c0);
+    if (cl == CH) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          oh[(c0 + 4 * g + j) * vstride] = static_cast<bf16>(o0[j]);
-          oh[(c0 + 16 + 4 * g + j) * vstride] = static_cast<bf16>(o1[j]);
-        }
-      } else {
+      for (int j = 0; j < 4; ++j) {
+        oh[(c0 + 4 * g + j) * vstride] = static_cast<bf16>(o0[j]);
+        oh[(c0 + 16 + 4 * g + j) * vstride] = static_cast<bf16>(o1[j]);
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r0 = 4 * g + j, r1 = 16 + 4 * g + j;
-          if (r0 < cl) oh[(c0 + r0) * vstride] = static_cast<bf16>(o0[j]);
-          if (r1 < cl) oh[(c0 + r1) * vstride] = static_cast<bf16>(o1[j]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = 4 * g + j, r1 = 16 + 4 * g + j;
+        if (r0 < cl) oh[(c0 + r0) * vstride] = static_cast<bf16>(o0[j]);
+        if (r1 < cl) oh[(c0 + r1) * vstride] = static_cast<bf16>(o1[j]);
       }
     }
+  };
+  lds_barrier();  // chunk 0 and the state operands of chunk 0
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) out(c - 1);  // Delta(c - 1) since B(c - 1)
+    const unsigned char *st = ring + (c % NST) * STAGE;
+    pb0 = lds8(st + REC_PB + pl);
+    pb1 = lds8(st + REC_PB + 1024 + pl);
+    qs0 = z;
+    qs1 = z;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 sbv = lds8(sop(c, tt));
+      qs0 = mma32(lds8(st + REC_QE + tt * 1024 + pl), sbv, qs0);
+      qs1 = mma32(lds8(st + REC_QE + (4 + tt) * 1024 + pl), sbv, qs1);
+    }
+    lds_barrier();  // B(c)
   }
+  out(nch - 1);
 }
 
 int64_t kda_slots(const Problem &p) { return p.total / CH + p.num_seqs; }
@@ -779,7 +786,7 @@ hipError_t launch_kda_chain(const Problem &pr, const FwdArgs &x, const void *wor
   cp.nb = nb;
   cp.units = (int)units;
   cp.nslots = kda_slots(pr);
-  const size_t smem = (size_t)NST * STAGE + 2 * 5 * 1024;
+  const size_t smem = (size_t)NST * STAGE + 2 * 2 * 5 * 1024;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_chain_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
