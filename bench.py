@@ -69,9 +69,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # 50 untimed prefill launches (about 12 ms): after 3 the GPU has not yet
-    # reached its full clock and a launch measures about 12 % slower
-    ap.add_argument("--warmup", type=int, default=50)
+    # 100 untimed prefill launches (about 22 ms): after 3 the GPU has not yet
+    # reached its full clock and a launch measures about 12 % slower, after
+    # 50 still about 5 %
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -107,16 +108,18 @@ def main():
     for _ in range(args.warmup):
         prefill_step()
     torch.cuda.synchronize(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # one pair of events around the K launches: an event after every launch
+    # would add about 4 us of gap per launch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
         prefill_step()
-        ev[i + 1].record(stream)
+    ev[1].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    total_ms = ev[0].elapsed_time(ev[-1])
+    total_ms = ev[0].elapsed_time(ev[1])
+    per_launch_ms = [total_ms / args.steps]  # the average launch, back to back
     ms_per_step = total_ms / args.steps
     tokens_per_s = T * args.steps / (total_ms / 1e3)
     flops = prefill_flops(T, w.H_k, w.H_v, w.d_k, w.d_v, w.chunk)
