@@ -233,6 +233,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
                      "traffic": profiled_traffic("chunked_mfma_kernel"),
+                     "mfma_busy": profiled_traffic("chunked_mfma_kernel", "mfma_busy_frac"),
                      "kernel": "chunked prefill", "flop_per_launch": flops,
                      "avg_launch_ms": avg_s * 1e3,
                      "hbm_view": {"bytes_per_launch": pbytes,
@@ -605,11 +606,12 @@ def kda_legs(gdr, dev, stream, steps):
     }
 
 
-def profiled_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed hardware-counter
-    profile (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
-    size), or None when that kernel's sources changed after the counters
-    were taken (the recorded sha256 no longer matches)."""
+def profiled_traffic(kernel, field="traffic_bytes"):
+    """A hardware-counter figure of `kernel` from the committed profile: by
+    default its HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, scaled by a
+    plain copy of known size); `mfma_busy_frac` is the share of SIMD-cycles
+    its matrix pipes were busy.  None when that kernel's sources changed
+    after the counters were taken (the recorded sha256 no longer matches)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -617,9 +619,10 @@ def profiled_traffic(kernel):
         h = hashlib.sha256()
         for f in rec["sources"]:
             h.update(open(os.path.join(ROOT, f), "rb").read())
+        value = rec[field]
     except (OSError, KeyError, ValueError):
         return None
-    return rec["traffic_bytes"] if h.hexdigest() == rec["sha256"] else None
+    return value if h.hexdigest() == rec["sha256"] else None
 
 
 def gdr_chunked_dtype(gdr, w):
