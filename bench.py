@@ -593,7 +593,9 @@ def kda_legs(gdr, dev, stream, steps):
                     "one_launch_ms": one_ms,
                     "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                  "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
-                                 "flop_per_launch": flops}},
+                                 "flop_per_launch": flops,
+                                 "mfma_busy": {"prep": profiled_traffic("kda_prep_kernel", "mfma_busy_frac"),
+                                               "chain": profiled_traffic("kda_chain_kernel", "mfma_busy_frac")}}},
         "varlen": {"workload": f"{len(var_lens)} packed sequences, lengths {var_lens} (seed 0), "
                                "48 value heads sharing 16 key heads, d_k=d_v=128, per-channel "
                                "gates, chunk 32, bf16, carried fp32 state; two launches",
