@@ -209,3 +209,20 @@ def kda_inputs(w: Workload, seed: int = 0, device="cpu", a_mean=0.0):
         N = lead[1]
         out["dense"]["a"] = out["a"].transpose(0, 1).reshape((N * w.steps, w.H_v, w.d_k)).contiguous()
     return out
+
+
+def coherent_keys(w: Workload, seed: int, eps: float, device="cpu"):
+    """Keys that repeat a direction: k_t = u + eps * n_t, with u ~ N(0, I)
+    drawn once per (sequence, key head) and n_t ~ N(0, I) per token, from a
+    generator seeded seed + 4243 (the other tensors of make_inputs are left
+    as they are).  At d_k = 128 the mean |cos| of two keys is about
+    1 / (1 + eps^2): eps = 1 gives about 0.5, eps = 0.33 about 0.9, against
+    about 0.07 for independent draws.  Shape and dtype of make_inputs' k
+    (dense or packed batches; not the decode layout)."""
+    gen = torch.Generator(device=device).manual_seed(seed + 4243)
+    lens = w.seq_lengths
+    u = _normal((len(lens), w.H_k, w.d_k), gen, device)
+    n = _normal((sum(lens), w.H_k, w.d_k), gen, device)
+    idx = torch.repeat_interleave(torch.arange(len(lens), device=device),
+                                  torch.tensor(lens, device=device))
+    return (u[idx] + eps * n).to(w.torch_dtype)
