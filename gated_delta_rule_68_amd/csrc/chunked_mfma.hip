@@ -15,24 +15,32 @@
 // fp32 to the products (the 1/|k_i| of P is applied to the rows of Delta).
 // Only differences gamma_r - gamma_i with i <= r are exponentiated.
 //
-// (I + A)^-1 is applied in 16-row blocks,
-//   Delta_1 = T_11 R_1,  Delta_2 = T_22 (R_2 - A_21 Delta_1),  T_bb = (I + A_bb)^-1,
-// each T_bb formed on the matrix cores from the identity, exact for the
-// strictly lower (nilpotent, N^16 = 0) N = A_bb,
-//   (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8).
+// (I + A)^-1 is formed whole for every chunk, in fp32, and rounded to bf16
+// only as the operand of Delta = T R.  With T = [[T11, 0], [T21, T22]] in
+// 16-row blocks:
+//   T11 = (I + A11)^-1   by a backward sweep on its transpose, (I + A11^T) T11^T = I
+//   T22 = (I + A22)^-1   by a forward sweep,                   (I + A22) T22 = I
+//   T21 = -T22 (A21 T11) by two fp32 matrix-core products.
+// Each sweep is 15 dependent steps; in step i the finished row i is broadcast
+// to the other rows of its 16-lane DPP row (row_newbcast) and subtracted with
+// the coefficient each row holds, one fused multiply-add per register.  A
+// product series such as (I - N)(I + N^2)(I + N^4)(I + N^8) is exact in real
+// arithmetic but not usable here: when keys repeat a direction under long
+// memory its powers grow like binomial coefficients, and bf16 roundings
+// before the cancellation leave O(1) errors in T.
 //
 // Work split.  A workgroup owns (sequence, value head, 32 columns of d_v); the
 // columns of S evolve independently.  Eight waves, one workgroup barrier per
 // chunk; chunk c lives in LDS buffer c % NSTAGE from the step its rows are
 // requested until the step its outputs are written:
 //   * 2 state waves each keep a [128 x 16] slice of S in MFMA accumulators for
-//     the whole sequence and run chunk c: K S, R, the block solve for Delta
-//     and S <- Gam_last S + K^T D Delta; they hand the state at chunk entry
+//     the whole sequence and run chunk c: K S, R, Delta = T R and
+//     S <- Gam_last S + K^T D Delta; they hand the state at chunk entry
 //     and diag(1/|k|) Delta (bf16) to
 //   * 2 output waves, which form Q S of chunk c in the same step and the
 //     outputs O = P Delta + Gam Q S of chunk c one step later;
-//   * 2 "prepare" waves form chunk c+1's matrices: P0 the Gram blocks of K,
-//     T_11, T_22 and -A_21; P1 the norms of q and the output mask P;
+//   * 2 "prepare" waves form chunk c+1's matrices: P0 the Gram blocks of K
+//     and the whole T = (I + A)^-1; P1 the norms of q and the output mask P;
 //   * 2 staging waves request the rows of chunk c+2+AHEAD: the k, q, v rows
 //     and the raw gates go straight from global memory into LDS
 //     (global_load_lds), never through registers; as soon as chunk c+3 has
@@ -64,7 +72,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
 // d_v is a template parameter of the kernel (64 or 128)
@@ -87,25 +94,12 @@ constexpr int ST1_OPS = 8 + 1 + 1;   // q rows, half of v, a and b
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// 16x16x16 product on operands packed as bf16 bit patterns (see pk4)
-__device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ bf16x4 pack4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   return __builtin_shufflevector(pack4(lo), pack4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-// Four floats rounded to bf16 and packed two per 32-bit word, as the
-// 16x16x16 product takes them.
-__device__ __forceinline__ s16x4 pk4(f32x4 x) {
-  const bf16x2 lo = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
-  const bf16x2 hi = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
-  return __builtin_bit_cast(s16x4, u32x2{__builtin_bit_cast(uint32_t, lo),
-                                         __builtin_bit_cast(uint32_t, hi)});
 }
 __device__ __forceinline__ f32x4 ld4(const float *p) {
   const float4 v = *reinterpret_cast<const float4 *>(p);
@@ -192,8 +186,9 @@ struct Stage {
   alignas(16) bf16 V[CH * BV];   // v rows, this workgroup's columns     (both)
   // per lane (m, g), written and read by lanes of the same index:
   alignas(16) bf16x8 P[2][64];   // P without 1/|k_i|: rows m, 16 + m at chunk slots 8g.. (P1)
-  alignas(16) bf16x4 T[2][64];   // (I + A_bb)^-1 of the diagonal blocks: [m][4g..4g+3] (P0)
-  alignas(16) bf16x4 nA21[64];   // -A_21: [m][4g..4g+3]                 (P0)
+  // T = (I + A)^-1 as A operands of Delta = T R in slot order (P0):
+  alignas(16) bf16x4 T0[64];     // rows 0..15: T11[m][4g..4g+3] (slots 8g+4.. are T12 = 0)
+  alignas(16) bf16x8 T1[64];     // rows 16..31: T21[m][4g..4g+3], T22[m][4g..4g+3]
   alignas(16) uint32_t ab[2 * CH]; // raw a_r (low half of word r), b_r (word 32 + r) (staging wave 1)
   alignas(16) float gam[CH];     // cumulative log decay                 (staging wave 1, a step early)
   alignas(16) float beta[CH];    //                                      (staging wave 1, a step early)
@@ -210,6 +205,10 @@ struct Smem {
   // handed from the state waves to the output waves, per state wave and lane:
   alignas(16) bf16x8 sb[2][NC][4][64];  // state at chunk entry, bf16 B operands (ring by chunk)
   alignas(16) bf16x8 db[2][NC][64];     // diag(1/|k|) Delta of the chunk, bf16 (ring by chunk)
+  // P0's own exchange inside one chunk: column m of -A11, row m of -A22 and
+  // row m of A21 (columns in the order 4j + g), 80-byte rows so that 16 rows
+  // read at one column fill distinct 16-byte bank slots
+  alignas(16) float p0x[3][16][20];
 };
 
 struct MfmaParams {
@@ -460,42 +459,70 @@ __device__ __forceinline__ void stage_gates(Stage &S, int lane, int cl, float ne
   }
 }
 
-// (I + N)^-1 for the two strictly lower 16x16 diagonal blocks N0, N1 of A,
-// each given in both lane layouts:
-//   na[j] = N[m][4g+j] (A operand layout), nb[j] = N[4g+j][m] (B/accumulator layout).
-// The identity (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) is exact since
-// N^16 = 0, and its factors commute.  t0a, t1a get T[m][4g+j] (A layout) and
-// t0b gets T0[4g+j][m] (B layout).  Transposes ride along: the accumulator of
-// X Y is the B layout of X Y, that of Y^T X^T its A layout.  The two blocks
-// are interleaved step by step so that each waits on the other's latency.
-template <bool WANT_B>
-__device__ __forceinline__ void unit_lower_inverse2(f32x4 na0, f32x4 nb0, f32x4 na1, f32x4 nb1,
-                                                    int m, int g, f32x4 &t0a, f32x4 &t0b,
-                                                    f32x4 &t1a) {
-  const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-  const s16x4 a0 = pk4(na0), b0 = pk4(nb0), a1 = pk4(na1), b1 = pk4(nb1);
-  // squares: N^(2^k) in B layout (b*) and A layout (a*)
-  const s16x4 b0_2 = pk4(mma16(a0, b0, z)), b1_2 = pk4(mma16(a1, b1, z));
-  const s16x4 a0_2 = pk4(mma16(b0, a0, z)), a1_2 = pk4(mma16(b1, a1, z));
-  const s16x4 b0_4 = pk4(mma16(a0_2, b0_2, z)), b1_4 = pk4(mma16(a1_2, b1_2, z));
-  const s16x4 a0_4 = pk4(mma16(b0_2, a0_2, z)), a1_4 = pk4(mma16(b1_2, a1_2, z));
-  const s16x4 b0_8 = pk4(mma16(a0_4, b0_4, z)), b1_8 = pk4(mma16(a1_4, b1_4, z));
-  const s16x4 a0_8 = WANT_B ? pk4(mma16(b0_4, a0_4, z)) : s16x4{0, 0, 0, 0};
-  f32x4 id;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) id[j] = (m == 4 * g + j) ? 1.f : 0.f;
-  // A layout: P_{k+1}^T = P_k^T + (N^(2^k))^T P_k^T, P_1 = I - N
-  // B layout: Q_{k+1} = Q_k + N^(2^k) Q_k,          Q_1 = I - N
-  f32x4 p0 = id - na0, p1 = id - na1, q0 = id - nb0;
-  p0 = mma16(b0_2, pk4(p0), p0);
-  p1 = mma16(b1_2, pk4(p1), p1);
-  if (WANT_B) q0 = mma16(a0_2, pk4(q0), q0);
-  p0 = mma16(b0_4, pk4(p0), p0);
-  p1 = mma16(b1_4, pk4(p1), p1);
-  if (WANT_B) q0 = mma16(a0_4, pk4(q0), q0);
-  t0a = mma16(b0_8, pk4(p0), p0);
-  t1a = mma16(b1_8, pk4(p1), p1);
-  t0b = WANT_B ? mma16(a0_8, pk4(q0), q0) : q0;
+// The two substitution sweeps of P0, interleaved, 15 steps:
+//  * backward, X = T11^T, lane (r, g) holding X[r][4j + g] in x[j]: in step s
+//    row i = 15 - s is final and every row r adds cB[i] X[i] (cB[i] holds
+//    -A11[i][r], zero unless r < i).  X[i][4j + g] = T11[4j + g][i] is zero
+//    when 4j + g < i, so registers j < (i - 3) / 4 are skipped;
+//  * forward, Y = T22, lane (m, g) holding Y[m][4g + j] in y[j]: in step s
+//    row i = s is final and every row m adds cF[i] Y[i] (cF[i] holds
+//    -A22[m][i], zero unless i < m).  Y[i][4g + j] is zero when 4g + j > i,
+//    so registers j > i are skipped.
+// One update is one v_fmac_f32 whose first source is row i's register,
+// broadcast to its 16-lane DPP row by row_newbcast.  Each step is one asm
+// statement that starts with s_nop 1: a DPP source must be written at least
+// two wait states before it is read, and within a step every register is
+// read and written once.
+#define GDR_FX(j, i) "v_fmac_f32_dpp %" #j ", %" #j ", %8 row_newbcast:" #i " row_mask:0xf bank_mask:0xf\n\t"
+#define GDR_FY(j, i) "v_fmac_f32_dpp %" #j ", %" #j ", %9 row_newbcast:" #i " row_mask:0xf bank_mask:0xf\n\t"
+#define GDR_X1(i) GDR_FX(3, i)
+#define GDR_X2(i) GDR_FX(3, i) GDR_FX(2, i)
+#define GDR_X3(i) GDR_FX(3, i) GDR_FX(2, i) GDR_FX(1, i)
+#define GDR_X4(i) GDR_FX(3, i) GDR_FX(2, i) GDR_FX(1, i) GDR_FX(0, i)
+#define GDR_Y1(i) GDR_FY(4, i)
+#define GDR_Y2(i) GDR_FY(4, i) GDR_FY(5, i)
+#define GDR_Y3(i) GDR_FY(4, i) GDR_FY(5, i) GDR_FY(6, i)
+#define GDR_Y4(i) GDR_FY(4, i) GDR_FY(5, i) GDR_FY(6, i) GDR_FY(7, i)
+#define GDR_STEP(XS, YS, ib, jf)                                                          \
+  asm volatile("s_nop 1\n\t" XS YS                                                        \
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(y[0]), "+v"(y[1]), \
+                 "+v"(y[2]), "+v"(y[3])                                                   \
+               : "v"(cB[ib]), "v"(cF[jf]))
+__device__ __forceinline__ void sweeps(float (&x)[4], float (&y)[4], const float (&cB)[16],
+                                       const float (&cF)[16]) {
+  GDR_STEP(GDR_X1(15), GDR_Y1(0), 15, 0);
+  GDR_STEP(GDR_X1(14), GDR_Y2(1), 14, 1);
+  GDR_STEP(GDR_X1(13), GDR_Y3(2), 13, 2);
+  GDR_STEP(GDR_X1(12), GDR_Y4(3), 12, 3);
+  GDR_STEP(GDR_X2(11), GDR_Y4(4), 11, 4);
+  GDR_STEP(GDR_X2(10), GDR_Y4(5), 10, 5);
+  GDR_STEP(GDR_X2(9), GDR_Y4(6), 9, 6);
+  GDR_STEP(GDR_X2(8), GDR_Y4(7), 8, 7);
+  GDR_STEP(GDR_X3(7), GDR_Y4(8), 7, 8);
+  GDR_STEP(GDR_X3(6), GDR_Y4(9), 6, 9);
+  GDR_STEP(GDR_X3(5), GDR_Y4(10), 5, 10);
+  GDR_STEP(GDR_X3(4), GDR_Y4(11), 4, 11);
+  GDR_STEP(GDR_X4(3), GDR_Y4(12), 3, 12);
+  GDR_STEP(GDR_X4(2), GDR_Y4(13), 2, 13);
+  GDR_STEP(GDR_X4(1), GDR_Y4(14), 1, 14);
+  // the sweeps' last writes before the matrix-core reads of x and y
+  asm volatile("s_nop 7" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(y[0]),
+               "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
+}
+#undef GDR_STEP
+#undef GDR_Y4
+#undef GDR_Y3
+#undef GDR_Y2
+#undef GDR_Y1
+#undef GDR_X4
+#undef GDR_X3
+#undef GDR_X2
+#undef GDR_X1
+#undef GDR_FY
+#undef GDR_FX
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Row operands of one chunk for the prepare waves: rows m and 16 + m of k
@@ -516,50 +543,83 @@ __device__ __forceinline__ void read_row_ops(const Stage &S, RowOps &o, int m, i
   }
 }
 
-// P0: Gram blocks of k, T_11, T_22 and -A_21 of one chunk (1/|k| from staging).
-// Lane (m, g) holds the Gram entries (k_i . k_m), i = 4g + j, of each block;
-// exactly one of i < m, i > m holds off the diagonal, so one decay factor
-// exp(-|gam_m - gam_i|) serves both the A-operand (row m) and the B-operand
-// (column m) layout of N.
-__device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S, const RowOps &o,
-                                           int lane) {
+// P0: the Gram blocks of k and T = (I + A)^-1 of one chunk, in fp32, written
+// as bf16 A operands for the state waves (1/|k| from staging).  Lane (m, g)
+// holds the Gram entries (k_i . k_m), i = 4g + j, of each block, which give
+// column m of A11, row m of A22 (the Gram matrix is symmetric) and row m of
+// A21; a round trip through P0's own LDS rows hands every lane the whole
+// column (row) its sweep needs.  Every decay factor is exp(gam_r - gam_i)
+// with i <= r, at most 1.
+__device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S,
+                                           float (&xs)[3][16][20], const RowOps &o, int lane) {
   const int m = lane & 15, g = lane >> 4;
-  const int cl = S.cl;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
-  const f32x4 bt_lo = ld4(&S.beta[4 * g]), bt_hi = ld4(&S.beta[16 + 4 * g]);
-  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
-  const float bt_m0 = S.beta[m], bt_m1 = S.beta[16 + m];
+  const f32x4 bt_lo = ld4(&S.beta[4 * g]);
   const f32x4 ik_lo = ld4(&S.ik[4 * g]), ik_hi = ld4(&S.ik[16 + 4 * g]);
-  const float ik_m0 = S.ik[m], ik_m1 = S.ik[16 + m];
-  f32x4 t00 = z, t11 = z, t01 = z;  // (K K^T) blocks: rows 4g+j, column m (+16)
+  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
+  const float ik_m0 = S.ik[m], bik_m1 = S.beta[16 + m] * S.ik[16 + m];
+  f32x4 t00 = z, t11 = z, t01 = z;  // (k_i . k_m) of blocks 00, 11; (k_i . k_{16+m}) of 10
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     t00 = mma32(o.k0[kb], o.k0[kb], t00);
     t11 = mma32(o.k1[kb], o.k1[kb], t11);
     t01 = mma32(o.k0[kb], o.k1[kb], t01);
   }
-  // A in both layouts for the two diagonal blocks, and -A_21 in A layout.
-  f32x4 na0, nb0, na1, nb1, na21;
-  const float bik_m1 = bt_m1 * ik_m1;
+  f32x4 cA, rA;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = 4 * g + j;
-    const float x0 = t00[j] * ik_m0 * ik_lo[j] * fast_exp(-fabsf(gm_m0 - gm_lo[j]));
-    na0[j] = (i < m) ? bt_m0 * x0 : 0.f;
-    nb0[j] = (i > m) ? bt_lo[j] * x0 : 0.f;
-    const float x1 = t11[j] * ik_m1 * ik_hi[j] * fast_exp(-fabsf(gm_m1 - gm_hi[j]));
-    na1[j] = (i < m) ? bt_m1 * x1 : 0.f;
-    nb1[j] = (i > m) ? bt_hi[j] * x1 : 0.f;
-    // A_21[m][i] = beta_{16+m} exp(gam_{16+m} - gam_i) ik_{16+m} ik_i (k_i . k_{16+m})
-    na21[j] = -bik_m1 * ik_lo[j] * fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * t01[j];
+    // -A11[i][m] = -beta_i exp(gam_i - gam_m) ik_i ik_m (k_i . k_m), i > m
+    const float c0 = bt_lo[j] * ik_lo[j] * ik_m0 * fast_exp(fminf(gm_lo[j] - gm_m0, 0.f)) * t00[j];
+    cA[j] = (i > m) ? -c0 : 0.f;
+    // -A22[m][i] = -beta_{16+m} exp(gam_{16+m} - gam_{16+i}) ik_{16+m} ik_{16+i} (k . k), i < m
+    const float c1 = bik_m1 * ik_hi[j] * fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * t11[j];
+    rA[j] = (i < m) ? -c1 : 0.f;
+    // A21[m][i] = beta_{16+m} exp(gam_{16+m} - gam_i) ik_{16+m} ik_i (k_i . k_{16+m})
+    xs[2][m][4 * j + g] = bik_m1 * ik_lo[j] * fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * t01[j];
   }
-  // T11, T22 (the state waves apply T21 = -T22 A21 T11 as a block solve)
-  f32x4 t11a, t11b, t22a;
-  unit_lower_inverse2<false>(na0, nb0, na1, nb1, m, g, t11a, t11b, t22a);
-  S.T[0][lane] = pack4(t11a);
-  S.T[1][lane] = pack4(t22a);
-  S.nA21[lane] = pack4(na21);
+  *reinterpret_cast<f32x4 *>(&xs[0][m][4 * g]) = cA;
+  *reinterpret_cast<f32x4 *>(&xs[1][m][4 * g]) = rA;
+  wave_lds_sync();
+  float cB[16], cF[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 u = ld4(&xs[0][m][4 * q]), w = ld4(&xs[1][m][4 * q]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cB[4 * q + j] = u[j];
+      cF[4 * q + j] = w[j];
+    }
+  }
+  const f32x4 a21 = ld4(&xs[2][m][4 * g]);  // A21[m][4kk + g] in register kk
+  float x[4], y[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = (m == 4 * j + g) ? 1.f : 0.f;
+    y[j] = (m == 4 * g + j) ? 1.f : 0.f;
+  }
+  sweeps(x, y, cB, cF);
+  // M = A21 T11: contraction index 4kk + g in step kk (x[kk] = T11[4kk + g][n])
+  f32x4 mm = z;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) mm = mma_f32(a21[kk], x[kk], mm);
+  // T22 M: contraction index 4g + kk in step kk (y[kk] = T22[m][4g + kk],
+  // mm[kk] = M[4g + kk][n]); lane (n, g) gets (T22 M)[4g + j][n] = -T21[4g + j][n]
+  f32x4 t21 = z;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) t21 = mma_f32(y[kk], mm[kk], t21);
+  // bf16 operands: T22 row m stays in this lane; T11 and T21 columns scatter
+  // to the lanes that own their rows
+  bf16 *T0 = reinterpret_cast<bf16 *>(S.T0);
+  bf16 *T1 = reinterpret_cast<bf16 *>(S.T1);
+  *reinterpret_cast<bf16x4 *>(T1 + 8 * lane + 4) = pack4(f32x4{y[0], y[1], y[2], y[3]});
+  const int dst = 16 * (m >> 2), e = m & 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    T0[4 * (dst + 4 * j + g) + e] = (bf16)x[j];
+    T1[8 * (dst + 4 * g + j) + e] = (bf16)(-t21[j]);
+  }
 }
 
 // P1: scale/|q_r| from the Gram diagonal of q, and the output mask without the
@@ -737,9 +797,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         const bool more = c + 1 < nch;
         const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
         // this chunk's prepared tile and row factors
-        const s16x4 t11 = __builtin_bit_cast(s16x4, st.T[0][lane]);
-        const s16x4 t22 = __builtin_bit_cast(s16x4, st.T[1][lane]);
-        const s16x4 na21 = __builtin_bit_cast(s16x4, st.nA21[lane]);
+        const bf16x4 tt0 = st.T0[lane];
+        const bf16x8 tt1 = st.T1[lane];
         const f32x4 bt0 = ld4(&st.beta[4 * g]), bt1 = ld4(&st.beta[16 + 4 * g]);
         const f32x4 gm0 = ld4(&st.Gam[4 * g]), gm1 = ld4(&st.Gam[16 + 4 * g]);
         const f32x4 ik0 = ld4(&st.ik[4 * g]), ik1 = ld4(&st.ik[16 + 4 * g]);
@@ -764,11 +823,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           R0[j] = bt0[j] * ((float)vv[j] - gm0[j] * ik0[j] * ks[0][j]);
           R1[j] = bt1[j] * ((float)vv[4 + j] - gm1[j] * ik1[j] * ks[1][j]);
         }
-        // Delta_1 = T11 R1, Delta_2 = T22 (R2 - A21 Delta_1); SSD: no erase, Delta = R
+        // Delta = T R, both 16-row blocks from the one bf16 operand of R in
+        // slot order; SSD: no erase, Delta = R
         f32x4 d1 = R0, d2 = R1;
         if constexpr (!SSD) {
-          d1 = mma16(t11, pk4(R0), z);
-          d2 = mma16(t22, pk4(mma16(na21, pk4(d1), R1)), z);
+          const bf16x8 Rb = pack8(R0, R1);
+          d1 = mma32(cat8(tt0, bf16x4{0, 0, 0, 0}), Rb, z);
+          d2 = mma32(tt1, Rb, z);
         }
         // diag(ik) Delta for the outputs of this chunk
         sm.db[c & 1][cw][lane] = pack8(ik0 * d1, ik1 * d2);
@@ -861,7 +922,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
           else
             prepare_p_ssd<1>(sm.st[c % NSTAGE], ops, lane);
         } else if (wave == W_P0) {
-          prepare_p0(p, sm.st[c % NSTAGE], ops, lane);
+          prepare_p0(p, sm.st[c % NSTAGE], sm.p0x, ops, lane);
         } else {
           prepare_p1(p, sm.st[c % NSTAGE], ops, lane);
         }
