@@ -37,6 +37,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", "chunked_path", "conv_silu",
+           "chunked_workspace", "chunked_workspace_bytes", "workspace_error",
            "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version",
            "ssd_recurrent_fwd", "ssd_chunked_fwd", "kda_recurrent_fwd", "kda_chunked_fwd",
            "kda_chunked_fwd_split"]
@@ -46,7 +47,7 @@ _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_F32, GDR_BF16 = 0, 1
 _STATUS = {0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_SHAPE", 3: "GDR_ERR_UNSUPPORTED",
-           4: "GDR_ERR_ALIGN", 5: "GDR_ERR_LAUNCH", 6: "GDR_ERR_ALIAS"}
+           4: "GDR_ERR_ALIGN", 5: "GDR_ERR_WORKSPACE", 6: "GDR_ERR_LAUNCH", 7: "GDR_ERR_ALIAS"}
 
 
 class GdrError(RuntimeError):
@@ -79,8 +80,10 @@ def _bind(lib):
     lib.gdr_gates.restype = ctypes.c_int
     lib.gdr_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdr_recurrent_fwd.restype = ctypes.c_int
-    lib.gdr_chunked_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdr_chunked_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
     lib.gdr_chunked_fwd.restype = ctypes.c_int
+    lib.gdr_chunked_workspace_bytes.argtypes = [sp]
+    lib.gdr_chunked_workspace_bytes.restype = ctypes.c_size_t
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_chunked_path.argtypes = [sp]
@@ -229,7 +232,8 @@ def gates(q, k, a, b, A_log, dt_bias, *, scale=None, l2_eps=1e-6, num_seqs=None,
 
 
 def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_seqs, chunk,
-         scale, l2_eps, o, final_state, output_final_state, inplace, kda=False, fused=None):
+         scale, l2_eps, o, final_state, output_final_state, inplace, kda=False, fused=None,
+         workspace=None):
     dense_T = q.shape[1] if q.dim() == 4 else None
     q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
     a, b = _flatten(a, 2 if kda else 1), _flatten(b, 1)
@@ -279,6 +283,17 @@ def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_
                    lib().gdr_kda_chunked_workspace(ctypes.byref(shape), ctypes.byref(nbytes)))
         ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev) if nbytes.value else None
         args += [_ptr(ws), ctypes.c_size_t(nbytes.value)]
+    elif fn_name == "gdr_chunked_fwd":
+        # the cooperative form's workspace: "auto" allocates a zero-filled one
+        # of the size the library reports (none when that is 0)
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+            nb = int(lib().gdr_chunked_workspace_bytes(ctypes.byref(shape)))
+            workspace = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb else None
+        if workspace is not None:
+            _check(workspace, "workspace", dev, torch.uint8)
+        args += [_ptr(workspace), ctypes.c_size_t(0 if workspace is None else workspace.numel())]
     rc = fn(*args, _stream(dev))
     _raise(fn_name, rc)
     if dense_T is not None:
@@ -308,10 +323,47 @@ def recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, cu_seqle
 
 def chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32, cu_seqlens=None,
                 num_seqs=None, scale=None, l2_eps=1e-6, o=None, final_state=None,
-                output_final_state=True, inplace=False):
-    """Chunked (prefill) form with ``chunk`` tokens per triangular solve."""
+                output_final_state=True, inplace=False, workspace="auto"):
+    """Chunked (prefill) form with ``chunk`` tokens per triangular solve.
+
+    ``workspace``: "auto" (a zero-filled uint8 tensor of the size
+    gdr_chunked_workspace_bytes reports, allocated for this call), a tensor
+    from ``chunked_workspace`` that the caller keeps across calls, or None (no
+    workspace: the chain workgroups form every chunk's triangular inverse and
+    output mask themselves)."""
     return _fwd("gdr_chunked_fwd", q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens,
-                num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state, inplace)
+                num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state, inplace,
+                workspace=workspace)
+
+
+def chunked_workspace_bytes(H_k, H_v, d_k, d_v, dtype, num_seqs=1, chunk=32) -> int:
+    """gdr_chunked_workspace_bytes for a batch of ``num_seqs`` sequences of
+    this head shape (independent of their lengths)."""
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else (
+        GDR_F32 if dtype in ("f32", "float32") else GDR_BF16)
+    s = _make_shape(num_seqs, H_k, H_v, d_k, d_v, None, num_seqs, code, chunk, None, 1e-6)
+    return int(lib().gdr_chunked_workspace_bytes(ctypes.byref(s)))
+
+
+def chunked_workspace(H_k, H_v, d_k, d_v, dtype, num_seqs=1, chunk=32, device="cuda"):
+    """A zero-filled workspace for chunked_fwd on batches of this shape, to
+    keep across calls (the library leaves it zero-filled after each call);
+    None when the shape has no cooperative form.  Calls sharing one
+    workspace must not overlap in time."""
+    nb = chunked_workspace_bytes(H_k, H_v, d_k, d_v, dtype, num_seqs, chunk)
+    return torch.zeros(nb, dtype=torch.uint8, device=device) if nb else None
+
+
+def workspace_error(workspace) -> int:
+    """The error words of a chunked_fwd workspace, ORed (synchronises): nonzero
+    if a wait of the cooperative form ran out (its results are then invalid)."""
+    if workspace is None:
+        return 0
+    # one 128-byte line per XCD: arrival and completion counters, error word
+    acc = 0
+    for v in workspace[:2048].view(torch.int32).view(16, 32)[:, 2].cpu().tolist():
+        acc |= int(v)
+    return acc
 
 
 def fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32, cu_seqlens=None,

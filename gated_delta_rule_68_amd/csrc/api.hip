@@ -103,7 +103,7 @@ gdr_status launched(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_LA
 gdr_status check_workspace(const Problem &pr, const FwdArgs &x, const void *workspace,
                            size_t workspace_bytes, size_t need) {
   if (!workspace) return GDR_ERR_NULL;
-  if (workspace_bytes < need) return GDR_ERR_SHAPE;
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
   if (!aligned_to(workspace, 256)) return GDR_ERR_ALIGN;
   const size_t es = elem_size(pr.dtype);
   const size_t T = (size_t)pr.total;
@@ -136,6 +136,7 @@ const char *gdr_status_string(gdr_status s) {
     case GDR_ERR_SHAPE: return "inconsistent shape";
     case GDR_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
     case GDR_ERR_ALIGN: return "tensor pointer breaks its alignment rule";
+    case GDR_ERR_WORKSPACE: return "workspace smaller than the call needs";
     case GDR_ERR_LAUNCH: return "kernel launch failed";
     case GDR_ERR_ALIAS: return "an output overlaps an input it may not alias";
   }
@@ -202,7 +203,7 @@ gdr_status gdr_recurrent_fwd(const gdr_shape *shape, const void *q, const void *
 gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k, const void *v,
                            const void *a, const void *b, const float *A_log, const float *dt_bias,
                            const float *initial_state, void *o, float *final_state,
-                           hipStream_t stream) {
+                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
   using namespace gdr;
   Problem pr;
   gdr_status st = resolve(shape, pr);
@@ -211,9 +212,26 @@ gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
   FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
   st = check_fwd(pr, x);
   if (st != GDR_OK) return st;
-  if (chunked_mfma_supports(pr)) return launched(launch_chunked_mfma(pr, x, stream));
+  if (chunked_mfma_supports(pr)) {
+    const size_t need = workspace ? chunked_coop_workspace_bytes(pr) : 0;
+    if (need > 0 && pr.total > 0) {
+      st = check_workspace(pr, x, workspace, workspace_bytes, need);
+      if (st != GDR_OK) return st;
+      if (launch_chunked_coop(pr, x, workspace, stream) == hipSuccess) return GDR_OK;
+      (void)hipGetLastError();  // a refused cooperative launch: run the fused kernel
+    }
+    return launched(launch_chunked_mfma(pr, x, stream));
+  }
   if (!chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
   return launched(launch_chunked_vec(pr, x, stream));
+}
+
+size_t gdr_chunked_workspace_bytes(const gdr_shape *shape) {
+  using namespace gdr;
+  Problem pr;
+  if (resolve(shape, pr) != GDR_OK) return 0;
+  if (!chunked_mfma_supports(pr)) return 0;
+  return chunked_coop_workspace_bytes(pr);
 }
 
 gdr_status gdr_conv_silu(const gdr_shape *shape, int32_t width, const void *x, const float *weight,

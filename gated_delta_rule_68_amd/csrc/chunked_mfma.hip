@@ -1,7 +1,7 @@
 // Chunked (UT-transform) form on the gfx950 matrix cores: bf16 operands, fp32
-// accumulation, fp32 state.  Instantiated for d_k = d_v = 128 and 32-token
-// chunks (the shape the GatedDeltaRule.ixx File Reference, "Detailed
-// Description", gives: one triangular solve per 32 steps).
+// accumulation, fp32 state.  Instantiated for d_k = 128, d_v = 64 or 128 and
+// 32-token chunks (the shape the GatedDeltaRule.ixx File Reference,
+// "Detailed Description", gives: one triangular solve per 32 steps).
 //
 // Algebra (per chunk of c <= 32 tokens, S the state at chunk entry, gamma the
 // in-chunk cumulative log decay, Gamma = exp(gamma); rows r, i in-chunk):
@@ -29,31 +29,51 @@
 // memory its powers grow like binomial coefficients, and bf16 roundings
 // before the cancellation leave O(1) errors in T.
 //
-// Work split.  A workgroup owns (sequence, value head, 32 columns of d_v); the
-// columns of S evolve independently.  Eight waves, one workgroup barrier per
-// chunk; chunk c lives in LDS buffer c % NSTAGE from the step its rows are
-// requested until the step its outputs are written:
+// Everything a chunk needs besides its k, q and v rows and the state -- T, P
+// and the row factors -- is one 5 KB record (Rec).  Two kernels use it:
+//
+// Fused kernel (chunked_mfma_kernel).  A workgroup owns (sequence, value
+// head, 32 columns of d_v); the columns of S evolve independently.  Eight
+// waves, one workgroup barrier per chunk; chunk c lives in LDS buffer
+// c % NSTAGE from the step its rows are requested until the step its outputs
+// are written:
 //   * 2 state waves each keep a [128 x 16] slice of S in MFMA accumulators for
 //     the whole sequence and run chunk c: K S, R, Delta = T R and
 //     S <- Gam_last S + K^T D Delta; they hand the state at chunk entry
 //     and diag(1/|k|) Delta (bf16) to
 //   * 2 output waves, which form Q S of chunk c in the same step and the
 //     outputs O = P Delta + Gam Q S of chunk c one step later;
-//   * 2 "prepare" waves form chunk c+1's matrices: P0 the Gram blocks of K
+//   * 2 "prepare" waves form chunk c+1's record: P0 the Gram blocks of K
 //     and the whole T = (I + A)^-1; P1 the norms of q and the output mask P;
 //   * 2 staging waves request the rows of chunk c+2+AHEAD: the k, q, v rows
 //     and the raw gates go straight from global memory into LDS
 //     (global_load_lds), never through registers; as soon as chunk c+3 has
 //     landed, staging wave 0 derives the norms of its k rows and staging
 //     wave 1 its gates.
+// The four workgroups of a value head each form the same records.
+//
+// Cooperative kernel (chunked_coop_kernel), one launch with every workgroup
+// resident (one per compute unit).  Workgroups find their role by the
+// accelerator complex die (XCD) they run on: per (sequence, key head) group,
+// the chain workgroups of its value heads and four producer workgroups sit on
+// one XCD and share its L2.  Producer p forms the records of chunks
+// c = p mod 4 for all value heads of the group, once, and writes them to a
+// ring of R slots per value head in the workspace; a chain workgroup (state,
+// output and staging waves as above, no prepare waves) copies each record
+// into LDS with its rows once the producer's flag for that chunk is set, and
+// publishes how far it has copied, which is when the producer may reuse the
+// slot.  Flags and counters are read past the L1 and scalar caches, in the
+// shared L2.  Every wait is bounded: a wait that runs out marks the
+// workspace's error word instead of hanging.
+//
 // The k and q tiles are stored unpadded with their 16-byte pieces XOR-swizzled
 // per row, so that the operand reads (16 rows at one column) and the
 // transposing reads (8 rows at 2 columns) each touch every bank once.
 //
 // Operand lane orders (v_mfma_f32_16x16x32_bf16: lane l = 16 g + m holds A row
 // m / B column m at k = 8g..8g+7, and accumulator rows 4g..4g+3 of column m;
-// v_mfma_f32_16x16x16_bf16 the same with k = 4g..4g+3).  An accumulator pair
-// covering rows 0..15 and 16..31 gives lane l the rows 4g..4g+3 and
+// v_mfma_f32_16x16x4_f32: A row m / B column m at k = g).  An accumulator
+// pair covering rows 0..15 and 16..31 gives lane l the rows 4g..4g+3 and
 // 16+4g..16+4g+3 of its column, which is a valid B operand if the contraction
 // index is visited in "slot" order: slot 8g+j is position 4g+j (j < 4) or
 // 16+4g+j-4 (j >= 4) of a 32-block.  The chunk-position operands (T, P and
@@ -74,22 +94,39 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
-// d_v is a template parameter of the kernel (64 or 128)
+// d_v is a template parameter of the kernels (64 or 128)
 constexpr int CH = 32;      // tokens per chunk
-constexpr int NC = 2;       // consumer waves (16 columns each)
+constexpr int NC = 2;       // state (and output) waves, 16 columns each
 constexpr int BV = 16 * NC;
-constexpr int NWAVES = 8;
+constexpr int NWAVES = 8;   // fused kernel
 constexpr int NSTAGE = 5;   // chunk buffers in LDS
 constexpr int AHEAD = 2;    // chunks whose rows are in flight beyond the one being published
 static_assert(AHEAD <= NSTAGE - 3, "a buffer is refilled only after its chunk was consumed");
+static_assert(AHEAD == 2, "the cooperative staging wave fetches flags two steps ahead of AHEAD");
 
-// wave roles (wave w runs on SIMD w % 4): the state waves share a SIMD with
-// the light staging waves, the output waves one with P0 and P1
+// fused kernel: wave roles (wave w runs on SIMD w % 4): the state waves share
+// a SIMD with the light staging waves, the output waves one with P0 and P1
 constexpr int W_C0 = 0, W_P0 = 2, W_P1 = 3, W_ST0 = 4, W_O0 = 6;
 
-// vector-memory operations one staging wave issues per chunk
+// vector-memory operations one staging wave issues per chunk (fused kernel)
 constexpr int ST0_OPS = 8 + 1;       // k rows, half of v
 constexpr int ST1_OPS = 8 + 1 + 1;   // q rows, half of v, a and b
+
+// cooperative kernel: six waves; chain workgroups use waves 0, 1 (state, SIMD
+// 0, 1), 2, 3 (output, SIMD 2, 3) and 4, 5 (staging, SIMD 0, 1)
+constexpr int NWAVES_C = 6;
+constexpr int CW_O0 = 2, CW_ST0 = 4;
+constexpr int REC_BYTES = 7168;           // one record; 7 loads of 1 KB per wave
+constexpr int REC_DMAS = REC_BYTES / 1024;
+constexpr int CST0_OPS = 8 + 1 + REC_DMAS;  // k rows, half of v, the record (+ 1 flag a step)
+constexpr int CST1_OPS = 8 + 1;             // q rows, half of v
+constexpr int PRODUCERS = 4;              // producer workgroups per group
+constexpr int RING = 16;                  // record slots per value head
+constexpr int MAX_GV = 3;                 // value heads per key head on this path
+constexpr int PROD_OPS = 8 + 8 + 8 + MAX_GV;  // a producer's loads per chunk: k, q, previous k rows, a and b
+constexpr int XCD_CUS = 32;               // compute units per XCD on gfx950
+constexpr int MAX_XCD = 16;
+constexpr int SPIN_LIMIT = 1 << 20;       // polls before a wait gives up (well under a second)
 
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -180,24 +217,45 @@ __device__ __forceinline__ int kq_off(int r, int d) {
   return r * DK + ((((d >> 3) ^ swz(r & 15)) << 3) | (d & 7));
 }
 
+// Everything one chunk needs besides its rows and the state, for one value
+// head: written by P0, P1 and the staging waves (fused kernel) or by a
+// producer workgroup (cooperative kernel), read by the state and output
+// waves.  Lane-ordered tiles are written and read by lanes of the same index.
+struct alignas(16) Rec {
+  // T = (I + A)^-1 as A operands of Delta = T R in slot order:
+  bf16x4 T0[64];       // rows 0..15: T11[m][4g..4g+3] (slots 8g+4.. are T12 = 0)
+  bf16x8 T1[64];       // rows 16..31: T21[m][4g..4g+3], T22[m][4g..4g+3]
+  bf16x8 P[2][64];     // P without 1/|k_i|: rows m, 16 + m at chunk slots 8g..
+  // cooperative kernel: the raw cross Gram K_c K_{c-1}^T of this chunk's k
+  // rows against the previous chunk's, as the A operand of K_c S_c =
+  // Gam_last(c-1) K_c S_{c-1} + GX D_{c-1} Delta_{c-1} (rows 16 mt + m, the
+  // previous chunk's positions in slot order)
+  bf16x8 GX[2][64];
+  float bt[CH];        // beta_r (0 past the end)
+  float bgk[CH];       // beta_r Gam_r / |k_r|: the factor of (K S) in R
+  float tk[CH];        // exp(gam_last - gam_r) / |k_r|: the factor of Delta in the update
+  float ik[CH];        // 1 / |k_r| (0 past the end)
+  float Gm[CH];        // Gam_r = exp(gam_r)
+  float iq[CH];        // scale / |q_r| (0 past the end)
+  float Gc;            // exp(gam_last)
+  int cl;              // valid rows of the chunk
+  unsigned char pad[REC_BYTES - 5632 - 6 * 4 * CH - 8];
+};
+static_assert(sizeof(Rec) == REC_BYTES, "record size");
+
+// A record under construction with the chunk's decays.
+struct Prep {
+  Rec r;
+  alignas(16) float gam[CH];   // cumulative log decay
+  alignas(16) float tail[CH];  // exp(gam_last - gam)
+};
+
 struct Stage {
   alignas(16) bf16 K[CH * DK];   // k rows, swizzled                     (loaded by staging wave 0)
   alignas(16) bf16 Q[CH * DK];   // q rows, swizzled                     (staging wave 1)
   alignas(16) bf16 V[CH * BV];   // v rows, this workgroup's columns     (both)
-  // per lane (m, g), written and read by lanes of the same index:
-  alignas(16) bf16x8 P[2][64];   // P without 1/|k_i|: rows m, 16 + m at chunk slots 8g.. (P1)
-  // T = (I + A)^-1 as A operands of Delta = T R in slot order (P0):
-  alignas(16) bf16x4 T0[64];     // rows 0..15: T11[m][4g..4g+3] (slots 8g+4.. are T12 = 0)
-  alignas(16) bf16x8 T1[64];     // rows 16..31: T21[m][4g..4g+3], T22[m][4g..4g+3]
-  alignas(16) uint32_t ab[2 * CH]; // raw a_r (low half of word r), b_r (word 32 + r) (staging wave 1)
-  alignas(16) float gam[CH];     // cumulative log decay                 (staging wave 1, a step early)
-  alignas(16) float beta[CH];    //                                      (staging wave 1, a step early)
-  alignas(16) float Gam[CH];     // exp(gam)                             (staging wave 1, a step early)
-  alignas(16) float tail[CH];    // exp(gam_last - gam)                  (staging wave 1, a step early)
-  alignas(16) float ik[CH];      // 1/|k_r| (0 past the end)             (staging wave 0, a step early)
-  alignas(16) float iq[CH];      // scale/|q_r| (0 past the end)         (P1)
-  alignas(16) float Gc;          // exp(gam_last)                        (staging wave 1, a step early)
-  int cl;                        // valid rows of the chunk              (staging wave 1, a step early)
+  Prep pp;                       // the chunk's record (+ decays: fused kernel only)
+  alignas(16) uint32_t ab[2 * CH]; // raw a_r (low half of word r), b_r (word 32 + r) (fused kernel)
 };
 
 struct Smem {
@@ -209,7 +267,35 @@ struct Smem {
   // row m of A21 (columns in the order 4j + g), 80-byte rows so that 16 rows
   // read at one column fill distinct 16-byte bank slots
   alignas(16) float p0x[3][16][20];
+  // cooperative kernel: flag words of chunks c, fetched ahead into word block c % 4
+  alignas(16) uint32_t fl[4][64];
 };
+
+// A producer workgroup's LDS (cooperative kernel): its chunk's rows (two
+// buffers: the next chunk lands while this one is worked on), the raw gates
+// of the group's value heads, their records and the T waves' exchange rows.
+struct ProdSmem {
+  alignas(16) bf16 K[2][CH * DK];
+  alignas(16) bf16 Q[2][CH * DK];
+  alignas(16) bf16 Kp[2][CH * DK];  // k rows of the chunk before (for the cross Gram)
+  alignas(16) uint32_t ab[2][MAX_GV][2 * CH];
+  alignas(16) float ikn[CH];   // 1/|k_r| of the chunk
+  alignas(16) float iqn[CH];   // scale/|q_r|
+  Prep pp[MAX_GV];
+  alignas(16) float xs[MAX_GV][3][16][20];
+  alignas(16) uint32_t prg[MAX_GV][64];  // progress words, fetched by T wave j
+};
+
+// Workspace of the cooperative kernel: one 128-byte line per XCD (arrival
+// and completion counters, error word), then one block per (sequence, key
+// head) group, used only by workgroups on that group's XCD: flags[gv][RING]
+// (chunk + 1 of the record in each slot), progress[gv * nvb] (chunks each
+// chain workgroup has copied), then the records [gv][RING].
+struct XcdLine {
+  uint32_t arrive, done, err, pad[29];
+};
+constexpr size_t WS_HEAD = sizeof(XcdLine) * MAX_XCD;
+constexpr size_t GRP_FLAGS = 0, GRP_PROGRESS = 256, GRP_RECS = 512;
 
 struct MfmaParams {
   const bf16 *q, *k, *v, *a, *b;
@@ -222,8 +308,11 @@ struct MfmaParams {
   int num_seqs;
   int H_k, H_v;
   float scale, eps;
+  // cooperative kernel
+  unsigned char *ws;
+  size_t grp_stride;
+  int nxcd, slots, gs, groups;
 };
-
 // State rows held in registers.  Accumulator tile t (t = 0..7) of a
 // consumer holds, in lane (m, g) register j, the state row
 //   d(t, g, j) = 32 (t / 2) + 8 g + 4 ((t ^ g) % 2) + j
@@ -236,16 +325,24 @@ struct MfmaParams {
 __device__ __forceinline__ int state_row(int t, int g, int j) {
   return 32 * (t >> 1) + 8 * g + 4 * ((t ^ g) & 1) + j;
 }
-// Rows 32kb + 8g .. + 7 of the state in natural order, from the tile pair
-// (2kb, 2kb + 1) of lane group g.
-__device__ __forceinline__ bf16x8 state_operand(const f32x4 &t0, const f32x4 &t1, int g) {
-  const bf16x4 a = pack4(t0), b = pack4(t1);
-  return (g & 1) ? cat8(b, a) : cat8(a, b);
+// Rows 32kb + 8g .. + 7 of the state from the tile pair (2kb, 2kb + 1) of
+// lane group g, in "tile order": natural for even g, the two halves of four
+// exchanged for odd g (tile 2kb holds the upper four there).  No lane choice
+// is made here, on the chain of chunks; the d_k operands that meet the state
+// in a product take the same order instead (row_op_t).
+__device__ __forceinline__ bf16x8 state_operand(const f32x4 &t0, const f32x4 &t1) {
+  return cat8(pack4(t0), pack4(t1));
 }
 
 // Operand of row r, 32-block kb of d_k: columns 32kb + 8g .. 32kb + 8g + 7.
 __device__ __forceinline__ bf16x8 row_op(const bf16 *X, int r, int kb, int g) {
   return *reinterpret_cast<const bf16x8 *>(X + kq_off(r, 32 * kb + 8 * g));
+}
+// The same columns in tile order (see state_operand): the operand of a
+// product with the state.
+__device__ __forceinline__ bf16x8 row_op_t(const bf16 *X, int r, int kb, int g) {
+  const bf16x8 x = row_op(X, r, kb, g);
+  return (g & 1) ? __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3) : x;
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
@@ -264,6 +361,11 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16 *addr) {
 __device__ __forceinline__ void dma16(const bf16 *src, bf16 *lds) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
                                    (__attribute__((address_space(3))) void *)(lds), 16, 0, 0);
+}
+// The same, read past the L1 (sc0): for memory another workgroup of the XCD
+// wrote during this launch (the cooperative kernel's records).
+__device__ __forceinline__ void dma16_l2(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lds), 16, 0, 1);
 }
 
 // Map the launch index to a work unit so that the gs units of one (sequence,
@@ -404,15 +506,18 @@ __device__ __forceinline__ float sumsq_words(const uint32_t *w, int n, float s) 
   return s;
 }
 
-// 1/|k_r| of one chunk (staging wave 0, once its k rows have landed): lane l
-// sums the squares of half a row (row l / 2) -- the swizzle keeps the 8 pieces
-// of a 128-byte half together -- and its neighbour the other half.  Starting
-// each lane at piece r % 8 spreads the lanes of every read over all banks.
-__device__ __forceinline__ void stage_k_norms(Stage &S, int lane, int cl, float eps) {
+
+// scale/|x_r| of the 32 rows of a swizzled k or q tile (one wave, once the
+// rows have landed), into out[r] (0 for rows r >= cl): lane l sums the squares
+// of half a row (row l / 2) -- the swizzle keeps the 8 pieces of a 128-byte
+// half together -- and its neighbour the other half.  Starting each lane at
+// piece r % 8 spreads the lanes of every read over all banks.
+__device__ __forceinline__ void tile_norms(const bf16 *X, float *out, int lane, int cl, float eps,
+                                           float scale) {
   const int r = lane >> 1, half = lane & 1;
   const int pos = half ^ (swz(r & 15) >> 3);  // where the 8 pieces of this half are stored
   u32x4 x[8];
-  lds_read_128B_now(S.K + r * DK + 64 * pos, r & 7, x);
+  lds_read_128B_now(X + r * DK + 64 * pos, r & 7, x);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};  // independent chains
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -421,26 +526,26 @@ __device__ __forceinline__ void stage_k_norms(Stage &S, int lane, int cl, float 
   }
   float ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   ss += dpp<0xB1>(ss);  // quad_perm [1,0,3,2]: add the other half of the row
-  if (half == 0) S.ik[r] = r < cl ? rsqrtf(ss + eps) : 0.f;
+  if (half == 0) out[r] = r < cl ? scale * rsqrtf(ss + eps) : 0.f;
 }
 
-// Gates of one chunk (staging wave 1, once its raw a and b have landed):
-// row r = lane % 32.
+// Gates of one chunk (one wave, once its raw a and b have landed in `ab`):
+// row r = lane % 32.  Writes the decays of `S` and its record's bt, Gm, Gc, cl.
 // SSD (the Mamba-2 SSD recurrence on the same scan): a is delta, neg_exp_A is
 // A itself, g = A delta and beta = delta.
 template <bool SSD>
-__device__ __forceinline__ void stage_gates(Stage &S, int lane, int cl, float neg_exp_A,
-                                            float dtb) {
+__device__ __forceinline__ void stage_gates(Prep &S, const uint32_t *ab, int lane, int cl,
+                                            float neg_exp_A, float dtb) {
   const int r = lane & 31;
   const bool valid = r < cl;
   float g, bt;
   if constexpr (SSD) {
-    const float dl = __uint_as_float(lds_read_u32_now(&S.ab[r]) << 16);
+    const float dl = __uint_as_float(lds_read_u32_now(&ab[r]) << 16);
     g = valid ? neg_exp_A * dl : 0.f;
     bt = valid ? dl : 0.f;
   } else {
-    const float a_r = __uint_as_float(lds_read_u32_now(&S.ab[r]) << 16) + dtb;
-    const float b_r = __uint_as_float(lds_read_u32_now(&S.ab[CH + r]) << 16);
+    const float a_r = __uint_as_float(lds_read_u32_now(&ab[r]) << 16) + dtb;
+    const float b_r = __uint_as_float(lds_read_u32_now(&ab[CH + r]) << 16);
     const float sp = fmaxf(a_r, 0.f) + fast_log(1.f + fast_exp(-fabsf(a_r)));
     g = valid ? neg_exp_A * sp : 0.f;
     bt = valid ? __builtin_amdgcn_rcpf(1.f + fast_exp(-b_r)) : 0.f;
@@ -449,16 +554,15 @@ __device__ __forceinline__ void stage_gates(Stage &S, int lane, int cl, float ne
   const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 31));
   if (lane < 32) {
     S.gam[r] = cum;
-    S.beta[r] = bt;
-    S.Gam[r] = fast_exp(cum);
+    S.r.bt[r] = bt;
+    S.r.Gm[r] = fast_exp(cum);
     S.tail[r] = fast_exp(last - cum);
   }
   if (lane == 0) {
-    S.Gc = fast_exp(last);
-    S.cl = cl;
+    S.r.Gc = fast_exp(last);
+    S.r.cl = cl;
   }
 }
-
 // The two substitution sweeps of P0, interleaved, 15 steps:
 //  * backward, X = T11^T, lane (r, g) holding X[r][4j + g] in x[j]: in step s
 //    row i = 15 - s is final and every row r adds cB[i] X[i] (cB[i] holds
@@ -531,34 +635,42 @@ struct RowOps {
   bf16x8 k0[4], k1[4], q0[4], q1[4];
 };
 template <bool WITH_Q>
-__device__ __forceinline__ void read_row_ops(const Stage &S, RowOps &o, int m, int g) {
+__device__ __forceinline__ void read_row_ops(const bf16 *K, const bf16 *Q, RowOps &o, int m, int g) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    o.k0[kb] = row_op(S.K, m, kb, g);
-    o.k1[kb] = row_op(S.K, 16 + m, kb, g);
+    o.k0[kb] = row_op(K, m, kb, g);
+    o.k1[kb] = row_op(K, 16 + m, kb, g);
     if (WITH_Q) {
-      o.q0[kb] = row_op(S.Q, m, kb, g);
-      o.q1[kb] = row_op(S.Q, 16 + m, kb, g);
+      o.q0[kb] = row_op(Q, m, kb, g);
+      o.q1[kb] = row_op(Q, 16 + m, kb, g);
     }
   }
 }
 
-// P0: the Gram blocks of k and T = (I + A)^-1 of one chunk, in fp32, written
-// as bf16 A operands for the state waves (1/|k| from staging).  Lane (m, g)
-// holds the Gram entries (k_i . k_m), i = 4g + j, of each block, which give
-// column m of A11, row m of A22 (the Gram matrix is symmetric) and row m of
-// A21; a round trip through P0's own LDS rows hands every lane the whole
-// column (row) its sweep needs.  Every decay factor is exp(gam_r - gam_i)
-// with i <= r, at most 1.
-__device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S,
-                                           float (&xs)[3][16][20], const RowOps &o, int lane) {
+// T = (I + A)^-1 of one chunk (P0 of the fused kernel, a T wave of a
+// producer): the Gram blocks of k and the whole inverse in fp32, written as
+// bf16 A operands, and the record's row factors bgk and tk.  Needs the
+// chunk's decays, beta and 1/|k|.  Lane (m, g) holds the Gram entries
+// (k_i . k_m), i = 4g + j, of each block, which give column m of A11, row m
+// of A22 (the Gram matrix is symmetric) and row m of A21; a round trip
+// through the wave's own LDS rows `xs` hands every lane the whole column
+// (row) its sweep needs.  Every decay factor is exp(gam_r - gam_i) with
+// i <= r, at most 1.
+__device__ __forceinline__ void prepare_T(Prep &S, float (&xs)[3][16][20], const RowOps &o,
+                                          int lane) {
+  Rec &R = S.r;
   const int m = lane & 15, g = lane >> 4;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
-  const f32x4 bt_lo = ld4(&S.beta[4 * g]);
-  const f32x4 ik_lo = ld4(&S.ik[4 * g]), ik_hi = ld4(&S.ik[16 + 4 * g]);
+  const f32x4 bt_lo = ld4(&R.bt[4 * g]);
+  const f32x4 ik_lo = ld4(&R.ik[4 * g]), ik_hi = ld4(&R.ik[16 + 4 * g]);
   const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
-  const float ik_m0 = S.ik[m], bik_m1 = S.beta[16 + m] * S.ik[16 + m];
+  const float ik_m0 = R.ik[m], bik_m1 = R.bt[16 + m] * R.ik[16 + m];
+  if (lane < CH) {
+    const float ik = R.ik[lane];
+    R.bgk[lane] = R.bt[lane] * R.Gm[lane] * ik;
+    R.tk[lane] = S.tail[lane] * ik;
+  }
   f32x4 t00 = z, t11 = z, t01 = z;  // (k_i . k_m) of blocks 00, 11; (k_i . k_{16+m}) of 10
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -611,8 +723,8 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S,
   for (int kk = 0; kk < 4; ++kk) t21 = mma_f32(y[kk], mm[kk], t21);
   // bf16 operands: T22 row m stays in this lane; T11 and T21 columns scatter
   // to the lanes that own their rows
-  bf16 *T0 = reinterpret_cast<bf16 *>(S.T0);
-  bf16 *T1 = reinterpret_cast<bf16 *>(S.T1);
+  bf16 *T0 = reinterpret_cast<bf16 *>(R.T0);
+  bf16 *T1 = reinterpret_cast<bf16 *>(R.T1);
   *reinterpret_cast<bf16x4 *>(T1 + 8 * lane + 4) = pack4(f32x4{y[0], y[1], y[2], y[3]});
   const int dst = 16 * (m >> 2), e = m & 3;
 #pragma unroll
@@ -622,31 +734,39 @@ __device__ __forceinline__ void prepare_p0(const MfmaParams &p, Stage &S,
   }
 }
 
-// P1: scale/|q_r| from the Gram diagonal of q, and the output mask without the
-// row norms, P[r][i] = exp(gam_r - gam_i) (q_r . k_i) for i <= r, of one chunk
-// (scale/|q_r| and 1/|k_i| are applied by the output waves).
-__device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const RowOps &o,
-                                           int lane) {
+// The output mask without the row norms, P[r][i] = exp(gam_r - gam_i)
+// (q_r . k_i) for i <= r, of one chunk (scale/|q_r| and 1/|k_i| are applied
+// by the output waves), into the record.  IQ_GRAM (P1 of the fused kernel):
+// also scale/|q_r| from the Gram diagonal of q, into the record; otherwise
+// (a P wave of a producer) the norms are already there.
+template <bool IQ_GRAM>
+__device__ __forceinline__ void prepare_P(Prep &S, const RowOps &o, int lane, float eps,
+                                          float scale) {
   const int m = lane & 15, g = lane >> 4;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
   const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
   f32x4 p00 = z, p10 = z, p11 = z;  // (K Q^T) blocks: (q_r . k_i), r = 16 rb + m, i = 16 ib + 4g + j
-  f32x4 qq0 = z, qq1 = z;           // Gram diagonal blocks of q
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     p00 = mma32(o.k0[kb], o.q0[kb], p00);
     p10 = mma32(o.k0[kb], o.q1[kb], p10);
     p11 = mma32(o.k1[kb], o.q1[kb], p11);
-    qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
-    qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
   }
-  // scale/|q_r| from the diagonal: lane (m, g = m/4) holds |q_m|^2 in register m%4
-  if (g == (m >> 2)) {
-    const int cl = S.cl;
-    const int j = m & 3;
-    S.iq[m] = (m < cl) ? rsqrtf(qq0[j] + p.eps) * p.scale : 0.f;
-    S.iq[16 + m] = (16 + m < cl) ? rsqrtf(qq1[j] + p.eps) * p.scale : 0.f;
+  if constexpr (IQ_GRAM) {
+    f32x4 qq0 = z, qq1 = z;  // Gram diagonal blocks of q
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      qq0 = mma32(o.q0[kb], o.q0[kb], qq0);
+      qq1 = mma32(o.q1[kb], o.q1[kb], qq1);
+    }
+    // lane (m, g = m/4) holds |q_m|^2 in register m%4
+    if (g == (m >> 2)) {
+      const int cl = S.r.cl;
+      const int j = m & 3;
+      S.r.iq[m] = (m < cl) ? rsqrtf(qq0[j] + eps) * scale : 0.f;
+      S.r.iq[16 + m] = (16 + m < cl) ? rsqrtf(qq1[j] + eps) * scale : 0.f;
+    }
   }
   f32x4 v00, v10, v11;
 #pragma unroll
@@ -657,17 +777,17 @@ __device__ __forceinline__ void prepare_p1(const MfmaParams &p, Stage &S, const 
     v11[j] = (i <= m) ? fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * p11[j] : 0.f;
   }
   // row r of P at slots 8g..8g+3 (columns 4g..4g+3) and 8g+4.. (columns 16+4g..)
-  S.P[0][lane] = pack8(v00, z);
-  S.P[1][lane] = pack8(v10, v11);
+  S.r.P[0][lane] = pack8(v00, z);
+  S.r.P[1][lane] = pack8(v10, v11);
 }
 
 // SSD mode: the output mask of one chunk split over both prepare waves (P0
 // has no erase work to do there): PART 0 takes rows 0..15 (one diagonal
-// block), PART 1 rows 16..31 (the block below it and the second diagonal
-// block), each writing its own P slot.  Otherwise as prepare_p1 with q
-// unnormalised.
+// block) and the update factors, PART 1 rows 16..31 (the block below it and
+// the second diagonal block), each writing its own P slot.  Otherwise as
+// prepare_P with q unnormalised.
 template <int PART>
-__device__ __forceinline__ void prepare_p_ssd(Stage &S, const RowOps &o, int lane) {
+__device__ __forceinline__ void prepare_p_ssd(Prep &S, const RowOps &o, int lane) {
   const int m = lane & 15, g = lane >> 4;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
@@ -682,11 +802,16 @@ __device__ __forceinline__ void prepare_p_ssd(Stage &S, const RowOps &o, int lan
       const int i = 4 * g + j;
       v00[j] = (i <= m) ? fast_exp(fminf(gm_m0 - gm_lo[j], 0.f)) * p00[j] : 0.f;
     }
-    S.P[0][lane] = pack8(v00, z);
+    S.r.P[0][lane] = pack8(v00, z);
+    if (lane < CH) {
+      const float ik = S.r.ik[lane];
+      S.r.bgk[lane] = S.r.bt[lane] * S.r.Gm[lane] * ik;
+      S.r.tk[lane] = S.tail[lane] * ik;
+    }
     if (g == 0) {
-      const int cl = S.cl;
-      S.iq[m] = (m < cl) ? 1.0f : 0.f;
-      S.iq[16 + m] = (16 + m < cl) ? 1.0f : 0.f;
+      const int cl = S.r.cl;
+      S.r.iq[m] = (m < cl) ? 1.0f : 0.f;
+      S.r.iq[16 + m] = (16 + m < cl) ? 1.0f : 0.f;
     }
   } else {
     f32x4 p10 = z, p11 = z;
@@ -702,13 +827,268 @@ __device__ __forceinline__ void prepare_p_ssd(Stage &S, const RowOps &o, int lan
       v10[j] = fast_exp(fminf(gm_m1 - gm_lo[j], 0.f)) * p10[j];
       v11[j] = (i <= m) ? fast_exp(fminf(gm_m1 - gm_hi[j], 0.f)) * p11[j] : 0.f;
     }
-    S.P[1][lane] = pack8(v10, v11);
+    S.r.P[1][lane] = pack8(v10, v11);
+  }
+}
+
+// ------------------------------------------------------------------ waves
+// State wave cw (16 columns): chunk c in step c + LAG: K S, R, Delta = T R,
+// S <- Gam_last S + K^T D Delta; it hands the state at chunk entry (before
+// step c + LAG) and the scaled Delta (during step c + LAG) to its output
+// wave.  Passes nsteps + 1 barriers.
+//
+// LOOK (cooperative kernel, LAG = 2): K S of the next chunk is formed one
+// step early from the update it depends on,
+//   K_{c+1} S_{c+1} = Gam_last(c) (K_{c+1} S_c) + (K_{c+1} K_c^T) (D_c Delta_c),
+// with K_{c+1} S_c taken from the state at chunk c's entry, which is known
+// when step c starts, and the cross Gram from chunk c+1's record.  The
+// dependent chain of a step is then the two products of the cross Gram, R,
+// the two of T R and D Delta; the K S and update products of a step
+// depend only on the previous step.
+template <int DV, bool SSD, int LAG, bool LOOK = false>
+__device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw, int lane,
+                                           int nch, int nsteps, size_t state_off, int col0,
+                                           uint32_t *progress = nullptr) {
+  static_assert(!LOOK || (LAG == 2 && !SSD), "look-ahead needs the rows of chunk c+1 in step c+1");
+  const int m = lane & 15, g = lane >> 4;
+  const int col = col0 + 16 * cw + m;
+  f32x4 S[8];  // S[state_row(t, g, j)][col]
+  if (p.s0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[t][j] = p.s0[state_off + (size_t)state_row(t, g, j) * DV + col];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 Sb[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1]);
+  // LDS operands: the k^T tiles of this chunk (A operands of the state
+  // update) are read once the first products are issued; the k rows (A
+  // operands of K S: of chunk c + 1 with LOOK, else of chunk c) and v of the
+  // next step are read after the state update, so that they are in
+  // registers when the next step starts.
+  bf16x8 Kr[2][4], Kt[8], vv;
+  const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 pn[2] = {z, z};               // LOOK: K_{c+1} S_c
+  bf16x8 dpp = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};  // LOOK: D_c Delta_c
+  float gcp = 1.0f;                   // LOOK: Gam_last of chunk c
+  auto read_rows = [&](const Stage &sn) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) Kr[mt][kb] = row_op_t(sn.K, 16 * mt + m, kb, g);
+  };
+  auto read_kt = [&](const Stage &sn) {
+    // A operand of tile t: row m is state row state_row(t, m / 4, m % 4),
+    // contraction over chunk positions in slot order, i.e. lane (m, g) gets
+    // k[4g + j][state_row(t, m / 4, m % 4)] and k[16 + 4g + j][...], j = 0..3
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = 4 * g + (m >> 2), d = state_row(t, m & 3, 0);
+      Kt[t] = cat8(tr_read(sn.K + kq_off(r, d)), tr_read(sn.K + kq_off(16 + r, d)));
+    }
+  };
+  auto read_v = [&](const Stage &sn) {
+    // v[4g + j][col] and v[16 + 4g + j][col]
+    const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
+    vv = cat8(tr_read(sn.V + v_off(vr, vc)), tr_read(sn.V + v_off(16 + vr, vc)));
+  };
+  auto hand_state = [&](int c) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sm.sb[c & 1][cw][kb][lane] = Sb[kb];
+  };
+  // K S products of the rows in Kr with the state operand Sb
+  auto k_times_s = [&](f32x4 (&acc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) acc[mt] = mma32(Kr[mt][kb], Sb[kb], acc[mt]);
+    }
+  };
+  block_sync();
+  for (int it = 0; it < nsteps; ++it) {
+    const int c = it - LAG;
+    // cooperative kernel: chunks up to `it` have landed in LDS (records
+    // included), so their slots may be refilled
+    if (progress && cw == 0 && lane == 0) *progress = (uint32_t)(min(it, nch - 1) + 1);
+    if constexpr (LOOK) {
+      if (c == -1 && nch > 0) {
+        // K_0 S_0 for the first chunk
+        k_times_s(pn);
+      }
+    }
+    if (c >= 0 && c < nch) {
+      const Stage &st = sm.st[c % NSTAGE];
+      const Rec &rc = st.pp.r;
+      const bool more = c + 1 < nch;
+      // this chunk's tiles and row factors
+      const bf16x4 tt0 = rc.T0[lane];
+      const bf16x8 tt1 = rc.T1[lane];
+      const f32x4 bt0 = ld4(&rc.bt[4 * g]), bt1 = ld4(&rc.bt[16 + 4 * g]);
+      const f32x4 bk0 = ld4(&rc.bgk[4 * g]), bk1 = ld4(&rc.bgk[16 + 4 * g]);
+      const f32x4 ik0 = ld4(&rc.ik[4 * g]), ik1 = ld4(&rc.ik[16 + 4 * g]);
+      const f32x4 tk0 = ld4(&rc.tk[4 * g]), tk1 = ld4(&rc.tk[16 + 4 * g]);
+      const float gc = rc.Gc;
+      // ks[mt]: (K S)[16mt + 4g + j][m]
+      f32x4 ks[2] = {z, z};
+      if constexpr (LOOK) {
+        ks[0] = pn[0] * gcp;
+        ks[1] = pn[1] * gcp;
+        if (c > 0) {
+          ks[0] = mma32(rc.GX[0][lane], dpp, ks[0]);
+          ks[1] = mma32(rc.GX[1][lane], dpp, ks[1]);
+        }
+        // K_{c+1} S_c for the next step (Kr holds chunk c + 1's rows)
+        pn[0] = z;
+        pn[1] = z;
+        if (more) k_times_s(pn);
+      } else if constexpr (!SSD) {
+        k_times_s(ks);
+      }
+      // Gam_last S while the matrix cores run K S
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[t] *= gc;
+      __builtin_amdgcn_sched_barrier(0);
+      read_kt(st);
+      __builtin_amdgcn_sched_barrier(0);
+      // R = beta V - beta Gam ik (K S), rows 4g..4g+3 and 16+4g..16+4g+3
+      f32x4 R0, R1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        R0[j] = bt0[j] * (float)vv[j] - bk0[j] * ks[0][j];
+        R1[j] = bt1[j] * (float)vv[4 + j] - bk1[j] * ks[1][j];
+      }
+      // Delta = T R, both 16-row blocks from the one bf16 operand of R in
+      // slot order; SSD: no erase, Delta = R
+      f32x4 d1 = R0, d2 = R1;
+      if constexpr (!SSD) {
+        const bf16x8 Rb = pack8(R0, R1);
+        d1 = mma32(cat8(tt0, bf16x4{0, 0, 0, 0}), Rb, z);
+        d2 = mma32(tt1, Rb, z);
+      }
+      // S <- Gam_last S + K^T diag(tail ik) Delta
+      const bf16x8 Dp = pack8(tk0 * d1, tk1 * d2);
+      if constexpr (LOOK) {
+        dpp = Dp;
+        gcp = gc;
+      }
+      // diag(ik) Delta for the outputs of this chunk
+      sm.db[c & 1][cw][lane] = pack8(ik0 * d1, ik1 * d2);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[t] = mma32(Kt[t], Dp, S[t]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1]);
+      if (more) hand_state(c + 1);
+    } else if (c == -1 && nch > 0) {
+      hand_state(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the handed-over writes are done
+    {
+      // operands of the next step, read unconditionally (the chunk index
+      // clamped into the sequence) so that the loads write the loop's
+      // registers directly and stay in flight across the barrier: k rows of
+      // chunk c + 2 (LOOK) or c + 1, v of chunk c + 1
+      const Stage &sr = sm.st[max(min(c + 1, nch - 1), 0) % NSTAGE];
+      if constexpr (LOOK) {
+        read_rows(sm.st[max(min(c + 2, nch - 1), 0) % NSTAGE]);
+      } else if constexpr (!SSD) {
+        read_rows(sr);
+      }
+      read_v(sr);
+    }
+    // no wait for the reads in flight: their buffers are refilled only
+    // steps later, and their registers are waited for where they are used
+    block_sync<63, false>();
+  }
+  if (p.sT) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p.sT[state_off + (size_t)state_row(t, g, j) * DV + col] = S[t][j];
+  }
+}
+
+// Output wave cw: in step it, O of chunk it - LAG - 1 =
+// (diag(ik) Delta)^T P^T + (Gam iq Q S)^T, then (Q S)^T of chunk it - LAG
+// from the state handed over at its entry.  Passes nsteps + 1 barriers.
+template <int DV, int LAG>
+__device__ __forceinline__ void output_wave(const MfmaParams &p, Smem &sm, int cw, int lane,
+                                            int nch, int nsteps, int64_t t0, int64_t t1, int h,
+                                            int col0) {
+  const int m = lane & 15, g = lane >> 4;
+  f32x4 qsT[2];
+  block_sync();
+  for (int it = 0; it < nsteps; ++it) {
+    const int co = it - LAG - 1;
+    if (co >= 0 && co < nch) {
+      const Rec &rc = sm.st[co % NSTAGE].pp.r;
+      const bf16x8 Db = sm.db[co & 1][cw][lane];
+      const bf16x8 pr0 = rc.P[0][lane];
+      const bf16x8 pr1 = rc.P[1][lane];
+      const float gm0 = rc.Gm[m], gm1 = rc.Gm[16 + m];
+      const float iq0 = rc.iq[m], iq1 = rc.iq[16 + m];
+      // lane (m, g) gets O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P diag(ik) Delta)
+      const f32x4 oc0 = mma32(Db, pr0, qsT[0] * gm0) * iq0;
+      const f32x4 oc1 = mma32(Db, pr1, qsT[1] * gm1) * iq1;
+      const int64_t row = t0 + (int64_t)co * CH + m;
+      bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g;
+      if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
+      if (row + 16 < t1) *reinterpret_cast<bf16x4 *>(orow + (int64_t)16 * p.H_v * DV) = pack4(oc1);
+    }
+    const int c = it - LAG;
+    if (c >= 0 && c < nch) {
+      const Stage &st = sm.st[c % NSTAGE];
+      const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 Sb[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Sb[kb] = sm.sb[c & 1][cw][kb][lane];
+      // qsT[mt]: (Q S)[16mt + m][4g + j]
+      qsT[0] = z;
+      qsT[1] = z;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          qsT[mt] = mma32(Sb[kb], row_op_t(st.Q, 16 * mt + m, kb, g), qsT[mt]);
+      }
+    }
+    block_sync<63, false>();
+  }
+}
+
+// Chunk c of a sequence [t0, t1) (clamped to the last one: requests past the
+// end re-read it into a buffer no one reads again) -> first row and valid rows.
+__device__ __forceinline__ void rows_of(int c, int nch, int64_t t0, int64_t t1, int64_t &row0,
+                                        int &cl) {
+  c = min(c, nch - 1);
+  row0 = t0 + (int64_t)c * CH;
+  const int64_t rem = t1 - row0;
+  cl = rem < CH ? (int)rem : CH;
+}
+
+// Request the k (or q) rows of chunk c and one half of its v tile (this
+// workgroup's columns): 8 + 1 loads.
+template <int DV>
+__device__ __forceinline__ void request_rows(const bf16 *x, const bf16 *v, int H_k, int H_v,
+                                             int hk, int h, int col0, int64_t row0, int cl,
+                                             const RowOffsets &ko, uint32_t voff, bf16 *tile,
+                                             bf16 *vtile, int half, int lane) {
+  if (cl == CH) {
+    dma_rows_full(x + (row0 * H_k + hk) * DK, ko, tile);
+    dma16(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(v + (row0 * H_v + h) * DV) + voff),
+          vtile + 512 * half);
+  } else {
+    dma_rows(x, H_k, hk, row0, cl, tile, lane);
+    dma_v_half(v, H_v, h, col0, row0, cl, vtile, half, lane, DV);
   }
 }
 
 // DVT: d_v (64 or 128; d_k is 128).  SSD: the Mamba-2 SSD recurrence on the
 // same scan -- no norms, no erase (T = I, Delta = diag(beta) V with no K S),
-// g = A delta, beta = delta; the prepare wave P0 is idle.
+// g = A delta, beta = delta; the prepare wave P0 only forms half of P.
 template <int DVT, bool SSD>
 __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p) {
   constexpr int DV = DVT;
@@ -739,172 +1119,9 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
   const int nsteps = nch + 3;
 
   if (wave >= W_C0 && wave < W_C0 + NC) {
-    // ------------------------------------------------------------ state waves
-    // chunk c in step c + 2: K S, R, Delta = T R, S <- Gam_last S + K^T D Delta;
-    // they hand the state at chunk entry (before step c + 2) and the scaled
-    // Delta (during step c + 2) to the output waves.
-    const int cw = wave - W_C0;
-    const int col = col0 + 16 * cw + m;
-    f32x4 S[8];  // S[state_row(t, g, j)][col]
-    if (p.s0) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[t][j] = p.s0[state_off + (size_t)state_row(t, g, j) * DV + col];
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    bf16x8 Sb[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1], g);
-    // LDS operands: the k^T tiles of this chunk (A operands of the state
-    // update) are read once the K S products are issued; the k rows (A
-    // operands of K S) and v of the next chunk are read after the state
-    // update, so that they are in registers when the next step starts.  The
-    // rows of chunk c+1 are in LDS from step c+1 on.
-    bf16x8 Kr[2][4], Kt[8], vv;
-    auto read_rows = [&](const Stage &sn) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) Kr[mt][kb] = row_op(sn.K, 16 * mt + m, kb, g);
-    };
-    auto read_kt = [&](const Stage &sn) {
-      // A operand of tile t: row m is state row state_row(t, m / 4, m % 4),
-      // contraction over chunk positions in slot order, i.e. lane (m, g) gets
-      // k[4g + j][state_row(t, m / 4, m % 4)] and k[16 + 4g + j][...], j = 0..3
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int r = 4 * g + (m >> 2), d = state_row(t, m & 3, 0);
-        Kt[t] = cat8(tr_read(sn.K + kq_off(r, d)), tr_read(sn.K + kq_off(16 + r, d)));
-      }
-    };
-    auto read_v = [&](const Stage &sn) {
-      // v[4g + j][col] and v[16 + 4g + j][col]
-      const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
-      vv = cat8(tr_read(sn.V + v_off(vr, vc)), tr_read(sn.V + v_off(16 + vr, vc)));
-    };
-    auto hand_state = [&](int c) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sm.sb[c & 1][cw][kb][lane] = Sb[kb];
-    };
-    block_sync();
-    for (int it = 0; it < nsteps; ++it) {
-      const int c = it - 2;
-      if (c >= 0 && c < nch) {
-        const Stage &st = sm.st[c % NSTAGE];
-        const bool more = c + 1 < nch;
-        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-        // this chunk's prepared tile and row factors
-        const bf16x4 tt0 = st.T0[lane];
-        const bf16x8 tt1 = st.T1[lane];
-        const f32x4 bt0 = ld4(&st.beta[4 * g]), bt1 = ld4(&st.beta[16 + 4 * g]);
-        const f32x4 gm0 = ld4(&st.Gam[4 * g]), gm1 = ld4(&st.Gam[16 + 4 * g]);
-        const f32x4 ik0 = ld4(&st.ik[4 * g]), ik1 = ld4(&st.ik[16 + 4 * g]);
-        const f32x4 tl0 = ld4(&st.tail[4 * g]), tl1 = ld4(&st.tail[16 + 4 * g]);
-        const float gc = st.Gc;
-        // ks[mt]: (K S)[16mt + 4g + j][m]
-        f32x4 ks[2] = {z, z};
-        if constexpr (!SSD) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) ks[mt] = mma32(Kr[mt][kb], Sb[kb], ks[mt]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        read_kt(st);
-        __builtin_amdgcn_sched_barrier(0);
-        // R = beta (V - Gam ik K S), rows 4g..4g+3 and 16+4g..16+4g+3
-        f32x4 R0, R1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          R0[j] = bt0[j] * ((float)vv[j] - gm0[j] * ik0[j] * ks[0][j]);
-          R1[j] = bt1[j] * ((float)vv[4 + j] - gm1[j] * ik1[j] * ks[1][j]);
-        }
-        // Delta = T R, both 16-row blocks from the one bf16 operand of R in
-        // slot order; SSD: no erase, Delta = R
-        f32x4 d1 = R0, d2 = R1;
-        if constexpr (!SSD) {
-          const bf16x8 Rb = pack8(R0, R1);
-          d1 = mma32(cat8(tt0, bf16x4{0, 0, 0, 0}), Rb, z);
-          d2 = mma32(tt1, Rb, z);
-        }
-        // diag(ik) Delta for the outputs of this chunk
-        sm.db[c & 1][cw][lane] = pack8(ik0 * d1, ik1 * d2);
-        // S <- Gam_last S + K^T diag(tail ik) Delta
-        const bf16x8 Dp = pack8(tl0 * ik0 * d1, tl1 * ik1 * d2);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = mma32(Kt[t], Dp, S[t] * gc);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1], g);
-        if (more) hand_state(c + 1);
-      } else if (c == -1 && nch > 0) {
-        hand_state(0);
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the handed-over writes are done
-      {
-        // operands of the next step's chunk c + 1, read unconditionally (the
-        // index clamped into the sequence) so that the loads write the loop's
-        // registers directly and stay in flight across the barrier
-        const Stage &sr = sm.st[max(min(c + 1, nch - 1), 0) % NSTAGE];
-        if constexpr (!SSD) read_rows(sr);
-        read_v(sr);
-      }
-      // no wait for the reads in flight: their buffers are refilled only
-      // steps later, and their registers are waited for where they are used
-      block_sync<63, false>();
-    }
-    if (p.sT) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p.sT[state_off + (size_t)state_row(t, g, j) * DV + col] = S[t][j];
-    }
+    state_wave<DV, SSD, 2>(p, sm, wave - W_C0, lane, nch, nsteps, state_off, col0);
   } else if (wave >= W_O0 && wave < W_O0 + NC) {
-    // ----------------------------------------------------------- output waves
-    // step it: O of chunk it - 3 = (diag(ik) Delta)^T P^T + (Gam iq Q S)^T,
-    // then (Q S)^T of chunk it - 2 from the state handed over at its entry.
-    const int cw = wave - W_O0;
-    f32x4 qsT[2];
-    block_sync();
-    for (int it = 0; it < nsteps; ++it) {
-      const int co = it - 3;
-      if (co >= 0 && co < nch) {
-        const Stage &st = sm.st[co % NSTAGE];
-        const bf16x8 Db = sm.db[co & 1][cw][lane];
-        const bf16x8 pr0 = st.P[0][lane];
-        const bf16x8 pr1 = st.P[1][lane];
-        const float gm0 = st.Gam[m], gm1 = st.Gam[16 + m];
-        const float iq0 = st.iq[m], iq1 = st.iq[16 + m];
-        // lane (m, g) gets O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P diag(ik) Delta)
-        const f32x4 oc0 = mma32(Db, pr0, qsT[0] * gm0) * iq0;
-        const f32x4 oc1 = mma32(Db, pr1, qsT[1] * gm1) * iq1;
-        const int64_t row = t0 + (int64_t)co * CH + m;
-        bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g;
-        if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
-        if (row + 16 < t1) *reinterpret_cast<bf16x4 *>(orow + (int64_t)16 * p.H_v * DV) = pack4(oc1);
-      }
-      const int c = it - 2;
-      if (c >= 0 && c < nch) {
-        const Stage &st = sm.st[c % NSTAGE];
-        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 Sb[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) Sb[kb] = sm.sb[c & 1][cw][kb][lane];
-        // qsT[mt]: (Q S)[16mt + m][4g + j]
-        qsT[0] = z;
-        qsT[1] = z;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            qsT[mt] = mma32(Sb[kb], row_op(st.Q, 16 * mt + m, kb, g), qsT[mt]);
-        }
-      }
-      block_sync<63, false>();
-    }
+    output_wave<DV, 2>(p, sm, wave - W_O0, lane, nch, nsteps, t0, t1, h, col0);
   } else if (wave == W_P0 || wave == W_P1) {
     // ---------------------------------------------------------------- prepare
     // Each step also reads the row operands of the next chunk (published
@@ -914,25 +1131,26 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     block_sync();
     for (int it = 0; it < nsteps; ++it) {
       const int c = it - 1;
-      // (SSD: no erase, so P0 has nothing to prepare and only keeps the barriers)
       if (c >= 0 && c < nch) {
+        Prep &pp = sm.st[c % NSTAGE].pp;
         if constexpr (SSD) {
           if (wave == W_P0)
-            prepare_p_ssd<0>(sm.st[c % NSTAGE], ops, lane);
+            prepare_p_ssd<0>(pp, ops, lane);
           else
-            prepare_p_ssd<1>(sm.st[c % NSTAGE], ops, lane);
+            prepare_p_ssd<1>(pp, ops, lane);
         } else if (wave == W_P0) {
-          prepare_p0(p, sm.st[c % NSTAGE], sm.p0x, ops, lane);
+          prepare_T(pp, sm.p0x, ops, lane);
         } else {
-          prepare_p1(p, sm.st[c % NSTAGE], ops, lane);
+          prepare_P<true>(pp, ops, lane, p.eps, p.scale);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS writes are done
       if (it < nch) {
+        const Stage &sn = sm.st[it % NSTAGE];
         if (wave == W_P0 && !SSD)
-          read_row_ops<false>(sm.st[it % NSTAGE], ops, m, g);
+          read_row_ops<false>(sn.K, sn.Q, ops, m, g);
         else
-          read_row_ops<true>(sm.st[it % NSTAGE], ops, m, g);
+          read_row_ops<true>(sn.K, sn.Q, ops, m, g);
       }
       block_sync<63, false>();
     }
@@ -951,14 +1169,6 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
     const int vhalf = wave - W_ST0;
     const uint32_t voff =
         (uint32_t)(((16 * vhalf + (lane >> 2)) * p.H_v * DV + col0 + 8 * v_src_piece(lane)) * (int)sizeof(bf16));
-    // chunk c (clamped to the last one: requests past the end re-read it into
-    // a buffer no one reads again) -> first row and valid rows
-    auto rows_of = [&](int c, int64_t &row0, int &cl) {
-      c = min(c, nch - 1);
-      row0 = t0 + (int64_t)c * CH;
-      const int64_t rem = t1 - row0;
-      cl = rem < CH ? (int)rem : CH;
-    };
     // Step it requests chunk it + AHEAD and waits for chunk it + 1 (read by
     // P1 in step it + 1); an extra first barrier publishes chunk 0.
     if (wave == W_ST0) {
@@ -966,24 +1176,19 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       auto request = [&](int c) {
         int64_t row0;
         int cl;
-        rows_of(c, row0, cl);
+        rows_of(c, nch, t0, t1, row0, cl);
         Stage &S = sm.st[c % NSTAGE];
-        if (cl == CH) {
-          dma_rows_full(p.k + (row0 * p.H_k + hk) * DK, ko, S.K);
-          dma16(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(p.v + (row0 * p.H_v + h) * DV) + voff), S.V);
-        } else {
-          dma_rows(p.k, p.H_k, hk, row0, cl, S.K, lane);
-          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 0, lane, DV);
-        }
+        request_rows<DV>(p.k, p.v, p.H_k, p.H_v, hk, h, col0, row0, cl, ko, voff, S.K, S.V, 0, lane);
       };
       // 1/|k| of chunk c once its rows have landed (c < nch)
       auto norms = [&](int c) {
         const int64_t rem = L - (int64_t)c * CH;
         const int cl = rem < CH ? (int)rem : CH;
+        Rec &rc = sm.st[c % NSTAGE].pp.r;
         if constexpr (SSD) {  // keys are not normalised
-          if (lane < CH) sm.st[c % NSTAGE].ik[lane] = lane < cl ? 1.0f : 0.0f;
+          if (lane < CH) rc.ik[lane] = lane < cl ? 1.0f : 0.0f;
         } else {
-          stage_k_norms(sm.st[c % NSTAGE], lane, cl, p.eps);
+          tile_norms(sm.st[c % NSTAGE].K, rc.ik, lane, cl, p.eps, 1.0f);
         }
       };
       for (int c = 0; c < AHEAD; ++c) request(c);
@@ -1001,15 +1206,9 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       auto request = [&](int c) {
         int64_t row0;
         int cl;
-        rows_of(c, row0, cl);
+        rows_of(c, nch, t0, t1, row0, cl);
         Stage &S = sm.st[c % NSTAGE];
-        if (cl == CH) {
-          dma_rows_full(p.q + (row0 * p.H_k + hk) * DK, ko, S.Q);
-          dma16(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(p.v + (row0 * p.H_v + h) * DV) + voff), S.V + 512);
-        } else {
-          dma_rows(p.q, p.H_k, hk, row0, cl, S.Q, lane);
-          dma_v_half(p.v, p.H_v, h, col0, row0, cl, S.V, 1, lane, DV);
-        }
+        request_rows<DV>(p.q, p.v, p.H_k, p.H_v, hk, h, col0, row0, cl, ko, voff, S.Q, S.V, 1, lane);
         dma_ab(p.a, SSD ? p.a : p.b, p.H_v, h, row0, cl, S.ab, lane);  // SSD: no b
       };
       const float neg_exp_A = SSD ? p.A_log[h] : -expf(p.A_log[h]);  // SSD: A itself
@@ -1017,7 +1216,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
       // gates of chunk c once its raw a, b have landed (c < nch)
       auto gates = [&](int c) {
         const int64_t rem = L - (int64_t)c * CH;
-        stage_gates<SSD>(sm.st[c % NSTAGE], lane, rem < CH ? (int)rem : CH, neg_exp_A, dtb);
+        Stage &S = sm.st[c % NSTAGE];
+        stage_gates<SSD>(S.pp, S.ab, lane, rem < CH ? (int)rem : CH, neg_exp_A, dtb);
       };
       for (int c = 0; c < AHEAD; ++c) request(c);
       vm_wait<ST1_OPS * (AHEAD - 1)>();  // chunk 0 has landed
@@ -1034,9 +1234,305 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
   }
 }
 
+// ---------------------------------------------------------- cooperative kernel
+// A 32-bit word read from the L2, past the scalar cache (glc), complete when
+// the statement ends.  `p` is uniform across the wave.
+__device__ __forceinline__ uint32_t load_l2_u32(const uint32_t *p) {
+  uint32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+// Wait until *p >= want; false, with the XCD's error word marked, if the
+// bounded number of polls runs out.  Once the error word is marked every
+// later wait on that XCD gives up at once, so a broken launch ends in about
+// one wait's bound instead of one per chunk.
+__device__ __forceinline__ bool wait_at_least(const uint32_t *p, uint32_t want, uint32_t *err) {
+  for (int i = 0; i < SPIN_LIMIT; ++i) {
+    if (load_l2_u32(p) >= want) return true;
+    if ((i & 63) == 63 && load_l2_u32(err) != 0u) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if ((threadIdx.x & 63) == 0) atomicOr(err, 1u);
+  return false;
+}
+
+__device__ __forceinline__ unsigned char *group_base(const MfmaParams &p, int grp) {
+  return p.ws + WS_HEAD + (size_t)grp * p.grp_stride;
+}
+
+// Producer workgroup phi of group (n, hk): the records of chunks
+// c = phi, phi + PRODUCERS, ... for the gv value heads hk gv .. hk gv + gv - 1.
+// Waves j < gv form T of value head j and store its record, waves 3 + j its
+// P; waves 3 and 4 take the norms of k and q, wave 5 the loads (one chunk
+// ahead).  Three workgroup barriers per chunk.  A record's flag is set one
+// chunk later, after its stores have long reached the L2, so no wave waits
+// on its own stores; before storing a record into the slot of chunk
+// c - RING, its T wave checks (from progress words it fetched at the start of
+// the chunk) that every chain workgroup of the group has copied that chunk.
+__device__ void producer(const MfmaParams &p, unsigned char *smem, int grp, int phi, int gv,
+                         int nvb, uint32_t *err) {
+  ProdSmem &ps = *reinterpret_cast<ProdSmem *>(smem);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int n = grp / p.H_k, hk = grp % p.H_k;
+  const int nc = gv * nvb;  // chain workgroups of the group
+  int64_t t0, t1;
+  seq_bounds(p.cu, p.seq_len, n, t0, t1);
+  const int nch = (int)((t1 - t0 + CH - 1) / CH);
+  unsigned char *base = group_base(p, grp);
+  uint32_t *flags = reinterpret_cast<uint32_t *>(base + GRP_FLAGS);
+  const uint32_t *progress = reinterpret_cast<const uint32_t *>(base + GRP_PROGRESS);
+  unsigned char *recs = base + GRP_RECS;
+  const RowOffsets ko = row_offsets(p.H_k, lane);
+  auto load = [&](int c, int buf) {  // wave 5: PROD_OPS loads
+    int64_t row0;
+    int cl;
+    rows_of(c, nch, t0, t1, row0, cl);
+    if (cl == CH) {
+      dma_rows_full(p.k + (row0 * p.H_k + hk) * DK, ko, ps.K[buf]);
+      dma_rows_full(p.q + (row0 * p.H_k + hk) * DK, ko, ps.Q[buf]);
+    } else {
+      dma_rows(p.k, p.H_k, hk, row0, cl, ps.K[buf], lane);
+      dma_rows(p.q, p.H_k, hk, row0, cl, ps.Q[buf], lane);
+    }
+    // the chunk before (always full); chunk 0 re-reads itself, its cross
+    // Gram is not used
+    dma_rows_full(p.k + ((row0 - (c > 0 ? CH : 0)) * p.H_k + hk) * DK, ko, ps.Kp[buf]);
+#pragma unroll
+    for (int j = 0; j < MAX_GV; ++j)
+      dma_ab(p.a, p.b, p.H_v, hk * gv + min(j, gv - 1), row0, cl, ps.ab[buf][j], lane);
+  };
+  if (wave == 5 && phi < nch) load(phi, 0);
+  int prev = -1;  // T waves: the chunk whose record stores are in flight
+  for (int c = phi, k = 0; c < nch; c += PRODUCERS, ++k) {
+    const int buf = k & 1;
+    const int64_t rem = t1 - (t0 + (int64_t)c * CH);
+    const int cl = rem < CH ? (int)rem : CH;
+    if (wave == 5) {
+      if (c + PRODUCERS < nch) {
+        load(c + PRODUCERS, buf ^ 1);
+        vm_wait<PROD_OPS>();  // chunk c has landed
+      } else {
+        vm_wait<0>();
+      }
+    }
+    __syncthreads();
+    if (wave < gv) {
+      const int h = hk * gv + wave;
+      stage_gates<false>(ps.pp[wave], ps.ab[buf][wave], lane, cl, -expf(p.A_log[h]), p.dt_bias[h]);
+    } else if (wave == 3) {
+      tile_norms(ps.K[buf], ps.ikn, lane, cl, p.eps, 1.0f);
+    } else if (wave == 4) {
+      tile_norms(ps.Q[buf], ps.iqn, lane, cl, p.eps, p.scale);
+    } else if (wave == 5) {
+      // GX = K_c K_{c-1}^T: lane (n, g) of output tile (rb, cb) gets
+      // (k_{c-1}[16 cb + 4g + j] . k_c[16 rb + n]) = GX[16 rb + n][16 cb + 4g + j],
+      // which is its own A operand piece: tile rb, slots 8g + 4 cb + j
+      const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 gx[2][2] = {{z, z}, {z, z}};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 a0 = row_op(ps.Kp[buf], m, kb, g), a1 = row_op(ps.Kp[buf], 16 + m, kb, g);
+        const bf16x8 b0 = row_op(ps.K[buf], m, kb, g), b1 = row_op(ps.K[buf], 16 + m, kb, g);
+        gx[0][0] = mma32(a0, b0, gx[0][0]);
+        gx[0][1] = mma32(a1, b0, gx[0][1]);
+        gx[1][0] = mma32(a0, b1, gx[1][0]);
+        gx[1][1] = mma32(a1, b1, gx[1][1]);
+      }
+      const bf16x8 t0p = pack8(gx[0][0], gx[0][1]), t1p = pack8(gx[1][0], gx[1][1]);
+      for (int j = 0; j < gv; ++j) {
+        ps.pp[j].r.GX[0][lane] = t0p;
+        ps.pp[j].r.GX[1][lane] = t1p;
+      }
+    }
+    __syncthreads();
+    RowOps ops;
+    if (wave < gv) {
+      Prep &pp = ps.pp[wave];
+      if (c >= RING)  // progress words, one per lane (past the L1)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void *>(&progress[min(lane, nc - 1)]),
+            (__attribute__((address_space(3))) void *)(&ps.prg[wave][0]), 4, 0, 1);
+      if (lane < CH) {
+        pp.r.ik[lane] = ps.ikn[lane];
+        pp.r.iq[lane] = ps.iqn[lane];
+      }
+      wave_lds_sync();
+      read_row_ops<false>(ps.K[buf], ps.Q[buf], ops, m, g);
+      prepare_T(pp, ps.xs[wave], ops, lane);
+    } else if (wave >= 3 && wave - 3 < gv) {
+      read_row_ops<true>(ps.K[buf], ps.Q[buf], ops, m, g);
+      prepare_P<false>(ps.pp[wave - 3], ops, lane, p.eps, p.scale);
+    }
+    __syncthreads();
+    if (wave < gv) {
+      vm_wait<0>();  // the previous record's stores and the progress words
+      if (prev >= 0 && lane == 0) flags[wave * RING + prev % RING] = (uint32_t)(prev + 1);
+      if (c >= RING) {
+        // the slot held chunk c - RING: every chain workgroup must have copied it
+        const uint32_t need = (uint32_t)(c - RING + 1);
+        const uint32_t seen = lds_read_u32_now(&ps.prg[wave][lane]);
+        if (__ballot(seen < need) != 0)
+          for (int r = 0; r < nc; ++r) wait_at_least(&progress[r], need, err);
+      }
+      // the record into its slot: 5 x 1 KB, 16 bytes per lane, not waited for
+      const uint4 *src = reinterpret_cast<const uint4 *>(&ps.pp[wave].r);
+      uint4 *dst = reinterpret_cast<uint4 *>(recs + ((size_t)wave * RING + c % RING) * REC_BYTES);
+#pragma unroll
+      for (int i = 0; i < REC_DMAS; ++i) dst[64 * i + lane] = src[64 * i + lane];
+      prev = c;
+    }
+  }
+  vm_wait<0>();
+  if (wave < gv && prev >= 0 && lane == 0) flags[wave * RING + prev % RING] = (uint32_t)(prev + 1);
+}
+
+// Staging wave of a chain workgroup (cooperative kernel): k rows, the first
+// half of v and the record (wave 0), or q rows and the second half of v
+// (wave 1).  Step it requests chunk it + AHEAD and waits for chunk it + 1; an
+// extra first barrier publishes chunk 0.  Wave 0 fetches the producer's flag
+// of chunk c two steps before it requests the chunk (into LDS, past the L1)
+// and only polls the flag itself if it was not yet set then.  Passes
+// nsteps + 1 barriers.
+template <int DV>
+__device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, int which, int lane,
+                                             int nch, int nsteps, int64_t t0, int64_t t1, int hk,
+                                             int h, int col0, const uint32_t *flag,
+                                             const unsigned char *recs, uint32_t *err) {
+  if (nch == 0) {  // nothing to load; keep the barrier count
+    for (int it = 0; it <= nsteps; ++it) block_sync();
+    return;
+  }
+  const RowOffsets ko = row_offsets(p.H_k, lane);
+  const uint32_t voff =
+      (uint32_t)(((16 * which + (lane >> 2)) * p.H_v * DV + col0 + 8 * v_src_piece(lane)) * (int)sizeof(bf16));
+  auto rows = [&](int c) {  // 9 loads
+    int64_t row0;
+    int cl;
+    rows_of(c, nch, t0, t1, row0, cl);
+    Stage &S = sm.st[c % NSTAGE];
+    if (which == 0)
+      request_rows<DV>(p.k, p.v, p.H_k, p.H_v, hk, h, col0, row0, cl, ko, voff, S.K, S.V, 0, lane);
+    else
+      request_rows<DV>(p.q, p.v, p.H_k, p.H_v, hk, h, col0, row0, cl, ko, voff, S.Q, S.V, 1, lane);
+  };
+  auto fetch_flag = [&](int c) {  // 1 load
+    const int cc = min(c, nch - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(&flag[cc % RING]),
+                                     (__attribute__((address_space(3))) void *)(&sm.fl[c & 3][0]),
+                                     4, 0, 1);
+  };
+  auto record = [&](int c, bool fetched) {  // REC_DMAS loads
+    const int cc = min(c, nch - 1);
+    if (!fetched || lds_read_u32_now(&sm.fl[c & 3][0]) < (uint32_t)(cc + 1))
+      wait_at_least(&flag[cc % RING], (uint32_t)(cc + 1), err);
+    const unsigned char *rec = recs + (size_t)(cc % RING) * REC_BYTES;
+    Stage &S = sm.st[c % NSTAGE];
+#pragma unroll
+    for (int i = 0; i < REC_DMAS; ++i)
+      dma16_l2(rec + 1024 * i + 16 * lane, reinterpret_cast<unsigned char *>(&S.pp.r) + 1024 * i);
+  };
+  if (which == 0) {
+    fetch_flag(2);
+    fetch_flag(3);
+    for (int c = 0; c < AHEAD; ++c) {
+      record(c, false);
+      rows(c);
+    }
+    vm_wait<CST0_OPS * (AHEAD - 1)>();  // chunk 0 has landed, flags 2 and 3 too
+    block_sync<CST0_OPS * (AHEAD - 1)>();
+    for (int it = 0; it < nsteps; ++it) {
+      fetch_flag(it + AHEAD + 2);
+      record(it + AHEAD, true);
+      rows(it + AHEAD);
+      vm_wait<CST0_OPS + 1>();  // chunk it + 1 has landed, and the flag of it + 3
+      block_sync<CST0_OPS + 1>();
+    }
+  } else {
+    for (int c = 0; c < AHEAD; ++c) rows(c);
+    vm_wait<CST1_OPS * (AHEAD - 1)>();  // chunk 0 has landed
+    block_sync<CST1_OPS * (AHEAD - 1)>();
+    for (int it = 0; it < nsteps; ++it) {
+      rows(it + AHEAD);
+      vm_wait<CST1_OPS * (AHEAD - 1)>();  // chunk it + 1 has landed
+      block_sync<CST1_OPS * (AHEAD - 1)>();
+    }
+  }
+  vm_wait<0>();
+}
+
+// One workgroup per compute unit, all resident (cooperative launch).  Role by
+// arrival order on this workgroup's XCD: slot s of XCD x holds group
+// s * nxcd + x, whose first gv * nvb arrivals are its chain workgroups
+// (value head j = r / nvb, 32 columns vb = r % nvb) and the next PRODUCERS
+// its producers.  The last workgroup of an XCD to finish clears that XCD's
+// counters, flags and progress words for the next call.
+template <int DVT>
+__global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams p) {
+  constexpr int DV = DVT;
+  constexpr int NVB = DV / BV;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+  __shared__ int role_index, last_of_xcd;
+  XcdLine *xl = reinterpret_cast<XcdLine *>(p.ws);
+  const int x = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) % p.nxcd;  // XCC_ID
+  if (threadIdx.x == 0) role_index = (int)atomicAdd(&xl[x].arrive, 1u);
+  __syncthreads();
+  const int idx = role_index;
+  const int slot = idx / p.gs, r = idx % p.gs;
+  const int grp = slot * p.nxcd + x;
+  const int gv = p.H_v / p.H_k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (slot < p.slots && grp < p.groups) {
+    unsigned char *base = group_base(p, grp);
+    if (r < gv * NVB) {
+      const int j = r / NVB, vb = r % NVB;
+      const int n = grp / p.H_k, hk = grp % p.H_k, h = hk * gv + j;
+      int64_t t0, t1;
+      seq_bounds(p.cu, p.seq_len, n, t0, t1);
+      const int nch = (int)((t1 - t0 + CH - 1) / CH);
+      const int nsteps = nch + 3;  // state: chunk it-2, outputs: chunk it-3
+      const size_t state_off = ((size_t)n * p.H_v + h) * DK * DV;
+      const int col0 = vb * BV;
+      if (wave < NC) {
+        state_wave<DV, false, 2, true>(p, sm, wave, lane, nch, nsteps, state_off, col0,
+                                       reinterpret_cast<uint32_t *>(base + GRP_PROGRESS) + r);
+      } else if (wave < CW_ST0) {
+        output_wave<DV, 2>(p, sm, wave - CW_O0, lane, nch, nsteps, t0, t1, h, col0);
+      } else {
+        coop_staging<DV>(p, sm, wave - CW_ST0, lane, nch, nsteps, t0, t1, hk, h, col0,
+                         reinterpret_cast<const uint32_t *>(base + GRP_FLAGS) + j * RING,
+                         base + GRP_RECS + (size_t)j * RING * REC_BYTES, &xl[x].err);
+      }
+    } else {
+      producer(p, smem_raw, grp, r - gv * NVB, gv, NVB, &xl[x].err);
+    }
+  }
+  vm_wait<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) last_of_xcd = atomicAdd(&xl[x].done, 1u) == (uint32_t)(XCD_CUS - 1);
+  __syncthreads();
+  if (last_of_xcd) {
+    // every workgroup of this XCD has finished: clear its groups' flags and
+    // progress words, then its counters
+    for (int s = 0; s < p.slots; ++s) {
+      const int gg = s * p.nxcd + x;
+      if (gg >= p.groups) break;
+      uint32_t *w = reinterpret_cast<uint32_t *>(group_base(p, gg));
+      for (int i = threadIdx.x; i < (int)(GRP_RECS / 4); i += blockDim.x) w[i] = 0u;
+    }
+    vm_wait<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      xl[x].arrive = 0u;
+      xl[x].done = 0u;
+    }
+  }
+}
+
 template <int DVT, bool SSD>
 hipError_t launch_kernel(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  MfmaParams p;
+  MfmaParams p{};
   p.q = static_cast<const bf16 *>(x.q);
   p.k = static_cast<const bf16 *>(x.k);
   p.v = static_cast<const bf16 *>(x.v);
@@ -1065,6 +1561,87 @@ hipError_t launch_kernel(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The cooperative kernel's layout for a problem, or ok = false when the
+// problem does not take it: the rule (not SSD) in bf16 with d_k = 128,
+// d_v = 64 or 128, chunk 32, at most MAX_GV value heads per key head, and
+// every (sequence, key head) group's chain and producer workgroups fitting
+// one XCD of the current device at once.
+struct CoopPlan {
+  bool ok = false;
+  int nxcd = 0, slots = 0, gs = 0, groups = 0;
+  size_t grp_stride = 0, bytes = 0;
+};
+// The cooperative kernel keeps one workgroup per compute unit only if two of
+// its LDS footprints do not fit one.
+static_assert(2 * sizeof(Smem) > 160 * 1024, "one workgroup per compute unit");
+static_assert(sizeof(ProdSmem) <= sizeof(Smem), "a producer's LDS fits the launch's");
+
+CoopPlan coop_plan(const Problem &pr) {
+  CoopPlan c;
+  if (pr.mode != kModeRule || pr.dtype != GDR_BF16 || pr.d_k != DK || pr.chunk != CH) return c;
+  if (pr.d_v != 64 && pr.d_v != 128) return c;
+  const int gv = pr.H_v / pr.H_k;
+  if (gv > MAX_GV) return c;
+  const int64_t groups = (int64_t)pr.num_seqs * pr.H_k;
+  if (groups <= 0) return c;
+  // the current device's compute units; with no device to ask (a host-only
+  // size query), the full gfx950: 8 XCDs of 32
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    ncu = 8 * XCD_CUS;
+  }
+  if (ncu <= 0 || ncu % XCD_CUS != 0 || ncu / XCD_CUS > MAX_XCD) return c;
+  c.nxcd = ncu / XCD_CUS;
+  c.gs = gv * (pr.d_v / BV) + PRODUCERS;
+  c.slots = XCD_CUS / c.gs;
+  if ((groups + c.nxcd - 1) / c.nxcd > c.slots) return c;
+  c.groups = (int)groups;
+  c.grp_stride = GRP_RECS + (size_t)gv * RING * REC_BYTES;
+  c.bytes = WS_HEAD + (size_t)c.groups * c.grp_stride;
+  c.ok = true;
+  return c;
+}
+
+template <int DVT>
+hipError_t launch_coop(const Problem &pr, const FwdArgs &x, const CoopPlan &c, void *ws,
+                       hipStream_t s) {
+  MfmaParams p{};
+  p.q = static_cast<const bf16 *>(x.q);
+  p.k = static_cast<const bf16 *>(x.k);
+  p.v = static_cast<const bf16 *>(x.v);
+  p.a = static_cast<const bf16 *>(x.a);
+  p.b = static_cast<const bf16 *>(x.b);
+  p.A_log = x.A_log;
+  p.dt_bias = x.dt_bias;
+  p.s0 = x.s0;
+  p.o = static_cast<bf16 *>(x.o);
+  p.sT = x.sT;
+  p.cu = pr.cu;
+  p.seq_len = pr.seq_len;
+  p.num_seqs = pr.num_seqs;
+  p.H_k = pr.H_k;
+  p.H_v = pr.H_v;
+  p.scale = pr.scale;
+  p.eps = pr.eps;
+  p.ws = static_cast<unsigned char *>(ws);
+  p.grp_stride = c.grp_stride;
+  p.nxcd = c.nxcd;
+  p.slots = c.slots;
+  p.gs = c.gs;
+  p.groups = c.groups;
+  const size_t smem = sizeof(Smem);
+  auto kern = chunked_coop_kernel<DVT>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (err != hipSuccess) return err;
+  void *args[] = {&p};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kern),
+                                    dim3((unsigned)(XCD_CUS * c.nxcd)), dim3(64 * NWAVES_C), args,
+                                    (unsigned)smem, s);
+}
+
 }  // namespace
 
 bool chunked_mfma_supports(const Problem &p) {
@@ -1076,6 +1653,17 @@ hipError_t launch_chunked_mfma(const Problem &pr, const FwdArgs &x, hipStream_t 
   if (pr.mode == 1)
     return pr.d_v == 64 ? launch_kernel<64, true>(pr, x, s) : launch_kernel<128, true>(pr, x, s);
   return pr.d_v == 64 ? launch_kernel<64, false>(pr, x, s) : launch_kernel<128, false>(pr, x, s);
+}
+
+size_t chunked_coop_workspace_bytes(const Problem &pr) {
+  const CoopPlan c = coop_plan(pr);
+  return c.ok ? c.bytes : 0;
+}
+
+hipError_t launch_chunked_coop(const Problem &pr, const FwdArgs &x, void *ws, hipStream_t s) {
+  const CoopPlan c = coop_plan(pr);
+  if (!c.ok) return hipErrorInvalidValue;
+  return pr.d_v == 64 ? launch_coop<64>(pr, x, c, ws, s) : launch_coop<128>(pr, x, c, ws, s);
 }
 
 }  // namespace gdr

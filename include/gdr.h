@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 7
+#define GDR_ABI_VERSION 8
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -75,8 +75,9 @@ typedef enum gdr_status {
   GDR_ERR_SHAPE = 2,       /* inconsistent sizes (H_v % H_k, totals, negatives)  */
   GDR_ERR_UNSUPPORTED = 3, /* a valid shape this build has no kernel for         */
   GDR_ERR_ALIGN = 4,       /* a tensor pointer breaks its alignment rule         */
-  GDR_ERR_LAUNCH = 5,      /* the HIP runtime refused a kernel launch            */
-  GDR_ERR_ALIAS = 6        /* an output overlaps an input it may not alias       */
+  GDR_ERR_WORKSPACE = 5,   /* a workspace smaller than the call needs            */
+  GDR_ERR_LAUNCH = 6,      /* the HIP runtime refused a kernel launch            */
+  GDR_ERR_ALIAS = 7        /* an output overlaps an input it may not alias       */
 } gdr_status;
 
 typedef enum gdr_dtype {
@@ -144,15 +145,34 @@ GDR_API gdr_status gdr_recurrent_fwd(const gdr_shape *shape, const void *q, cons
  * "Detailed Description"; Track L pull request, L2: chunk-parallel
  * UT-transform whose only non-GEMM step is the (I + A)^-1 forward
  * substitution).  Chunks restart at every sequence start; the last chunk of a
- * sequence may be partial.  Arguments as gdr_recurrent_fwd.
- * bf16 with d_k = d_v = 128 and chunk = 32 runs on the matrix cores with bf16
- * operands and fp32 accumulation and state; every other supported shape runs
- * a vector fp32 kernel.
+ * sequence may be partial.  Arguments as gdr_recurrent_fwd, plus:
+ *   workspace       : device memory of gdr_chunked_workspace_bytes(shape)
+ *                     bytes, 256-byte aligned, zero-filled before its first
+ *                     use (the library leaves it zero-filled again when a call
+ *                     completes), overlapping no other argument; or NULL
+ *   workspace_bytes : its size; below the reported size is GDR_ERR_WORKSPACE
+ * bf16 with d_k = 128, d_v = 64 or 128 and chunk = 32 runs on the matrix
+ * cores with bf16 operands and fp32 accumulation and state; every other
+ * supported shape runs a vector fp32 kernel and ignores the workspace.  On
+ * the matrix cores, with a workspace and when the batch's chains fit the GPU
+ * at once (gdr_chunked_workspace_bytes > 0), one cooperative launch splits
+ * the work: producer workgroups form every chunk's triangular inverse,
+ * output mask and row factors once per value head, and the chain workgroups
+ * of that value head read them through the workspace (a ring of records per
+ * value head, so its size does not depend on the sequence length).  Without
+ * a workspace, or when the cooperative launch is refused, every chain
+ * workgroup forms them itself.  Both give the same results up to float
+ * reassociation.  Calls that share one workspace must not overlap in time.
  */
 GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k, const void *v,
                            const void *a, const void *b, const float *A_log, const float *dt_bias,
                            const float *initial_state, void *o, float *final_state,
-                           hipStream_t stream);
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace gdr_chunked_fwd uses for `shape`: 0 when the shape has
+ * no cooperative path (or is invalid), else a size that depends on num_seqs,
+ * H_k, H_v and d_v but not on the sequence lengths. */
+GDR_API size_t gdr_chunked_workspace_bytes(const gdr_shape *shape);
 
 /*
  * gdr_conv_silu -- the short causal convolution and SiLU that turn the in_proj
@@ -307,7 +327,7 @@ GDR_API gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, co
  *  - with workspace == NULL: one launch that does both per chunk on the
  *    chain (d_v = 64 or 128).
  * Other shapes and fp32 inputs run on the vector ALUs in fp32 and ignore the
- * workspace.  workspace_bytes below the reported size returns GDR_ERR_SHAPE.
+ * workspace.  workspace_bytes below the reported size returns GDR_ERR_WORKSPACE.
  */
 GDR_API gdr_status gdr_kda_recurrent_fwd(const gdr_shape *shape, const void *q, const void *k,
                                          const void *v, const void *a, const void *b,

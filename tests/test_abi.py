@@ -32,6 +32,7 @@ def declared_symbols():
 def test_header_declares_the_abi():
     assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_split",
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
+                                  "gdr_chunked_workspace_bytes",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
                                   "gdr_kda_chunked_fwd", "gdr_kda_chunked_fwd_split",
                                   "gdr_kda_chunked_split_workspace", "gdr_kda_chunked_workspace",
@@ -60,11 +61,11 @@ def test_abi_version_matches_header(gdr):
 def test_status_strings(gdr):
     lib = gdr.lib()
     seen = set()
-    for code in range(7):
+    for code in range(8):
         s = lib.gdr_status_string(code).decode()
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert lib.gdr_status_string(99).decode() == "unknown status"
 
 
@@ -112,7 +113,7 @@ def call(gdr, fn, s, ptrs=None):
     p = [fake(i) for i in range(10)] if ptrs is None else ptrs
     f = getattr(gdr.lib(), fn)
     arg = ctypes.byref(s) if s is not None else None
-    if fn == "gdr_kda_chunked_fwd":  # no workspace: the one-launch form
+    if fn in ("gdr_kda_chunked_fwd", "gdr_chunked_fwd"):  # no workspace
         return f(arg, *p[:10], None, 0, None)
     return f(arg, *p[:10], None)
 
@@ -163,16 +164,16 @@ def test_misaligned(gdr):
 def test_aliasing(gdr):
     p = [fake(i) for i in range(10)]
     p[8] = fake(0)  # o on top of q
-    assert call(gdr, "gdr_recurrent_fwd", shape(gdr), p) == 6
+    assert call(gdr, "gdr_recurrent_fwd", shape(gdr), p) == 7
     p = [fake(i) for i in range(10)]
     p[9] = fake(7, off=16)  # final_state shifted into initial_state
-    assert call(gdr, "gdr_chunked_fwd", shape(gdr), p) == 6
+    assert call(gdr, "gdr_chunked_fwd", shape(gdr), p) == 7
 
 
 def test_gates_output_alias(gdr):
     p = [fake(i) for i in range(10)]
     p[6] = fake(0)  # q_hat over q
-    assert call(gdr, "gdr_gates", shape(gdr), p) == 6
+    assert call(gdr, "gdr_gates", shape(gdr), p) == 7
 
 
 def test_binding_refuses_cpu_tensors(gdr):
@@ -228,9 +229,9 @@ def test_conv_silu_validation(gdr):
     assert conv_call(gdr, shape(gdr), weight=fake(1, off=4)) == 4     # weights move in 16 bytes
     assert conv_call(gdr, shape(gdr), bias=fake(2, off=8)) == 4
     assert conv_call(gdr, shape(gdr, dtype=1), s_in=fake(3, off=1)) == 4
-    assert conv_call(gdr, shape(gdr), q=fake(0)) == 6                 # q over x
-    assert conv_call(gdr, shape(gdr), k=fake(4, off=64)) == 6         # k inside q
-    assert conv_call(gdr, shape(gdr), s_out=fake(3, off=16)) == 6     # shifted over the history
+    assert conv_call(gdr, shape(gdr), q=fake(0)) == 7                 # q over x
+    assert conv_call(gdr, shape(gdr), k=fake(4, off=64)) == 7         # k inside q
+    assert conv_call(gdr, shape(gdr), s_out=fake(3, off=16)) == 7     # shifted over the history
 
 
 def test_gated_rmsnorm_validation(gdr):
@@ -241,8 +242,8 @@ def test_gated_rmsnorm_validation(gdr):
     assert norm_call(gdr, shape(gdr), weight=None) == 1
     assert norm_call(gdr, shape(gdr), o=None) == 1
     assert norm_call(gdr, shape(gdr), z=fake(1, off=4)) == 4
-    assert norm_call(gdr, shape(gdr), out=fake(0, off=16)) == 6       # shifted over o
-    assert norm_call(gdr, shape(gdr), out=fake(2)) == 6               # over the weight
+    assert norm_call(gdr, shape(gdr), out=fake(0, off=16)) == 7       # shifted over o
+    assert norm_call(gdr, shape(gdr), out=fake(2)) == 7               # over the weight
     assert norm_call(gdr, shape(gdr, d_v=24)) == 3
 
 
@@ -293,10 +294,10 @@ def test_split_validation(gdr):
     assert split_call(gdr, s, 48) == 2                       # does not divide seq_len
     assert split_call(gdr, s, 16, ws=ctypes.c_void_p(0)) == 1
     _, need = workspace_bytes(gdr, s, 16)
-    assert split_call(gdr, s, 16, ws_bytes=need - 1) == 2
+    assert split_call(gdr, s, 16, ws_bytes=need - 1) == 5    # GDR_ERR_WORKSPACE
     assert split_call(gdr, s, 16, ws=fake(20, off=128)) == 4
-    assert split_call(gdr, s, 16, ws=fake(8)) == 6           # over o
-    assert split_call(gdr, s, 16, o=fake(0)) == 6            # o over q, as gdr_chunked_fwd
+    assert split_call(gdr, s, 16, ws=fake(8)) == 7           # over o
+    assert split_call(gdr, s, 16, o=fake(0)) == 7            # o over q, as gdr_chunked_fwd
 
 
 # ------------------------------------------------------------- the SSD recurrence
@@ -319,9 +320,9 @@ def test_ssd_validation(gdr, fn):
     assert ssd_call(gdr, fn, shape(gdr), C=None) == 1
     assert ssd_call(gdr, fn, shape(gdr), B=fake(3, off=8)) == 4          # rows need 16 bytes
     assert ssd_call(gdr, fn, shape(gdr), A=fake(2, off=2)) == 4
-    assert ssd_call(gdr, fn, shape(gdr), y=fake(0)) == 6                 # y over x
-    assert ssd_call(gdr, fn, shape(gdr), sT=fake(7)) == 6                # state over y
-    assert ssd_call(gdr, fn, shape(gdr), sT=fake(5, off=16)) == 6        # shifted in place
+    assert ssd_call(gdr, fn, shape(gdr), y=fake(0)) == 7                 # y over x
+    assert ssd_call(gdr, fn, shape(gdr), sT=fake(7)) == 7                # state over y
+    assert ssd_call(gdr, fn, shape(gdr), sT=fake(5, off=16)) == 7        # shifted in place
 
 
 def test_ssd_chunk_checked(gdr):
@@ -353,11 +354,11 @@ def test_kda_validation(gdr, fn):
     # output 64 bytes past its start overlaps it
     p = [fake(i) for i in range(10)]
     p[8] = fake(3, off=64)
-    assert call(gdr, fn, shape(gdr), p) == 6
+    assert call(gdr, fn, shape(gdr), p) == 7
     # ... and so does a final state 64 bytes past the start of dt_bias (2 x 16 fp32)
     p = [fake(i) for i in range(10)]
     p[9] = fake(6, off=64)
-    assert call(gdr, fn, shape(gdr), p) == 6
+    assert call(gdr, fn, shape(gdr), p) == 7
 
 
 def test_kda_chunk_sizes(gdr):
@@ -385,10 +386,10 @@ def test_kda_workspace_checked(gdr):
     s = shape(gdr, dtype=1, d_k=128, d_v=64, chunk=32)
     need = (4 // 32 + 1) * 2 * 29696
     p = [fake(i) for i in range(10)]
-    assert f(ctypes.byref(s), *p, fake(10), need - 1, None) == 2        # too small
+    assert f(ctypes.byref(s), *p, fake(10), need - 1, None) == 5        # too small
     assert f(ctypes.byref(s), *p, fake(10, off=16), need, None) == 4    # not 256-byte aligned
-    assert f(ctypes.byref(s), *p, fake(0, off=256), need, None) == 6    # over q
-    assert f(ctypes.byref(s), *p, fake(8, off=-4096), need, None) == 6  # runs into o
+    assert f(ctypes.byref(s), *p, fake(0, off=256), need, None) == 7    # over q
+    assert f(ctypes.byref(s), *p, fake(8, off=-4096), need, None) == 7  # runs into o
 
 
 def test_kda_split_workspace_holds_the_prep(gdr):
@@ -409,3 +410,50 @@ def test_kda_split_workspace_holds_the_prep(gdr):
     assert kda_.value == rule.value
     assert lib.gdr_kda_chunked_split_workspace(ctypes.byref(s), 1024, ctypes.byref(kda_)) == 0
     assert kda_.value == 0  # one segment
+
+
+# ------------------------------------------ the cooperative chunked form's workspace
+def chunked_ws_bytes(gdr, **kw):
+    return int(gdr.lib().gdr_chunked_workspace_bytes(ctypes.byref(shape(gdr, **kw))))
+
+
+def test_chunked_workspace_constant_in_sequence_length(gdr):
+    """The workspace of gdr_chunked_fwd does not grow with the context: the
+    same bytes for 64 and for 32768 tokens (the state is fixed-size,
+    GatedDeltaRule.ixx File Reference, "Detailed Description")."""
+    def prefill(T):
+        return chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=16, H_v=48,
+                                num_seqs=1, seq_len=T, total_tokens=T)
+    short, long_ = prefill(64), prefill(32768)
+    assert short == long_ > 0
+    # a ring of 16 records of 7 KB per value head, and 512 bytes of flags per
+    # (sequence, key head) group, after 2 KB of per-XCD counters
+    assert short == 2048 + 16 * (512 + 3 * 16 * 7168)
+    # packed batches: lengths do not matter either
+    s = shape(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=2, H_v=6, num_seqs=3, seq_len=0,
+              total_tokens=5000)
+    s.cu_seqlens = fake(30).value
+    assert int(gdr.lib().gdr_chunked_workspace_bytes(ctypes.byref(s))) == 2048 + 6 * (512 + 3 * 16 * 7168)
+
+
+def test_chunked_workspace_zero_without_cooperative_form(gdr):
+    assert chunked_ws_bytes(gdr) == 0                                    # fp32: vector kernel
+    assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=16) == 0
+    assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=1, H_v=4) == 0  # 4 per key head
+    # more (sequence, key head) groups than the device holds at once: 256
+    # sequences of 16 key heads
+    assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=16, H_v=48,
+                            num_seqs=256, seq_len=1, total_tokens=256) == 0
+    assert int(gdr.lib().gdr_chunked_workspace_bytes(None)) == 0
+    assert chunked_ws_bytes(gdr, H_v=3, H_k=2) == 0                      # invalid shape
+
+
+def test_chunked_workspace_checked(gdr):
+    f = gdr.lib().gdr_chunked_fwd
+    s = shape(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=1, H_v=3)
+    need = int(f and gdr.lib().gdr_chunked_workspace_bytes(ctypes.byref(s)))
+    assert need > 0
+    p = [fake(i) for i in range(10)]
+    assert f(ctypes.byref(s), *p, fake(10), need - 1, None) == 5        # too small
+    assert f(ctypes.byref(s), *p, fake(10, off=16), need, None) == 4    # not 256-byte aligned
+    assert f(ctypes.byref(s), *p, fake(0, off=256), need, None) == 7    # over q

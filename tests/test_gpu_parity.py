@@ -268,16 +268,20 @@ def test_empty_and_zero_length(form):
 
 def test_constant_memory_in_sequence_length():
     """The state does not grow with context: the library allocates nothing,
-    so peak memory is the inputs and outputs alone at every length."""
-    w = synth.custom(1, 1, 128, 128, "bf16", lengths=[32768])
-    inp = synth.make_inputs(w, 12, device=DEV)
-    torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats()
-    base = torch.cuda.memory_allocated()
-    o, S = run("chunked", inp, w)
-    torch.cuda.synchronize()
-    extra = torch.cuda.max_memory_allocated() - base
-    assert extra <= o.numel() * o.element_size() + S.numel() * 4 + 4096
+    so peak memory is the outputs and the workspace alone, and the workspace
+    has the same size at every length."""
+    ws_bytes = gdr.chunked_workspace_bytes(1, 1, 128, 128, "bf16", 1)
+    for T in (64, 32768):
+        w = synth.custom(1, 1, 128, 128, "bf16", lengths=[T])
+        inp = synth.make_inputs(w, 12, device=DEV)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        o, S = run("chunked", inp, w)  # workspace "auto": allocated by the binding
+        torch.cuda.synchronize()
+        extra = torch.cuda.max_memory_allocated() - base
+        assert extra <= o.numel() * o.element_size() + S.numel() * 4 + ws_bytes + 4096, T
+        assert gdr.chunked_workspace_bytes(1, 1, 128, 128, "bf16", 1) == ws_bytes
 
 
 def test_gates_kernel():
