@@ -101,7 +101,10 @@ constexpr int BV = 16 * NC;
 constexpr int NWAVES = 8;   // fused kernel
 constexpr int NSTAGE = 5;   // chunk buffers in LDS
 constexpr int AHEAD = 2;    // chunks whose rows are in flight beyond the one being published
-static_assert(AHEAD <= NSTAGE - 3, "a buffer is refilled only after its chunk was consumed");
+// Chunk c's buffer is refilled with chunk c + NSTAGE (rows, and the record in
+// the cooperative kernel) from step c + NSTAGE - AHEAD on; its last reads are
+// in step c + 2 (the state and output waves run chunk it - 2 in step it).
+static_assert(AHEAD + 2 < NSTAGE, "a buffer is refilled only after its chunk was consumed");
 static_assert(AHEAD == 2, "the cooperative staging wave fetches flags two steps ahead of AHEAD");
 
 // fused kernel: wave roles (wave w runs on SIMD w % 4): the state waves share
@@ -112,10 +115,11 @@ constexpr int W_C0 = 0, W_P0 = 2, W_P1 = 3, W_ST0 = 4, W_O0 = 6;
 constexpr int ST0_OPS = 8 + 1;       // k rows, half of v
 constexpr int ST1_OPS = 8 + 1 + 1;   // q rows, half of v, a and b
 
-// cooperative kernel: six waves; chain workgroups use waves 0, 1 (state, SIMD
-// 0, 1), 2, 3 (output, SIMD 2, 3) and 4, 5 (staging, SIMD 0, 1)
-constexpr int NWAVES_C = 6;
-constexpr int CW_O0 = 2, CW_ST0 = 4;
+// cooperative kernel: eight waves; chain workgroups use waves 0, 1 (state,
+// SIMD 0, 1), 2, 3 (output, SIMD 2, 3), 4, 5 (staging, SIMD 0, 1) and 6, 7
+// (K S, SIMD 2, 3)
+constexpr int NWAVES_C = 8;
+constexpr int CW_O0 = 2, CW_ST0 = 4, CW_KS0 = 6;
 constexpr int REC_BYTES = 7168;           // one record; 7 loads of 1 KB per wave
 constexpr int REC_DMAS = REC_BYTES / 1024;
 constexpr int CST0_OPS = 8 + 1 + REC_DMAS;  // k rows, half of v, the record (+ 1 flag a step)
@@ -263,26 +267,32 @@ struct Smem {
   // handed from the state waves to the output waves, per state wave and lane:
   alignas(16) bf16x8 sb[2][NC][4][64];  // state at chunk entry, bf16 B operands (ring by chunk)
   alignas(16) bf16x8 db[2][NC][64];     // diag(1/|k|) Delta of the chunk, bf16 (ring by chunk)
-  // P0's own exchange inside one chunk: column m of -A11, row m of -A22 and
-  // row m of A21 (columns in the order 4j + g), 80-byte rows so that 16 rows
-  // read at one column fill distinct 16-byte bank slots
-  alignas(16) float p0x[3][16][20];
+  union {
+    // fused kernel, P0's own exchange inside one chunk: column m of -A11,
+    // row m of -A22 and row m of A21 (columns in the order 4j + g), 80-byte
+    // rows so that 16 rows read at one column fill distinct 16-byte bank slots
+    float p0x[3][16][20];
+    // cooperative kernel: K_{c+1} S_c from the K S waves to the state waves,
+    // per state wave, 16-row block and lane (ring by chunk)
+    f32x4 ksn[2][NC][2][64];
+  };
   // cooperative kernel: flag words of chunks c, fetched ahead into word block c % 4
   alignas(16) uint32_t fl[4][64];
 };
 
-// A producer workgroup's LDS (cooperative kernel): its chunk's rows (two
-// buffers: the next chunk lands while this one is worked on), the raw gates
-// of the group's value heads, their records and the T waves' exchange rows.
+// A producer workgroup's LDS (cooperative kernel): its chunk's rows and raw
+// gates (two buffers: the next chunk lands while this one is worked on), the
+// records under construction (two buffers: a record is copied out in the
+// iteration after the one that formed it), the T waves' exchange rows, the P
+// waves' decays and the progress words.
 struct ProdSmem {
   alignas(16) bf16 K[2][CH * DK];
   alignas(16) bf16 Q[2][CH * DK];
   alignas(16) bf16 Kp[2][CH * DK];  // k rows of the chunk before (for the cross Gram)
   alignas(16) uint32_t ab[2][MAX_GV][2 * CH];
-  alignas(16) float ikn[CH];   // 1/|k_r| of the chunk
-  alignas(16) float iqn[CH];   // scale/|q_r|
-  Prep pp[MAX_GV];
+  Prep pp[2][MAX_GV];
   alignas(16) float xs[MAX_GV][3][16][20];
+  alignas(16) float gp[MAX_GV][CH];      // P wave j: the chunk's cumulative log decay
   alignas(16) uint32_t prg[MAX_GV][64];  // progress words, fetched by T wave j
 };
 
@@ -362,10 +372,16 @@ __device__ __forceinline__ void dma16(const bf16 *src, bf16 *lds) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
                                    (__attribute__((address_space(3))) void *)(lds), 16, 0, 0);
 }
-// The same, read past the L1 (sc0): for memory another workgroup of the XCD
-// wrote during this launch (the cooperative kernel's records).
+// Cache policy of a load that must see what another compute unit of the XCD
+// stored during this launch: device scope (sc1), which the per-CU L1 cannot
+// serve from a line it still holds; sc0 alone is workgroup scope and may hit
+// a stale L1 line.
+constexpr int CPOL_DEVICE = 16;
+// The same, at device scope: the cooperative kernel's records, flags and
+// progress words.
 __device__ __forceinline__ void dma16_l2(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lds), 16, 0, 1);
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lds), 16, 0,
+                                   CPOL_DEVICE);
 }
 
 // Map the launch index to a work unit so that the gs units of one (sequence,
@@ -563,6 +579,17 @@ __device__ __forceinline__ void stage_gates(Prep &S, const uint32_t *ab, int lan
     S.r.cl = cl;
   }
 }
+// The cumulative log decay of one chunk's rows alone (a producer's P wave):
+// row r = lane % 32, into gam[r].
+__device__ __forceinline__ void chunk_decays(float *gam, const uint32_t *ab, int lane, int cl,
+                                             float neg_exp_A, float dtb) {
+  const int r = lane & 31;
+  const float a_r = __uint_as_float(lds_read_u32_now(&ab[r]) << 16) + dtb;
+  const float sp = fmaxf(a_r, 0.f) + fast_log(1.f + fast_exp(-fabsf(a_r)));
+  const float cum = scan32(r < cl ? neg_exp_A * sp : 0.f);
+  if (lane < 32) gam[r] = cum;
+}
+
 // The two substitution sweeps of P0, interleaved, 15 steps:
 //  * backward, X = T11^T, lane (r, g) holding X[r][4j + g] in x[j]: in step s
 //    row i = 15 - s is final and every row r adds cB[i] X[i] (cB[i] holds
@@ -736,16 +763,16 @@ __device__ __forceinline__ void prepare_T(Prep &S, float (&xs)[3][16][20], const
 
 // The output mask without the row norms, P[r][i] = exp(gam_r - gam_i)
 // (q_r . k_i) for i <= r, of one chunk (scale/|q_r| and 1/|k_i| are applied
-// by the output waves), into the record.  IQ_GRAM (P1 of the fused kernel):
+// by the output waves), into the record; gam the chunk's cumulative log decay.  IQ_GRAM (P1 of the fused kernel):
 // also scale/|q_r| from the Gram diagonal of q, into the record; otherwise
 // (a P wave of a producer) the norms are already there.
 template <bool IQ_GRAM>
-__device__ __forceinline__ void prepare_P(Prep &S, const RowOps &o, int lane, float eps,
-                                          float scale) {
+__device__ __forceinline__ void prepare_P(Prep &S, const float *gam, const RowOps &o, int lane,
+                                          float eps, float scale) {
   const int m = lane & 15, g = lane >> 4;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-  const f32x4 gm_lo = ld4(&S.gam[4 * g]), gm_hi = ld4(&S.gam[16 + 4 * g]);
-  const float gm_m0 = S.gam[m], gm_m1 = S.gam[16 + m];
+  const f32x4 gm_lo = ld4(&gam[4 * g]), gm_hi = ld4(&gam[16 + 4 * g]);
+  const float gm_m0 = gam[m], gm_m1 = gam[16 + m];
   f32x4 p00 = z, p10 = z, p11 = z;  // (K Q^T) blocks: (q_r . k_i), r = 16 rb + m, i = 16 ib + 4g + j
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -832,49 +859,54 @@ __device__ __forceinline__ void prepare_p_ssd(Prep &S, const RowOps &o, int lane
 }
 
 // ------------------------------------------------------------------ waves
-// State wave cw (16 columns): chunk c in step c + LAG: K S, R, Delta = T R,
+// State wave for NT tiles of 16 columns (tiles cw0 .. cw0 + NT - 1 of the
+// workgroup's 32): chunk c in step c + LAG: K S, R, Delta = T R,
 // S <- Gam_last S + K^T D Delta; it hands the state at chunk entry (before
-// step c + LAG) and the scaled Delta (during step c + LAG) to its output
-// wave.  Passes nsteps + 1 barriers.
+// step c + LAG) and the scaled Delta (during step c + LAG) to the output
+// waves.  The k operands are read once for all tiles, and the tiles'
+// independent chains interleave.  Passes nsteps + 1 barriers.
 //
-// LOOK (cooperative kernel, LAG = 2): K S of the next chunk is formed one
-// step early from the update it depends on,
+// LOOK (cooperative kernel, LAG = 2): K S of a chunk is formed from the
+// update it depends on,
 //   K_{c+1} S_{c+1} = Gam_last(c) (K_{c+1} S_c) + (K_{c+1} K_c^T) (D_c Delta_c),
-// with K_{c+1} S_c taken from the state at chunk c's entry, which is known
-// when step c starts, and the cross Gram from chunk c+1's record.  The
-// dependent chain of a step is then the two products of the cross Gram, R,
-// the two of T R and D Delta; the K S and update products of a step
-// depend only on the previous step.
-template <int DV, bool SSD, int LAG, bool LOOK = false>
-__device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw, int lane,
+// with the cross Gram from chunk c+1's record and K_{c+1} S_c formed by a K S
+// wave (ks_wave) in the step before, from the state handed over at chunk c's
+// entry.  The state wave then reads no k rows and runs no K S products: the
+// dependent chain of its step is the two products of the cross Gram, R, the
+// two of T R, D Delta and the update.
+template <int DV, bool SSD, int LAG, bool LOOK, int NT>
+__device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw0, int lane,
                                            int nch, int nsteps, size_t state_off, int col0,
                                            uint32_t *progress = nullptr) {
   static_assert(!LOOK || (LAG == 2 && !SSD), "look-ahead needs the rows of chunk c+1 in step c+1");
   const int m = lane & 15, g = lane >> 4;
-  const int col = col0 + 16 * cw + m;
-  f32x4 S[8];  // S[state_row(t, g, j)][col]
-  if (p.s0) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[t][j] = p.s0[state_off + (size_t)state_row(t, g, j) * DV + col];
-  } else {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bf16x8 Sb[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1]);
-  // LDS operands: the k^T tiles of this chunk (A operands of the state
-  // update) are read once the first products are issued; the k rows (A
-  // operands of K S: of chunk c + 1 with LOOK, else of chunk c) and v of the
-  // next step are read after the state update, so that they are in
-  // registers when the next step starts.
-  bf16x8 Kr[2][4], Kt[8], vv;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 pn[2] = {z, z};               // LOOK: K_{c+1} S_c
-  bf16x8 dpp = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};  // LOOK: D_c Delta_c
-  float gcp = 1.0f;                   // LOOK: Gam_last of chunk c
+  f32x4 S[NT][8];  // S[u][t]: state rows state_row(t, g, j), column col0 + 16 (cw0 + u) + m
+  bf16x8 Sb[NT][4];  // its bf16 B operands
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int col = col0 + 16 * (cw0 + u) + m;
+    if (p.s0) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[u][t][j] = p.s0[state_off + (size_t)state_row(t, g, j) * DV + col];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[u][t] = z;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) Sb[u][kb] = state_operand(S[u][2 * kb], S[u][2 * kb + 1]);
+  }
+  // LDS operands: the k^T tiles of this chunk (A operands of the state
+  // update) are read once the first products are issued; the k rows of the
+  // next chunk (A operands of K S; not with LOOK) and its v are read after the
+  // state update, so that they are in registers when the next step starts.
+  bf16x8 Kr[2][4], Kt[8], vv[NT];
+  bf16x8 dpp[NT];       // LOOK: D_c Delta_c of the chunk before
+  float gcp = 1.0f;     // LOOK: Gam_last of the chunk before
+#pragma unroll
+  for (int u = 0; u < NT; ++u) dpp[u] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
   auto read_rows = [&](const Stage &sn) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -893,19 +925,25 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
   };
   auto read_v = [&](const Stage &sn) {
     // v[4g + j][col] and v[16 + 4g + j][col]
-    const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
-    vv = cat8(tr_read(sn.V + v_off(vr, vc)), tr_read(sn.V + v_off(16 + vr, vc)));
+    const int vr = 4 * g + (m >> 2);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int vc = 16 * (cw0 + u) + 4 * (m & 3);
+      vv[u] = cat8(tr_read(sn.V + v_off(vr, vc)), tr_read(sn.V + v_off(16 + vr, vc)));
+    }
   };
   auto hand_state = [&](int c) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sm.sb[c & 1][cw][kb][lane] = Sb[kb];
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sm.sb[c & 1][cw0 + u][kb][lane] = Sb[u][kb];
   };
-  // K S products of the rows in Kr with the state operand Sb
-  auto k_times_s = [&](f32x4 (&acc)[2]) {
+  // K S products of the rows in Kr with the state operand of tile u
+  auto k_times_s = [&](int u, f32x4 (&acc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) acc[mt] = mma32(Kr[mt][kb], Sb[kb], acc[mt]);
+      for (int mt = 0; mt < 2; ++mt) acc[mt] = mma32(Kr[mt][kb], Sb[u][kb], acc[mt]);
     }
   };
   block_sync();
@@ -913,13 +951,7 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
     const int c = it - LAG;
     // cooperative kernel: chunks up to `it` have landed in LDS (records
     // included), so their slots may be refilled
-    if (progress && cw == 0 && lane == 0) *progress = (uint32_t)(min(it, nch - 1) + 1);
-    if constexpr (LOOK) {
-      if (c == -1 && nch > 0) {
-        // K_0 S_0 for the first chunk
-        k_times_s(pn);
-      }
-    }
+    if (progress && cw0 == 0 && lane == 0) *progress = (uint32_t)(min(it, nch - 1) + 1);
     if (c >= 0 && c < nch) {
       const Stage &st = sm.st[c % NSTAGE];
       const Rec &rc = st.pp.r;
@@ -932,71 +964,84 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
       const f32x4 ik0 = ld4(&rc.ik[4 * g]), ik1 = ld4(&rc.ik[16 + 4 * g]);
       const f32x4 tk0 = ld4(&rc.tk[4 * g]), tk1 = ld4(&rc.tk[16 + 4 * g]);
       const float gc = rc.Gc;
-      // ks[mt]: (K S)[16mt + 4g + j][m]
-      f32x4 ks[2] = {z, z};
+      // ks[u][mt]: (K S)[16mt + 4g + j][m] of tile u
+      f32x4 ks[NT][2];
       if constexpr (LOOK) {
-        ks[0] = pn[0] * gcp;
-        ks[1] = pn[1] * gcp;
-        if (c > 0) {
-          ks[0] = mma32(rc.GX[0][lane], dpp, ks[0]);
-          ks[1] = mma32(rc.GX[1][lane], dpp, ks[1]);
+        // K_c S_{c-1} (K_0 S_0 for the first chunk) from the K S wave
+        const bf16x8 gx0 = rc.GX[0][lane], gx1 = rc.GX[1][lane];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          ks[u][0] = sm.ksn[c & 1][cw0 + u][0][lane];
+          ks[u][1] = sm.ksn[c & 1][cw0 + u][1][lane];
+          if (c > 0) {
+            ks[u][0] = mma32(gx0, dpp[u], ks[u][0] * gcp);
+            ks[u][1] = mma32(gx1, dpp[u], ks[u][1] * gcp);
+          }
         }
-        // K_{c+1} S_c for the next step (Kr holds chunk c + 1's rows)
-        pn[0] = z;
-        pn[1] = z;
-        if (more) k_times_s(pn);
-      } else if constexpr (!SSD) {
-        k_times_s(ks);
+      } else {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          ks[u][0] = z;
+          ks[u][1] = z;
+          if constexpr (!SSD) k_times_s(u, ks[u]);
+        }
       }
       // Gam_last S while the matrix cores run K S
 #pragma unroll
-      for (int t = 0; t < 8; ++t) S[t] *= gc;
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[u][t] *= gc;
       __builtin_amdgcn_sched_barrier(0);
       read_kt(st);
       __builtin_amdgcn_sched_barrier(0);
-      // R = beta V - beta Gam ik (K S), rows 4g..4g+3 and 16+4g..16+4g+3
-      f32x4 R0, R1;
+      bf16x8 Dp[NT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        R0[j] = bt0[j] * (float)vv[j] - bk0[j] * ks[0][j];
-        R1[j] = bt1[j] * (float)vv[4 + j] - bk1[j] * ks[1][j];
+      for (int u = 0; u < NT; ++u) {
+        // R = beta V - beta Gam ik (K S), rows 4g..4g+3 and 16+4g..16+4g+3
+        f32x4 R0, R1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          R0[j] = bt0[j] * (float)vv[u][j] - bk0[j] * ks[u][0][j];
+          R1[j] = bt1[j] * (float)vv[u][4 + j] - bk1[j] * ks[u][1][j];
+        }
+        // Delta = T R, both 16-row blocks from the one bf16 operand of R in
+        // slot order; SSD: no erase, Delta = R
+        f32x4 d1 = R0, d2 = R1;
+        if constexpr (!SSD) {
+          const bf16x8 Rb = pack8(R0, R1);
+          d1 = mma32(cat8(tt0, bf16x4{0, 0, 0, 0}), Rb, z);
+          d2 = mma32(tt1, Rb, z);
+        }
+        Dp[u] = pack8(tk0 * d1, tk1 * d2);
+        // diag(ik) Delta for the outputs of this chunk
+        sm.db[c & 1][cw0 + u][lane] = pack8(ik0 * d1, ik1 * d2);
       }
-      // Delta = T R, both 16-row blocks from the one bf16 operand of R in
-      // slot order; SSD: no erase, Delta = R
-      f32x4 d1 = R0, d2 = R1;
-      if constexpr (!SSD) {
-        const bf16x8 Rb = pack8(R0, R1);
-        d1 = mma32(cat8(tt0, bf16x4{0, 0, 0, 0}), Rb, z);
-        d2 = mma32(tt1, Rb, z);
-      }
-      // S <- Gam_last S + K^T diag(tail ik) Delta
-      const bf16x8 Dp = pack8(tk0 * d1, tk1 * d2);
       if constexpr (LOOK) {
-        dpp = Dp;
+#pragma unroll
+        for (int u = 0; u < NT; ++u) dpp[u] = Dp[u];
         gcp = gc;
       }
-      // diag(ik) Delta for the outputs of this chunk
-      sm.db[c & 1][cw][lane] = pack8(ik0 * d1, ik1 * d2);
+      // S <- Gam_last S + K^T diag(tail ik) Delta
 #pragma unroll
-      for (int t = 0; t < 8; ++t) S[t] = mma32(Kt[t], Dp, S[t]);
+      for (int u = 0; u < NT; ++u) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) Sb[kb] = state_operand(S[2 * kb], S[2 * kb + 1]);
+        for (int t = 0; t < 8; ++t) S[u][t] = mma32(Kt[t], Dp[u], S[u][t]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Sb[u][kb] = state_operand(S[u][2 * kb], S[u][2 * kb + 1]);
+      }
       if (more) hand_state(c + 1);
-    } else if (c == -1 && nch > 0) {
+    } else if (c == (LOOK ? -2 : -1) && nch > 0) {
+      // the initial state (LOOK: a step early, for the K S wave's K_0 S_0)
       hand_state(0);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the handed-over writes are done
     {
       // operands of the next step, read unconditionally (the chunk index
       // clamped into the sequence) so that the loads write the loop's
-      // registers directly and stay in flight across the barrier: k rows of
-      // chunk c + 2 (LOOK) or c + 1, v of chunk c + 1
+      // registers directly and stay in flight across the barrier: k rows
+      // (not with LOOK) and v of chunk c + 1
       const Stage &sr = sm.st[max(min(c + 1, nch - 1), 0) % NSTAGE];
-      if constexpr (LOOK) {
-        read_rows(sm.st[max(min(c + 2, nch - 1), 0) % NSTAGE]);
-      } else if constexpr (!SSD) {
-        read_rows(sr);
-      }
+      if constexpr (!SSD && !LOOK) read_rows(sr);
       read_v(sr);
     }
     // no wait for the reads in flight: their buffers are refilled only
@@ -1005,55 +1050,106 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
   }
   if (p.sT) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int u = 0; u < NT; ++u) {
+      const int col = col0 + 16 * (cw0 + u) + m;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p.sT[state_off + (size_t)state_row(t, g, j) * DV + col] = S[t][j];
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p.sT[state_off + (size_t)state_row(t, g, j) * DV + col] = S[u][t][j];
+    }
   }
 }
 
-// Output wave cw: in step it, O of chunk it - LAG - 1 =
-// (diag(ik) Delta)^T P^T + (Gam iq Q S)^T, then (Q S)^T of chunk it - LAG
-// from the state handed over at its entry.  Passes nsteps + 1 barriers.
-template <int DV, int LAG>
-__device__ __forceinline__ void output_wave(const MfmaParams &p, Smem &sm, int cw, int lane,
+// K S wave of tile cw (cooperative kernel, alongside a LOOK state wave): in
+// step it, K_{it-1} S_{it-2} (K_0 S_0 in step 1) from the state the state wave
+// handed over at the entry of chunk it - 2 (0), for the state wave's step
+// it + 1.  Passes nsteps + 1 barriers.
+template <int LAG>
+__device__ __forceinline__ void ks_wave(Smem &sm, int cw, int lane, int nch, int nsteps) {
+  static_assert(LAG == 2, "the state wave runs chunk it - 2 in step it");
+  const int m = lane & 15, g = lane >> 4;
+  const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+  block_sync();
+  for (int it = 0; it < nsteps; ++it) {
+    const int cn = it - 1;  // the chunk whose rows multiply the state
+    if (cn >= 0 && cn < nch) {
+      const int cs = max(it - 2, 0);  // the state's chunk
+      const Stage &st = sm.st[cn % NSTAGE];
+      f32x4 acc[2] = {z, z};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 sb = sm.sb[cs & 1][cw][kb][lane];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[mt] = mma32(row_op_t(st.K, 16 * mt + m, kb, g), sb, acc[mt]);
+      }
+      sm.ksn[cn & 1][cw][0][lane] = acc[0];
+      sm.ksn[cn & 1][cw][1][lane] = acc[1];
+    }
+    block_sync<63, true>();
+  }
+}
+
+// Output wave for NT tiles of 16 columns (tiles cw0 ..): in step it, O of
+// chunk it - LAG - 1 = (diag(ik) Delta)^T P^T + (Gam iq Q S)^T, then (Q S)^T
+// of chunk it - LAG from the state handed over at its entry (the q operands
+// are read once for all tiles).  The record entries of a chunk's outputs
+// (P, Gam, iq) are read in the step of its Q S and held in registers, so
+// that no wave reads a chunk's buffer after step c + LAG.  Passes nsteps + 1
+// barriers.
+template <int DV, int LAG, int NT>
+__device__ __forceinline__ void output_wave(const MfmaParams &p, Smem &sm, int cw0, int lane,
                                             int nch, int nsteps, int64_t t0, int64_t t1, int h,
                                             int col0) {
   const int m = lane & 15, g = lane >> 4;
-  f32x4 qsT[2];
+  f32x4 qsT[NT][2];
+  bf16x8 pr0, pr1;
+  float gm0, gm1, iq0, iq1;
   block_sync();
   for (int it = 0; it < nsteps; ++it) {
     const int co = it - LAG - 1;
     if (co >= 0 && co < nch) {
-      const Rec &rc = sm.st[co % NSTAGE].pp.r;
-      const bf16x8 Db = sm.db[co & 1][cw][lane];
-      const bf16x8 pr0 = rc.P[0][lane];
-      const bf16x8 pr1 = rc.P[1][lane];
-      const float gm0 = rc.Gm[m], gm1 = rc.Gm[16 + m];
-      const float iq0 = rc.iq[m], iq1 = rc.iq[16 + m];
-      // lane (m, g) gets O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P diag(ik) Delta)
-      const f32x4 oc0 = mma32(Db, pr0, qsT[0] * gm0) * iq0;
-      const f32x4 oc1 = mma32(Db, pr1, qsT[1] * gm1) * iq1;
       const int64_t row = t0 + (int64_t)co * CH + m;
-      bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * cw + 4 * g;
-      if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
-      if (row + 16 < t1) *reinterpret_cast<bf16x4 *>(orow + (int64_t)16 * p.H_v * DV) = pack4(oc1);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const bf16x8 Db = sm.db[co & 1][cw0 + u][lane];
+        // lane (m, g) gets O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P diag(ik) Delta)
+        const f32x4 oc0 = mma32(Db, pr0, qsT[u][0] * gm0) * iq0;
+        const f32x4 oc1 = mma32(Db, pr1, qsT[u][1] * gm1) * iq1;
+        bf16 *orow = p.o + (row * p.H_v + h) * DV + col0 + 16 * (cw0 + u) + 4 * g;
+        if (row < t1) *reinterpret_cast<bf16x4 *>(orow) = pack4(oc0);
+        if (row + 16 < t1) *reinterpret_cast<bf16x4 *>(orow + (int64_t)16 * p.H_v * DV) = pack4(oc1);
+      }
     }
     const int c = it - LAG;
     if (c >= 0 && c < nch) {
       const Stage &st = sm.st[c % NSTAGE];
       const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 Sb[4];
+      bf16x8 Sb[NT][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) Sb[kb] = sm.sb[c & 1][cw][kb][lane];
-      // qsT[mt]: (Q S)[16mt + m][4g + j]
-      qsT[0] = z;
-      qsT[1] = z;
+      for (int u = 0; u < NT; ++u) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Sb[u][kb] = sm.sb[c & 1][cw0 + u][kb][lane];
+        qsT[u][0] = z;
+        qsT[u][1] = z;
+      }
+      // qsT[u][mt]: (Q S)[16mt + m][4g + j]
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          qsT[mt] = mma32(Sb[kb], row_op_t(st.Q, 16 * mt + m, kb, g), qsT[mt]);
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 qop = row_op_t(st.Q, 16 * mt + m, kb, g);
+#pragma unroll
+          for (int u = 0; u < NT; ++u) qsT[u][mt] = mma32(Sb[u][kb], qop, qsT[u][mt]);
+        }
       }
+      // this chunk's output factors, for the next step
+      const Rec &rc = st.pp.r;
+      pr0 = rc.P[0][lane];
+      pr1 = rc.P[1][lane];
+      gm0 = rc.Gm[m];
+      gm1 = rc.Gm[16 + m];
+      iq0 = rc.iq[m];
+      iq1 = rc.iq[16 + m];
     }
     block_sync<63, false>();
   }
@@ -1119,9 +1215,9 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
   const int nsteps = nch + 3;
 
   if (wave >= W_C0 && wave < W_C0 + NC) {
-    state_wave<DV, SSD, 2>(p, sm, wave - W_C0, lane, nch, nsteps, state_off, col0);
+    state_wave<DV, SSD, 2, false, 1>(p, sm, wave - W_C0, lane, nch, nsteps, state_off, col0);
   } else if (wave >= W_O0 && wave < W_O0 + NC) {
-    output_wave<DV, 2>(p, sm, wave - W_O0, lane, nch, nsteps, t0, t1, h, col0);
+    output_wave<DV, 2, 1>(p, sm, wave - W_O0, lane, nch, nsteps, t0, t1, h, col0);
   } else if (wave == W_P0 || wave == W_P1) {
     // ---------------------------------------------------------------- prepare
     // Each step also reads the row operands of the next chunk (published
@@ -1141,7 +1237,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
         } else if (wave == W_P0) {
           prepare_T(pp, sm.p0x, ops, lane);
         } else {
-          prepare_P<true>(pp, ops, lane, p.eps, p.scale);
+          prepare_P<true>(pp, pp.gam, ops, lane, p.eps, p.scale);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS writes are done
@@ -1238,8 +1334,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunked_mfma_kernel(MfmaParams p)
 // A 32-bit word read from the L2, past the scalar cache (glc), complete when
 // the statement ends.  `p` is uniform across the wave.
 __device__ __forceinline__ uint32_t load_l2_u32(const uint32_t *p) {
+  // the address in scalar registers, whatever the compiler could prove
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint64_t sa = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
   uint32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sa) : "memory");
   return v;
 }
 // Wait until *p >= want; false, with the XCD's error word marked, if the
@@ -1256,21 +1356,43 @@ __device__ __forceinline__ bool wait_at_least(const uint32_t *p, uint32_t want, 
   return false;
 }
 
+// Wait until progress[r] >= want for every r < nc (nc <= 64): lane r reads
+// word r from the L2, all words in one round trip per poll.  Bounded as
+// wait_at_least.
+__device__ __forceinline__ bool progress_at_least(const uint32_t *progress, int nc, uint32_t want,
+                                                  int lane, uint32_t *err) {
+  for (int i = 0; i < SPIN_LIMIT; ++i) {
+    const uint32_t v = lane < nc ? __hip_atomic_load(&progress[lane], __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : want;
+    if (__ballot(v < want) == 0) return true;
+    if ((i & 63) == 63 && load_l2_u32(err) != 0u) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if ((threadIdx.x & 63) == 0) atomicOr(err, 1u);
+  return false;
+}
+
 __device__ __forceinline__ unsigned char *group_base(const MfmaParams &p, int grp) {
   return p.ws + WS_HEAD + (size_t)grp * p.grp_stride;
 }
 
 // Producer workgroup phi of group (n, hk): the records of chunks
 // c = phi, phi + PRODUCERS, ... for the gv value heads hk gv .. hk gv + gv - 1.
-// Waves j < gv form T of value head j and store its record, waves 3 + j its
-// P; waves 3 and 4 take the norms of k and q, wave 5 the loads (one chunk
-// ahead).  Three workgroup barriers per chunk.  A record's flag is set one
-// chunk later, after its stores have long reached the L2, so no wave waits
-// on its own stores; before storing a record into the slot of chunk
-// c - RING, its T wave checks (from progress words it fetched at the start of
-// the chunk) that every chain workgroup of the group has copied that chunk.
-__device__ void producer(const MfmaParams &p, unsigned char *smem, int grp, int phi, int gv,
-                         int nvb, uint32_t *err) {
+// Every wave works on its own from the chunk's rows: T wave j (wave j < gv)
+// takes value head j's gates, the norms of k and T, P wave j (wave 3 + j)
+// that head's decays, the norms of q, the cross Gram and P; the last wave
+// also loads the next chunk.  One workgroup barrier per chunk, after which the
+// rows of this chunk have landed and the records of the chunk before are
+// whole: T wave j then copies that record into its slot (16 bytes per lane,
+// not waited for) and forms this chunk's into the other record buffer.  A
+// record's flag is set one iteration after its copy, once its stores have long
+// reached the L2, so no wave waits on its own stores; before storing a record
+// into the slot of chunk c - RING, its T wave checks (from progress words it
+// fetched an iteration earlier, or by polling) that every chain workgroup of
+// the group has copied that chunk.
+__device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *smem, int grp, int phi,
+                                         int gv, int nvb, uint32_t *err) {
   ProdSmem &ps = *reinterpret_cast<ProdSmem *>(smem);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
@@ -1284,7 +1406,8 @@ __device__ void producer(const MfmaParams &p, unsigned char *smem, int grp, int 
   const uint32_t *progress = reinterpret_cast<const uint32_t *>(base + GRP_PROGRESS);
   unsigned char *recs = base + GRP_RECS;
   const RowOffsets ko = row_offsets(p.H_k, lane);
-  auto load = [&](int c, int buf) {  // wave 5: PROD_OPS loads
+  constexpr int LOADER = NWAVES_C - 1;
+  auto load = [&](int c, int buf) {  // PROD_OPS loads
     int64_t row0;
     int cl;
     rows_of(c, nch, t0, t1, row0, cl);
@@ -1302,29 +1425,68 @@ __device__ void producer(const MfmaParams &p, unsigned char *smem, int grp, int 
     for (int j = 0; j < MAX_GV; ++j)
       dma_ab(p.a, p.b, p.H_v, hk * gv + min(j, gv - 1), row0, cl, ps.ab[buf][j], lane);
   };
-  if (wave == 5 && phi < nch) load(phi, 0);
-  int prev = -1;  // T waves: the chunk whose record stores are in flight
+  const bool t_wave = wave < gv;
+  const int pj = wave - 3;
+  const bool p_wave = pj >= 0 && pj < gv;
+  const int j = t_wave ? wave : pj;  // value head of this wave's record part
+  const int h = hk * gv + j;
+  const float neg_exp_A = (t_wave || p_wave) ? -expf(p.A_log[h]) : 0.f;
+  const float dtb = (t_wave || p_wave) ? p.dt_bias[h] : 0.f;
+  // T waves: copy the record of chunk `prev` (formed in the last iteration)
+  // into its slot, after the slot check
+  auto copy_out = [&](int prev, int pbuf) {
+    if (prev >= RING) {
+      // the slot held chunk prev - RING: every chain workgroup must have copied it
+      const uint32_t need = (uint32_t)(prev - RING + 1);
+      const uint32_t seen = lds_read_u32_now(&ps.prg[j][lane]);
+      if (__ballot(seen < need) != 0) progress_at_least(progress, nc, need, lane, err);
+    }
+    const uint4 *src = reinterpret_cast<const uint4 *>(&ps.pp[pbuf][j].r);
+    uint4 *dst = reinterpret_cast<uint4 *>(recs + ((size_t)j * RING + prev % RING) * REC_BYTES);
+#pragma unroll
+    for (int i = 0; i < REC_DMAS; ++i) dst[64 * i + lane] = src[64 * i + lane];
+  };
+  if (wave == LOADER && phi < nch) load(phi, 0);
+  int prev = -1;    // T waves: the chunk formed in the last iteration
+  int stored = -1;  // T waves: the chunk whose record stores are in flight
   for (int c = phi, k = 0; c < nch; c += PRODUCERS, ++k) {
     const int buf = k & 1;
     const int64_t rem = t1 - (t0 + (int64_t)c * CH);
     const int cl = rem < CH ? (int)rem : CH;
-    if (wave == 5) {
-      if (c + PRODUCERS < nch) {
-        load(c + PRODUCERS, buf ^ 1);
-        vm_wait<PROD_OPS>();  // chunk c has landed
-      } else {
-        vm_wait<0>();
-      }
+    if (wave == LOADER || t_wave) {
+      // loader: chunk c has landed; T waves: the stores of `stored` and the
+      // progress words are done
+      vm_wait<0>();
+      if (t_wave && stored >= 0 && lane == 0) flags[j * RING + stored % RING] = (uint32_t)(stored + 1);
     }
     __syncthreads();
-    if (wave < gv) {
-      const int h = hk * gv + wave;
-      stage_gates<false>(ps.pp[wave], ps.ab[buf][wave], lane, cl, -expf(p.A_log[h]), p.dt_bias[h]);
-    } else if (wave == 3) {
-      tile_norms(ps.K[buf], ps.ikn, lane, cl, p.eps, 1.0f);
-    } else if (wave == 4) {
-      tile_norms(ps.Q[buf], ps.iqn, lane, cl, p.eps, p.scale);
-    } else if (wave == 5) {
+    if (wave == LOADER && c + PRODUCERS < nch) load(c + PRODUCERS, buf ^ 1);
+    if (t_wave) {
+      if (prev >= 0) {
+        copy_out(prev, buf ^ 1);
+        stored = prev;
+      } else {
+        stored = -1;
+      }
+      // progress words for the next iteration's slot check (past the L1)
+      if (c >= RING)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void *>(&progress[min(lane, nc - 1)]),
+            (__attribute__((address_space(3))) void *)(&ps.prg[j][0]), 4, 0, CPOL_DEVICE);
+      Prep &pp = ps.pp[buf][j];
+      stage_gates<false>(pp, ps.ab[buf][j], lane, cl, neg_exp_A, dtb);
+      tile_norms(ps.K[buf], pp.r.ik, lane, cl, p.eps, 1.0f);
+      wave_lds_sync();
+      RowOps ops;
+      read_row_ops<false>(ps.K[buf], ps.Q[buf], ops, m, g);
+      prepare_T(pp, ps.xs[j], ops, lane);
+      prev = c;
+    } else if (p_wave) {
+      Prep &pp = ps.pp[buf][j];
+      chunk_decays(ps.gp[j], ps.ab[buf][j], lane, cl, neg_exp_A, dtb);
+      tile_norms(ps.Q[buf], pp.r.iq, lane, cl, p.eps, p.scale);
+      RowOps ops;
+      read_row_ops<true>(ps.K[buf], ps.Q[buf], ops, m, g);
       // GX = K_c K_{c-1}^T: lane (n, g) of output tile (rb, cb) gets
       // (k_{c-1}[16 cb + 4g + j] . k_c[16 rb + n]) = GX[16 rb + n][16 cb + 4g + j],
       // which is its own A operand piece: tile rb, slots 8g + 4 cb + j
@@ -1333,58 +1495,29 @@ __device__ void producer(const MfmaParams &p, unsigned char *smem, int grp, int 
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const bf16x8 a0 = row_op(ps.Kp[buf], m, kb, g), a1 = row_op(ps.Kp[buf], 16 + m, kb, g);
-        const bf16x8 b0 = row_op(ps.K[buf], m, kb, g), b1 = row_op(ps.K[buf], 16 + m, kb, g);
-        gx[0][0] = mma32(a0, b0, gx[0][0]);
-        gx[0][1] = mma32(a1, b0, gx[0][1]);
-        gx[1][0] = mma32(a0, b1, gx[1][0]);
-        gx[1][1] = mma32(a1, b1, gx[1][1]);
+        gx[0][0] = mma32(a0, ops.k0[kb], gx[0][0]);
+        gx[0][1] = mma32(a1, ops.k0[kb], gx[0][1]);
+        gx[1][0] = mma32(a0, ops.k1[kb], gx[1][0]);
+        gx[1][1] = mma32(a1, ops.k1[kb], gx[1][1]);
       }
-      const bf16x8 t0p = pack8(gx[0][0], gx[0][1]), t1p = pack8(gx[1][0], gx[1][1]);
-      for (int j = 0; j < gv; ++j) {
-        ps.pp[j].r.GX[0][lane] = t0p;
-        ps.pp[j].r.GX[1][lane] = t1p;
-      }
-    }
-    __syncthreads();
-    RowOps ops;
-    if (wave < gv) {
-      Prep &pp = ps.pp[wave];
-      if (c >= RING)  // progress words, one per lane (past the L1)
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void *>(&progress[min(lane, nc - 1)]),
-            (__attribute__((address_space(3))) void *)(&ps.prg[wave][0]), 4, 0, 1);
-      if (lane < CH) {
-        pp.r.ik[lane] = ps.ikn[lane];
-        pp.r.iq[lane] = ps.iqn[lane];
-      }
+      pp.r.GX[0][lane] = pack8(gx[0][0], gx[0][1]);
+      pp.r.GX[1][lane] = pack8(gx[1][0], gx[1][1]);
       wave_lds_sync();
-      read_row_ops<false>(ps.K[buf], ps.Q[buf], ops, m, g);
-      prepare_T(pp, ps.xs[wave], ops, lane);
-    } else if (wave >= 3 && wave - 3 < gv) {
-      read_row_ops<true>(ps.K[buf], ps.Q[buf], ops, m, g);
-      prepare_P<false>(ps.pp[wave - 3], ops, lane, p.eps, p.scale);
-    }
-    __syncthreads();
-    if (wave < gv) {
-      vm_wait<0>();  // the previous record's stores and the progress words
-      if (prev >= 0 && lane == 0) flags[wave * RING + prev % RING] = (uint32_t)(prev + 1);
-      if (c >= RING) {
-        // the slot held chunk c - RING: every chain workgroup must have copied it
-        const uint32_t need = (uint32_t)(c - RING + 1);
-        const uint32_t seen = lds_read_u32_now(&ps.prg[wave][lane]);
-        if (__ballot(seen < need) != 0)
-          for (int r = 0; r < nc; ++r) wait_at_least(&progress[r], need, err);
-      }
-      // the record into its slot: 5 x 1 KB, 16 bytes per lane, not waited for
-      const uint4 *src = reinterpret_cast<const uint4 *>(&ps.pp[wave].r);
-      uint4 *dst = reinterpret_cast<uint4 *>(recs + ((size_t)wave * RING + c % RING) * REC_BYTES);
-#pragma unroll
-      for (int i = 0; i < REC_DMAS; ++i) dst[64 * i + lane] = src[64 * i + lane];
-      prev = c;
+      prepare_P<false>(pp, ps.gp[j], ops, lane, p.eps, p.scale);
     }
   }
-  vm_wait<0>();
-  if (wave < gv && prev >= 0 && lane == 0) flags[wave * RING + prev % RING] = (uint32_t)(prev + 1);
+  // the last record: whole after the barrier, stored, flagged once stored
+  __syncthreads();
+  if (t_wave) {
+    vm_wait<0>();
+    if (stored >= 0 && lane == 0) flags[j * RING + stored % RING] = (uint32_t)(stored + 1);
+    if (prev >= 0) {
+      const int nk = (nch - 1 - phi) / PRODUCERS + 1;  // iterations run
+      copy_out(prev, (nk - 1) & 1);
+      vm_wait<0>();
+      if (lane == 0) flags[j * RING + prev % RING] = (uint32_t)(prev + 1);
+    }
+  }
 }
 
 // Staging wave of a chain workgroup (cooperative kernel): k rows, the first
@@ -1420,7 +1553,7 @@ __device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, int 
     const int cc = min(c, nch - 1);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(&flag[cc % RING]),
                                      (__attribute__((address_space(3))) void *)(&sm.fl[c & 3][0]),
-                                     4, 0, 1);
+                                     4, 0, CPOL_DEVICE);
   };
   auto record = [&](int c, bool fetched) {  // REC_DMAS loads
     const int cc = min(c, nch - 1);
@@ -1494,11 +1627,13 @@ __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams 
       const int nsteps = nch + 3;  // state: chunk it-2, outputs: chunk it-3
       const size_t state_off = ((size_t)n * p.H_v + h) * DK * DV;
       const int col0 = vb * BV;
-      if (wave < NC) {
-        state_wave<DV, false, 2, true>(p, sm, wave, lane, nch, nsteps, state_off, col0,
-                                       reinterpret_cast<uint32_t *>(base + GRP_PROGRESS) + r);
+      if (wave < CW_O0) {
+        state_wave<DV, false, 2, true, 1>(p, sm, wave, lane, nch, nsteps, state_off, col0,
+                                          reinterpret_cast<uint32_t *>(base + GRP_PROGRESS) + r);
       } else if (wave < CW_ST0) {
-        output_wave<DV, 2>(p, sm, wave - CW_O0, lane, nch, nsteps, t0, t1, h, col0);
+        output_wave<DV, 2, 1>(p, sm, wave - CW_O0, lane, nch, nsteps, t0, t1, h, col0);
+      } else if (wave >= CW_KS0) {
+        ks_wave<2>(sm, wave - CW_KS0, lane, nch, nsteps);
       } else {
         coop_staging<DV>(p, sm, wave - CW_ST0, lane, nch, nsteps, t0, t1, hk, h, col0,
                          reinterpret_cast<const uint32_t *>(base + GRP_FLAGS) + j * RING,
