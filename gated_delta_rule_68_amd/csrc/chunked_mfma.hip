@@ -230,10 +230,12 @@ struct alignas(16) Rec {
   bf16x4 T0[64];       // rows 0..15: T11[m][4g..4g+3] (slots 8g+4.. are T12 = 0)
   bf16x8 T1[64];       // rows 16..31: T21[m][4g..4g+3], T22[m][4g..4g+3]
   bf16x8 P[2][64];     // P without 1/|k_i|: rows m, 16 + m at chunk slots 8g..
-  // cooperative kernel: the raw cross Gram K_c K_{c-1}^T of this chunk's k
-  // rows against the previous chunk's, as the A operand of K_c S_c =
-  // Gam_last(c-1) K_c S_{c-1} + GX D_{c-1} Delta_{c-1} (rows 16 mt + m, the
-  // previous chunk's positions in slot order)
+  // cooperative kernel: -diag(bgk) K_c K_{c-1}^T, the cross Gram of this
+  // chunk's raw k rows against the previous chunk's scaled by minus this
+  // chunk's bgk, as the A operand of its share of R: with K_c S_c =
+  // Gam_last(c-1) K_c S_{c-1} + (K_c K_{c-1}^T) D_{c-1} Delta_{c-1}, R gains
+  // GX D_{c-1} Delta_{c-1} (rows 16 mt + m, the previous chunk's positions
+  // in slot order)
   bf16x8 GX[2][64];
   float bt[CH];        // beta_r (0 past the end)
   float bgk[CH];       // beta_r Gam_r / |k_r|: the factor of (K S) in R
@@ -272,9 +274,9 @@ struct Smem {
     // row m of -A22 and row m of A21 (columns in the order 4j + g), 80-byte
     // rows so that 16 rows read at one column fill distinct 16-byte bank slots
     float p0x[3][16][20];
-    // cooperative kernel: K_{c+1} S_c from the K S waves to the state waves,
-    // per state wave, 16-row block and lane (ring by chunk)
-    f32x4 ksn[2][NC][2][64];
+    // cooperative kernel: the K S waves' part of R of a chunk, for the state
+    // waves, per state wave, 16-row block and lane (ring by chunk)
+    f32x4 rp[2][NC][2][64];
   };
   // cooperative kernel: flag words of chunks c, fetched ahead into word block c % 4
   alignas(16) uint32_t fl[4][64];
@@ -292,7 +294,9 @@ struct ProdSmem {
   alignas(16) uint32_t ab[2][MAX_GV][2 * CH];
   Prep pp[2][MAX_GV];
   alignas(16) float xs[MAX_GV][3][16][20];
-  alignas(16) float gp[MAX_GV][CH];      // P wave j: the chunk's cumulative log decay
+  alignas(16) float gp[MAX_GV][CH];      // P wave j: the chunk's cumulative log decay,
+  alignas(16) float bgm[MAX_GV][CH];     //   beta Gam
+  alignas(16) float ikp[MAX_GV][CH];     //   and 1/|k|
   alignas(16) uint32_t prg[MAX_GV][64];  // progress words, fetched by T wave j
 };
 
@@ -579,15 +583,22 @@ __device__ __forceinline__ void stage_gates(Prep &S, const uint32_t *ab, int lan
     S.r.cl = cl;
   }
 }
-// The cumulative log decay of one chunk's rows alone (a producer's P wave):
-// row r = lane % 32, into gam[r].
-__device__ __forceinline__ void chunk_decays(float *gam, const uint32_t *ab, int lane, int cl,
-                                             float neg_exp_A, float dtb) {
+// The cumulative log decay of one chunk's rows and beta_r Gam_r, formed as
+// stage_gates forms them (a producer's P wave): row r = lane % 32, into
+// gam[r] and bgm[r].
+__device__ __forceinline__ void chunk_decays(float *gam, float *bgm, const uint32_t *ab, int lane,
+                                             int cl, float neg_exp_A, float dtb) {
   const int r = lane & 31;
+  const bool valid = r < cl;
   const float a_r = __uint_as_float(lds_read_u32_now(&ab[r]) << 16) + dtb;
+  const float b_r = __uint_as_float(lds_read_u32_now(&ab[CH + r]) << 16);
   const float sp = fmaxf(a_r, 0.f) + fast_log(1.f + fast_exp(-fabsf(a_r)));
-  const float cum = scan32(r < cl ? neg_exp_A * sp : 0.f);
-  if (lane < 32) gam[r] = cum;
+  const float bt = valid ? __builtin_amdgcn_rcpf(1.f + fast_exp(-b_r)) : 0.f;
+  const float cum = scan32(valid ? neg_exp_A * sp : 0.f);
+  if (lane < 32) {
+    gam[r] = cum;
+    bgm[r] = bt * fast_exp(cum);
+  }
 }
 
 // The two substitution sweeps of P0, interleaved, 15 steps:
@@ -869,11 +880,13 @@ __device__ __forceinline__ void prepare_p_ssd(Prep &S, const RowOps &o, int lane
 // LOOK (cooperative kernel, LAG = 2): K S of a chunk is formed from the
 // update it depends on,
 //   K_{c+1} S_{c+1} = Gam_last(c) (K_{c+1} S_c) + (K_{c+1} K_c^T) (D_c Delta_c),
-// with the cross Gram from chunk c+1's record and K_{c+1} S_c formed by a K S
-// wave (ks_wave) in the step before, from the state handed over at chunk c's
-// entry.  The state wave then reads no k rows and runs no K S products: the
-// dependent chain of its step is the two products of the cross Gram, R, the
-// two of T R, D Delta and the update.
+// so that R of chunk c+1 splits into a part a K S wave (ks_wave) forms in the
+// step before, from v and from the state handed over at chunk c's entry,
+//   beta V - beta Gam ik Gam_last(c) (K_{c+1} S_c),
+// and one product with the record's cross Gram, scaled by -beta Gam ik on the
+// producer side.  The state wave then reads neither k rows nor v and runs no
+// K S products: the dependent chain of its step is the two products of the
+// cross Gram, the two of T R, D Delta and the update.
 template <int DV, bool SSD, int LAG, bool LOOK, int NT>
 __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw0, int lane,
                                            int nch, int nsteps, size_t state_off, int col0,
@@ -959,26 +972,37 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
       // this chunk's tiles and row factors
       const bf16x4 tt0 = rc.T0[lane];
       const bf16x8 tt1 = rc.T1[lane];
-      const f32x4 bt0 = ld4(&rc.bt[4 * g]), bt1 = ld4(&rc.bt[16 + 4 * g]);
-      const f32x4 bk0 = ld4(&rc.bgk[4 * g]), bk1 = ld4(&rc.bgk[16 + 4 * g]);
       const f32x4 ik0 = ld4(&rc.ik[4 * g]), ik1 = ld4(&rc.ik[16 + 4 * g]);
       const f32x4 tk0 = ld4(&rc.tk[4 * g]), tk1 = ld4(&rc.tk[16 + 4 * g]);
       const float gc = rc.Gc;
-      // ks[u][mt]: (K S)[16mt + 4g + j][m] of tile u
-      f32x4 ks[NT][2];
+      f32x4 bt0, bt1, bk0, bk1;  // not with LOOK
+      if constexpr (!LOOK) {
+        bt0 = ld4(&rc.bt[4 * g]);
+        bt1 = ld4(&rc.bt[16 + 4 * g]);
+        bk0 = ld4(&rc.bgk[4 * g]);
+        bk1 = ld4(&rc.bgk[16 + 4 * g]);
+      }
+      // Rr[u][mt]: R[16mt + 4g + j][m] of tile u,
+      //   R = beta V - beta Gam ik (K S), rows 4g..4g+3 and 16+4g..16+4g+3
+      f32x4 Rr[NT][2];
       if constexpr (LOOK) {
-        // K_c S_{c-1} (K_0 S_0 for the first chunk) from the K S wave
+        // the K S wave's beta V - beta Gam ik Gam_last(c-1) (K_c S_{c-1}) (all
+        // of R for the first chunk), plus the record's -diag(beta Gam ik) K_c
+        // K_{c-1}^T times D_{c-1} Delta_{c-1}
         const bf16x8 gx0 = rc.GX[0][lane], gx1 = rc.GX[1][lane];
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
-          ks[u][0] = sm.ksn[c & 1][cw0 + u][0][lane];
-          ks[u][1] = sm.ksn[c & 1][cw0 + u][1][lane];
+          Rr[u][0] = sm.rp[c & 1][cw0 + u][0][lane];
+          Rr[u][1] = sm.rp[c & 1][cw0 + u][1][lane];
           if (c > 0) {
-            ks[u][0] = mma32(gx0, dpp[u], ks[u][0] * gcp);
-            ks[u][1] = mma32(gx1, dpp[u], ks[u][1] * gcp);
+            Rr[u][0] = mma32(gx0, dpp[u], Rr[u][0]);
+            Rr[u][1] = mma32(gx1, dpp[u], Rr[u][1]);
           }
         }
-      } else {
+      }
+      // ks[u][mt]: (K S)[16mt + 4g + j][m] of tile u (not with LOOK)
+      f32x4 ks[NT][2];
+      if constexpr (!LOOK) {
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
           ks[u][0] = z;
@@ -986,7 +1010,7 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
           if constexpr (!SSD) k_times_s(u, ks[u]);
         }
       }
-      // Gam_last S while the matrix cores run K S
+      // Gam_last S while the matrix cores run
 #pragma unroll
       for (int u = 0; u < NT; ++u)
 #pragma unroll
@@ -994,16 +1018,19 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
       __builtin_amdgcn_sched_barrier(0);
       read_kt(st);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!LOOK) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            Rr[u][0][j] = bt0[j] * (float)vv[u][j] - bk0[j] * ks[u][0][j];
+            Rr[u][1][j] = bt1[j] * (float)vv[u][4 + j] - bk1[j] * ks[u][1][j];
+          }
+      }
       bf16x8 Dp[NT];
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
-        // R = beta V - beta Gam ik (K S), rows 4g..4g+3 and 16+4g..16+4g+3
-        f32x4 R0, R1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          R0[j] = bt0[j] * (float)vv[u][j] - bk0[j] * ks[u][0][j];
-          R1[j] = bt1[j] * (float)vv[u][4 + j] - bk1[j] * ks[u][1][j];
-        }
+        const f32x4 R0 = Rr[u][0], R1 = Rr[u][1];
         // Delta = T R, both 16-row blocks from the one bf16 operand of R in
         // slot order; SSD: no erase, Delta = R
         f32x4 d1 = R0, d2 = R1;
@@ -1041,8 +1068,10 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
       // registers directly and stay in flight across the barrier: k rows
       // (not with LOOK) and v of chunk c + 1
       const Stage &sr = sm.st[max(min(c + 1, nch - 1), 0) % NSTAGE];
-      if constexpr (!SSD && !LOOK) read_rows(sr);
-      read_v(sr);
+      if constexpr (!LOOK) {
+        if constexpr (!SSD) read_rows(sr);
+        read_v(sr);
+      }
     }
     // no wait for the reads in flight: their buffers are refilled only
     // steps later, and their registers are waited for where they are used
@@ -1061,9 +1090,11 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
 }
 
 // K S wave of tile cw (cooperative kernel, alongside a LOOK state wave): in
-// step it, K_{it-1} S_{it-2} (K_0 S_0 in step 1) from the state the state wave
-// handed over at the entry of chunk it - 2 (0), for the state wave's step
-// it + 1.  Passes nsteps + 1 barriers.
+// step it, for chunk c = it - 1, the part of R that does not wait for the
+// previous chunk's Delta,
+//   beta V - beta Gam ik Gam_last(c-1) (K_c S_{c-1})   (beta V - beta Gam ik K_0 S_0 for c = 0),
+// from the state the state wave handed over at the entry of chunk c - 1 (0),
+// for the state wave's step it + 1.  Passes nsteps + 1 barriers.
 template <int LAG>
 __device__ __forceinline__ void ks_wave(Smem &sm, int cw, int lane, int nch, int nsteps) {
   static_assert(LAG == 2, "the state wave runs chunk it - 2 in step it");
@@ -1071,10 +1102,11 @@ __device__ __forceinline__ void ks_wave(Smem &sm, int cw, int lane, int nch, int
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   block_sync();
   for (int it = 0; it < nsteps; ++it) {
-    const int cn = it - 1;  // the chunk whose rows multiply the state
+    const int cn = it - 1;  // the chunk whose R is prepared
     if (cn >= 0 && cn < nch) {
       const int cs = max(it - 2, 0);  // the state's chunk
       const Stage &st = sm.st[cn % NSTAGE];
+      const Rec &rc = st.pp.r;
       f32x4 acc[2] = {z, z};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -1082,8 +1114,20 @@ __device__ __forceinline__ void ks_wave(Smem &sm, int cw, int lane, int nch, int
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) acc[mt] = mma32(row_op_t(st.K, 16 * mt + m, kb, g), sb, acc[mt]);
       }
-      sm.ksn[cn & 1][cw][0][lane] = acc[0];
-      sm.ksn[cn & 1][cw][1][lane] = acc[1];
+      // v[4g + j][col] and v[16 + 4g + j][col]
+      const int vr = 4 * g + (m >> 2), vc = 16 * cw + 4 * (m & 3);
+      const bf16x8 vv = cat8(tr_read(st.V + v_off(vr, vc)), tr_read(st.V + v_off(16 + vr, vc)));
+      const float gcp = cn > 0 ? sm.st[(cn - 1) % NSTAGE].pp.r.Gc : 1.0f;
+      const f32x4 bt0 = ld4(&rc.bt[4 * g]), bt1 = ld4(&rc.bt[16 + 4 * g]);
+      const f32x4 bk0 = ld4(&rc.bgk[4 * g]) * gcp, bk1 = ld4(&rc.bgk[16 + 4 * g]) * gcp;
+      f32x4 r0, r1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        r0[j] = bt0[j] * (float)vv[j] - bk0[j] * acc[0][j];
+        r1[j] = bt1[j] * (float)vv[4 + j] - bk1[j] * acc[1][j];
+      }
+      sm.rp[cn & 1][cw][0][lane] = r0;
+      sm.rp[cn & 1][cw][1][lane] = r1;
     }
     block_sync<63, true>();
   }
@@ -1483,7 +1527,8 @@ __device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *sme
       prev = c;
     } else if (p_wave) {
       Prep &pp = ps.pp[buf][j];
-      chunk_decays(ps.gp[j], ps.ab[buf][j], lane, cl, neg_exp_A, dtb);
+      chunk_decays(ps.gp[j], ps.bgm[j], ps.ab[buf][j], lane, cl, neg_exp_A, dtb);
+      tile_norms(ps.K[buf], ps.ikp[j], lane, cl, p.eps, 1.0f);
       tile_norms(ps.Q[buf], pp.r.iq, lane, cl, p.eps, p.scale);
       RowOps ops;
       read_row_ops<true>(ps.K[buf], ps.Q[buf], ops, m, g);
@@ -1500,8 +1545,12 @@ __device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *sme
         gx[1][0] = mma32(a0, ops.k1[kb], gx[1][0]);
         gx[1][1] = mma32(a1, ops.k1[kb], gx[1][1]);
       }
-      pp.r.GX[0][lane] = pack8(gx[0][0], gx[0][1]);
-      pp.r.GX[1][lane] = pack8(gx[1][0], gx[1][1]);
+      wave_lds_sync();  // bgm and ikp
+      // rows scaled by -bgk = -(beta Gam) / |k|, as the T wave forms bgk
+      const float s0 = -(ps.bgm[j][m] * ps.ikp[j][m]);
+      const float s1 = -(ps.bgm[j][16 + m] * ps.ikp[j][16 + m]);
+      pp.r.GX[0][lane] = pack8(gx[0][0] * s0, gx[0][1] * s0);
+      pp.r.GX[1][lane] = pack8(gx[1][0] * s1, gx[1][1] * s1);
       wave_lds_sync();
       prepare_P<false>(pp, ps.gp[j], ops, lane, p.eps, p.scale);
     }
