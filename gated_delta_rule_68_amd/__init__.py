@@ -39,6 +39,7 @@ import torch
 __all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", "chunked_path", "conv_silu",
            "chunked_workspace", "chunked_workspace_bytes", "workspace_error",
            "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version",
+           "chunked_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
            "ssd_recurrent_fwd", "ssd_chunked_fwd", "kda_recurrent_fwd", "kda_chunked_fwd",
            "kda_chunked_fwd_split"]
 
@@ -82,6 +83,8 @@ def _bind(lib):
     lib.gdr_recurrent_fwd.restype = ctypes.c_int
     lib.gdr_chunked_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
     lib.gdr_chunked_fwd.restype = ctypes.c_int
+    lib.gdr_chunked_fwd_noalloc.argtypes = [sp] + [vp] * 10 + [vp]
+    lib.gdr_chunked_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_chunked_workspace_bytes.argtypes = [sp]
     lib.gdr_chunked_workspace_bytes.restype = ctypes.c_size_t
     lib.gdr_status_string.argtypes = [ctypes.c_int]
@@ -334,6 +337,21 @@ def chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32, 
     return _fwd("gdr_chunked_fwd", q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens,
                 num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state, inplace,
                 workspace=workspace)
+
+
+def chunked_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32,
+                        cu_seqlens=None, num_seqs=None, scale=None, l2_eps=1e-6, o=None,
+                        final_state=None, output_final_state=True, inplace=False):
+    """gdr_chunked_fwd_noalloc: the chunked form with the library's own
+    per-device scratch as its cooperative workspace (no device allocation in
+    the library; pass ``o`` and ``final_state`` to allocate nothing here
+    either)."""
+    return _fwd("gdr_chunked_fwd_noalloc", q, k, v, a, b, A_log, dt_bias, initial_state,
+                cu_seqlens, num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state,
+                inplace)
+
+
+NOALLOC_SCRATCH_BYTES = 6 << 20  # GDR_NOALLOC_SCRATCH_BYTES
 
 
 def chunked_workspace_bytes(H_k, H_v, d_k, d_v, dtype, num_seqs=1, chunk=32) -> int:

@@ -1,9 +1,17 @@
 // C-ABI entry points: synchronous validation, then dispatch to a kernel
 // family.  Nothing here allocates, frees or synchronises.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "gdr_internal.h"
+
+// The workspace of gdr_chunked_fwd_noalloc: one copy in each GPU's memory,
+// zero at load, held until the process ends.  Host code never uses this name
+// as an address (on the host it is only a handle): the device address comes
+// from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
 
 namespace gdr {
 namespace {
@@ -122,6 +130,35 @@ gdr_status check_workspace(const Problem &pr, const FwdArgs &x, const void *work
   return GDR_OK;
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call per device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+gdr_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GDR_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return GDR_ERR_UNSUPPORTED;
+  void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return GDR_ERR_LAUNCH;
+      }
+      scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GDR_OK;
+}
+
 }  // namespace
 }  // namespace gdr
 
@@ -218,6 +255,36 @@ gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
       st = check_workspace(pr, x, workspace, workspace_bytes, need);
       if (st != GDR_OK) return st;
       if (launch_chunked_coop(pr, x, workspace, stream) == hipSuccess) return GDR_OK;
+      (void)hipGetLastError();  // a refused cooperative launch: run the fused kernel
+    }
+    return launched(launch_chunked_mfma(pr, x, stream));
+  }
+  if (!chunked_vec_supports(pr)) return GDR_ERR_UNSUPPORTED;
+  return launched(launch_chunked_vec(pr, x, stream));
+}
+
+gdr_status gdr_chunked_fwd_noalloc(const gdr_shape *shape, const void *q, const void *k,
+                                   const void *v, const void *a, const void *b,
+                                   const float *A_log, const float *dt_bias,
+                                   const float *initial_state, void *o, float *final_state,
+                                   hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
+  FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
+  st = check_fwd(pr, x);
+  if (st != GDR_OK) return st;
+  if (chunked_mfma_supports(pr)) {
+    const size_t need = chunked_coop_workspace_bytes(pr);
+    if (need > GDR_NOALLOC_SCRATCH_BYTES) return GDR_ERR_WORKSPACE;
+    if (need > 0 && pr.total > 0) {
+      void *ws = nullptr;
+      st = scratch_of_current_device(&ws);
+      if (st != GDR_OK) return st;
+      if (clear_chunked_coop(pr, ws, stream) != hipSuccess) return GDR_ERR_LAUNCH;
+      if (launch_chunked_coop(pr, x, ws, stream) == hipSuccess) return GDR_OK;
       (void)hipGetLastError();  // a refused cooperative launch: run the fused kernel
     }
     return launched(launch_chunked_mfma(pr, x, stream));

@@ -1844,6 +1844,27 @@ size_t chunked_coop_workspace_bytes(const Problem &pr) {
   return c.ok ? c.bytes : 0;
 }
 
+// Block g < groups clears group g's flags and progress words, block `groups`
+// the per-XCD lines.
+__global__ __launch_bounds__(128) void clear_coop_kernel(unsigned char *ws, int groups,
+                                                         size_t grp_stride) {
+  static_assert(GRP_RECS == 128 * 4 && WS_HEAD == 128 * 16, "one store per thread");
+  const int b = blockIdx.x;
+  if (b < groups) {
+    reinterpret_cast<uint32_t *>(ws + WS_HEAD + (size_t)b * grp_stride)[threadIdx.x] = 0u;
+  } else {
+    reinterpret_cast<uint4 *>(ws)[threadIdx.x] = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+hipError_t clear_chunked_coop(const Problem &pr, void *ws, hipStream_t s) {
+  const CoopPlan c = coop_plan(pr);
+  if (!c.ok) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(clear_coop_kernel, dim3((unsigned)(c.groups + 1)), dim3(128), 0, s,
+                     static_cast<unsigned char *>(ws), c.groups, c.grp_stride);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunked_coop(const Problem &pr, const FwdArgs &x, void *ws, hipStream_t s) {
   const CoopPlan c = coop_plan(pr);
   if (!c.ok) return hipErrorInvalidValue;

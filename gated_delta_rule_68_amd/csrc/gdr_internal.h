@@ -103,6 +103,10 @@ bool chunked_mfma_supports(const Problem &p);
 size_t chunked_coop_workspace_bytes(const Problem &p);
 hipError_t launch_chunked_coop(const Problem &p, const FwdArgs &x, void *workspace,
                                hipStream_t s);
+// Zero, on stream s, what launch_chunked_coop needs zero in a workspace of
+// chunked_coop_workspace_bytes(p) bytes (its counters, error words, flags and
+// progress words; not the records), with a fill kernel.
+hipError_t clear_chunked_coop(const Problem &p, void *workspace, hipStream_t s);
 // KDA chunked form in two launches (per-chunk operands for every chunk of the
 // batch into a workspace, then the chains): bf16, d_k = 128, d_v a multiple
 // of 16, chunk 32.  kda_two_pass_bytes is 0 for other shapes.

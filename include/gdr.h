@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 8
+#define GDR_ABI_VERSION 9
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -173,6 +173,35 @@ GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const 
  * no cooperative path (or is invalid), else a size that depends on num_seqs,
  * H_k, H_v and d_v but not on the sequence lengths. */
 GDR_API size_t gdr_chunked_workspace_bytes(const gdr_shape *shape);
+
+/* Size of the scratch array gdr_chunked_fwd_noalloc uses as its workspace. */
+#define GDR_NOALLOC_SCRATCH_BYTES (6u << 20)
+
+/*
+ * gdr_chunked_fwd_noalloc -- gdr_chunked_fwd for callers that cannot allocate
+ * device memory: code under stream capture, tight serving loops, harnesses
+ * that forbid allocation.  The call allocates and frees nothing.  Its
+ * cooperative workspace is the library's own scratch array of
+ * GDR_NOALLOC_SCRATCH_BYTES bytes in each GPU's memory, held until the
+ * process ends.  Arguments, results and errors as gdr_chunked_fwd without the
+ * workspace arguments, plus:
+ *   - a shape whose cooperative workspace (gdr_chunked_workspace_bytes)
+ *     exceeds GDR_NOALLOC_SCRATCH_BYTES returns GDR_ERR_WORKSPACE and runs
+ *     nothing;
+ *   - a shape with no cooperative path runs what gdr_chunked_fwd runs without
+ *     a workspace;
+ *   - the first call on a device looks up that device's copy of the array
+ *     (the device must be current); failure is GDR_ERR_LAUNCH;
+ *   - each call clears the array's counters and flags on `stream` before its
+ *     launch (a small fill kernel, no memset);
+ *   - all calls on one GPU share that GPU's array: calls that overlap in time
+ *     on one GPU (other streams, other threads) race.
+ */
+GDR_API gdr_status gdr_chunked_fwd_noalloc(const gdr_shape *shape, const void *q, const void *k,
+                                           const void *v, const void *a, const void *b,
+                                           const float *A_log, const float *dt_bias,
+                                           const float *initial_state, void *o,
+                                           float *final_state, hipStream_t stream);
 
 /*
  * gdr_conv_silu -- the short causal convolution and SiLU that turn the in_proj

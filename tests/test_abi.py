@@ -30,7 +30,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_split",
+    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_noalloc",
+                                  "gdr_chunked_fwd_split",
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_chunked_workspace_bytes",
                                   "gdr_conv_silu", "gdr_gated_rmsnorm", "gdr_gates",
@@ -457,3 +458,31 @@ def test_chunked_workspace_checked(gdr):
     assert f(ctypes.byref(s), *p, fake(10), need - 1, None) == 5        # too small
     assert f(ctypes.byref(s), *p, fake(10, off=16), need, None) == 4    # not 256-byte aligned
     assert f(ctypes.byref(s), *p, fake(0, off=256), need, None) == 7    # over q
+
+
+# ------------------------------------------ the allocation-free chunked entry point
+def test_noalloc_validates_like_chunked(gdr):
+    fn = "gdr_chunked_fwd_noalloc"
+    assert call(gdr, fn, None) == 1
+    assert call(gdr, fn, shape(gdr, H_v=3, H_k=2)) == 2
+    assert call(gdr, fn, shape(gdr, chunk=48)) == 3
+    p = [fake(i) for i in range(10)]
+    p[8] = fake(0)  # o on top of q
+    assert call(gdr, fn, shape(gdr), p) == 7
+
+
+def test_noalloc_scratch_limit(gdr):
+    """The scratch holds the prefill layer's cooperative workspace (16 key
+    heads, 48 value heads, one sequence); a shape that needs more is refused
+    with GDR_ERR_WORKSPACE before anything runs."""
+    m = re.search(r"#define GDR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == gdr.NOALLOC_SCRATCH_BYTES
+    prefill = dict(dtype=1, d_k=128, d_v=128, chunk=32, H_k=16, H_v=48, num_seqs=1,
+                   seq_len=8192, total_tokens=8192)
+    assert 0 < chunked_ws_bytes(gdr, **prefill) <= limit
+    big = dict(dtype=1, d_k=128, d_v=64, chunk=32, H_k=24, H_v=72, num_seqs=1, seq_len=64,
+               total_tokens=64)
+    assert chunked_ws_bytes(gdr, **big) > limit
+    far = [ctypes.c_void_p(BASE + i * 0x4000000) for i in range(10)]  # 64 MiB apart: no alias
+    assert call(gdr, "gdr_chunked_fwd_noalloc", shape(gdr, **big), far) == 5
