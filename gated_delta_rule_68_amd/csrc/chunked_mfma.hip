@@ -127,7 +127,6 @@ constexpr int CST1_OPS = 8 + 1;             // q rows, half of v
 constexpr int PRODUCERS = 4;              // producer workgroups per group
 constexpr int RING = 16;                  // record slots per value head
 constexpr int MAX_GV = 3;                 // value heads per key head on this path
-constexpr int PROD_OPS = 8 + 8 + 8 + MAX_GV;  // a producer's loads per chunk: k, q, previous k rows, a and b
 constexpr int XCD_CUS = 32;               // compute units per XCD on gfx950
 constexpr int MAX_XCD = 16;
 constexpr int SPIN_LIMIT = 1 << 20;       // polls before a wait gives up (well under a second)
@@ -353,10 +352,15 @@ __device__ __forceinline__ bf16x8 row_op(const bf16 *X, int r, int kb, int g) {
   return *reinterpret_cast<const bf16x8 *>(X + kq_off(r, 32 * kb + 8 * g));
 }
 // The same columns in tile order (see state_operand): the operand of a
-// product with the state.
+// product with the state.  The two 8-byte halves are read separately, each
+// from the address its lane needs, rather than exchanged in registers
+// afterwards; the reads stay free of bank conflicts (in each pass of 32
+// lanes, lanes of even g take the lower halves of 16 distinct pieces and
+// lanes of odd g the upper halves of 16 others).
 __device__ __forceinline__ bf16x8 row_op_t(const bf16 *X, int r, int kb, int g) {
-  const bf16x8 x = row_op(X, r, kb, g);
-  return (g & 1) ? __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3) : x;
+  const bf16 *p = X + kq_off(r, 32 * kb + 8 * g);
+  const int sw = (g & 1) * 4;  // elements
+  return cat8(*reinterpret_cast<const bf16x4 *>(p + sw), *reinterpret_cast<const bf16x4 *>(p + (sw ^ 4)));
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
@@ -912,12 +916,12 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
     for (int kb = 0; kb < 4; ++kb) Sb[u][kb] = state_operand(S[u][2 * kb], S[u][2 * kb + 1]);
   }
   // LDS operands: the k^T tiles of this chunk (A operands of the state
-  // update) are read once the first products are issued; the k rows of the
-  // next chunk (A operands of K S; not with LOOK) and its v are read after the
-  // state update, so that they are in registers when the next step starts.
+  // update) are read once the first products are issued, with LOOK at the
+  // end of the step before; the k rows of the next chunk (A operands of K S;
+  // not with LOOK) and its v are read after the state update, so that they
+  // are in registers when the next step starts.
   bf16x8 Kr[2][4], Kt[8], vv[NT];
   bf16x8 dpp[NT];       // LOOK: D_c Delta_c of the chunk before
-  float gcp = 1.0f;     // LOOK: Gam_last of the chunk before
 #pragma unroll
   for (int u = 0; u < NT; ++u) dpp[u] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
   auto read_rows = [&](const Stage &sn) {
@@ -1016,7 +1020,7 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
 #pragma unroll
         for (int t = 0; t < 8; ++t) S[u][t] *= gc;
       __builtin_amdgcn_sched_barrier(0);
-      read_kt(st);
+      if constexpr (!LOOK) read_kt(st);  // LOOK: read at the end of the step before
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!LOOK) {
 #pragma unroll
@@ -1046,7 +1050,6 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
       if constexpr (LOOK) {
 #pragma unroll
         for (int u = 0; u < NT; ++u) dpp[u] = Dp[u];
-        gcp = gc;
       }
       // S <- Gam_last S + K^T diag(tail ik) Delta
 #pragma unroll
@@ -1065,12 +1068,14 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
     {
       // operands of the next step, read unconditionally (the chunk index
       // clamped into the sequence) so that the loads write the loop's
-      // registers directly and stay in flight across the barrier: k rows
-      // (not with LOOK) and v of chunk c + 1
+      // registers directly and stay in flight across the barrier: of chunk
+      // c + 1, the k rows and v, or with LOOK the k^T tiles
       const Stage &sr = sm.st[max(min(c + 1, nch - 1), 0) % NSTAGE];
       if constexpr (!LOOK) {
         if constexpr (!SSD) read_rows(sr);
         read_v(sr);
+      } else {
+        read_kt(sr);
       }
     }
     // no wait for the reads in flight: their buffers are refilled only
@@ -1451,7 +1456,7 @@ __device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *sme
   unsigned char *recs = base + GRP_RECS;
   const RowOffsets ko = row_offsets(p.H_k, lane);
   constexpr int LOADER = NWAVES_C - 1;
-  auto load = [&](int c, int buf) {  // PROD_OPS loads
+  auto load = [&](int c, int buf) {  // 8 + 8 + 8 + MAX_GV loads: k, q, previous k rows, a and b
     int64_t row0;
     int cl;
     rows_of(c, nch, t0, t1, row0, cl);
