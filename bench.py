@@ -30,6 +30,7 @@ METRIC = "prefill tokens/s (T=8192, 48 heads) + decode HBM GB/s, % of roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
+PREFILL_KERNEL = "chunked_coop_kernel"  # the prefill launch with a workspace
 
 
 def prefill_flops(T, H_k, H_v, d_k, d_v, C):
@@ -100,10 +101,14 @@ def main():
     T, N = w.total_tokens, 1
     o = torch.empty((T, w.H_v, w.d_v), dtype=w.torch_dtype, device=dev)
     S = torch.empty((N, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    # the cooperative form's workspace, allocated (zero-filled) once and kept
+    # across launches, as a caller would
+    ws = gdr.chunked_workspace(w.H_k, w.H_v, w.d_k, w.d_v, w.dtype, N, chunk=w.chunk, device=dev)
 
-    def prefill_step():
+    def prefill_step(workspace=ws):
         gdr.chunked_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"],
-                        inp["dt_bias"], None, chunk=w.chunk, num_seqs=1, o=o, final_state=S)
+                        inp["dt_bias"], None, chunk=w.chunk, num_seqs=1, o=o, final_state=S,
+                        workspace=workspace)
 
     for _ in range(args.warmup):
         prefill_step()
@@ -126,6 +131,36 @@ def main():
     pbytes = prefill_bytes(T, N, w.H_k, w.H_v, w.d_k, w.d_v, 2, s0=False)
     avg_s = (sum(per_launch_ms) / len(per_launch_ms)) / 1e3
     achieved_tf = flops / avg_s / 1e12
+    ws_error = gdr.workspace_error(ws) if ws is not None else 0
+    if ws_error:
+        raise RuntimeError(f"cooperative prefill: workspace error word {ws_error:#x}")
+
+    # the same launch with every cache cold: a 1 GiB write before each one
+    # evicts the L2s and the last-level cache
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold_ms = []
+    for i in range(5):
+        flush.fill_(float(i))
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ce[0].record(stream)
+        prefill_step()
+        ce[1].record(stream)
+        torch.cuda.synchronize(dev)
+        cold_ms.append(ce[0].elapsed_time(ce[1]))
+    del flush
+    # the one-launch form (no workspace: every chain workgroup forms its own
+    # triangular inverses), for comparison
+    for _ in range(10):
+        prefill_step(None)
+    torch.cuda.synchronize(dev)
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    fe[0].record(stream)
+    for _ in range(10):
+        prefill_step(None)
+    fe[1].record(stream)
+    torch.cuda.synchronize(dev)
+    fused_ms = fe[0].elapsed_time(fe[1]) / 10
+    mfma_probe = mfma_rate_probe(gdr, dev, stream)
 
     # ------------------------------------------------------------ decode
     wd = synth.workload("decode")
@@ -198,20 +233,7 @@ def main():
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        heads = max(1, min(args.cpu_heads, w.H_v))
-        threads = min(16, os.cpu_count() or 1)
-        q64, k64, v64, a64, b64 = (oracle.f64(inp[x]) for x in ("q", "k", "v", "a", "b"))
-        A64, D64 = oracle.f64(inp["A_log"]), oracle.f64(inp["dt_bias"])
-        pairs = [(0, h) for h in range(heads)]
-        c0 = time.perf_counter()
-        oracle.fwd(q64, k64, v64, a64, b64, A64, D64, num_seqs=1, pairs=pairs, n_threads=threads)
-        c_s = time.perf_counter() - c0
-        layer_s = c_s * w.H_v / heads
-        cpu = {"value": T / layer_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"fp64 sequential oracle on {heads} of {w.H_v} value heads x {T} tokens "
-                         f"of the prefill workload ({c_s:.1f} s wall), scaled to the "
-                         f"{w.H_v}-head layer"}
+        cpu = cpu_baseline(w, inp, T, args.cpu_heads)
 
     line = {
         "metric": METRIC,
@@ -232,10 +254,17 @@ def main():
                    "chunk": w.chunk},
         "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
-                     "traffic": profiled_traffic("chunked_mfma_kernel"),
-                     "mfma_busy": profiled_traffic("chunked_mfma_kernel", "mfma_busy_frac"),
-                     "kernel": "chunked prefill", "flop_per_launch": flops,
+                     "traffic": profiled_traffic(PREFILL_KERNEL),
+                     "kernel": PREFILL_KERNEL if ws is not None else "chunked_mfma_kernel",
+                     "flop_per_launch": flops,
                      "avg_launch_ms": avg_s * 1e3,
+                     "cold_cache_launch_ms": sum(cold_ms) / len(cold_ms),
+                     "one_launch_form_ms": fused_ms,
+                     "measured_mfma_peak": mfma_probe,
+                     "mfma_busy_profiled": {
+                         "value": profiled_traffic(PREFILL_KERNEL, "mfma_busy_frac"),
+                         "source": "profiles/traffic.json: hardware counters of a profiled run "
+                                   "of this kernel's sources, not of this run"},
                      "hbm_view": {"bytes_per_launch": pbytes,
                                   "achieved_GBs": pbytes / avg_s / 1e9,
                                   "frac": pbytes / avg_s / 1e9 / PEAK_HBM_GBS}},
@@ -606,6 +635,116 @@ def kda_legs(gdr, dev, stream, steps):
                                 "frac": var_flops / (var_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                                 "flop_per_launch": var_flops}},
     }
+
+
+def mfma_rate_probe(gdr, dev, stream):
+    """The dense bf16 matrix-core rate this GPU sustains on back-to-back
+    independent v_mfma_f32_16x16x32_bf16 (libgdr_probe.so), in TFLOP/s, beside
+    the published peak."""
+    import ctypes
+    import torch
+    path = os.path.join(os.path.dirname(gdr.library_path()), "libgdr_probe.so")
+    if not os.path.exists(path):
+        return None
+    probe = ctypes.CDLL(path)
+    probe.gdr_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.gdr_probe_mfma_bf16.restype = ctypes.c_int
+    probe.gdr_probe_mfma_bf16_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.gdr_probe_mfma_bf16_flop.restype = ctypes.c_double
+    blocks, iters, reps = 1024, 2000, 5  # four workgroups of four waves per CU
+    out = torch.empty(blocks, dtype=torch.float32, device=dev)
+    h = ctypes.c_void_p(stream.cuda_stream)
+    for _ in range(2):
+        if probe.gdr_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), h) != 0:
+            return None
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        probe.gdr_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), h)
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    s = ev[0].elapsed_time(ev[1]) / reps / 1e3
+    tf = probe.gdr_probe_mfma_bf16_flop(blocks, iters) / s / 1e12
+    return {"value": tf, "unit": "TFLOP/s", "frac_of_published": tf / PEAK_BF16_TFLOPS,
+            "kernel": "independent v_mfma_f32_16x16x32_bf16, 8 accumulators a wave, "
+                      "16 waves a CU"}
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, inp, T, cpu_heads):
+    """The fp64 oracle timed on this host: the prefill layer (the bench
+    workload) on `threads` threads, plus every configuration's oracle time
+    (bounded samples, scaled) and 1-thread times for configurations 1-3."""
+    import oracle
+    import synth
+    # one GPU's share of the host: the GPU boxes give 16 cores to a GPU,
+    # whatever the machine's count
+    threads = min(16, os.cpu_count() or 1)
+
+    def run(wl, x, pairs=None, n_threads=threads, dense=None):
+        src = dense if dense is not None else x
+        q, k, v, a, b = (oracle.f64(src[n]) for n in ("q", "k", "v", "a", "b"))
+        A, D = oracle.f64(x["A_log"]), oracle.f64(x["dt_bias"])
+        s0 = None if x["initial_state"] is None else oracle.f64(x["initial_state"])
+        cu = x["cu_host"] if x["cu_seqlens"] is not None else None
+        N = len(x["cu_host"]) - 1
+        t0 = time.perf_counter()
+        if dense is not None:
+            oracle.fwd(q, k, v, a, b, A, D, initial_state=s0, num_seqs=N, pairs=pairs,
+                       n_threads=n_threads)
+        else:
+            oracle.fwd(q, k, v, a, b, A, D, initial_state=s0, cu_seqlens=cu,
+                       num_seqs=None if cu else N, pairs=pairs, n_threads=n_threads)
+        return time.perf_counter() - t0
+
+    heads = max(1, min(cpu_heads, w.H_v))
+    pairs = [(0, h) for h in range(heads)]
+    c_s = run(w, inp, pairs)
+    layer_s = c_s * w.H_v / heads
+    table = []
+
+    def entry(name, wl, x, n_threads, frac_pairs=1.0, dense=None, tokens=None):
+        N = len(x["cu_host"]) - 1
+        all_pairs = [(n, h) for n in range(N) for h in range(wl.H_v)]
+        npairs = max(1, int(round(len(all_pairs) * frac_pairs)))
+        sel = all_pairs[:: max(1, len(all_pairs) // npairs)][:npairs]
+        sec = run(wl, x, sel if npairs < len(all_pairs) else None, n_threads, dense)
+        scale = len(all_pairs) / len(sel)
+        toks = tokens if tokens is not None else x["cu_host"][-1]
+        table.append({"config": name, "threads": n_threads, "pairs_run": len(sel),
+                      "pairs": len(all_pairs), "seconds_run": sec,
+                      "seconds_full": sec * scale, "tokens_per_s_full": toks / (sec * scale)})
+
+    for cfg, name in ((1, "tiny"), (2, "one_head")):
+        wl = synth.workload(name)
+        x = synth.make_inputs(wl, 0)
+        for th in (1, threads):
+            entry(cfg, wl, x, th)
+    entry(3, w, inp, threads)
+    entry(3, w, inp, 1, frac_pairs=4 / w.H_v)
+    wd = synth.workload("decode")
+    xd = synth.make_inputs(wd, 0)
+    entry(4, wd, xd, threads, dense=xd["dense"], tokens=wd.num_seqs * wd.steps)
+    wv = synth.workload("varlen", seed=0)
+    xv = synth.make_inputs(wv, 0)
+    entry(5, wv, xv, threads, frac_pairs=0.25)
+    return {"value": T / layer_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": f"fp64 sequential oracle (plain C, OpenMP over (sequence, head) pairs) "
+                      f"on {heads} of {w.H_v} value heads x {T} tokens of the prefill "
+                      f"workload ({c_s:.2f} s wall on {threads} threads), scaled to the "
+                      f"{w.H_v}-head layer",
+            "per_config": table}
 
 
 def profiled_traffic(kernel, field="traffic_bytes"):

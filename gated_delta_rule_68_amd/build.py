@@ -21,6 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
+PROBE_LIB = os.path.join(HERE, "libgdr_probe.so")
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 CXXFLAGS = [
@@ -38,6 +39,9 @@ CXXFLAGS = [
 # element (measured: chain 282-303 us -> 251 us on the prefill layer).
 FILE_FLAGS = {
     "kda_prep_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the rate probe: accumulators stay in the VGPRs the products write, so
+    # its loop is matrix instructions only
+    "mfma_peak.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
@@ -57,19 +61,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every csrc/*.hip and link libgdr.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    workers = max(1, min(len(srcs), os.cpu_count() or 1, 8))
-    with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every csrc/*.hip and link libgdr.so (and csrc/probe/*.hip into
+    libgdr_probe.so, the benchmark's matrix-core rate probe); returns the
+    path of libgdr.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+    workers = max(1, min(len(srcs) + len(probes), os.cpu_count() or 1, 8))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(_compile, srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    if probes:
+        _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources for {ARCH}")
     return LIB

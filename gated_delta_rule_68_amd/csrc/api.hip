@@ -255,7 +255,7 @@ gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
       st = check_workspace(pr, x, workspace, workspace_bytes, need);
       if (st != GDR_OK) return st;
       if (launch_chunked_coop(pr, x, workspace, stream) == hipSuccess) return GDR_OK;
-      (void)hipGetLastError();  // a refused cooperative launch: run the fused kernel
+      (void)hipGetLastError();  // a failed launch: run the fused kernel
     }
     return launched(launch_chunked_mfma(pr, x, stream));
   }
@@ -285,7 +285,7 @@ gdr_status gdr_chunked_fwd_noalloc(const gdr_shape *shape, const void *q, const 
       if (st != GDR_OK) return st;
       if (clear_chunked_coop(pr, ws, stream) != hipSuccess) return GDR_ERR_LAUNCH;
       if (launch_chunked_coop(pr, x, ws, stream) == hipSuccess) return GDR_OK;
-      (void)hipGetLastError();  // a refused cooperative launch: run the fused kernel
+      (void)hipGetLastError();  // a failed launch: run the fused kernel
     }
     return launched(launch_chunked_mfma(pr, x, stream));
   }

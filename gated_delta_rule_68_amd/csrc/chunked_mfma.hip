@@ -52,17 +52,20 @@
 //     wave 1 its gates.
 // The four workgroups of a value head each form the same records.
 //
-// Cooperative kernel (chunked_coop_kernel), one launch with every workgroup
-// resident (one per compute unit).  Workgroups find their role by the
+// Cooperative kernel (chunked_coop_kernel), one launch of one workgroup per
+// compute unit, all resident together.  Workgroups find their role by the
 // accelerator complex die (XCD) they run on: per (sequence, key head) group,
-// the chain workgroups of its value heads and four producer workgroups sit on
+// four producer workgroups and the chain workgroups of its value heads sit on
 // one XCD and share its L2.  Producer p forms the records of chunks
 // c = p mod 4 for all value heads of the group, once, and writes them to a
-// ring of R slots per value head in the workspace; a chain workgroup (state,
-// output and staging waves as above, no prepare waves) copies each record
-// into LDS with its rows once the producer's flag for that chunk is set, and
-// publishes how far it has copied, which is when the producer may reuse the
-// slot.  Flags and counters are read past the L1 and scalar caches, in the
+// ring of RING slots per value head in the workspace.  A chain workgroup has
+// two state, two output, two staging and two K S waves (one of each kind per
+// 16-column tile, staging shared): its staging wave copies each record into
+// LDS with the chunk's rows once the producer's flag for that chunk is set,
+// and publishes how far it has copied, which is when the producer may reuse
+// the slot; the K S waves form the part of each chunk's R that does not wait
+// for the chunk before (see state_wave, LOOK).  Flags, progress words and
+// records are read at device scope, past the L1 and scalar caches, in the
 // shared L2.  Every wait is bounded: a wait that runs out marks the
 // workspace's error word instead of hanging.
 //
@@ -1648,12 +1651,13 @@ __device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, int 
   vm_wait<0>();
 }
 
-// One workgroup per compute unit, all resident (cooperative launch).  Role by
-// arrival order on this workgroup's XCD: slot s of XCD x holds group
-// s * nxcd + x, whose first gv * nvb arrivals are its chain workgroups
-// (value head j = r / nvb, 32 columns vb = r % nvb) and the next PRODUCERS
-// its producers.  The last workgroup of an XCD to finish clears that XCD's
-// counters, flags and progress words for the next call.
+// One workgroup per compute unit (its LDS admits no second one), all
+// resident together.  Role by arrival order on this workgroup's XCD: slot s
+// of XCD x holds group s * nxcd + x, whose first PRODUCERS arrivals are its
+// producers and the next gv * nvb its chain workgroups (value head j = r /
+// nvb, 32 columns vb = r % nvb), so a chain workgroup never waits on a
+// producer that has not started.  The last workgroup of an XCD to finish
+// clears that XCD's counters, flags and progress words for the next call.
 template <int DVT>
 __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams p) {
   constexpr int DV = DVT;
@@ -1672,8 +1676,9 @@ __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (slot < p.slots && grp < p.groups) {
     unsigned char *base = group_base(p, grp);
-    if (r < gv * NVB) {
-      const int j = r / NVB, vb = r % NVB;
+    if (r >= PRODUCERS) {
+      const int rc = r - PRODUCERS;  // chain workgroup index in the group
+      const int j = rc / NVB, vb = rc % NVB;
       const int n = grp / p.H_k, hk = grp % p.H_k, h = hk * gv + j;
       int64_t t0, t1;
       seq_bounds(p.cu, p.seq_len, n, t0, t1);
@@ -1683,7 +1688,7 @@ __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams 
       const int col0 = vb * BV;
       if (wave < CW_O0) {
         state_wave<DV, false, 2, true, 1>(p, sm, wave, lane, nch, nsteps, state_off, col0,
-                                          reinterpret_cast<uint32_t *>(base + GRP_PROGRESS) + r);
+                                          reinterpret_cast<uint32_t *>(base + GRP_PROGRESS) + rc);
       } else if (wave < CW_ST0) {
         output_wave<DV, 2, 1>(p, sm, wave - CW_O0, lane, nch, nsteps, t0, t1, h, col0);
       } else if (wave >= CW_KS0) {
@@ -1694,7 +1699,7 @@ __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams 
                          base + GRP_RECS + (size_t)j * RING * REC_BYTES, &xl[x].err);
       }
     } else {
-      producer(p, smem_raw, grp, r - gv * NVB, gv, NVB, &xl[x].err);
+      producer(p, smem_raw, grp, r, gv, NVB, &xl[x].err);
     }
   }
   vm_wait<0>();
@@ -1825,10 +1830,15 @@ hipError_t launch_coop(const Problem &pr, const FwdArgs &x, const CoopPlan &c, v
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
-  void *args[] = {&p};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kern),
-                                    dim3((unsigned)(XCD_CUS * c.nxcd)), dim3(64 * NWAVES_C), args,
-                                    (unsigned)smem, s);
+  // An ordinary launch of one workgroup per compute unit: on a device that
+  // runs nothing else they all start at once.  (A cooperative launch, which
+  // guarantees that, costs about 20 us more per call on this runtime.)  A
+  // kernel of another stream that holds compute units only delays the
+  // workgroups it displaces; the bounded waits mark the error word if that
+  // lasts beyond their limit.
+  hipLaunchKernelGGL(kern, dim3((unsigned)(XCD_CUS * c.nxcd)), dim3(64 * NWAVES_C),
+                     (unsigned)smem, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace

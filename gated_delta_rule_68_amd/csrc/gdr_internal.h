@@ -94,12 +94,12 @@ bool chunked_vec_supports(const Problem &p);
 bool chunked_kda_supports(const Problem &p);
 hipError_t launch_chunked_kda(const Problem &p, const FwdArgs &x, hipStream_t s);
 bool chunked_mfma_supports(const Problem &p);
-// The matrix-core chunked form as one cooperative launch (producer workgroups
-// form every chunk's record once per value head, the chain workgroups read
-// them through the workspace): 0 bytes when the problem or the current device
-// does not take it.  launch_chunked_coop needs a zero-filled workspace of that
-// size and leaves it zero-filled; a refused cooperative launch returns its
-// error before anything runs.
+// The matrix-core chunked form as one launch of one workgroup per compute
+// unit (producer workgroups form every chunk's record once per value head, the
+// chain workgroups read them through the workspace): 0 bytes when the problem
+// or the current device does not take it.  launch_chunked_coop needs a
+// zero-filled workspace of that size and leaves it zero-filled; a failed
+// launch returns its error before anything runs.
 size_t chunked_coop_workspace_bytes(const Problem &p);
 hipError_t launch_chunked_coop(const Problem &p, const FwdArgs &x, void *workspace,
                                hipStream_t s);

@@ -155,14 +155,20 @@ GDR_API gdr_status gdr_recurrent_fwd(const gdr_shape *shape, const void *q, cons
  * cores with bf16 operands and fp32 accumulation and state; every other
  * supported shape runs a vector fp32 kernel and ignores the workspace.  On
  * the matrix cores, with a workspace and when the batch's chains fit the GPU
- * at once (gdr_chunked_workspace_bytes > 0), one cooperative launch splits
- * the work: producer workgroups form every chunk's triangular inverse,
- * output mask and row factors once per value head, and the chain workgroups
- * of that value head read them through the workspace (a ring of records per
- * value head, so its size does not depend on the sequence length).  Without
- * a workspace, or when the cooperative launch is refused, every chain
- * workgroup forms them itself.  Both give the same results up to float
+ * at once (gdr_chunked_workspace_bytes > 0), one launch of one workgroup per
+ * compute unit splits the work: producer workgroups form every chunk's
+ * triangular inverse, output mask and row factors once per value head, and
+ * the chain workgroups of that value head read them through the workspace (a
+ * ring of records per value head, so its size does not depend on the
+ * sequence length).  Without a workspace, or when that launch fails, every
+ * chain workgroup forms them itself.  Both give the same results up to float
  * reassociation.  Calls that share one workspace must not overlap in time.
+ * The workgroups of that launch wait on one another, so they must all run
+ * together: kernels of other streams that hold compute units only delay it,
+ * but if a workgroup cannot start within about a second, the waits give up,
+ * the results are not valid, and the 32-bit word at byte offset 8 + 128 i
+ * (i < 16) of the workspace is left nonzero for some i (every such word is
+ * zero after a call that completed normally).
  */
 GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k, const void *v,
                            const void *a, const void *b, const float *A_log, const float *dt_bias,
