@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
   conv_silu(x, weight, H_k, H_v, d_k, d_v, bias=None, conv_state=None, ...)
             -> q, k, v, final_conv_state   (the layer's step before the rule)
   gated_rmsnorm(o, z, weight, eps=1e-6)  -> out   (the layer's step after it)
+  chunked_fwd_gated_rmsnorm(q, k, v, a, b, A_log, dt_bias, z, norm_weight, ...)
+            -> out, final_state   (the chunked form with that norm fused)
   chunked_fwd_split(..., segment_len)    -> o, final_state   (segments of each
             sequence in parallel: a two-level scan for long, few-head prefill)
 
@@ -39,7 +41,7 @@ import torch
 __all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", "chunked_path", "conv_silu",
            "chunked_workspace", "chunked_workspace_bytes", "workspace_error",
            "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version",
-           "chunked_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "chunked_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "chunked_fwd_gated_rmsnorm",
            "ssd_recurrent_fwd", "ssd_chunked_fwd", "kda_recurrent_fwd", "kda_chunked_fwd",
            "kda_chunked_fwd_split"]
 
@@ -83,6 +85,9 @@ def _bind(lib):
     lib.gdr_recurrent_fwd.restype = ctypes.c_int
     lib.gdr_chunked_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
     lib.gdr_chunked_fwd.restype = ctypes.c_int
+    lib.gdr_chunked_fwd_gated_rmsnorm.argtypes = ([sp] + [vp] * 10 + [ctypes.c_float] +
+                                                  [vp, vp, vp, ctypes.c_size_t, vp])
+    lib.gdr_chunked_fwd_gated_rmsnorm.restype = ctypes.c_int
     lib.gdr_chunked_fwd_noalloc.argtypes = [sp] + [vp] * 10 + [vp]
     lib.gdr_chunked_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_chunked_workspace_bytes.argtypes = [sp]
@@ -236,7 +241,7 @@ def gates(q, k, a, b, A_log, dt_bias, *, scale=None, l2_eps=1e-6, num_seqs=None,
 
 def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_seqs, chunk,
          scale, l2_eps, o, final_state, output_final_state, inplace, kda=False, fused=None,
-         workspace=None):
+         workspace=None, norm=None):
     dense_T = q.shape[1] if q.dim() == 4 else None
     q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
     a, b = _flatten(a, 2 if kda else 1), _flatten(b, 1)
@@ -276,8 +281,18 @@ def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_
     elif final_state is not None:
         _check(final_state, "final_state", dev, torch.float32, st_shape)
     fn = getattr(lib(), fn_name)
-    args = [ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
-            _ptr(dt_bias), _ptr(initial_state), _ptr(o), _ptr(final_state)]
+    if norm is not None:
+        # gdr_chunked_fwd_gated_rmsnorm: z, the weight and eps before out
+        z, nw, neps = norm
+        z = _flatten(z, 2)
+        _check(z, "z", dev, dt, (total, H_v, d_v))
+        _check(nw, "norm_weight", dev, torch.float32, (d_v,))
+        args = [ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+                _ptr(dt_bias), _ptr(initial_state), _ptr(z), _ptr(nw), ctypes.c_float(neps),
+                _ptr(o), _ptr(final_state)]
+    else:
+        args = [ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+                _ptr(dt_bias), _ptr(initial_state), _ptr(o), _ptr(final_state)]
     if fused is not None:
         # gdr_kda_chunked_fwd: a workspace from torch selects the two-launch form
         nbytes = ctypes.c_size_t(0)
@@ -286,7 +301,7 @@ def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_
                    lib().gdr_kda_chunked_workspace(ctypes.byref(shape), ctypes.byref(nbytes)))
         ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev) if nbytes.value else None
         args += [_ptr(ws), ctypes.c_size_t(nbytes.value)]
-    elif fn_name == "gdr_chunked_fwd":
+    elif fn_name in ("gdr_chunked_fwd", "gdr_chunked_fwd_gated_rmsnorm"):
         # the cooperative form's workspace: "auto" allocates a zero-filled one
         # of the size the library reports (none when that is 0)
         if isinstance(workspace, str):
@@ -337,6 +352,21 @@ def chunked_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32, 
     return _fwd("gdr_chunked_fwd", q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens,
                 num_seqs, chunk, scale, l2_eps, o, final_state, output_final_state, inplace,
                 workspace=workspace)
+
+
+def chunked_fwd_gated_rmsnorm(q, k, v, a, b, A_log, dt_bias, z, norm_weight, initial_state=None, *,
+                              norm_eps=1e-6, chunk=32, cu_seqlens=None, num_seqs=None, scale=None,
+                              l2_eps=1e-6, out=None, final_state=None, output_final_state=True,
+                              inplace=False, workspace="auto"):
+    """The chunked form followed by the gated RMSNorm of its output,
+    out = o / sqrt(mean(o^2) + norm_eps) * norm_weight * SiLU(z) per (token,
+    value head) row: one launch where chunked_fwd makes its cooperative launch
+    (``workspace`` as there), else chunked_fwd and gated_rmsnorm in turn.
+    z [total, H_v, d_v] (or [N, T, H_v, d_v]) in the input dtype, norm_weight
+    fp32 [d_v]; returns out (shaped as chunked_fwd's o) and final_state."""
+    return _fwd("gdr_chunked_fwd_gated_rmsnorm", q, k, v, a, b, A_log, dt_bias, initial_state,
+                cu_seqlens, num_seqs, chunk, scale, l2_eps, out, final_state, output_final_state,
+                inplace, workspace=workspace, norm=(z, norm_weight, float(norm_eps)))
 
 
 def chunked_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, chunk=32,

@@ -375,6 +375,56 @@ gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, const void *
   return launched(launch_gated_rmsnorm(pr, a, stream));
 }
 
+gdr_status gdr_chunked_fwd_gated_rmsnorm(const gdr_shape *shape, const void *q, const void *k,
+                                         const void *v, const void *a, const void *b,
+                                         const float *A_log, const float *dt_bias,
+                                         const float *initial_state, const void *z,
+                                         const float *norm_weight, float norm_eps, void *out,
+                                         float *final_state, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
+  if (!(norm_eps >= 0.0f) || !std::isfinite(norm_eps)) return GDR_ERR_SHAPE;
+  if (!norm_weight) return GDR_ERR_NULL;
+  if (pr.total > 0 && !z) return GDR_ERR_NULL;
+  if (z && !aligned16(z)) return GDR_ERR_ALIGN;
+  if (!aligned_to(norm_weight, 4)) return GDR_ERR_ALIGN;
+  FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state};
+  st = check_fwd(pr, x);
+  if (st != GDR_OK) return st;
+  // z and the weight are read to the end: out and final_state must not
+  // overlap them
+  const size_t es = elem_size(pr.dtype);
+  const size_t obytes = (size_t)pr.total * pr.H_v * pr.d_v * es;
+  const Range rz = span(z, obytes), rw = span(norm_weight, (size_t)pr.d_v * 4);
+  const Range rout = span(out, obytes);
+  const Range rsT = span(final_state, final_state ? (size_t)pr.num_seqs * pr.H_v * pr.d_k * pr.d_v * 4 : 0);
+  for (const Range &r : {rz, rw}) {
+    if (r.hi == r.lo) continue;
+    if (rout.hi > rout.lo && overlap(r, rout)) return GDR_ERR_ALIAS;
+    if (rsT.hi > rsT.lo && overlap(r, rsT)) return GDR_ERR_ALIAS;
+  }
+  const NormArgs nm{out, z, norm_weight, norm_eps, out};
+  if (chunked_mfma_supports(pr)) {
+    const size_t need = workspace ? chunked_coop_workspace_bytes(pr) : 0;
+    if (need > 0 && pr.total > 0) {
+      st = check_workspace(pr, x, workspace, workspace_bytes, need);
+      if (st != GDR_OK) return st;
+      for (const Range &r : {rz, rw})
+        if (r.hi > r.lo && overlap(r, span(workspace, need))) return GDR_ERR_ALIAS;
+      if (launch_chunked_coop_norm(pr, x, nm, workspace, stream) == hipSuccess) return GDR_OK;
+      (void)hipGetLastError();  // a failed launch: the two passes below
+    }
+  }
+  st = gdr_chunked_fwd(shape, q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state,
+                       workspace, workspace_bytes, stream);
+  if (st != GDR_OK) return st;
+  return launched(launch_gated_rmsnorm(pr, nm, stream));
+}
+
 namespace gdr {
 namespace {
 // Segmented chunked form: shape rules, then the workspace layout.

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 9
+#define GDR_ABI_VERSION 10
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -261,6 +261,34 @@ GDR_API gdr_status gdr_conv_silu(const gdr_shape *shape, int32_t width, const vo
 GDR_API gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, const void *z,
                                      const float *weight, float eps, void *out,
                                      hipStream_t stream);
+
+/*
+ * gdr_chunked_fwd_gated_rmsnorm -- gdr_chunked_fwd followed by
+ * gdr_gated_rmsnorm of its output, the rule's output and the norm that ends
+ * the layer after it (flashprove issue "P1: Qwen3.8-27B port, tracking"):
+ *     out = o / sqrt(mean(o^2) + norm_eps) * norm_weight * SiLU(z)
+ * per (token, value head) row, o the rule's output.  Arguments as
+ * gdr_chunked_fwd with o replaced by out, plus:
+ *   z           : dtype [total, H_v, d_v] (16-byte aligned); must not overlap
+ *                 out
+ *   norm_weight : fp32 [d_v]
+ *   norm_eps    : >= 0 and finite, else GDR_ERR_SHAPE
+ * The workspace is gdr_chunked_fwd's (gdr_chunked_workspace_bytes).  Where
+ * gdr_chunked_fwd would make its one cooperative launch, the norm runs inside
+ * it: o is never written to memory in full, the output workgroups of each
+ * value head exchange the sums of squares of their columns through the
+ * workspace and normalise o in fp32 before rounding it once.  Otherwise the
+ * call runs gdr_chunked_fwd into out and then gdr_gated_rmsnorm in place.
+ * Error behaviour as gdr_chunked_fwd.
+ */
+GDR_API gdr_status gdr_chunked_fwd_gated_rmsnorm(const gdr_shape *shape, const void *q,
+                                                 const void *k, const void *v, const void *a,
+                                                 const void *b, const float *A_log,
+                                                 const float *dt_bias, const float *initial_state,
+                                                 const void *z, const float *norm_weight,
+                                                 float norm_eps, void *out, float *final_state,
+                                                 void *workspace, size_t workspace_bytes,
+                                                 hipStream_t stream);
 
 /*
  * gdr_chunked_fwd_split -- the chunked form with every sequence cut into

@@ -30,7 +30,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd", "gdr_chunked_fwd_noalloc",
+    assert declared_symbols() == ["gdr_abi_version", "gdr_chunked_fwd",
+                                  "gdr_chunked_fwd_gated_rmsnorm", "gdr_chunked_fwd_noalloc",
                                   "gdr_chunked_fwd_split",
                                   "gdr_chunked_path", "gdr_chunked_split_workspace",
                                   "gdr_chunked_workspace_bytes",
@@ -427,14 +428,17 @@ def test_chunked_workspace_constant_in_sequence_length(gdr):
                                 num_seqs=1, seq_len=T, total_tokens=T)
     short, long_ = prefill(64), prefill(32768)
     assert short == long_ > 0
-    # a ring of 16 records of 7 KB per value head, and 512 bytes of flags per
-    # (sequence, key head) group, after 2 KB of per-XCD counters
-    assert short == 2048 + 16 * (512 + 3 * 16 * 7168)
+    # a ring of 16 records of 7 KB per value head and a ring of 8 chunks (+ a
+    # spare slot) of the fused norm's partial sums ([32 rows][8 tiles] fp32)
+    # per value head, and 512 bytes of flags per (sequence, key head) group,
+    # after 2 KB of per-XCD counters
+    per_head = 16 * 7168 + 9 * 32 * 8 * 4
+    assert short == 2048 + 16 * (512 + 3 * per_head)
     # packed batches: lengths do not matter either
     s = shape(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=2, H_v=6, num_seqs=3, seq_len=0,
               total_tokens=5000)
     s.cu_seqlens = fake(30).value
-    assert int(gdr.lib().gdr_chunked_workspace_bytes(ctypes.byref(s))) == 2048 + 6 * (512 + 3 * 16 * 7168)
+    assert int(gdr.lib().gdr_chunked_workspace_bytes(ctypes.byref(s))) == 2048 + 6 * (512 + 3 * per_head)
 
 
 def test_chunked_workspace_zero_without_cooperative_form(gdr):
@@ -486,3 +490,47 @@ def test_noalloc_scratch_limit(gdr):
     assert chunked_ws_bytes(gdr, **big) > limit
     far = [ctypes.c_void_p(BASE + i * 0x4000000) for i in range(10)]  # 64 MiB apart: no alias
     assert call(gdr, "gdr_chunked_fwd_noalloc", shape(gdr, **big), far) == 5
+
+
+# ------------------------------------------- chunked form with the norm fused
+def call_norm(gdr, s, z=None, w=None, eps=1e-6, out=None, ws=None, ws_bytes=0, ptrs=None):
+    """gdr_chunked_fwd_gated_rmsnorm with fake pointers: q..dt_bias, s0 from
+    slots 0..7, z slot 10, weight slot 11, out slot 8, final state slot 9."""
+    p = [fake(i) for i in range(12)] if ptrs is None else ptrs
+    f = gdr.lib().gdr_chunked_fwd_gated_rmsnorm
+    arg = ctypes.byref(s) if s is not None else None
+    return f(arg, *p[:8], p[10] if z is None else z, p[11] if w is None else w,
+             ctypes.c_float(eps), p[8] if out is None else out, p[9], ws, ctypes.c_size_t(ws_bytes),
+             None)
+
+
+def test_norm_fused_null_shape(gdr):
+    assert call_norm(gdr, None) == 1
+
+
+@pytest.mark.parametrize("eps", [-1.0, float("nan"), float("inf")])
+def test_norm_fused_bad_eps(gdr, eps):
+    assert call_norm(gdr, shape(gdr), eps=eps) == 2
+
+
+def test_norm_fused_null_weight_and_z(gdr):
+    assert call_norm(gdr, shape(gdr), w=ctypes.c_void_p(0)) == 1
+    assert call_norm(gdr, shape(gdr), z=ctypes.c_void_p(0)) == 1
+
+
+def test_norm_fused_alignment(gdr):
+    assert call_norm(gdr, shape(gdr), z=fake(10, 8)) == 4       # z rows move in 16-byte vectors
+    assert call_norm(gdr, shape(gdr), w=fake(11, 2)) == 4       # fp32 weight
+
+
+def test_norm_fused_alias(gdr):
+    # z (4 tokens x 2 heads x 16 fp32 = 512 bytes) overlapping out, exactly or shifted
+    assert call_norm(gdr, shape(gdr), z=fake(8)) == 7
+    assert call_norm(gdr, shape(gdr), z=fake(8, 256)) == 7
+    # the weight inside the final state
+    assert call_norm(gdr, shape(gdr), w=fake(9, 64)) == 7
+
+
+def test_norm_fused_shape_errors_come_first(gdr):
+    assert call_norm(gdr, shape(gdr, H_v=3, H_k=2)) == 2
+    assert call_norm(gdr, shape(gdr, chunk=8)) == 3
