@@ -327,7 +327,7 @@ constexpr size_t WS_HEAD = sizeof(XcdLine) * MAX_XCD;
 constexpr size_t GRP_FLAGS = 0, GRP_PROGRESS = 256, GRP_RECS = 512;
 // with the gated RMSNorm fused: per value head j, NPART_MAX progress words
 // of its output tiles at GRP_NORMPUB + 32 j, and after the records a ring of
-// RPART chunks of [32 rows][NPART_MAX tiles] fp32 partial sums of squares
+// RPART chunks of [NPART_MAX tiles][32 rows] fp32 partial sums of squares
 // (and one spare slot that takes the stores of steps without a chunk)
 constexpr size_t GRP_NORMPUB = 320;
 constexpr int NPART_MAX = 8;   // 16-column tiles of a value head (d_v = 128)
@@ -1711,32 +1711,32 @@ __device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, bf16
 // kernel).  Chunk c's O is formed in step F = c + LAG + 1 as output_wave forms
 // it and kept in registers; the sums of squares of each of its rows over this
 // tile's 16 columns go to slot c % RPART of the value head's partial ring
-// (word [row][me], me the tile's index among the head's NP tiles).  No step
-// waits on a round trip to the L2 that it started itself:
+// (the 32 words [me][row], me the tile's index among the head's NP tiles).
+// No step waits on a round trip to the L2 that it started itself:
 //   F + 1: the word pub[me] says that chunk c's sums are there (pub[me] =
 //          the number of chunks published);
 //   F + 2: the NP words pub[] of the value head are loaded;
 //   F + 3: if all of them show chunk c (else, rarely, a bounded wait for
-//          them), the NP sums of its rows and z are loaded (lane (m, g)
-//          loads tiles NP g / 4 .. NP (g + 1) / 4 - 1 of rows m, 16 + m);
+//          them), the sums of its rows and z are loaded (lane (m, g) loads
+//          tiles NP g / 4 .. NP (g + 1) / 4 - 1 of rows m and 16 + m);
 //   F + 4: out = O / sqrt(mean(O^2) + eps) * w * SiLU(z) is stored in place
 //          of O.
-// Every step issues the same ten vector-memory operations in the same order
-// (the publication word, five loads, the two partial sums, the two output
-// rows), whatever the chunk: steps without a chunk, and rows past the end,
-// store into the ring's spare slot RPART instead.  The counter of those
-// operations completes in issue order, so waiting until at most the two
-// newest (the output rows) are outstanding at the start of a step covers
-// everything the step needs from the one before.  The stages run on clamped
-// indices in one block, so that the compiler can interleave the finish's
-// arithmetic with the LDS reads of the Q S product.  Passes nsteps + 1
-// barriers (nsteps = chunks + LAG + 5).
+// Every step issues the same vector-memory operations in the same order (the
+// publication word, the row sums, the loads, the two output rows), whatever
+// the chunk: steps without a chunk, and rows past the end, store into the
+// ring's spare slot RPART instead.  The counter of those operations completes
+// in issue order, so waiting until at most the two newest (the output rows)
+// are outstanding at the start of a step covers everything the step needs
+// from the one before.  The stages run on clamped indices in one block, so
+// that the compiler can interleave the finish's arithmetic with the LDS reads
+// of the Q S product.  Passes nsteps + 1 barriers (nsteps = chunks + LAG + 5).
 template <int DV, int LAG>
 __device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, int cw, int lane,
                                                  int nch, int nsteps, int64_t t0, int64_t t1,
                                                  int h, int col0, float *part, uint32_t *pub,
                                                  int me, uint32_t *err) {
   constexpr int NP = DV / 16;
+  constexpr int NQ = NP / 4;  // tiles of a row's sums each lane loads
   static_assert(NP == 8 || NP == 4, "d_v = 128 or 64");
   static_assert(RPART >= 6, "a partial slot is reused only after all its reads");
   if (nch == 0) {  // nothing to form; keep the barrier count
@@ -1760,13 +1760,13 @@ __device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, 
   f32x4 qsT[2] = {z4, z4};
   bf16x8 pr0 = {}, pr1 = {};
   float gm0 = 0.f, gm1 = 0.f, iq0 = 0.f, iq1 = 0.f;
-  // O rows m and 16 + m of the chunks formed 1, 2, 3 and 4 steps before
+  // O rows m and 16 + m of the chunks formed 1, 2, 3 and 4 steps before (at
+  // the start of a step)
   f32x4 o1[2] = {z4, z4}, o2[2] = {z4, z4}, o3[2] = {z4, z4}, o4[2] = {z4, z4};
   bf16x4 zr0 = {}, zr1 = {};  // z of the chunk finished in this step
-  // this lane's share of its rows' partial sums: NP / 4 tiles each, in one
-  // atomic load per row
-  using uq = typename std::conditional<NP == 8, uint64_t, uint32_t>::type;
-  uq ps0 = 0, ps1 = 0;
+  float ps0[NQ], ps1[NQ];     // this lane's share of its rows' partial sums
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) ps0[i] = ps1[i] = 0.f;
   uint32_t pv = 0;  // pub[lane % NP] as loaded in the step before
   auto clampc = [&](int c) { return min(max(c, 0), nch - 1); };
   block_sync();
@@ -1774,6 +1774,7 @@ __device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, 
     const int F = it - LAG - 1;  // the chunk formed in this step
     const int c = it - LAG;      // the chunk whose Q S is formed
     // LDS operands of this step, issued first
+    const bf16x8 Db = sm.db[clampc(F) & 1][cw][lane];
     const Stage &st = sm.st[clampc(c) % NSTAGE];
     bf16x8 Sb[4], qo[4][2];
 #pragma unroll
@@ -1782,7 +1783,6 @@ __device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, 
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) qo[kb][mt] = row_op_t(st.Q, 16 * mt + m, kb, g);
     }
-    const bf16x8 Db = sm.db[clampc(F) & 1][cw][lane];
     const Rec &rc = st.pp.r;
     const bf16x8 npr0 = rc.P[0][lane], npr1 = rc.P[1][lane];
     const float ngm0 = rc.Gm[m], ngm1 = rc.Gm[16 + m], niq0 = rc.iq[m], niq1 = rc.iq[16 + m];
@@ -1790,20 +1790,37 @@ __device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, 
     asm volatile("" ::: "memory");
     // F + 1: chunks before F have their sums stored and landed
     pub[me] = (uint32_t)min(max(F, 0), nch);
+    // F: O of chunk F (lane (m, g): O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P
+    // diag(ik) Delta)) and its rows' sums of squares over this tile, stored
+    // early (lanes of g = 0, 1 store rows m, 16 + m; g = 2, 3 the same again)
+    const f32x4 of0 = o4[0], of1 = o4[1];  // O of chunk F - 4, finished below
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      o4[mt] = o3[mt];
+      o3[mt] = o2[mt];
+      o2[mt] = o1[mt];
+    }
+    o1[0] = mma32(Db, pr0, qsT[0] * gm0) * iq0;
+    o1[1] = mma32(Db, pr1, qsT[1] * gm1) * iq1;
+    {
+      float s0 = o1[0][0] * o1[0][0] + o1[0][1] * o1[0][1] + o1[0][2] * o1[0][2] + o1[0][3] * o1[0][3];
+      float s1 = o1[1][0] * o1[1][0] + o1[1][1] * o1[1][1] + o1[1][2] * o1[1][2] + o1[1][3] * o1[1][3];
+      s0 = sum_xor32(sum_xor16(s0));
+      s1 = sum_xor32(sum_xor16(s1));
+      float *slot = (F >= 0 && F < nch) ? part + (size_t)(F % RPART) * CH * NPART_MAX : spare;
+      slot[me * CH + 16 * (g & 1) + m] = (g & 1) ? s1 : s0;
+    }
     // F + 3 (for chunk F - 3): wait, rarely, until every tile has published it
     const int cl = F - 3;
     if (cl >= 0 && cl < nch && __ballot(pv < (uint32_t)(cl + 1)) != 0)
       progress_at_least(pub, NP, (uint32_t)(cl + 1), lane, err);
     // F + 4: finish chunk F - 4 from the sums and z loaded in the step before
     const int cf = F - 4;
-    float ss0, ss1;
-    if constexpr (NP == 8) {
-      const f32x2 q0 = __builtin_bit_cast(f32x2, ps0), q1 = __builtin_bit_cast(f32x2, ps1);
-      ss0 = q0[0] + q0[1];
-      ss1 = q1[0] + q1[1];
-    } else {
-      ss0 = __builtin_bit_cast(float, ps0);
-      ss1 = __builtin_bit_cast(float, ps1);
+    float ss0 = ps0[0], ss1 = ps1[0];
+#pragma unroll
+    for (int i = 1; i < NQ; ++i) {
+      ss0 += ps0[i];
+      ss1 += ps1[i];
     }
     ss0 = sum_xor32(sum_xor16(ss0));
     ss1 = sum_xor32(sum_xor16(ss1));
@@ -1813,42 +1830,24 @@ __device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float za = (float)zr0[j], zc = (float)zr1[j];
-      y0[j] = o4[0][j] * r0 * w[j] * (za * __builtin_amdgcn_rcpf(1.f + fast_exp(-za)));
-      y1[j] = o4[1][j] * r1 * w[j] * (zc * __builtin_amdgcn_rcpf(1.f + fast_exp(-zc)));
+      y0[j] = of0[j] * r0 * w[j] * (za * __builtin_amdgcn_rcpf(1.f + fast_exp(-za)));
+      y1[j] = of1[j] * r1 * w[j] * (zc * __builtin_amdgcn_rcpf(1.f + fast_exp(-zc)));
     }
     // F + 3: chunk F - 3's sums and z (rows past the end read the last row)
     {
-      const float *slot = part + (size_t)(clampc(cl) % RPART) * CH * NPART_MAX + (NP / 4) * g;
-      ps0 = __hip_atomic_load(reinterpret_cast<const uq *>(slot + m * NPART_MAX), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-      ps1 = __hip_atomic_load(reinterpret_cast<const uq *>(slot + (16 + m) * NPART_MAX),
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float *slot = part + (size_t)(clampc(cl) % RPART) * CH * NPART_MAX;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const float *tile = slot + (NQ * g + i) * CH;
+        ps0[i] = __hip_atomic_load(tile + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ps1[i] = __hip_atomic_load(tile + 16 + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       const int64_t row = t0 + (int64_t)clampc(cl) * CH + m;
       zr0 = *reinterpret_cast<const bf16x4 *>(p.z + (min(row, tlast) * p.H_v + h) * DV + col);
       zr1 = *reinterpret_cast<const bf16x4 *>(p.z + (min(row + 16, tlast) * p.H_v + h) * DV + col);
     }
     // F + 2: the publication words for chunk F - 2
     pv = __hip_atomic_load(&pub[lane % NP], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      o4[mt] = o3[mt];
-      o3[mt] = o2[mt];
-      o2[mt] = o1[mt];
-    }
-    // F: O of chunk F (lane (m, g): O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P
-    // diag(ik) Delta)) and its rows' sums of squares over this tile
-    o1[0] = mma32(Db, pr0, qsT[0] * gm0) * iq0;
-    o1[1] = mma32(Db, pr1, qsT[1] * gm1) * iq1;
-    float s0 = o1[0][0] * o1[0][0] + o1[0][1] * o1[0][1] + o1[0][2] * o1[0][2] + o1[0][3] * o1[0][3];
-    float s1 = o1[1][0] * o1[1][0] + o1[1][1] * o1[1][1] + o1[1][2] * o1[1][2] + o1[1][3] * o1[1][3];
-    s0 = sum_xor32(sum_xor16(s0));
-    s1 = sum_xor32(sum_xor16(s1));
-    {
-      // every lane of a row stores the same sum
-      float *slot = (F >= 0 && F < nch) ? part + (size_t)(F % RPART) * CH * NPART_MAX : spare;
-      slot[m * NPART_MAX + me] = s0;
-      slot[(16 + m) * NPART_MAX + me] = s1;
-    }
     // Q S of chunk c, and its output factors, for the next step
     qsT[0] = z4;
     qsT[1] = z4;
