@@ -129,6 +129,7 @@ constexpr int CST0_OPS = 8 + 1 + REC_DMAS;  // k rows, half of v, the record (+ 
 constexpr int CST1_OPS = 8 + 1;             // q rows, half of v
 constexpr int PRODUCERS = 4;              // producer workgroups per group
 constexpr int RING = 16;                  // record slots per value head
+constexpr int TOUCH_AHEAD = PRODUCERS;  // chunks a producer touches k and q ahead of its copy
 constexpr int MAX_GV = 3;                 // value heads per key head on this path
 constexpr int XCD_CUS = 32;               // compute units per XCD on gfx950
 constexpr int MAX_XCD = 16;
@@ -312,6 +313,7 @@ struct ProdSmem {
   alignas(16) float bgm[MAX_GV][CH];     //   beta Gam
   alignas(16) float ikp[MAX_GV][CH];     //   and 1/|k|
   alignas(16) uint32_t prg[MAX_GV][64];  // progress words, fetched by T wave j
+  alignas(16) uint32_t vtouch[64];       // scratch of the loader's v touches (never read)
 };
 
 // Workspace of the cooperative kernel: one 128-byte line per XCD (arrival
@@ -510,6 +512,14 @@ __device__ __forceinline__ void dma_v_half(const bf16 *v, int H_v, int hv, int c
   const int r = 16 * half + (lane >> 2);
   const int rr = min(r, cl - 1);
   dma16(v + ((row0 + rr) * H_v + hv) * DV + col0 + 8 * v_src_piece(lane), tile + 512 * half);
+}
+
+// One 4-byte load per lane from src into the 256-byte scratch block at lds,
+// to bring src's line into the L2 ahead of a later copy (the data is never
+// read).
+__device__ __forceinline__ void touch4(const bf16 *src, uint32_t *lds) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
+                                   (__attribute__((address_space(3))) void *)(lds), 4, 0, 0);
 }
 
 // a and b of the 32 rows in one load: lane l < 32 takes a of row l, lane
@@ -1523,6 +1533,28 @@ __device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *sme
 #pragma unroll
     for (int j = 0; j < MAX_GV; ++j)
       dma_ab(p.a, p.b, p.H_v, hk * gv + min(j, gv - 1), row0, cl, ps.ab[buf][j], lane);
+    // touch the group's v rows of the chunk (gv d_v bf16 each: lpr 128-byte
+    // lines), one 4-byte load per line into a scratch block, so that the
+    // chain workgroups' copies of v, steps later, find them in the L2
+    const int lpr = gv * nvb * BV / 64;
+#pragma unroll
+    for (int t = 0; t < (CH * 2 * MAX_GV + 63) / 64; ++t) {
+      if (64 * t < CH * lpr) {
+        const int li = min(64 * t + lane, CH * lpr - 1);
+        const int r = min(li / lpr, cl - 1);
+        touch4(p.v + ((row0 + r) * p.H_v + hk * gv) * (nvb * BV) + 64 * (li % lpr), ps.vtouch);
+      }
+    }
+    // and the k and q rows of this producer's next chunk after c, which the
+    // next call of load copies (two 128-byte lines a row)
+    if (c + TOUCH_AHEAD < nch) {
+      int64_t nrow0;
+      int ncl;
+      rows_of(c + TOUCH_AHEAD, nch, t0, t1, nrow0, ncl);
+      const int64_t rr = nrow0 + min(lane >> 1, ncl - 1);
+      touch4(p.k + (rr * p.H_k + hk) * DK + 64 * (lane & 1), ps.vtouch);
+      touch4(p.q + (rr * p.H_k + hk) * DK + 64 * (lane & 1), ps.vtouch);
+    }
   };
   const bool t_wave = wave < gv;
   const int pj = wave - 3;
