@@ -942,6 +942,8 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
                                            int nch, int nsteps, size_t state_off, int col0,
                                            uint32_t *progress = nullptr) {
   static_assert(!LOOK || (LAG == 2 && !SSD), "look-ahead needs the rows of chunk c+1 in step c+1");
+  // cooperative kernel: issue priority over the staging wave on this SIMD
+  if (progress) __builtin_amdgcn_s_setprio(1);
   const int m = lane & 15, g = lane >> 4;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 S[NT][8];  // S[u][t]: state rows state_row(t, g, j), column col0 + 16 (cw0 + u) + m
@@ -1065,9 +1067,13 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
       for (int u = 0; u < NT; ++u)
 #pragma unroll
         for (int t = 0; t < 8; ++t) S[u][t] *= gc;
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!LOOK) read_kt(st);  // LOOK: read at the end of the step before
-      __builtin_amdgcn_sched_barrier(0);
+      // (without LOOK, the k^T reads go between two scheduling barriers; with
+      // it, the compiler may interleave the scaling with the products)
+      if constexpr (!LOOK) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_kt(st);  // LOOK: read at the end of the step before
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if constexpr (!LOOK) {
 #pragma unroll
         for (int u = 0; u < NT; ++u)
@@ -1146,9 +1152,13 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
 //   beta V - beta Gam ik Gam_last(c-1) (K_c S_{c-1})   (beta V - beta Gam ik K_0 S_0 for c = 0),
 // from the state the state wave handed over at the entry of chunk c - 1 (0),
 // for the state wave's step it + 1.  Passes nsteps + 1 barriers.
-template <int LAG>
+template <int LAG, int PRIO>
 __device__ __forceinline__ void ks_wave(Smem &sm, int cw, int lane, int nch, int nsteps) {
   static_assert(LAG == 2, "the state wave runs chunk it - 2 in step it");
+  // issue priority over the output wave on this SIMD (the state wave waits
+  // for this wave's part of R at the start of the next step), unless that
+  // output wave carries the fused norm and is the slower of the two
+  __builtin_amdgcn_s_setprio(PRIO);
   const int m = lane & 15, g = lane >> 4;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   block_sync();
@@ -1235,14 +1245,12 @@ __device__ __forceinline__ void output_wave(const MfmaParams &p, Smem &sm, int c
         qsT[u][0] = z;
         qsT[u][1] = z;
       }
-      // qsT[u][mt]: (Q S)[16mt + m][4g + j]; every q read is issued before the
-      // first product waits on one
+      // qsT[u][mt]: (Q S)[16mt + m][4g + j]
       bf16x8 qop[4][2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) qop[kb][mt] = row_op_t(st.Q, 16 * mt + m, kb, g);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -1963,7 +1971,7 @@ __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams 
           output_wave<DV, 2, 1>(p, sm, wave - CW_O0, lane, nch, nsteps, t0, t1, h, col0);
         }
       } else if (wave >= CW_KS0) {
-        ks_wave<2>(sm, wave - CW_KS0, lane, nch, nsteps);
+        ks_wave<2, NORM ? 0 : 3>(sm, wave - CW_KS0, lane, nch, nsteps);
       } else {
         coop_staging<DV, NORM>(p, sm, zs, wave - CW_ST0, lane, nch, nsteps, t0, t1, hk, h, col0,
                                reinterpret_cast<const uint32_t *>(base + GRP_FLAGS) + j * RING,
