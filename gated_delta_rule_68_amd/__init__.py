@@ -19,7 +19,7 @@ Entry points (same names as the C ABI):
             -> q, k, v, final_conv_state   (the layer's step before the rule)
   gated_rmsnorm(o, z, weight, eps=1e-6)  -> out   (the layer's step after it)
   chunked_fwd_gated_rmsnorm(q, k, v, a, b, A_log, dt_bias, z, norm_weight, ...)
-            -> out, final_state   (the chunked form with that norm fused)
+            -> out, final_state   (the chunked form, then that norm)
   chunked_fwd_split(..., segment_len)    -> o, final_state   (segments of each
             sequence in parallel: a two-level scan for long, few-head prefill)
 
@@ -360,10 +360,10 @@ def chunked_fwd_gated_rmsnorm(q, k, v, a, b, A_log, dt_bias, z, norm_weight, ini
                               inplace=False, workspace="auto"):
     """The chunked form followed by the gated RMSNorm of its output,
     out = o / sqrt(mean(o^2) + norm_eps) * norm_weight * SiLU(z) per (token,
-    value head) row: one launch where chunked_fwd makes its cooperative launch
-    (``workspace`` as there), else chunked_fwd and gated_rmsnorm in turn.
-    z [total, H_v, d_v] (or [N, T, H_v, d_v]) in the input dtype, norm_weight
-    fp32 [d_v]; returns out (shaped as chunked_fwd's o) and final_state."""
+    value head) row: gdr_chunked_fwd into out (``workspace`` as there), then
+    gdr_gated_rmsnorm in place.  z [total, H_v, d_v] (or [N, T, H_v, d_v]) in
+    the input dtype, norm_weight fp32 [d_v]; returns out (shaped as
+    chunked_fwd's o) and final_state."""
     return _fwd("gdr_chunked_fwd_gated_rmsnorm", q, k, v, a, b, A_log, dt_bias, initial_state,
                 cu_seqlens, num_seqs, chunk, scale, l2_eps, out, final_state, output_final_state,
                 inplace, workspace=workspace, norm=(z, norm_weight, float(norm_eps)))

@@ -407,18 +407,9 @@ gdr_status gdr_chunked_fwd_gated_rmsnorm(const gdr_shape *shape, const void *q, 
     if (rout.hi > rout.lo && overlap(r, rout)) return GDR_ERR_ALIAS;
     if (rsT.hi > rsT.lo && overlap(r, rsT)) return GDR_ERR_ALIAS;
   }
+  // the rule into out, then the norm in place: two launches (folding the
+  // norm into the rule's cooperative launch was measured slower)
   const NormArgs nm{out, z, norm_weight, norm_eps, out};
-  if (chunked_mfma_supports(pr)) {
-    const size_t need = workspace ? chunked_coop_workspace_bytes(pr) : 0;
-    if (need > 0 && pr.total > 0) {
-      st = check_workspace(pr, x, workspace, workspace_bytes, need);
-      if (st != GDR_OK) return st;
-      for (const Range &r : {rz, rw})
-        if (r.hi > r.lo && overlap(r, span(workspace, need))) return GDR_ERR_ALIAS;
-      if (launch_chunked_coop_norm(pr, x, nm, workspace, stream) == hipSuccess) return GDR_OK;
-      (void)hipGetLastError();  // a failed launch: the two passes below
-    }
-  }
   st = gdr_chunked_fwd(shape, q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state,
                        workspace, workspace_bytes, stream);
   if (st != GDR_OK) return st;

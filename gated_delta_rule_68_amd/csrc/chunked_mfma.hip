@@ -175,18 +175,6 @@ __device__ __forceinline__ float scan32(float x) {
 }
 
 // Order this wave's LDS writes before its later LDS reads of other lanes' data.
-// x[l] + x[l ^ 16] and x[l] + x[l ^ 32] in every lane l, without LDS: the two
-// results of a permlane swap of x with itself hold, between them, x of both
-// lanes of each pair.
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
@@ -320,21 +308,12 @@ struct ProdSmem {
 // and completion counters, error word), then one block per (sequence, key
 // head) group, used only by workgroups on that group's XCD: flags[gv][RING]
 // (chunk + 1 of the record in each slot), progress[gv * nvb] (chunks each
-// chain workgroup has copied), the norm's publication words (below), then
-// the records [gv][RING] and the norm's partial-sum rings [gv].
+// chain workgroup has copied), then the records [gv][RING].
 struct XcdLine {
   uint32_t arrive, done, err, pad[29];
 };
 constexpr size_t WS_HEAD = sizeof(XcdLine) * MAX_XCD;
 constexpr size_t GRP_FLAGS = 0, GRP_PROGRESS = 256, GRP_RECS = 512;
-// with the gated RMSNorm fused: per value head j, NPART_MAX progress words
-// of its output tiles at GRP_NORMPUB + 32 j, and after the records a ring of
-// RPART chunks of [NPART_MAX tiles][32 rows] fp32 partial sums of squares
-// (and one spare slot that takes the stores of steps without a chunk)
-constexpr size_t GRP_NORMPUB = 320;
-constexpr int NPART_MAX = 8;   // 16-column tiles of a value head (d_v = 128)
-constexpr int RPART = 8;       // chunks in the partial-sum ring (+ 1 spare slot)
-constexpr size_t PART_BYTES = (size_t)(RPART + 1) * CH * NPART_MAX * 4;
 
 struct MfmaParams {
   const bf16 *q, *k, *v, *a, *b;
@@ -351,11 +330,6 @@ struct MfmaParams {
   unsigned char *ws;
   size_t grp_stride;
   int nxcd, slots, gs, groups;
-  // cooperative kernel with the gated RMSNorm of o fused: z [total, H_v, DV]
-  // (o's dtype), the weight [DV], eps; o receives the normalised output
-  const bf16 *z;
-  const float *nw;
-  float neps;
 };
 // State rows held in registers.  Accumulator tile t (t = 0..7) of a
 // consumer holds, in lane (m, g) register j, the state row
@@ -1152,13 +1126,12 @@ __device__ __forceinline__ void state_wave(const MfmaParams &p, Smem &sm, int cw
 //   beta V - beta Gam ik Gam_last(c-1) (K_c S_{c-1})   (beta V - beta Gam ik K_0 S_0 for c = 0),
 // from the state the state wave handed over at the entry of chunk c - 1 (0),
 // for the state wave's step it + 1.  Passes nsteps + 1 barriers.
-template <int LAG, int PRIO>
+template <int LAG>
 __device__ __forceinline__ void ks_wave(Smem &sm, int cw, int lane, int nch, int nsteps) {
   static_assert(LAG == 2, "the state wave runs chunk it - 2 in step it");
-  // issue priority over the output wave on this SIMD (the state wave waits
-  // for this wave's part of R at the start of the next step), unless that
-  // output wave carries the fused norm and is the slower of the two
-  __builtin_amdgcn_s_setprio(PRIO);
+  // issue priority over the output wave on this SIMD: the state wave waits
+  // for this wave's part of R at the start of the next step
+  __builtin_amdgcn_s_setprio(3);
   const int m = lane & 15, g = lane >> 4;
   const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
   block_sync();
@@ -1666,20 +1639,16 @@ __device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *sme
 
 // Staging wave of a chain workgroup (cooperative kernel): k rows, the first
 // half of v and the record (wave 0), or q rows and the second half of v
-// (wave 1); with the gated RMSNorm fused (NORM), wave 1 also touches the
-// chunk's z rows (this workgroup's 64 bytes of each) so that they are in the
-// L2 when the output waves read them three steps later: one 4-byte load per
-// row into the scratch block zs, whose contents nothing reads.  Step it requests chunk it + AHEAD and waits for chunk it + 1; an
+// (wave 1).  Step it requests chunk it + AHEAD and waits for chunk it + 1; an
 // extra first barrier publishes chunk 0.  Wave 0 fetches the producer's flag
 // of chunk c two steps before it requests the chunk (into LDS, past the L1)
 // and only polls the flag itself if it was not yet set then.  Passes
 // nsteps + 1 barriers.
-template <int DV, bool NORM>
-__device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, bf16 *zs, int which,
-                                             int lane, int nch, int nsteps, int64_t t0, int64_t t1,
-                                             int hk, int h, int col0, const uint32_t *flag,
+template <int DV>
+__device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, int which, int lane,
+                                             int nch, int nsteps, int64_t t0, int64_t t1, int hk,
+                                             int h, int col0, const uint32_t *flag,
                                              const unsigned char *recs, uint32_t *err) {
-  constexpr int OPS0 = CST0_OPS, OPS1 = CST1_OPS + (NORM ? 1 : 0);
   if (nch == 0) {  // nothing to load; keep the barrier count
     for (int it = 0; it <= nsteps; ++it) block_sync();
     return;
@@ -1687,7 +1656,7 @@ __device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, bf16
   const RowOffsets ko = row_offsets(p.H_k, lane);
   const uint32_t voff =
       (uint32_t)(((16 * which + (lane >> 2)) * p.H_v * DV + col0 + 8 * v_src_piece(lane)) * (int)sizeof(bf16));
-  auto rows = [&](int c) {  // 9 loads (+ 1 with z)
+  auto rows = [&](int c) {  // 9 loads
     int64_t row0;
     int cl;
     rows_of(c, nch, t0, t1, row0, cl);
@@ -1696,11 +1665,6 @@ __device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, bf16
       request_rows<DV>(p.k, p.v, p.H_k, p.H_v, hk, h, col0, row0, cl, ko, voff, S.K, S.V, 0, lane);
     else
       request_rows<DV>(p.q, p.v, p.H_k, p.H_v, hk, h, col0, row0, cl, ko, voff, S.Q, S.V, 1, lane);
-    if (NORM && which == 1) {
-      const int64_t r = row0 + min(lane & 31, cl - 1);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(p.z + (r * p.H_v + h) * DV + col0),
-                                       (__attribute__((address_space(3))) void *)(zs), 4, 0, 0);
-    }
   };
   auto fetch_flag = [&](int c) {  // 1 load
     const int cc = min(c, nch - 1);
@@ -1725,193 +1689,24 @@ __device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, bf16
       record(c, false);
       rows(c);
     }
-    vm_wait<OPS0 * (AHEAD - 1)>();  // chunk 0 has landed, flags 2 and 3 too
-    block_sync<OPS0 * (AHEAD - 1)>();
+    vm_wait<CST0_OPS * (AHEAD - 1)>();  // chunk 0 has landed, flags 2 and 3 too
+    block_sync<CST0_OPS * (AHEAD - 1)>();
     for (int it = 0; it < nsteps; ++it) {
       fetch_flag(it + AHEAD + 2);
       record(it + AHEAD, true);
       rows(it + AHEAD);
-      vm_wait<OPS0 + 1>();  // chunk it + 1 has landed, and the flag of it + 3
-      block_sync<OPS0 + 1>();
+      vm_wait<CST0_OPS + 1>();  // chunk it + 1 has landed, and the flag of it + 3
+      block_sync<CST0_OPS + 1>();
     }
   } else {
     for (int c = 0; c < AHEAD; ++c) rows(c);
-    vm_wait<OPS1 * (AHEAD - 1)>();  // chunk 0 has landed
-    block_sync<OPS1 * (AHEAD - 1)>();
+    vm_wait<CST1_OPS * (AHEAD - 1)>();  // chunk 0 has landed
+    block_sync<CST1_OPS * (AHEAD - 1)>();
     for (int it = 0; it < nsteps; ++it) {
       rows(it + AHEAD);
-      vm_wait<OPS1 * (AHEAD - 1)>();  // chunk it + 1 has landed
-      block_sync<OPS1 * (AHEAD - 1)>();
+      vm_wait<CST1_OPS * (AHEAD - 1)>();  // chunk it + 1 has landed
+      block_sync<CST1_OPS * (AHEAD - 1)>();
     }
-  }
-  vm_wait<0>();
-}
-
-// Output wave of tile cw with the gated RMSNorm of o fused (cooperative
-// kernel).  Chunk c's O is formed in step F = c + LAG + 1 as output_wave forms
-// it and kept in registers; the sums of squares of each of its rows over this
-// tile's 16 columns go to slot c % RPART of the value head's partial ring
-// (the 32 words [me][row], me the tile's index among the head's NP tiles).
-// No step waits on a round trip to the L2 that it started itself:
-//   F + 1: the word pub[me] says that chunk c's sums are there (pub[me] =
-//          the number of chunks published);
-//   F + 2: the NP words pub[] of the value head are loaded;
-//   F + 3: if all of them show chunk c (else, rarely, a bounded wait for
-//          them), the sums of its rows and z are loaded (lane (m, g) loads
-//          tiles NP g / 4 .. NP (g + 1) / 4 - 1 of rows m and 16 + m);
-//   F + 4: out = O / sqrt(mean(O^2) + eps) * w * SiLU(z) is stored in place
-//          of O.
-// Every step issues the same vector-memory operations in the same order (the
-// publication word, the row sums, the loads, the two output rows), whatever
-// the chunk: steps without a chunk, and rows past the end, store into the
-// ring's spare slot RPART instead.  The counter of those operations completes
-// in issue order, so waiting until at most the two newest (the output rows)
-// are outstanding at the start of a step covers everything the step needs
-// from the one before.  The stages run on clamped indices in one block, so
-// that the compiler can interleave the finish's arithmetic with the LDS reads
-// of the Q S product.  Passes nsteps + 1 barriers (nsteps = chunks + LAG + 5).
-template <int DV, int LAG>
-__device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, int cw, int lane,
-                                                 int nch, int nsteps, int64_t t0, int64_t t1,
-                                                 int h, int col0, float *part, uint32_t *pub,
-                                                 int me, uint32_t *err) {
-  constexpr int NP = DV / 16;
-  constexpr int NQ = NP / 4;  // tiles of a row's sums each lane loads
-  static_assert(NP == 8 || NP == 4, "d_v = 128 or 64");
-  static_assert(RPART >= 6, "a partial slot is reused only after all its reads");
-  if (nch == 0) {  // nothing to form; keep the barrier count
-    for (int it = 0; it <= nsteps; ++it) block_sync<63, false>();
-    return;
-  }
-  const int m = lane & 15, g = lane >> 4;
-  const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int col = col0 + 16 * cw + 4 * g;  // this lane's 4 columns
-  // the weights and eps in registers, loaded before the loop (not reloaded
-  // from the kernel arguments in it, which would wait on every LDS read in
-  // flight)
-  f32x4 w = f32x4{p.nw[col], p.nw[col + 1], p.nw[col + 2], p.nw[col + 3]};
-  float neps = p.neps;
-  vm_wait<0>();
-  asm("" : "+v"(w), "+v"(neps));
-  const int64_t rstride = (int64_t)p.H_v * DV;  // elements from one token's row to the next
-  const int64_t tlast = t1 - 1;
-  float *spare = part + (size_t)RPART * CH * NPART_MAX;
-  bf16 *trash = reinterpret_cast<bf16 *>(spare) + 4 * lane;  // 8 bytes per lane
-  f32x4 qsT[2] = {z4, z4};
-  bf16x8 pr0 = {}, pr1 = {};
-  float gm0 = 0.f, gm1 = 0.f, iq0 = 0.f, iq1 = 0.f;
-  // O rows m and 16 + m of the chunks formed 1, 2, 3 and 4 steps before (at
-  // the start of a step)
-  f32x4 o1[2] = {z4, z4}, o2[2] = {z4, z4}, o3[2] = {z4, z4}, o4[2] = {z4, z4};
-  bf16x4 zr0 = {}, zr1 = {};  // z of the chunk finished in this step
-  float ps0[NQ], ps1[NQ];     // this lane's share of its rows' partial sums
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) ps0[i] = ps1[i] = 0.f;
-  uint32_t pv = 0;  // pub[lane % NP] as loaded in the step before
-  auto clampc = [&](int c) { return min(max(c, 0), nch - 1); };
-  block_sync();
-  for (int it = 0; it < nsteps; ++it) {
-    const int F = it - LAG - 1;  // the chunk formed in this step
-    const int c = it - LAG;      // the chunk whose Q S is formed
-    // LDS operands of this step, issued first
-    const bf16x8 Db = sm.db[clampc(F) & 1][cw][lane];
-    const Stage &st = sm.st[clampc(c) % NSTAGE];
-    bf16x8 Sb[4], qo[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      Sb[kb] = sm.sb[clampc(c) & 1][cw][kb][lane];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) qo[kb][mt] = row_op_t(st.Q, 16 * mt + m, kb, g);
-    }
-    const Rec &rc = st.pp.r;
-    const bf16x8 npr0 = rc.P[0][lane], npr1 = rc.P[1][lane];
-    const float ngm0 = rc.Gm[m], ngm1 = rc.Gm[16 + m], niq0 = rc.iq[m], niq1 = rc.iq[16 + m];
-    vm_wait<2>();  // all but the output rows stored in the step before
-    asm volatile("" ::: "memory");
-    // F + 1: chunks before F have their sums stored and landed
-    pub[me] = (uint32_t)min(max(F, 0), nch);
-    // F: O of chunk F (lane (m, g): O[16mt + m][4g..4g+3] = iq (Gam (Q S) + P
-    // diag(ik) Delta)) and its rows' sums of squares over this tile, stored
-    // early (lanes of g = 0, 1 store rows m, 16 + m; g = 2, 3 the same again)
-    const f32x4 of0 = o4[0], of1 = o4[1];  // O of chunk F - 4, finished below
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      o4[mt] = o3[mt];
-      o3[mt] = o2[mt];
-      o2[mt] = o1[mt];
-    }
-    o1[0] = mma32(Db, pr0, qsT[0] * gm0) * iq0;
-    o1[1] = mma32(Db, pr1, qsT[1] * gm1) * iq1;
-    {
-      float s0 = o1[0][0] * o1[0][0] + o1[0][1] * o1[0][1] + o1[0][2] * o1[0][2] + o1[0][3] * o1[0][3];
-      float s1 = o1[1][0] * o1[1][0] + o1[1][1] * o1[1][1] + o1[1][2] * o1[1][2] + o1[1][3] * o1[1][3];
-      s0 = sum_xor32(sum_xor16(s0));
-      s1 = sum_xor32(sum_xor16(s1));
-      float *slot = (F >= 0 && F < nch) ? part + (size_t)(F % RPART) * CH * NPART_MAX : spare;
-      slot[me * CH + 16 * (g & 1) + m] = (g & 1) ? s1 : s0;
-    }
-    // F + 3 (for chunk F - 3): wait, rarely, until every tile has published it
-    const int cl = F - 3;
-    if (cl >= 0 && cl < nch && __ballot(pv < (uint32_t)(cl + 1)) != 0)
-      progress_at_least(pub, NP, (uint32_t)(cl + 1), lane, err);
-    // F + 4: finish chunk F - 4 from the sums and z loaded in the step before
-    const int cf = F - 4;
-    float ss0 = ps0[0], ss1 = ps1[0];
-#pragma unroll
-    for (int i = 1; i < NQ; ++i) {
-      ss0 += ps0[i];
-      ss1 += ps1[i];
-    }
-    ss0 = sum_xor32(sum_xor16(ss0));
-    ss1 = sum_xor32(sum_xor16(ss1));
-    const float r0 = __builtin_amdgcn_rsqf(ss0 * (1.0f / DV) + neps);
-    const float r1 = __builtin_amdgcn_rsqf(ss1 * (1.0f / DV) + neps);
-    f32x4 y0, y1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float za = (float)zr0[j], zc = (float)zr1[j];
-      y0[j] = of0[j] * r0 * w[j] * (za * __builtin_amdgcn_rcpf(1.f + fast_exp(-za)));
-      y1[j] = of1[j] * r1 * w[j] * (zc * __builtin_amdgcn_rcpf(1.f + fast_exp(-zc)));
-    }
-    // F + 3: chunk F - 3's sums and z (rows past the end read the last row)
-    {
-      const float *slot = part + (size_t)(clampc(cl) % RPART) * CH * NPART_MAX;
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const float *tile = slot + (NQ * g + i) * CH;
-        ps0[i] = __hip_atomic_load(tile + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ps1[i] = __hip_atomic_load(tile + 16 + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      const int64_t row = t0 + (int64_t)clampc(cl) * CH + m;
-      zr0 = *reinterpret_cast<const bf16x4 *>(p.z + (min(row, tlast) * p.H_v + h) * DV + col);
-      zr1 = *reinterpret_cast<const bf16x4 *>(p.z + (min(row + 16, tlast) * p.H_v + h) * DV + col);
-    }
-    // F + 2: the publication words for chunk F - 2
-    pv = __hip_atomic_load(&pub[lane % NP], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Q S of chunk c, and its output factors, for the next step
-    qsT[0] = z4;
-    qsT[1] = z4;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) qsT[mt] = mma32(Sb[kb], qo[kb][mt], qsT[mt]);
-    pr0 = npr0;
-    pr1 = npr1;
-    gm0 = ngm0;
-    gm1 = ngm1;
-    iq0 = niq0;
-    iq1 = niq1;
-    // the two output rows of chunk F - 4, last
-    {
-      const bool cv = cf >= 0 && cf < nch;
-      const int64_t row = t0 + (int64_t)cf * CH + m;
-      bf16 *orow = p.o + (row * p.H_v + h) * DV + col;
-      bf16 *d0 = cv && row < t1 ? orow : trash;
-      bf16 *d1 = cv && row + 16 < t1 ? orow + 16 * rstride : trash;
-      *reinterpret_cast<bf16x4 *>(d0) = pack4(y0);
-      *reinterpret_cast<bf16x4 *>(d1) = pack4(y1);
-    }
-    block_sync<63, false>();
   }
   vm_wait<0>();
 }
@@ -1923,9 +1718,7 @@ __device__ __forceinline__ void output_wave_norm(const MfmaParams &p, Smem &sm, 
 // nvb, 32 columns vb = r % nvb), so a chain workgroup never waits on a
 // producer that has not started.  The last workgroup of an XCD to finish
 // clears that XCD's counters, flags and progress words for the next call.
-// NORM: o receives the gated RMSNorm of the rule's output (output_wave_norm);
-// the z touches' scratch block follows Smem in LDS.
-template <int DVT, bool NORM>
+template <int DVT>
 __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams p) {
   constexpr int DV = DVT;
   constexpr int NVB = DV / BV;
@@ -1950,32 +1743,20 @@ __global__ __launch_bounds__(64 * NWAVES_C) void chunked_coop_kernel(MfmaParams 
       int64_t t0, t1;
       seq_bounds(p.cu, p.seq_len, n, t0, t1);
       const int nch = (int)((t1 - t0 + CH - 1) / CH);
-      // state: chunk it-2, outputs: chunk it-3 (normalised: it-7)
-      const int nsteps = nch + (NORM ? 7 : 3);
+      const int nsteps = nch + 3;  // state: chunk it-2, outputs: chunk it-3
       const size_t state_off = ((size_t)n * p.H_v + h) * DK * DV;
       const int col0 = vb * BV;
-      bf16 *zs = reinterpret_cast<bf16 *>(smem_raw + sizeof(Smem));
       if (wave < CW_O0) {
         state_wave<DV, false, 2, true, 1>(p, sm, wave, lane, nch, nsteps, state_off, col0,
                                           reinterpret_cast<uint32_t *>(base + GRP_PROGRESS) + rc);
       } else if (wave < CW_ST0) {
-        if (NORM) {
-          const int cw = wave - CW_O0;
-          output_wave_norm<DV, 2>(
-              p, sm, cw, lane, nch, nsteps, t0, t1, h, col0,
-              reinterpret_cast<float *>(base + GRP_RECS + (size_t)gv * RING * REC_BYTES +
-                                        (size_t)j * PART_BYTES),
-              reinterpret_cast<uint32_t *>(base + GRP_NORMPUB) + j * NPART_MAX, vb * NC + cw,
-              &xl[x].err);
-        } else {
-          output_wave<DV, 2, 1>(p, sm, wave - CW_O0, lane, nch, nsteps, t0, t1, h, col0);
-        }
+        output_wave<DV, 2, 1>(p, sm, wave - CW_O0, lane, nch, nsteps, t0, t1, h, col0);
       } else if (wave >= CW_KS0) {
-        ks_wave<2, NORM ? 0 : 3>(sm, wave - CW_KS0, lane, nch, nsteps);
+        ks_wave<2>(sm, wave - CW_KS0, lane, nch, nsteps);
       } else {
-        coop_staging<DV, NORM>(p, sm, zs, wave - CW_ST0, lane, nch, nsteps, t0, t1, hk, h, col0,
-                               reinterpret_cast<const uint32_t *>(base + GRP_FLAGS) + j * RING,
-                               base + GRP_RECS + (size_t)j * RING * REC_BYTES, &xl[x].err);
+        coop_staging<DV>(p, sm, wave - CW_ST0, lane, nch, nsteps, t0, t1, hk, h, col0,
+                         reinterpret_cast<const uint32_t *>(base + GRP_FLAGS) + j * RING,
+                         base + GRP_RECS + (size_t)j * RING * REC_BYTES, &xl[x].err);
       }
     } else {
       producer(p, smem_raw, grp, r, gv, NVB, &xl[x].err);
@@ -2045,14 +1826,9 @@ struct CoopPlan {
   size_t grp_stride = 0, bytes = 0;
 };
 // The cooperative kernel keeps one workgroup per compute unit only if two of
-// its LDS footprints do not fit one; with the norm fused, the staging wave's
-// scratch block for the z touches follows.
-constexpr size_t ZS_BYTES = 256;
+// its LDS footprints do not fit one.
 static_assert(2 * sizeof(Smem) > 160 * 1024, "one workgroup per compute unit");
-static_assert(sizeof(Smem) % 16 == 0 && sizeof(Smem) + ZS_BYTES + 64 <= 160 * 1024,
-              "the z scratch block fits the compute unit's LDS");
-static_assert(GRP_PROGRESS + 4 * MAX_GV * (DK / BV) <= GRP_NORMPUB &&
-                  GRP_NORMPUB + 4 * NPART_MAX * MAX_GV <= GRP_RECS && 4 * MAX_GV * RING <= GRP_PROGRESS,
+static_assert(GRP_PROGRESS + 4 * MAX_GV * (DK / BV) <= GRP_RECS && 4 * MAX_GV * RING <= GRP_PROGRESS,
               "group header layout");
 static_assert(sizeof(ProdSmem) <= sizeof(Smem), "a producer's LDS fits the launch's");
 
@@ -2078,15 +1854,15 @@ CoopPlan coop_plan(const Problem &pr) {
   c.slots = XCD_CUS / c.gs;
   if ((groups + c.nxcd - 1) / c.nxcd > c.slots) return c;
   c.groups = (int)groups;
-  c.grp_stride = GRP_RECS + (size_t)gv * (RING * REC_BYTES + PART_BYTES);
+  c.grp_stride = GRP_RECS + (size_t)gv * RING * REC_BYTES;
   c.bytes = WS_HEAD + (size_t)c.groups * c.grp_stride;
   c.ok = true;
   return c;
 }
 
-template <int DVT, bool NORM>
+template <int DVT>
 hipError_t launch_coop(const Problem &pr, const FwdArgs &x, const CoopPlan &c, void *ws,
-                       const NormArgs *nm, hipStream_t s) {
+                       hipStream_t s) {
   MfmaParams p{};
   p.q = static_cast<const bf16 *>(x.q);
   p.k = static_cast<const bf16 *>(x.k);
@@ -2111,13 +1887,8 @@ hipError_t launch_coop(const Problem &pr, const FwdArgs &x, const CoopPlan &c, v
   p.slots = c.slots;
   p.gs = c.gs;
   p.groups = c.groups;
-  if (NORM) {
-    p.z = static_cast<const bf16 *>(nm->z);
-    p.nw = nm->weight;
-    p.neps = nm->eps;
-  }
-  const size_t smem = sizeof(Smem) + (NORM ? ZS_BYTES : 0);
-  auto kern = chunked_coop_kernel<DVT, NORM>;
+  const size_t smem = sizeof(Smem);
+  auto kern = chunked_coop_kernel<DVT>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
@@ -2174,16 +1945,7 @@ hipError_t clear_chunked_coop(const Problem &pr, void *ws, hipStream_t s) {
 hipError_t launch_chunked_coop(const Problem &pr, const FwdArgs &x, void *ws, hipStream_t s) {
   const CoopPlan c = coop_plan(pr);
   if (!c.ok) return hipErrorInvalidValue;
-  return pr.d_v == 64 ? launch_coop<64, false>(pr, x, c, ws, nullptr, s)
-                      : launch_coop<128, false>(pr, x, c, ws, nullptr, s);
-}
-
-hipError_t launch_chunked_coop_norm(const Problem &pr, const FwdArgs &x, const NormArgs &nm,
-                                    void *ws, hipStream_t s) {
-  const CoopPlan c = coop_plan(pr);
-  if (!c.ok) return hipErrorInvalidValue;
-  return pr.d_v == 64 ? launch_coop<64, true>(pr, x, c, ws, &nm, s)
-                      : launch_coop<128, true>(pr, x, c, ws, &nm, s);
+  return pr.d_v == 64 ? launch_coop<64>(pr, x, c, ws, s) : launch_coop<128>(pr, x, c, ws, s);
 }
 
 }  // namespace gdr

@@ -103,11 +103,6 @@ bool chunked_mfma_supports(const Problem &p);
 size_t chunked_coop_workspace_bytes(const Problem &p);
 hipError_t launch_chunked_coop(const Problem &p, const FwdArgs &x, void *workspace,
                                hipStream_t s);
-// launch_chunked_coop with the gated RMSNorm of the output fused: x.o
-// receives out = o / sqrt(mean(o^2) + eps) * weight * SiLU(z) per (token,
-// value head) row instead of o (bf16; z must not overlap x.o).
-hipError_t launch_chunked_coop_norm(const Problem &p, const FwdArgs &x, const NormArgs &nm,
-                                    void *workspace, hipStream_t s);
 // Zero, on stream s, what launch_chunked_coop needs zero in a workspace of
 // chunked_coop_workspace_bytes(p) bytes (its counters, error words, flags and
 // progress words; not the records), with a fill kernel.

@@ -273,13 +273,10 @@ GDR_API gdr_status gdr_gated_rmsnorm(const gdr_shape *shape, const void *o, cons
  *                 out
  *   norm_weight : fp32 [d_v]
  *   norm_eps    : >= 0 and finite, else GDR_ERR_SHAPE
- * The workspace is gdr_chunked_fwd's (gdr_chunked_workspace_bytes).  Where
- * gdr_chunked_fwd would make its one cooperative launch, the norm runs inside
- * it: o is never written to memory in full, the output workgroups of each
- * value head exchange the sums of squares of their columns through the
- * workspace and normalise o in fp32 before rounding it once.  Otherwise the
- * call runs gdr_chunked_fwd into out and then gdr_gated_rmsnorm in place.
- * Error behaviour as gdr_chunked_fwd.
+ * The call runs gdr_chunked_fwd into out (with the given workspace, as
+ * gdr_chunked_fwd uses it) and then gdr_gated_rmsnorm in place, two
+ * launches on `stream`.  Error behaviour as gdr_chunked_fwd; out and
+ * final_state must not overlap z or norm_weight.
  */
 GDR_API gdr_status gdr_chunked_fwd_gated_rmsnorm(const gdr_shape *shape, const void *q,
                                                  const void *k, const void *v, const void *a,

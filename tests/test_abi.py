@@ -428,11 +428,9 @@ def test_chunked_workspace_constant_in_sequence_length(gdr):
                                 num_seqs=1, seq_len=T, total_tokens=T)
     short, long_ = prefill(64), prefill(32768)
     assert short == long_ > 0
-    # a ring of 16 records of 7 KB per value head and a ring of 8 chunks (+ a
-    # spare slot) of the fused norm's partial sums ([32 rows][8 tiles] fp32)
-    # per value head, and 512 bytes of flags per (sequence, key head) group,
-    # after 2 KB of per-XCD counters
-    per_head = 16 * 7168 + 9 * 32 * 8 * 4
+    # a ring of 16 records of 7 KB per value head, and 512 bytes of flags per
+    # (sequence, key head) group, after 2 KB of per-XCD counters
+    per_head = 16 * 7168
     assert short == 2048 + 16 * (512 + 3 * per_head)
     # packed batches: lengths do not matter either
     s = shape(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=2, H_v=6, num_seqs=3, seq_len=0,

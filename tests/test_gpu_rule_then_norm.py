@@ -1,11 +1,8 @@
 """GPU checks of gdr_chunked_fwd_gated_rmsnorm, through the C ABI: the
-chunked form with the gated RMSNorm of its output fused into the cooperative
-launch (the output workgroups of a value head exchange their rows' sums of
-squares through the workspace), against the fp64 oracle of the rule followed
-by the oracle's gated RMSNorm, on every (sequence, value head) slice, at the
-bf16 bar of the rule; against the two separate passes it replaces; and its
-workspace protocol (no wait runs out, counters and flags left at zero,
-repeated calls give the same bits).
+chunked form followed by the gated RMSNorm of its output, against the fp64
+oracle of the rule followed by the oracle's gated RMSNorm, on every
+(sequence, value head) slice, at the bf16 bar of the rule; against the two
+calls it stands for; without a workspace; and its alias check.
 """
 import sys
 
@@ -56,12 +53,12 @@ def seqs(inp):
         dict(num_seqs=len(inp["cu_host"]) - 1)
 
 
-def fused(inp, z, nw, ws):
+def one_call(inp, z, nw, ws):
     return gdr.chunked_fwd_gated_rmsnorm(*rule_args(inp), z, nw, inp["initial_state"],
                                          norm_eps=EPS, chunk=32, workspace=ws, **seqs(inp))
 
 
-def two_passes(inp, z, nw, ws):
+def two_calls(inp, z, nw, ws):
     o, S = gdr.chunked_fwd(*rule_args(inp), inp["initial_state"], chunk=32, workspace=ws,
                            **seqs(inp))
     return gdr.gated_rmsnorm(o, z, nw, EPS), S
@@ -71,13 +68,6 @@ def workspace_for(w):
     ws = gdr.chunked_workspace(w.H_k, w.H_v, w.d_k, w.d_v, "bf16", len(w.seq_lengths), device=DEV)
     assert ws is not None, "this shape should take the cooperative form"
     return ws
-
-
-def check_clean(ws):
-    torch.cuda.synchronize()
-    assert gdr.workspace_error(ws) == 0
-    head = ws[:2048].view(torch.int32).view(16, 32)
-    assert int(head[:, 0].abs().sum()) == 0 and int(head[:, 1].abs().sum()) == 0
 
 
 def oracle_out(inp, z, nw):
@@ -90,8 +80,6 @@ CASES = [
     (2, 6, 128, [200]),
     (2, 6, 64, [300, 1, 64, 0, 97]),
     (1, 3, 128, [300, 129, 0]),
-    (1, 1, 128, [31, 32, 33]),
-    (2, 4, 128, [1000, 513]),
     (8, 24, 128, [129] * 2),
 ]
 
@@ -101,68 +89,50 @@ def _id(c):
 
 
 @pytest.mark.parametrize("case", CASES, ids=_id)
-def test_fused_norm_against_oracle(case):
+def test_rule_then_norm_against_oracle(case):
     H_k, H_v, d_v, lens = case
     w = synth.custom(H_k, H_v, 128, d_v, "bf16", lengths=lens, chunk=32)
-    note(f"[norm fused] {_id(case)}")
+    note(f"[rule + norm] {_id(case)}")
     inp = synth.make_inputs(w, 61, device=DEV)
     z, nw = gate_inputs(w, 62)
     ws = workspace_for(w)
-    out, S = fused(inp, z, nw, ws)
-    check_clean(ws)
+    out, S = one_call(inp, z, nw, ws)
+    torch.cuda.synchronize()
+    assert gdr.workspace_error(ws) == 0
     ref, S_ref = oracle_out(inp, z, nw)
     eo, es = U.compare_full(out, S, ref, S_ref, inp["cu_host"], w.H_v)
-    note(f"  fused: max rel err out={eo:.3e} S={es:.3e}")
+    note(f"  one call: max rel err out={eo:.3e} S={es:.3e}")
     assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], (eo, es)
-    # the two passes it replaces: the same state bits, the output within the bar
-    out2, S2 = two_passes(inp, z, nw, ws)
-    check_clean(ws)
-    assert torch.equal(S, S2)
-    eo2, _ = U.compare_full(out2, None, ref, None, inp["cu_host"], w.H_v)
-    note(f"  two passes: max rel err out={eo2:.3e}")
-    assert eo2 <= U.TOL["bf16"], eo2
-    # no workspace: the fused kernel and the norm kernel in turn
-    out3, S3 = fused(inp, z, nw, None)
+    # the two calls it stands for give the same bits
+    out2, S2 = two_calls(inp, z, nw, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(S, S2)
+    # no workspace: the one-launch form of the rule, then the norm
+    out3, S3 = one_call(inp, z, nw, None)
     torch.cuda.synchronize()
     eo3, es3 = U.compare_full(out3, S3, ref, S_ref, inp["cu_host"], w.H_v)
     note(f"  without a workspace: max rel err out={eo3:.3e} S={es3:.3e}")
     assert eo3 <= U.TOL["bf16"] and es3 <= U.TOL["bf16"], (eo3, es3)
 
 
-def test_fused_norm_repeats_bitwise_between_other_calls():
-    """Calls with and without the norm share one workspace: each leaves the
-    protocol state clean for the next, and the fused output repeats bit for
-    bit."""
-    w = synth.custom(2, 6, 128, 128, "bf16", lengths=[777, 64, 1], chunk=32)
-    a = synth.make_inputs(w, 63, device=DEV)
-    z, nw = gate_inputs(w, 64)
-    ws = workspace_for(w)
-    first = fused(a, z, nw, ws)
-    for i in range(3):
-        gdr.chunked_fwd(*rule_args(a), a["initial_state"], chunk=32, workspace=ws, **seqs(a))
-        again = fused(a, z, nw, ws)
-        torch.cuda.synchronize()
-        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1]), f"call {i + 1}"
-    check_clean(ws)
-
-
-def test_fused_norm_prefill_layer():
+def test_rule_then_norm_prefill_layer():
     """The prefill layer (8192 tokens, 48 value heads sharing 16 key heads):
     every head of the normalised output against the oracle."""
     w = synth.workload("prefill")
-    note("[norm fused] prefill layer, all 48 heads")
+    note("[rule + norm] prefill layer, all 48 heads")
     inp = synth.make_inputs(w, 0, device=DEV)
     z, nw = gate_inputs(w, 65)
     ws = workspace_for(w)
-    out, S = fused(inp, z, nw, ws)
-    check_clean(ws)
+    out, S = one_call(inp, z, nw, ws)
+    torch.cuda.synchronize()
+    assert gdr.workspace_error(ws) == 0
     ref, S_ref = oracle_out(inp, z, nw)
     eo, es = U.compare_full(out, S, ref, S_ref, inp["cu_host"], w.H_v)
     note(f"  max rel err out={eo:.3e} S={es:.3e}")
     assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], (eo, es)
 
 
-def test_fused_norm_rejects_z_overlapping_out():
+def test_rule_then_norm_rejects_z_overlapping_out():
     w = synth.custom(1, 3, 128, 128, "bf16", lengths=[64], chunk=32)
     inp = synth.make_inputs(w, 66, device=DEV)
     z, nw = gate_inputs(w, 67)
