@@ -130,6 +130,7 @@ constexpr int CST1_OPS = 8 + 1;             // q rows, half of v
 constexpr int PRODUCERS = 4;              // producer workgroups per group
 constexpr int RING = 16;                  // record slots per value head
 constexpr int TOUCH_AHEAD = PRODUCERS;  // chunks a producer touches k and q ahead of its copy
+constexpr int V_TOUCH_BEHIND = 8;       // chunks behind its copy that a producer touches v
 constexpr int MAX_GV = 3;                 // value heads per key head on this path
 constexpr int XCD_CUS = 32;               // compute units per XCD on gfx950
 constexpr int MAX_XCD = 16;
@@ -1514,16 +1515,22 @@ __device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *sme
 #pragma unroll
     for (int j = 0; j < MAX_GV; ++j)
       dma_ab(p.a, p.b, p.H_v, hk * gv + min(j, gv - 1), row0, cl, ps.ab[buf][j], lane);
-    // touch the group's v rows of the chunk (gv d_v bf16 each: lpr 128-byte
-    // lines), one 4-byte load per line into a scratch block, so that the
-    // chain workgroups' copies of v, steps later, find them in the L2
+    // touch the group's v rows of chunk c - V_TOUCH_BEHIND (gv d_v bf16
+    // each: lpr 128-byte lines), one 4-byte load per line into a scratch
+    // block, so that the chain workgroups' copies of v find them in the L2.
+    // The producers run up to RING chunks ahead of the chains; a chunk that
+    // far behind their front is still a few steps ahead of the chains, close
+    // enough that its lines are rarely evicted again before the copies.
     const int lpr = gv * nvb * BV / 64;
+    int64_t vrow0;
+    int vcl;
+    rows_of(max(c - V_TOUCH_BEHIND, 0), nch, t0, t1, vrow0, vcl);
 #pragma unroll
     for (int t = 0; t < (CH * 2 * MAX_GV + 63) / 64; ++t) {
-      if (64 * t < CH * lpr) {
+      if (c >= V_TOUCH_BEHIND && 64 * t < CH * lpr) {
         const int li = min(64 * t + lane, CH * lpr - 1);
-        const int r = min(li / lpr, cl - 1);
-        touch4(p.v + ((row0 + r) * p.H_v + hk * gv) * (nvb * BV) + 64 * (li % lpr), ps.vtouch);
+        const int r = min(li / lpr, vcl - 1);
+        touch4(p.v + ((vrow0 + r) * p.H_v + hk * gv) * (nvb * BV) + 64 * (li % lpr), ps.vtouch);
       }
     }
     // and the k and q rows of this producer's next chunk after c, which the
