@@ -1,5 +1,6 @@
 // C-ABI entry points: synchronous validation, then dispatch to a kernel
 // family.  Nothing here allocates, frees or synchronises.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -130,6 +131,55 @@ gdr_status check_workspace(const Problem &pr, const FwdArgs &x, const void *work
   return GDR_OK;
 }
 
+// Whether the cooperative form runs a batch: in one launch when all its
+// groups fit the device at once; else in consecutive launches of `per`
+// sequences, only when the sequences average at least kCoopMinTokens tokens
+// (each launch fills and drains a pipeline of a few chunks, which the
+// one-launch form, running every chain at once, does not).
+constexpr int64_t kCoopMinTokens = 1024;
+bool coop_runs(const Problem &pr, int per) {
+  if (per <= 0 || pr.total <= 0) return false;
+  return per >= pr.num_seqs || pr.total >= kCoopMinTokens * pr.num_seqs;
+}
+
+// The cooperative form over consecutive batches of `per` sequences on one
+// workspace (each launch leaves it zero-filled for the next).  A batch whose
+// launch fails runs the one-launch form instead.
+gdr_status run_coop_batches(const Problem &pr, const FwdArgs &x, int per, void *ws,
+                            hipStream_t stream) {
+  const size_t es = elem_size(pr.dtype);
+  const size_t state = (size_t)pr.H_v * pr.d_k * pr.d_v;  // fp32 per sequence
+  for (int s0 = 0; s0 < pr.num_seqs; s0 += per) {
+    Problem sub = pr;
+    sub.num_seqs = std::min(per, pr.num_seqs - s0);
+    FwdArgs y = x;
+    if (pr.cu) {
+      sub.cu = pr.cu + s0;  // token offsets stay absolute
+    } else {
+      const size_t row0 = (size_t)s0 * pr.seq_len;
+      sub.total = (int64_t)sub.num_seqs * pr.seq_len;
+      auto at = [&](const void *t, size_t per_row) {
+        return t ? static_cast<const void *>(static_cast<const char *>(t) + row0 * per_row * es)
+                 : nullptr;
+      };
+      y.q = at(x.q, (size_t)pr.H_k * pr.d_k);
+      y.k = at(x.k, (size_t)pr.H_k * pr.d_k);
+      y.v = at(x.v, (size_t)pr.H_v * pr.d_v);
+      y.a = at(x.a, (size_t)pr.H_v);
+      y.b = at(x.b, (size_t)pr.H_v);
+      y.o = const_cast<void *>(at(x.o, (size_t)pr.H_v * pr.d_v));
+    }
+    if (x.s0) y.s0 = x.s0 + (size_t)s0 * state;
+    if (x.sT) y.sT = x.sT + (size_t)s0 * state;
+    if (launch_chunked_coop(sub, y, ws, stream) != hipSuccess) {
+      (void)hipGetLastError();  // a failed launch: the one-launch form
+      const gdr_status st = launched(launch_chunked_mfma(sub, y, stream));
+      if (st != GDR_OK) return st;
+    }
+  }
+  return GDR_OK;
+}
+
 // Device address of `scratch` on the current device, looked up on the first
 // call per device (with that device current) and kept.
 constexpr int kMaxDevices = 64;
@@ -250,12 +300,11 @@ gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
   st = check_fwd(pr, x);
   if (st != GDR_OK) return st;
   if (chunked_mfma_supports(pr)) {
-    const size_t need = workspace ? chunked_coop_workspace_bytes(pr) : 0;
-    if (need > 0 && pr.total > 0) {
-      st = check_workspace(pr, x, workspace, workspace_bytes, need);
+    const int per = workspace ? chunked_coop_seqs_per_launch(pr) : 0;
+    if (coop_runs(pr, per)) {
+      st = check_workspace(pr, x, workspace, workspace_bytes, chunked_coop_workspace_bytes(pr));
       if (st != GDR_OK) return st;
-      if (launch_chunked_coop(pr, x, workspace, stream) == hipSuccess) return GDR_OK;
-      (void)hipGetLastError();  // a failed launch: run the fused kernel
+      return run_coop_batches(pr, x, per, workspace, stream);
     }
     return launched(launch_chunked_mfma(pr, x, stream));
   }
@@ -279,13 +328,15 @@ gdr_status gdr_chunked_fwd_noalloc(const gdr_shape *shape, const void *q, const 
   if (chunked_mfma_supports(pr)) {
     const size_t need = chunked_coop_workspace_bytes(pr);
     if (need > GDR_NOALLOC_SCRATCH_BYTES) return GDR_ERR_WORKSPACE;
-    if (need > 0 && pr.total > 0) {
+    const int per = chunked_coop_seqs_per_launch(pr);
+    if (coop_runs(pr, per)) {
       void *ws = nullptr;
       st = scratch_of_current_device(&ws);
       if (st != GDR_OK) return st;
-      if (clear_chunked_coop(pr, ws, stream) != hipSuccess) return GDR_ERR_LAUNCH;
-      if (launch_chunked_coop(pr, x, ws, stream) == hipSuccess) return GDR_OK;
-      (void)hipGetLastError();  // a failed launch: run the fused kernel
+      Problem first = pr;
+      first.num_seqs = per;
+      if (clear_chunked_coop(first, ws, stream) != hipSuccess) return GDR_ERR_LAUNCH;
+      return run_coop_batches(pr, x, per, ws, stream);
     }
     return launched(launch_chunked_mfma(pr, x, stream));
   }

@@ -1923,8 +1923,22 @@ hipError_t launch_chunked_mfma(const Problem &pr, const FwdArgs &x, hipStream_t 
   return pr.d_v == 64 ? launch_kernel<64, false>(pr, x, s) : launch_kernel<128, false>(pr, x, s);
 }
 
+int chunked_coop_seqs_per_launch(const Problem &pr) {
+  if (pr.num_seqs <= 0) return 0;
+  Problem one = pr;
+  one.num_seqs = 1;
+  const CoopPlan c = coop_plan(one);
+  if (!c.ok) return 0;
+  const int fit = c.slots * c.nxcd / pr.H_k;  // sequences whose groups fit at once
+  return fit < pr.num_seqs ? fit : pr.num_seqs;
+}
+
 size_t chunked_coop_workspace_bytes(const Problem &pr) {
-  const CoopPlan c = coop_plan(pr);
+  const int per = chunked_coop_seqs_per_launch(pr);
+  if (per <= 0) return 0;
+  Problem sub = pr;
+  sub.num_seqs = per;
+  const CoopPlan c = coop_plan(sub);
   return c.ok ? c.bytes : 0;
 }
 

@@ -101,6 +101,12 @@ bool chunked_mfma_supports(const Problem &p);
 // zero-filled workspace of that size and leaves it zero-filled; a failed
 // launch returns its error before anything runs.
 size_t chunked_coop_workspace_bytes(const Problem &p);
+// Sequences whose (sequence, key head) groups fit one cooperative launch at
+// once (at most p.num_seqs), or 0 when the problem has no cooperative form.
+// A batch of more sequences runs as consecutive launches of that many
+// sequences each on one workspace of chunked_coop_workspace_bytes(p) bytes,
+// which is sized for one such launch.
+int chunked_coop_seqs_per_launch(const Problem &p);
 hipError_t launch_chunked_coop(const Problem &p, const FwdArgs &x, void *workspace,
                                hipStream_t s);
 // Zero, on stream s, what launch_chunked_coop needs zero in a workspace of

@@ -154,14 +154,16 @@ GDR_API gdr_status gdr_recurrent_fwd(const gdr_shape *shape, const void *q, cons
  * bf16 with d_k = 128, d_v = 64 or 128 and chunk = 32 runs on the matrix
  * cores with bf16 operands and fp32 accumulation and state; every other
  * supported shape runs a vector fp32 kernel and ignores the workspace.  On
- * the matrix cores, with a workspace and when the batch's chains fit the GPU
- * at once (gdr_chunked_workspace_bytes > 0), one launch of one workgroup per
- * compute unit splits the work: producer workgroups form every chunk's
- * triangular inverse, output mask and row factors once per value head, and
- * the chain workgroups of that value head read them through the workspace (a
- * ring of records per value head, so its size does not depend on the
- * sequence length).  Without a workspace, or when that launch fails, every
- * chain workgroup forms them itself.  Both give the same results up to float
+ * the matrix cores, with a workspace (gdr_chunked_workspace_bytes > 0), a
+ * launch of one workgroup per compute unit splits the work: producer
+ * workgroups form every chunk's triangular inverse, output mask and row
+ * factors once per value head, and the chain workgroups of that value head
+ * read them through the workspace (a ring of records per value head, so its
+ * size does not depend on the sequence length).  When the batch's chains do
+ * not all fit the GPU at once, consecutive such launches each take as many
+ * sequences as fit, provided the sequences average at least 1024 tokens;
+ * otherwise, without a workspace, or where a launch fails, every chain
+ * workgroup forms them itself in one launch.  Both give the same results up to float
  * reassociation.  Calls that share one workspace must not overlap in time.
  * The workgroups of that launch wait on one another, so they must all run
  * together: kernels of other streams that hold compute units only delay it,
@@ -177,7 +179,8 @@ GDR_API gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const 
 
 /* Bytes of workspace gdr_chunked_fwd uses for `shape`: 0 when the shape has
  * no cooperative path (or is invalid), else a size that depends on num_seqs,
- * H_k, H_v and d_v but not on the sequence lengths. */
+ * H_k, H_v and d_v but not on the sequence lengths: that of one launch of the
+ * sequences that fit the device at once. */
 GDR_API size_t gdr_chunked_workspace_bytes(const gdr_shape *shape);
 
 /* Size of the scratch array gdr_chunked_fwd_noalloc uses as its workspace. */

@@ -443,12 +443,27 @@ def test_chunked_workspace_zero_without_cooperative_form(gdr):
     assert chunked_ws_bytes(gdr) == 0                                    # fp32: vector kernel
     assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=16) == 0
     assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=1, H_v=4) == 0  # 4 per key head
-    # more (sequence, key head) groups than the device holds at once: 256
-    # sequences of 16 key heads
-    assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=16, H_v=48,
-                            num_seqs=256, seq_len=1, total_tokens=256) == 0
+    # H_k groups of one sequence that do not fit the device at once: 48 key
+    # heads of 3 value heads (16 workgroups a group, 2 groups an XCD)
+    assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=48, H_v=144) == 0
     assert int(gdr.lib().gdr_chunked_workspace_bytes(None)) == 0
     assert chunked_ws_bytes(gdr, H_v=3, H_k=2) == 0                      # invalid shape
+
+
+def test_chunked_workspace_sized_for_one_launch(gdr):
+    """A batch with more (sequence, key head) groups than the device holds
+    at once runs as consecutive launches on one workspace, sized for the
+    sequences one launch holds: 256 sequences of 16 key heads need the
+    workspace of one such sequence."""
+    one = chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=16, H_v=48)
+    many = chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=16, H_v=48,
+                            num_seqs=256, seq_len=1, total_tokens=256)
+    assert many == one == 2048 + 16 * (512 + 3 * 16 * 7168)
+    # 2 key heads: 8 sequences (16 groups) a launch
+    eight = chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=2, H_v=6, num_seqs=8,
+                             seq_len=4, total_tokens=32)
+    assert chunked_ws_bytes(gdr, dtype=1, d_k=128, d_v=128, chunk=32, H_k=2, H_v=6, num_seqs=40,
+                            seq_len=4, total_tokens=160) == eight
 
 
 def test_chunked_workspace_checked(gdr):

@@ -138,3 +138,44 @@ def test_undersized_workspace_is_refused():
     with pytest.raises(gdr.GdrError) as e:
         run(inp, w, ws[:-256])
     assert e.value.status == 5
+
+
+BATCH_CASES = [
+    # H_k, H_v, d_v, lengths, dense: batches whose groups do not fit one
+    # launch, run as consecutive cooperative launches of the sequences that do
+    (16, 48, 128, [1100, 1024, 1500], False),   # one sequence a launch, packed
+    (16, 48, 128, [1056, 1056, 1056], True),    # the same, dense
+    (2, 6, 128, [1030] * 9 + [2100] * 9, False),  # 8 sequences a launch, 3 launches
+    (4, 8, 64, [1200] * 9, True),               # d_v 64, two value heads a key head
+]
+
+
+def _bid(c):
+    return f"H{c[1]}/{c[0]}_dv{c[2]}_N{len(c[3])}_{'dense' if c[4] else 'packed'}"
+
+
+@pytest.mark.parametrize("case", BATCH_CASES, ids=_bid)
+def test_cooperative_batches_against_oracle(case):
+    """More (sequence, key head) groups than one launch holds: consecutive
+    launches on one workspace, each left clean for the next; every slice
+    against the oracle, with initial states carried in."""
+    H_k, H_v, d_v, lens, dense = case
+    if dense:
+        w = synth.custom(H_k, H_v, 128, d_v, "bf16", seq_len=lens[0], num_seqs=len(lens), chunk=32)
+    else:
+        w = synth.custom(H_k, H_v, 128, d_v, "bf16", lengths=lens, chunk=32)
+    note(f"[coop batches] {_bid(case)}")
+    inp = synth.make_inputs(w, 55, device=DEV)
+    ws = workspace_for(w)
+    # the workspace is sized for one launch, not for the whole batch
+    assert ws.numel() < 2048 + len(lens) * H_k * (512 + (H_v // H_k) * 16 * 7168)
+    o, S = run(inp, w, ws)
+    check_clean(ws)
+    ref = U.oracle_full(inp, inp["cu_host"])
+    eo, es = U.compare_full(o, S, ref[0], ref[1], inp["cu_host"], w.H_v)
+    note(f"  max rel err o={eo:.3e} S={es:.3e}")
+    assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], (eo, es)
+    # the same bits again on the same workspace
+    o2, S2 = run(inp, w, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2)
