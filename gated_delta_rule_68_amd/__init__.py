@@ -321,14 +321,15 @@ def _fwd(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, num_
 
 def chunked_path(H_k, H_v, d_k, d_v, dtype, chunk=32) -> str:
     """Name of the kernel gdr_chunked_fwd runs for this shape: "matrix_bf16"
-    (matrix cores, bf16 operands, fp32 accumulation) or "vector_f32"."""
+    (matrix cores, bf16 operands, fp32 accumulation), "matrix_f32" (matrix
+    cores on fp32 operands) or "vector_f32"."""
     code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else (
         GDR_F32 if dtype in ("f32", "float32") else GDR_BF16)
     s = _make_shape(1, H_k, H_v, d_k, d_v, None, 1, code, chunk, None, 1e-6)
     rc = lib().gdr_chunked_path(ctypes.byref(s))
     if rc < 0:
         _raise("gdr_chunked_path", -rc)
-    return {0: "vector_f32", 1: "matrix_bf16"}[rc]
+    return {0: "vector_f32", 1: "matrix_bf16", 2: "matrix_f32"}[rc]
 
 
 def recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, cu_seqlens=None,

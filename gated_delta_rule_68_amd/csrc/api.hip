@@ -692,6 +692,7 @@ int gdr_chunked_path(const gdr_shape *shape) {
   if (st != GDR_OK) return -(int)st;
   if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return -(int)GDR_ERR_UNSUPPORTED;
   if (chunked_mfma_supports(pr)) return GDR_PATH_MATRIX_BF16;
+  if (chunked_f32mma_supports(pr)) return GDR_PATH_MATRIX_F32;
   if (chunked_vec_supports(pr)) return GDR_PATH_VECTOR_F32;
   return -(int)GDR_ERR_UNSUPPORTED;
 }

@@ -1,6 +1,7 @@
 // Chunked (UT-transform) form of the gated delta rule on the vector ALUs, in
-// fp32 throughout.  Serves every supported shape; the matrix-core kernel
-// (chunked_mfma.hip) takes over bf16 inputs at d_k = d_v = 128, chunk 32.
+// fp32 throughout.  Serves every supported shape; the matrix-core kernels
+// take over bf16 inputs at d_k = d_v = 128, chunk 32 (chunked_mfma.hip) and
+// fp32 inputs of the rule at d_k = 64 or 128, chunk 32 (chunked_f32mma.hip).
 //
 // The regrouping (GatedDeltaRule.ixx File Reference, "Detailed Description":
 // one triangular solve per chunk, same arithmetic as the recurrence; Track L
@@ -361,6 +362,7 @@ bool chunked_vec_supports(const Problem &p) {
 
 hipError_t launch_chunked_vec(const Problem &pr, const FwdArgs &x, hipStream_t s) {
   const bool f = pr.dtype == GDR_F32;
+  if (chunked_f32mma_supports(pr)) return launch_chunked_f32mma(pr, x, s);
   if (pr.mode == kModeSSD) return f ? launch_dk<float, kModeSSD>(pr, x, s) : launch_dk<bf16, kModeSSD>(pr, x, s);
   if (pr.mode == kModeKDA) return f ? launch_dk<float, kModeKDA>(pr, x, s) : launch_dk<bf16, kModeKDA>(pr, x, s);
   return f ? launch_dk<float, kModeRule>(pr, x, s) : launch_dk<bf16, kModeRule>(pr, x, s);

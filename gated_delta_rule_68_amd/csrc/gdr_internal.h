@@ -85,6 +85,11 @@ hipError_t launch_gated_rmsnorm(const Problem &p, const NormArgs &x, hipStream_t
 hipError_t launch_silu_gate(const Problem &p, void *y, const void *z, hipStream_t s);
 hipError_t launch_recurrent(const Problem &p, const FwdArgs &x, hipStream_t s);
 hipError_t launch_chunked_vec(const Problem &p, const FwdArgs &x, hipStream_t s);
+// fp32 inputs of the rule on the matrix cores in fp32 (d_k = 64 or 128,
+// d_v = 16, 32, 64 or 128, chunk 32); launch_chunked_vec runs it where it
+// applies.
+bool chunked_f32mma_supports(const Problem &p);
+hipError_t launch_chunked_f32mma(const Problem &p, const FwdArgs &x, hipStream_t s);
 hipError_t launch_chunked_mfma(const Problem &p, const FwdArgs &x, hipStream_t s);
 
 // Shapes each kernel family is instantiated for.

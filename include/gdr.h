@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 10
+#define GDR_ABI_VERSION 11
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -353,7 +353,7 @@ GDR_API gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t s
  * or initial_state itself.  The chunked form needs chunk 16, 32 or 64 and
  * runs on the matrix cores for bf16 with N = 128, P = 64 or 128 and
  * chunk 32 (gdr_chunked_path tells which, as for the rule), else on the
- * vector ALUs in fp32.  The gate is a second launch over y.
+ * vector ALUs in fp32 (fp32 inputs always take the vector ALUs here).  The gate is a second launch over y.
  */
 GDR_API gdr_status gdr_ssd_recurrent_fwd(const gdr_shape *shape, const void *x, const void *delta,
                                          const float *A, const void *B, const void *C,
@@ -436,10 +436,13 @@ GDR_API gdr_status gdr_kda_chunked_split_workspace(const gdr_shape *shape, int32
 
 /* Which kernel gdr_chunked_fwd runs for `shape`: GDR_PATH_VECTOR_F32 (fp32
  * on the vector ALUs), GDR_PATH_MATRIX_BF16 (matrix cores, bf16 operands,
- * fp32 accumulation and state), or the negated gdr_status that
+ * fp32 accumulation and state), GDR_PATH_MATRIX_F32 (fp32 inputs with
+ * d_k = 64 or 128, d_v a multiple of 16 and chunk 32: matrix cores with
+ * fp32 operands, products and state), or the negated gdr_status that
  * gdr_chunked_fwd would return for this shape (pointers are not checked). */
 #define GDR_PATH_VECTOR_F32 0
 #define GDR_PATH_MATRIX_BF16 1
+#define GDR_PATH_MATRIX_F32 2
 GDR_API int gdr_chunked_path(const gdr_shape *shape);
 
 /* Human-readable name of a status code (static storage, never NULL). */

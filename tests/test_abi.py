@@ -190,7 +190,10 @@ def test_binding_refuses_cpu_tensors(gdr):
 def test_chunked_path_selection(gdr):
     lib = gdr.lib()
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=128, chunk=32))) == 1
-    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=0, d_k=128, d_v=128, chunk=32))) == 0
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=0, d_k=128, d_v=128, chunk=32))) == 2
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=0, d_k=64, d_v=32, chunk=32))) == 2
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=0, d_k=128, d_v=128, chunk=16))) == 0
+    assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=0, d_k=32, d_v=128, chunk=32))) == 0
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=128, chunk=16))) == 0
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=64, d_v=128, chunk=32))) == 0
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, dtype=1, d_k=128, d_v=64, chunk=32))) == 1
@@ -198,7 +201,8 @@ def test_chunked_path_selection(gdr):
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, chunk=48))) == -3
     assert lib.gdr_chunked_path(ctypes.byref(shape(gdr, H_v=3, H_k=2))) == -2
     assert gdr.chunked_path(16, 48, 128, 128, "bf16", 32) == "matrix_bf16"
-    assert gdr.chunked_path(1, 1, 128, 128, "f32", 32) == "vector_f32"
+    assert gdr.chunked_path(1, 1, 128, 128, "f32", 32) == "matrix_f32"
+    assert gdr.chunked_path(1, 1, 128, 128, "f32", 64) == "vector_f32"
 
 
 # ------------------------------------------ the layer's steps either side of the rule

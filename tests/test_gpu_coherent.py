@@ -71,11 +71,10 @@ def args(inp):
 @pytest.mark.parametrize("eps,tag", EPS, ids=[t for _, t in EPS])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_coherent_keys_chunked(dtype, eps, tag):
-    """gdr_chunked_fwd: the matrix-core kernel (bf16) and the vector kernel
-    (fp32)."""
+    """gdr_chunked_fwd: the matrix-core kernels (bf16 and fp32 operands)."""
     w = workload(dtype)
     path = gdr.chunked_path(2, 6, 128, 128, dtype, 32)
-    assert path == ("matrix_bf16" if dtype == "bf16" else "vector_f32")
+    assert path == ("matrix_bf16" if dtype == "bf16" else "matrix_f32")
     note(f"[coherent] chunked {path} {tag} lens={w.seq_lengths}")
     inp = inputs(w, 41, eps)
     o, S = gdr.chunked_fwd(*args(inp), chunk=32, cu_seqlens=inp["cu_seqlens"])
