@@ -69,15 +69,21 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x + dpp<0x140>(x);  // row_mirror
 }
 
-// Inclusive prefix sum over lanes 0..31 (rows of 16 by DPP shifts, then row
-// 0's total into row 1).
-__device__ __forceinline__ float scan32(float x) {
-  x += dpp<0x111>(x);  // row_shr:1
-  x += dpp<0x112>(x);  // row_shr:2
-  x += dpp<0x114>(x);  // row_shr:4
-  x += dpp<0x118>(x);  // row_shr:8
-  x += dpp<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-  return x;
+// Inclusive prefix sum of x over lanes 0..31, added in lane order (one
+// running sum, as a sequential loop would form it): neighbouring sums then
+// differ by one rounded addition, and the zero rows past a chunk's end keep
+// the last real row's sum exactly, so exp(gamma_last - gamma_r) is exactly 1
+// for the last token.  A tree scan rounds neighbours differently, which
+// under strong decay (|gamma| in the hundreds) costs one ulp of gamma,
+// about 3e-5, in that factor.
+__device__ __forceinline__ float scan32(float x, int lane) {
+  float acc = 0.f, out = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), r));
+    out = lane == r ? acc : out;
+  }
+  return out;
 }
 
 // D (16 x 16) += A (16 x 4) B (4 x 16): lane l = 16 g + m holds A[m][g] and
@@ -181,7 +187,7 @@ __device__ __forceinline__ void load_rows(Rows<DK> &x, const Problem &pr, const 
 __device__ __forceinline__ void make_gates(Gates &G, float a, float b, int cl, float neg_exp_A,
                                            float dtb, int lane) {
   const int r = lane;
-  const float gr = scan32(r < cl ? log_decay(neg_exp_A, a, dtb) : 0.f);
+  const float gr = scan32(r < cl ? log_decay(neg_exp_A, a, dtb) : 0.f, lane);
   G.gam[r] = gr;
   G.beta[r] = r < cl ? sigmoid_f32(b) : 0.f;
   G.eg[r] = expf(gr);
