@@ -18,7 +18,8 @@
 // last chunk is padded with zero rows (k = q = v = 0, g = 0, beta = 0).
 //
 // Launch: one workgroup of four waves per (sequence, value head, 16 columns
-// of d_v), the state slice [d_k, 16] in LDS across the chunk loop.  The raw
+// of d_v), the state slice [d_k, 16] in LDS across the chunk loop; the
+// column blocks of a (sequence, head) share an XCD.  The raw
 // rows of chunk c + 1 are loaded into registers while chunk c is computed,
 // and chunk c + 1's gates are formed during chunk c (two gate buffers).
 // Per chunk, after the rows are stored and their norms taken:
@@ -203,9 +204,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunked_f32mma_kernel(const Probl
   float *o = static_cast<float *>(x.o);
   const int DV = pr.d_v;
   const int nvb = DV / BVF;
-  const int vb = blockIdx.x % nvb;
-  const int h = (blockIdx.x / nvb) % pr.H_v;
-  const int n = blockIdx.x / (nvb * pr.H_v);
+  // Workgroup b runs on XCD b % 8 (workgroups are dealt to the XCDs in
+  // turn).  The (sequence, value head) units go to the XCDs in contiguous
+  // blocks of uc, and all column blocks of a unit to its unit's XCD: they
+  // read the same k and q rows, which then come from one L2.
+  const int units = pr.num_seqs * pr.H_v, uc = (units + 7) / 8;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int unit = xcd * uc + slot / nvb;
+  if (unit >= units) return;  // the padding of the last XCD's block
+  const int vb = slot % nvb;
+  const int h = unit % pr.H_v;
+  const int n = unit / pr.H_v;
   const int hk = h / (pr.H_v / pr.H_k);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -459,8 +468,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunked_f32mma_kernel(const Probl
 
 template <int DK>
 hipError_t launch_dk(const Problem &pr, const FwdArgs &x, hipStream_t s) {
-  const int64_t grid = (int64_t)pr.num_seqs * pr.H_v * (pr.d_v / BVF);
-  if (grid == 0) return hipSuccess;
+  const int64_t units = (int64_t)pr.num_seqs * pr.H_v;
+  if (units == 0) return hipSuccess;
+  const int64_t grid = 8 * ((units + 7) / 8) * (pr.d_v / BVF);  // see the kernel's mapping
   const size_t smem = sizeof(F32Smem<DK>);
   auto kern = chunked_f32mma_kernel<DK>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
