@@ -510,27 +510,29 @@ def gated_rmsnorm(o, z, weight, eps=1e-6, *, out=None):
 
 
 def chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segment_len,
-                      chunk=32, num_seqs=None, scale=None, l2_eps=1e-6, o=None,
-                      final_state=None, output_final_state=True, inplace=False):
+                      chunk=32, cu_seqlens=None, num_seqs=None, scale=None, l2_eps=1e-6,
+                      o=None, final_state=None, output_final_state=True, inplace=False):
     """Chunked form with every sequence cut into segments of ``segment_len``
-    tokens run in parallel (two-level scan).  Dense batches, d_k == d_v; the
-    workspace is allocated here with torch."""
+    tokens run in parallel (two-level scan).  Dense batches (sequence length a
+    multiple of segment_len) or packed ones (cu_seqlens: any lengths, the last
+    segment of a sequence partial); the workspace is allocated here with
+    torch."""
     return _split("gdr_chunked_fwd_split", q, k, v, a, b, A_log, dt_bias, initial_state,
-                  segment_len, chunk, num_seqs, scale, l2_eps, o, final_state,
+                  segment_len, chunk, cu_seqlens, num_seqs, scale, l2_eps, o, final_state,
                   output_final_state, inplace, kda=False)
 
 
 def kda_chunked_fwd_split(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, segment_len,
-                          chunk=32, num_seqs=None, scale=None, l2_eps=1e-6, o=None,
-                          final_state=None, output_final_state=True, inplace=False):
+                          chunk=32, cu_seqlens=None, num_seqs=None, scale=None, l2_eps=1e-6,
+                          o=None, final_state=None, output_final_state=True, inplace=False):
     """The segmented chunked form for KDA (a [.., H_v, d_k], dt_bias [H_v, d_k])."""
     return _split("gdr_kda_chunked_fwd_split", q, k, v, a, b, A_log, dt_bias, initial_state,
-                  segment_len, chunk, num_seqs, scale, l2_eps, o, final_state,
+                  segment_len, chunk, cu_seqlens, num_seqs, scale, l2_eps, o, final_state,
                   output_final_state, inplace, kda=True)
 
 
-def _split(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, segment_len, chunk, num_seqs,
-           scale, l2_eps, o, final_state, output_final_state, inplace, kda):
+def _split(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, segment_len, chunk, cu_seqlens,
+           num_seqs, scale, l2_eps, o, final_state, output_final_state, inplace, kda):
     dense_T = q.shape[1] if q.dim() == 4 else None
     q, k, v = _flatten(q, 2), _flatten(k, 2), _flatten(v, 2)
     a, b = _flatten(a, 2 if kda else 1), _flatten(b, 1)
@@ -548,8 +550,10 @@ def _split(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, segment_len, c
     _check(b, "b", dev, dt, (total, H_v))
     _check(A_log, "A_log", dev, torch.float32, (H_v,))
     _check(dt_bias, "dt_bias", dev, torch.float32, (H_v, d_k) if kda else (H_v,))
-    shape = _make_shape(total, H_k, H_v, d_k, d_v, None, num_seqs, code, chunk, scale, l2_eps,
-                        dense_T)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    shape = _make_shape(total, H_k, H_v, d_k, d_v, cu_seqlens, num_seqs, code, chunk, scale,
+                        l2_eps, dense_T)
     N = shape.num_seqs
     st_shape = (N, H_v, d_k, d_v)
     if initial_state is not None:

@@ -474,18 +474,27 @@ bool chunked_any_supports(const Problem &pr) {
   if (pr.mode == kModeKDA) return chunked_kda_supports(pr) || chunked_vec_supports(pr);
   return chunked_mfma_supports(pr) || chunked_vec_supports(pr);
 }
+// Whether some sequence has more than one segment (a packed batch: unless
+// the whole batch fits one segment, since its lengths stay on the device);
+// otherwise the segmented form is the direct one.
+bool split_runs(const Problem &pr, int32_t segment_len) {
+  return pr.cu ? pr.total > segment_len : pr.seq_len / segment_len > 1;
+}
 gdr_status split_problem(const gdr_shape *shape, int32_t segment_len, Problem &pr,
                          int mode = kModeRule) {
   gdr_status st = resolve(shape, pr);
   if (st != GDR_OK) return st;
   pr.mode = mode;
   if (pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
-  if (pr.cu != nullptr || pr.d_k != pr.d_v) return GDR_ERR_UNSUPPORTED;
   if (segment_len <= 0 || segment_len % pr.chunk != 0) return GDR_ERR_SHAPE;
-  if (pr.seq_len % segment_len != 0) return GDR_ERR_SHAPE;
-  if (!chunked_any_supports(pr)) return GDR_ERR_UNSUPPORTED;
-  if ((int64_t)pr.num_seqs * (pr.seq_len / segment_len) > 0x7fffffffLL / pr.H_v)
-    return GDR_ERR_UNSUPPORTED;
+  if (pr.cu == nullptr && pr.seq_len % segment_len != 0) return GDR_ERR_SHAPE;
+  // the segments run on the kernels of the problem itself and, for the
+  // transition maps, of the same problem with d_k-wide values
+  Problem m = pr;
+  m.d_v = pr.d_k;
+  if (!chunked_any_supports(pr) || !chunked_any_supports(m)) return GDR_ERR_UNSUPPORTED;
+  const int64_t slots = split_slots(pr, segment_len);
+  if (slots > 0x7fffffffLL / pr.H_v / (pr.d_k > pr.d_v ? pr.d_k : pr.d_v)) return GDR_ERR_UNSUPPORTED;
   return GDR_OK;
 }
 }  // namespace
@@ -498,7 +507,7 @@ gdr_status gdr_chunked_split_workspace(const gdr_shape *shape, int32_t segment_l
   Problem pr;
   const gdr_status st = split_problem(shape, segment_len, pr);
   if (st != GDR_OK) return st;
-  *bytes = pr.seq_len / segment_len > 1 ? split_layout(pr, segment_len).bytes : 0;
+  *bytes = split_runs(pr, segment_len) ? split_layout(pr, segment_len).bytes : 0;
   return GDR_OK;
 }
 
@@ -509,7 +518,7 @@ gdr_status gdr_kda_chunked_split_workspace(const gdr_shape *shape, int32_t segme
   Problem pr;
   const gdr_status st = split_problem(shape, segment_len, pr, kModeKDA);
   if (st != GDR_OK) return st;
-  *bytes = pr.seq_len / segment_len > 1 ? split_layout(pr, segment_len).bytes : 0;
+  *bytes = split_runs(pr, segment_len) ? split_layout(pr, segment_len).bytes : 0;
   return GDR_OK;
 }
 
@@ -526,7 +535,7 @@ gdr_status split_call(int mode, const gdr_shape *shape, int32_t segment_len, con
   FwdArgs x{q, k, v, a, b, A_log, dt_bias, initial_state, o, final_state};
   st = check_fwd(pr, x);
   if (st != GDR_OK) return st;
-  if (pr.seq_len / segment_len <= 1) {  // one segment: the direct form
+  if (!split_runs(pr, segment_len)) {  // one segment a sequence: the direct form
     if (mode == kModeKDA)
       return launched(chunked_kda_supports(pr) ? launch_chunked_kda(pr, x, stream)
                                                : launch_chunked_vec(pr, x, stream));

@@ -69,11 +69,18 @@ struct NormArgs {
 
 // Workspace of the segmented chunked form (byte offsets, 256-byte aligned).
 struct SplitLayout {
-  int P;  // segments per sequence
+  int P;   // segments per sequence of a dense batch (0 for a packed one)
+  int NP;  // segment slots of the batch (packed: an upper bound, the rest empty)
   size_t zero_v, ident, M, Sloc, Sin;
+  size_t o_m;             // the M pass's d_k-wide outputs (when d_k != d_v)
+  size_t seg_cu, seg_off; // packed batches: the segments' prefix sums and offsets
   size_t prep;  // KDA on the two-launch form: the prep records (else == bytes)
   size_t bytes;
 };
+// Segment slots of the segmented form: N * (T / segment_len) for a dense
+// batch, total / segment_len + N for a packed one (every sequence of L tokens
+// has max(1, ceil(L / segment_len)) segments).
+int64_t split_slots(const Problem &p, int segment_len);
 SplitLayout split_layout(const Problem &p, int segment_len);
 hipError_t launch_chunked_split(const Problem &p, const FwdArgs &x, int segment_len,
                                 void *workspace, hipStream_t s);

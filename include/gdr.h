@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 11
+#define GDR_ABI_VERSION 12
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -303,16 +303,26 @@ GDR_API gdr_status gdr_chunked_fwd_gated_rmsnorm(const gdr_shape *shape, const v
  * short sequential pass (fp32), and the outputs with a third chunked launch
  * from those entry states: about three times the arithmetic of
  * gdr_chunked_fwd in exchange for segments-per-sequence times the parallelism.
+ * M is d_k x d_k: it comes from the same kernels run with d_k-wide values,
+ * so d_v may differ from d_k when both widths have a chunked kernel.
  * Results agree with gdr_chunked_fwd up to float reassociation.
- *   segment_len : a positive multiple of chunk that divides seq_len, else
- *                 GDR_ERR_SHAPE; segment_len == seq_len runs gdr_chunked_fwd
+ *   segment_len : a positive multiple of chunk, else GDR_ERR_SHAPE.  Dense
+ *                 batches: it must divide seq_len (GDR_ERR_SHAPE), and
+ *                 segment_len == seq_len runs gdr_chunked_fwd.  Packed
+ *                 batches (cu_seqlens): any lengths; a sequence of L tokens
+ *                 has max(1, ceil(L / segment_len)) segments, the last one
+ *                 partial, and the segment map is formed on the device from
+ *                 cu_seqlens (nothing is copied to the host); a batch of at
+ *                 most segment_len tokens in all runs gdr_chunked_fwd
  *   workspace   : device scratch of at least the bytes gdr_chunked_split_workspace
  *                 reports (256-byte aligned; may be NULL when that is 0); it
- *                 may overlap no other argument; contents are not kept
- * Dense batches (cu_seqlens == NULL) with d_k == d_v only, else
- * GDR_ERR_UNSUPPORTED.  Other arguments as gdr_chunked_fwd (final_state may
- * be initial_state).  Several kernels are launched; a launch failure after
- * the first leaves o and final_state unspecified.
+ *                 may overlap no other argument; contents are not kept.  It
+ *                 holds total / segment_len + num_seqs segment states for a
+ *                 packed batch, num_seqs * seq_len / segment_len for a dense one
+ * A shape whose (d_k, d_v) or (d_k, d_k) problem has no chunked kernel
+ * returns GDR_ERR_UNSUPPORTED.  Other arguments as gdr_chunked_fwd
+ * (final_state may be initial_state).  Several kernels are launched; a
+ * launch failure after the first leaves o and final_state unspecified.
  */
 GDR_API gdr_status gdr_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len,
                                          const void *q, const void *k, const void *v,

@@ -289,12 +289,39 @@ def test_split_workspace_size(gdr):
     assert workspace_bytes(gdr, s, 64) == (0, 0)  # one segment: no workspace
 
 
+def test_split_workspace_packed_and_wide_values(gdr):
+    """A packed batch holds total / segment_len + N segment slots (every
+    sequence of L tokens has max(1, ceil(L / segment_len)) segments), plus its
+    segment map; d_k != d_v adds the d_k x d_k maps and the M pass's d_k-wide
+    outputs."""
+    r256 = lambda b: (b + 255) // 256 * 256
+    cu = shape(gdr, num_seqs=3, seq_len=0, total_tokens=100, chunk=16)
+    cu.cu_seqlens = fake(30).value
+    rc, n = workspace_bytes(gdr, cu, 16)
+    NP = 100 // 16 + 3
+    st = NP * 2 * 16 * 16 * 4
+    assert rc == 0
+    assert n == r256(100 * 2 * 16 * 4) + 4 * r256(st) + r256((NP + 1) * 4) + r256(4 * 4)
+    assert workspace_bytes(gdr, cu, 112) == (0, 0)  # the whole batch fits one segment
+    assert workspace_bytes(gdr, cu, 96)[1] > 0
+    assert workspace_bytes(gdr, cu, 24)[0] == 2     # not a multiple of the chunk
+    # d_k = 32, d_v = 16, dense: M and the identities are d_k x d_k
+    s = shape(gdr, num_seqs=2, seq_len=64, total_tokens=128, chunk=16, d_k=32, d_v=16)
+    rc, n = workspace_bytes(gdr, s, 16)
+    NP = 2 * 4
+    st, stm = NP * 2 * 32 * 16 * 4, NP * 2 * 32 * 32 * 4
+    assert rc == 0
+    assert n == r256(128 * 2 * 32 * 4) + 2 * r256(stm) + 2 * r256(st) + r256(128 * 2 * 32 * 4)
+
+
 def test_split_validation(gdr):
     s = shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16)
-    assert split_call(gdr, shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16, d_v=32), 16) == 3
-    cu = shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16)
+    assert split_call(gdr, shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16,
+                                 d_k=16, d_v=256), 16) == 3   # no kernel for d_v = 256
+    cu = shape(gdr, num_seqs=1, seq_len=0, total_tokens=64, chunk=16)
     cu.cu_seqlens = fake(30).value
-    assert split_call(gdr, cu, 16) == 3                      # packed batches: no
+    assert split_call(gdr, cu, 24) == 2                      # packed: a multiple of the chunk
+    assert split_call(gdr, cu, 16, ws_bytes=workspace_bytes(gdr, cu, 16)[1] - 1) == 5
     assert split_call(gdr, s, 0) == 2
     assert split_call(gdr, s, 24) == 2                       # not a multiple of the chunk
     assert split_call(gdr, s, 48) == 2                       # does not divide seq_len

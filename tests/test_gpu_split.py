@@ -29,15 +29,22 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+def batch(w, inp):
+    """The batch arguments: cu_seqlens for a packed workload, else num_seqs."""
+    if w.lengths is not None:
+        return dict(cu_seqlens=inp["cu_seqlens"])
+    return dict(num_seqs=w.num_seqs)
+
+
 def run_split(w, inp, seg, **kw):
     return gdr.chunked_fwd_split(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"],
                                  inp["dt_bias"], inp["initial_state"], segment_len=seg,
-                                 chunk=w.chunk, num_seqs=w.num_seqs, **kw)
+                                 chunk=w.chunk, **batch(w, inp), **kw)
 
 
 def check(w, seed, seg):
-    note(f"[split] H={w.H_v}/{w.H_k} d={w.d_k} {w.dtype} N={w.num_seqs} T={w.seq_len} "
-         f"chunk={w.chunk} segment={seg} seed={seed}")
+    note(f"[split] H={w.H_v}/{w.H_k} d_k={w.d_k} d_v={w.d_v} {w.dtype} N={w.num_seqs} "
+         f"T={w.seq_len} lengths={w.lengths} chunk={w.chunk} segment={seg} seed={seed}")
     inp = synth.make_inputs(w, seed, device=DEV)
     o, S = run_split(w, inp, seg)
     torch.cuda.synchronize()
@@ -113,15 +120,87 @@ def test_split_long_memory_stress():
     check(wf, 38, 128)
 
 
+# ------------------------------------------- packed batches, d_k != d_v
+# lengths with partial last segments, an empty sequence, one token, a length
+# that is a whole number of segments and one shorter than a chunk
+PACKED = [300, 0, 1, 128, 1000, 257, 33]
+
+
+@pytest.mark.parametrize("d,dtype,chunk,seg", [(128, "bf16", 32, 128), (64, "f32", 16, 64),
+                                               (32, "f32", 32, 96)])
+def test_split_packed_ragged(d, dtype, chunk, seg):
+    """A packed batch: every sequence cut into max(1, ceil(L / seg)) segments
+    by the device-side segment map, the last one partial."""
+    w = synth.custom(1, 3, d, d, dtype, lengths=PACKED, chunk=chunk)
+    check(w, 50, seg)
+
+
+def test_split_packed_without_initial_state_and_in_place():
+    w = synth.custom(2, 4, 64, 64, "f32", lengths=[200, 65, 0, 96], chunk=32, init_state=False)
+    check(w, 51, 64)
+    w = synth.custom(2, 4, 64, 64, "f32", lengths=[200, 65, 0, 96], chunk=32)
+    inp = synth.make_inputs(w, 52, device=DEV)
+    o_ref, S_ref = U.oracle_full(inp, inp["cu_host"])
+    st = inp["initial_state"].clone()
+    o, S = run_split(w, dict(inp, initial_state=st), 64, inplace=True)
+    torch.cuda.synchronize()
+    assert S.data_ptr() == st.data_ptr()
+    eo, es = U.compare_full(o, S, o_ref, S_ref, inp["cu_host"], w.H_v)
+    assert eo <= U.TOL["f32"] and es <= U.TOL["f32"], (eo, es)
+
+
+@pytest.mark.parametrize("dk,dv,dtype,chunk,seg,packed", [
+    (128, 64, "bf16", 32, 256, False), (128, 64, "bf16", 32, 128, True),
+    (64, 32, "f32", 16, 64, False), (32, 64, "f32", 32, 64, True)])
+def test_split_key_and_value_widths_differ(dk, dv, dtype, chunk, seg, packed):
+    """d_k != d_v: the segment maps M are d_k x d_k, from the kernels run with
+    d_k-wide values into a workspace buffer rather than o."""
+    if packed:
+        w = synth.custom(1, 2, dk, dv, dtype, lengths=[500, 1, 260], chunk=chunk)
+    else:
+        w = synth.custom(1, 2, dk, dv, dtype, seq_len=4 * seg, num_seqs=2, chunk=chunk)
+    check(w, 53, seg)
+
+
+def test_split_packed_batch_in_one_segment_is_the_direct_form():
+    """A packed batch of at most segment_len tokens runs gdr_chunked_fwd
+    without a workspace (the one-launch form), bit for bit."""
+    w = synth.custom(1, 2, 128, 128, "bf16", lengths=[40, 0, 23], chunk=32)
+    inp = synth.make_inputs(w, 54, device=DEV)
+    o1, S1 = run_split(w, inp, 64)
+    o2, S2 = gdr.chunked_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"],
+                             inp["dt_bias"], inp["initial_state"], chunk=32,
+                             cu_seqlens=inp["cu_seqlens"], workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_split_varlen_workload_sampled():
+    """The varlen workload (8 packed sequences of U[512, 32768] tokens, 48/16
+    heads, carried state, stress sequences 6 and 7) in segments of 2048
+    tokens, against the oracle on two heads of every sequence."""
+    w = synth.workload("varlen", seed=0)
+    note(f"[split] varlen lengths={w.seq_lengths} segment=2048")
+    inp = synth.make_inputs(w, 0, device=DEV)
+    o, S = run_split(w, inp, 2048)
+    torch.cuda.synchronize()
+    cu = inp["cu_host"]
+    pairs = [(n, h) for n in range(w.num_seqs) for h in (0, 29)]
+    ref = U.oracle_pairs(inp, cu, pairs)
+    eo, es, per = U.compare_sampled(o, S, ref, cu)
+    note(f"  max rel err o={eo:.3e} S={es:.3e}")
+    assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], per
+
+
 # ---------------------------------------------------------------- KDA segments
 def check_kda(w, seed, seg, a_mean=0.0):
     from oracle import kda
-    note(f"[kda split] H={w.H_v}/{w.H_k} d={w.d_k} {w.dtype} N={w.num_seqs} T={w.seq_len} "
-         f"chunk={w.chunk} segment={seg} seed={seed}")
+    note(f"[kda split] H={w.H_v}/{w.H_k} d_k={w.d_k} d_v={w.d_v} {w.dtype} N={w.num_seqs} "
+         f"T={w.seq_len} lengths={w.lengths} chunk={w.chunk} segment={seg} seed={seed}")
     inp = synth.kda_inputs(w, seed, device=DEV, a_mean=a_mean)
     args = (inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
             inp["initial_state"])
-    o, S = gdr.kda_chunked_fwd_split(*args, segment_len=seg, chunk=w.chunk, num_seqs=w.num_seqs)
+    o, S = gdr.kda_chunked_fwd_split(*args, segment_len=seg, chunk=w.chunk, **batch(w, inp))
     torch.cuda.synchronize()
     o_ref, S_ref = kda.kda(*[t.cpu() if t is not None else None for t in args],
                            cu_seqlens=inp["cu_host"])
@@ -147,3 +226,12 @@ def test_kda_split_one_segment_is_the_direct_form_and_long_memory():
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
     wl = synth.custom(1, 1, 64, 64, "f32", seq_len=2048, num_seqs=1, chunk=32)
     check_kda(wl, 42, 256, a_mean=-6.0)  # long memory: the segment maps carry the state
+
+
+@pytest.mark.parametrize("dtype,chunk,seg,dv", [("bf16", 32, 256, 128), ("bf16", 32, 128, 64),
+                                                ("f32", 16, 64, 128)])
+def test_kda_split_packed(dtype, chunk, seg, dv):
+    """KDA on packed batches (bf16 chunk 32: one prep over all segment slots
+    serves the three chain passes), also with d_v != d_k."""
+    w = synth.custom(1, 2, 128, dv, dtype, lengths=[700, 0, 65, 1024, 1], chunk=chunk)
+    check_kda(w, 55, seg)
