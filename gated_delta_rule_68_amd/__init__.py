@@ -42,7 +42,8 @@ __all__ = ["gates", "recurrent_fwd", "chunked_fwd", "chunked_fwd_split", "fwd", 
            "chunked_workspace", "chunked_workspace_bytes", "workspace_error",
            "gated_rmsnorm", "library_path", "lib", "GdrError", "abi_version",
            "chunked_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "chunked_fwd_gated_rmsnorm",
-           "ssd_recurrent_fwd", "ssd_chunked_fwd", "kda_recurrent_fwd", "kda_chunked_fwd",
+           "ssd_recurrent_fwd", "ssd_chunked_fwd", "ssd_chunked_fwd_split", "kda_recurrent_fwd",
+           "kda_chunked_fwd",
            "kda_chunked_fwd_split"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -105,7 +106,10 @@ def _bind(lib):
     for name in ("gdr_chunked_fwd_split", "gdr_kda_chunked_fwd_split"):
         getattr(lib, name).argtypes = [sp, ctypes.c_int32] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
         getattr(lib, name).restype = ctypes.c_int
-    for name in ("gdr_chunked_split_workspace", "gdr_kda_chunked_split_workspace"):
+    lib.gdr_ssd_chunked_fwd_split.argtypes = [sp, ctypes.c_int32] + [vp] * 9 + [vp, ctypes.c_size_t, vp]
+    lib.gdr_ssd_chunked_fwd_split.restype = ctypes.c_int
+    for name in ("gdr_chunked_split_workspace", "gdr_kda_chunked_split_workspace",
+                 "gdr_ssd_chunked_split_workspace"):
         getattr(lib, name).argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         getattr(lib, name).restype = ctypes.c_int
     lib.gdr_kda_recurrent_fwd.argtypes = [sp] + [vp] * 11
@@ -586,7 +590,7 @@ def _split(fn_name, q, k, v, a, b, A_log, dt_bias, initial_state, segment_len, c
 
 
 def _ssd(fn_name, x, delta, A, B, C, initial_state, z, cu_seqlens, num_seqs, chunk, y,
-         final_state, output_final_state, inplace):
+         final_state, output_final_state, inplace, segment_len=None):
     dense_T = x.shape[1] if x.dim() == 4 else None
     x, B, C = _flatten(x, 2), _flatten(B, 2), _flatten(C, 2)
     delta = _flatten(delta, 1)
@@ -624,9 +628,19 @@ def _ssd(fn_name, x, delta, A, B, C, initial_state, z, cu_seqlens, num_seqs, chu
         final_state = torch.empty(st_shape, dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check(final_state, "final_state", dev, torch.float32, st_shape)
-    rc = getattr(lib(), fn_name)(ctypes.byref(shape), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
-                                 _ptr(C), _ptr(initial_state), _ptr(z), _ptr(y),
-                                 _ptr(final_state), _stream(dev))
+    ptrs = [_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(initial_state), _ptr(z),
+            _ptr(y), _ptr(final_state)]
+    if segment_len is None:
+        rc = getattr(lib(), fn_name)(ctypes.byref(shape), *ptrs, _stream(dev))
+    else:
+        nbytes = ctypes.c_size_t(0)
+        _raise("gdr_ssd_chunked_split_workspace",
+               lib().gdr_ssd_chunked_split_workspace(ctypes.byref(shape), int(segment_len),
+                                                     ctypes.byref(nbytes)))
+        ws = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
+        rc = getattr(lib(), fn_name)(ctypes.byref(shape), int(segment_len), *ptrs,
+                                     _ptr(ws) if nbytes.value else None, int(nbytes.value),
+                                     _stream(dev))
     _raise(fn_name, rc)
     if dense_T is not None:
         y = y.view(S, dense_T, H, P)
@@ -649,6 +663,17 @@ def ssd_chunked_fwd(x, delta, A, B, C, initial_state=None, *, z=None, chunk=32,
     """Mamba-2 SSD recurrence, chunked form (same arguments plus ``chunk``)."""
     return _ssd("gdr_ssd_chunked_fwd", x, delta, A, B, C, initial_state, z, cu_seqlens,
                 num_seqs, chunk, y, final_state, output_final_state, inplace)
+
+
+def ssd_chunked_fwd_split(x, delta, A, B, C, initial_state=None, *, segment_len, z=None,
+                          chunk=32, cu_seqlens=None, num_seqs=None, y=None, final_state=None,
+                          output_final_state=True, inplace=False):
+    """Mamba-2 SSD recurrence in the segmented chunked form (two-level scan;
+    arguments as ssd_chunked_fwd plus ``segment_len``, batches as
+    chunked_fwd_split); the workspace is allocated here with torch."""
+    return _ssd("gdr_ssd_chunked_fwd_split", x, delta, A, B, C, initial_state, z, cu_seqlens,
+                num_seqs, chunk, y, final_state, output_final_state, inplace,
+                segment_len=segment_len)
 
 
 def kda_recurrent_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, cu_seqlens=None,

@@ -575,15 +575,10 @@ namespace gdr {
 namespace {
 // SSD: the rule's kernels in mode 1 (q = C, k = B, v = x, a = delta, A_log
 // holds A, no b and no dt_bias); z gates the output afterwards.
-gdr_status ssd_call(const gdr_shape *shape, bool chunked, const void *x, const void *delta,
-                    const float *A, const void *B, const void *C, const float *initial_state,
-                    const void *z, void *y, float *final_state, hipStream_t stream) {
-  Problem pr;
-  gdr_status st = resolve(shape, pr);
-  if (st != GDR_OK) return st;
-  pr.mode = kModeSSD;
-  pr.scale = 1.0f;
-  if (chunked && pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
+// Pointer, alignment and aliasing checks of the SSD calls.
+gdr_status ssd_check(const Problem &pr, const void *x, const void *delta, const float *A,
+                     const void *B, const void *C, const float *initial_state, const void *z,
+                     void *y, float *final_state) {
   if (!A) return GDR_ERR_NULL;
   if (pr.total > 0 && (!x || !delta || !B || !C || !y)) return GDR_ERR_NULL;
   const void *rows[] = {x, B, C, z, y, initial_state, final_state};
@@ -610,6 +605,20 @@ gdr_status ssd_call(const gdr_shape *shape, bool chunked, const void *x, const v
   if (ry.hi > ry.lo && r0.hi > r0.lo && overlap(ry, r0)) return GDR_ERR_ALIAS;
   if (initial_state && final_state && initial_state != final_state && overlap(r0, rT))
     return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
+gdr_status ssd_call(const gdr_shape *shape, bool chunked, const void *x, const void *delta,
+                    const float *A, const void *B, const void *C, const float *initial_state,
+                    const void *z, void *y, float *final_state, hipStream_t stream) {
+  Problem pr;
+  gdr_status st = resolve(shape, pr);
+  if (st != GDR_OK) return st;
+  pr.mode = kModeSSD;
+  pr.scale = 1.0f;
+  if (chunked && pr.chunk != 16 && pr.chunk != 32 && pr.chunk != 64) return GDR_ERR_UNSUPPORTED;
+  st = ssd_check(pr, x, delta, A, B, C, initial_state, z, y, final_state);
+  if (st != GDR_OK) return st;
   FwdArgs a{C, B, x, delta, nullptr, A, nullptr, initial_state, y, final_state};
   hipError_t e;
   if (chunked) {
@@ -638,6 +647,44 @@ gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, const void
                                const float *initial_state, const void *z, void *y,
                                float *final_state, hipStream_t stream) {
   return gdr::ssd_call(shape, true, x, delta, A, B, C, initial_state, z, y, final_state, stream);
+}
+
+gdr_status gdr_ssd_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
+                                           size_t *bytes) {
+  using namespace gdr;
+  if (!bytes) return GDR_ERR_NULL;
+  Problem pr;
+  const gdr_status st = split_problem(shape, segment_len, pr, kModeSSD);
+  if (st != GDR_OK) return st;
+  *bytes = split_runs(pr, segment_len) ? split_layout(pr, segment_len).bytes : 0;
+  return GDR_OK;
+}
+
+gdr_status gdr_ssd_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len, const void *x,
+                                     const void *delta, const float *A, const void *B,
+                                     const void *C, const float *initial_state, const void *z,
+                                     void *y, float *final_state, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  using namespace gdr;
+  Problem pr;
+  gdr_status st = split_problem(shape, segment_len, pr, kModeSSD);
+  if (st != GDR_OK) return st;
+  pr.scale = 1.0f;
+  st = ssd_check(pr, x, delta, A, B, C, initial_state, z, y, final_state);
+  if (st != GDR_OK) return st;
+  // the rule's argument slots: C for q, B for k, x for v, delta for a, A for A_log
+  FwdArgs a{C, B, x, delta, nullptr, A, nullptr, initial_state, y, final_state};
+  hipError_t e;
+  if (!split_runs(pr, segment_len)) {  // one segment a sequence: the direct form
+    e = chunked_mfma_supports(pr) ? launch_chunked_mfma(pr, a, stream)
+                                  : launch_chunked_vec(pr, a, stream);
+  } else {
+    st = check_workspace(pr, a, workspace, workspace_bytes, split_layout(pr, segment_len).bytes);
+    if (st != GDR_OK) return st;
+    e = launch_chunked_split(pr, a, segment_len, workspace, stream);
+  }
+  if (e == hipSuccess && z) e = launch_silu_gate(pr, y, z, stream);
+  return launched(e);
 }
 
 gdr_status gdr_kda_recurrent_fwd(const gdr_shape *shape, const void *q, const void *k,

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 12
+#define GDR_ABI_VERSION 13
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -373,6 +373,29 @@ GDR_API gdr_status gdr_ssd_chunked_fwd(const gdr_shape *shape, const void *x, co
                                        const float *A, const void *B, const void *C,
                                        const float *initial_state, const void *z, void *y,
                                        float *final_state, hipStream_t stream);
+
+/*
+ * gdr_ssd_chunked_fwd_split -- the SSD recurrence of gdr_ssd_chunked_fwd in
+ * the segmented form of gdr_chunked_fwd_split (Track L pull request, L4 and
+ * L4.1 for the op, L2 for the cooperative-parallel chunk kernel it lists as
+ * not yet built).  The SSD update h <- exp(delta A) h + B (delta x)^T is
+ * affine in the state too, so each segment's S_out = M S_in + S_loc, M the
+ * segment run from the identity on x = 0 (a scaled identity here, formed by
+ * the same kernels).  Arguments, layouts and errors as gdr_ssd_chunked_fwd;
+ * segment_len, the workspace (gdr_ssd_chunked_split_workspace bytes) and the
+ * dense / packed rules as gdr_chunked_fwd_split.  The gate z applies to the
+ * outputs of the last pass.
+ */
+GDR_API gdr_status gdr_ssd_chunked_fwd_split(const gdr_shape *shape, int32_t segment_len,
+                                             const void *x, const void *delta, const float *A,
+                                             const void *B, const void *C,
+                                             const float *initial_state, const void *z, void *y,
+                                             float *final_state, void *workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace gdr_ssd_chunked_fwd_split needs (0 for one segment). */
+GDR_API gdr_status gdr_ssd_chunked_split_workspace(const gdr_shape *shape, int32_t segment_len,
+                                                   size_t *bytes);
 
 /*
  * gdr_kda_recurrent_fwd / gdr_kda_chunked_fwd -- the rule with one decay per

@@ -40,6 +40,7 @@ def test_header_declares_the_abi():
                                   "gdr_kda_chunked_split_workspace", "gdr_kda_chunked_workspace",
                                   "gdr_kda_recurrent_fwd",
                                   "gdr_recurrent_fwd", "gdr_ssd_chunked_fwd",
+                                  "gdr_ssd_chunked_fwd_split", "gdr_ssd_chunked_split_workspace",
                                   "gdr_ssd_recurrent_fwd", "gdr_status_string"]
 
 
@@ -331,6 +332,30 @@ def test_split_validation(gdr):
     assert split_call(gdr, s, 16, ws=fake(20, off=128)) == 4
     assert split_call(gdr, s, 16, ws=fake(8)) == 7           # over o
     assert split_call(gdr, s, 16, o=fake(0)) == 7            # o over q, as gdr_chunked_fwd
+
+
+def test_ssd_split_validation(gdr):
+    """The SSD's segmented form: the SSD's pointer checks, the split's
+    segment rules; its workspace equals the rule's for the same shape."""
+    lib = gdr.lib()
+    names = ["x", "delta", "A", "B", "C", "s0", "z", "y", "sT"]
+
+    def call(s, seg, ws_bytes=1 << 30, **over):
+        p = {n: fake(i) for i, n in enumerate(names)}
+        p.update(over)
+        return lib.gdr_ssd_chunked_fwd_split(ctypes.byref(s), seg, *[p[n] for n in names],
+                                             fake(20), ws_bytes, None)
+    s = shape(gdr, num_seqs=1, seq_len=64, total_tokens=64, chunk=16)
+    assert call(s, 24) == 2                      # not a multiple of the chunk
+    assert call(s, 48) == 2                      # does not divide seq_len
+    assert call(s, 16, A=None) == 1
+    assert call(s, 16, B=fake(3, off=8)) == 4    # rows need 16 bytes
+    assert call(s, 16, y=fake(0)) == 7           # y over x
+    n_ssd, n_rule = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.gdr_ssd_chunked_split_workspace(ctypes.byref(s), 16, ctypes.byref(n_ssd)) == 0
+    assert lib.gdr_chunked_split_workspace(ctypes.byref(s), 16, ctypes.byref(n_rule)) == 0
+    assert n_ssd.value == n_rule.value > 0
+    assert call(s, 16, ws_bytes=n_ssd.value - 1) == 5
 
 
 # ------------------------------------------------------------- the SSD recurrence

@@ -222,3 +222,55 @@ def test_ssd_rejects_bad_arguments():
     with pytest.raises(ValueError):
         gdr.ssd_chunked_fwd(inp["x"], inp["delta"], inp["A"], inp["B"][:, :, :64].contiguous(),
                             inp["C"])
+
+
+# ------------------------------------------------------- segmented form
+def run_split(inp, seg, chunk=32, num_seqs=None, **kw):
+    return gdr.ssd_chunked_fwd_split(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                     inp["initial_state"], segment_len=seg, z=inp["z"],
+                                     chunk=chunk, cu_seqlens=inp["cu_seqlens"],
+                                     num_seqs=num_seqs, **kw)
+
+
+def check_split(inp, dtype, seg, chunk=32, num_seqs=None, tag=""):
+    note(f"[ssd split] {tag} segment={seg} chunk={chunk} {dtype} N={inp['B'].shape[2]} "
+         f"P={inp['x'].shape[2]} cu={inp['cu_host']}")
+    y, S = run_split(inp, seg, chunk, num_seqs)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle_of(inp)
+    H = inp["x"].shape[1]
+    eo, es = U.compare_full(y.reshape(-1, H, inp["x"].shape[2]), S, y_ref, S_ref,
+                            inp["cu_host"], H)
+    tol = U.TOL[dtype]
+    note(f"  max rel err y={eo:.3e} state={es:.3e} (bar {tol:g})")
+    assert eo <= tol and es <= tol, (eo, es)
+    return y, S
+
+
+@pytest.mark.parametrize("dtype,N,P,chunk,seg", [("bf16", 128, 64, 32, 128),
+                                                 ("bf16", 128, 128, 32, 256),
+                                                 ("f32", 64, 32, 16, 64),
+                                                 ("f32", 16, 64, 32, 96)])
+def test_ssd_split_packed(dtype, N, P, chunk, seg):
+    """Packed batches with partial, empty and one-token sequences, the gate
+    and a carried state; the segment maps are N x N (P differs from N)."""
+    inp = synth.ssd_inputs(2, 4, N, P, dtype, lengths=[700, 0, 1, 257, 128], seed=60,
+                           device=DEV, gate=True)
+    check_split(inp, dtype, seg, chunk)
+
+
+def test_ssd_split_dense_long_and_slow_decay():
+    """A dense batch of long sequences whose state decays slowly (delta in
+    [1e-4, 1e-3]), so the state crosses segments almost whole."""
+    inp = synth.ssd_inputs(1, 2, 128, 64, "bf16", seq_len=4096, num_seqs=2, seed=61,
+                           device=DEV, delta_range=(1e-4, 1e-3))
+    check_split(inp, "bf16", 512, num_seqs=2, tag="slow decay")
+
+
+def test_ssd_split_one_segment_is_the_direct_form():
+    inp = synth.ssd_inputs(1, 2, 128, 64, "bf16", lengths=[40, 0, 23], seed=62, device=DEV,
+                           gate=True)
+    y1, S1 = run_split(inp, 64)
+    y2, S2 = run("chunked", inp, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(S1, S2)
