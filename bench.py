@@ -442,6 +442,35 @@ def split_legs(gdr, dev, stream, steps):
                                   "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
                                   "flop_per_launch": flops}}
         del inp, args
+    # one GPU's share of the prefill layer sharded 8 ways by key-head groups
+    # (6 value heads sharing 2 key heads, 8192 tokens): the direct forms fill
+    # an eighth of the compute units, the segmented form all of them
+    w = synth.custom(2, 6, 128, 128, "bf16", seq_len=8192, num_seqs=1, chunk=32)
+    inp = synth.make_inputs(w, 0, device=dev)
+    args = (inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+            inp["initial_state"])
+    T = w.total_tokens
+    ws = gdr.chunked_workspace(w.H_k, w.H_v, w.d_k, w.d_v, w.dtype, 1, chunk=32, device=dev)
+    coop_ms = timed(lambda: gdr.chunked_fwd(*args, chunk=32, num_seqs=1, workspace=ws))
+    direct_ms = timed(lambda: gdr.chunked_fwd(*args, chunk=32, num_seqs=1))
+    by_seg = {seg: timed(lambda: gdr.chunked_fwd_split(*args, segment_len=seg, chunk=32,
+                                                       num_seqs=1))
+              for seg in (512, 1024, 2048)}
+    best = min(by_seg, key=by_seg.get)
+    split_ms = by_seg[best]
+    flops = prefill_flops(T, w.H_k, w.H_v, w.d_k, w.d_v, w.chunk)
+    tf = flops / (split_ms / 1e3) / 1e12
+    res["shard_8way_6v_2k_8192_bf16"] = {
+        "workload": f"one GPU's share of the prefill layer sharded 8 ways by key-head groups: "
+                    f"1 sequence x {T} tokens, 6 value heads sharing 2 key heads, d_k=d_v=128, "
+                    f"bf16, chunk 32",
+        "direct_ms": coop_ms, "one_launch_ms": direct_ms,
+        "split_ms_by_segment": {str(k): v for k, v in by_seg.items()},
+        "split_ms": split_ms, "segment_len": best, "speedup": coop_ms / split_ms,
+        "tokens_per_s": T / (split_ms / 1e3),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "flop_per_launch": flops}}
+    del inp, args, ws
     # the per-channel-decay variant on one long head (its chunk step is slower
     # than the rule's, so the chain of chunks weighs more)
     w = synth.custom(1, 1, 128, 128, "bf16", seq_len=16384, num_seqs=1, chunk=32)

@@ -137,15 +137,19 @@ gdr_status check_workspace(const Problem &pr, const FwdArgs &x, const void *work
 // (each launch fills and drains a pipeline of a few chunks, which the
 // one-launch form, running every chain at once, does not).
 constexpr int64_t kCoopMinTokens = 1024;
+}  // namespace
 bool coop_runs(const Problem &pr, int per) {
   if (per <= 0 || pr.total <= 0) return false;
   return per >= pr.num_seqs || pr.total >= kCoopMinTokens * pr.num_seqs;
 }
+namespace {
+
+}  // namespace
 
 // The cooperative form over consecutive batches of `per` sequences on one
 // workspace (each launch leaves it zero-filled for the next).  A batch whose
 // launch fails runs the one-launch form instead.
-gdr_status run_coop_batches(const Problem &pr, const FwdArgs &x, int per, void *ws,
+hipError_t run_coop_batches(const Problem &pr, const FwdArgs &x, int per, void *ws,
                             hipStream_t stream) {
   const size_t es = elem_size(pr.dtype);
   const size_t state = (size_t)pr.H_v * pr.d_k * pr.d_v;  // fp32 per sequence
@@ -173,12 +177,14 @@ gdr_status run_coop_batches(const Problem &pr, const FwdArgs &x, int per, void *
     if (x.sT) y.sT = x.sT + (size_t)s0 * state;
     if (launch_chunked_coop(sub, y, ws, stream) != hipSuccess) {
       (void)hipGetLastError();  // a failed launch: the one-launch form
-      const gdr_status st = launched(launch_chunked_mfma(sub, y, stream));
-      if (st != GDR_OK) return st;
+      const hipError_t e = launch_chunked_mfma(sub, y, stream);
+      if (e != hipSuccess) return e;
     }
   }
-  return GDR_OK;
+  return hipSuccess;
 }
+
+namespace {
 
 // Device address of `scratch` on the current device, looked up on the first
 // call per device (with that device current) and kept.
@@ -304,7 +310,7 @@ gdr_status gdr_chunked_fwd(const gdr_shape *shape, const void *q, const void *k,
     if (coop_runs(pr, per)) {
       st = check_workspace(pr, x, workspace, workspace_bytes, chunked_coop_workspace_bytes(pr));
       if (st != GDR_OK) return st;
-      return run_coop_batches(pr, x, per, workspace, stream);
+      return launched(run_coop_batches(pr, x, per, workspace, stream));
     }
     return launched(launch_chunked_mfma(pr, x, stream));
   }
@@ -336,7 +342,7 @@ gdr_status gdr_chunked_fwd_noalloc(const gdr_shape *shape, const void *q, const 
       Problem first = pr;
       first.num_seqs = per;
       if (clear_chunked_coop(first, ws, stream) != hipSuccess) return GDR_ERR_LAUNCH;
-      return run_coop_batches(pr, x, per, ws, stream);
+      return launched(run_coop_batches(pr, x, per, ws, stream));
     }
     return launched(launch_chunked_mfma(pr, x, stream));
   }

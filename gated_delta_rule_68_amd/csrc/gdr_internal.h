@@ -73,6 +73,7 @@ struct SplitLayout {
   int NP;  // segment slots of the batch (packed: an upper bound, the rest empty)
   size_t zero_v, ident, M, Sloc, Sin;
   size_t o_m;             // the M pass's d_k-wide outputs (when d_k != d_v)
+  size_t coop;            // the cooperative form's workspace for the passes (else == seg_cu)
   size_t seg_cu, seg_off; // packed batches: the segments' prefix sums and offsets
   size_t prep;  // KDA on the two-launch form: the prep records (else == bytes)
   size_t bytes;
@@ -121,6 +122,15 @@ size_t chunked_coop_workspace_bytes(const Problem &p);
 int chunked_coop_seqs_per_launch(const Problem &p);
 hipError_t launch_chunked_coop(const Problem &p, const FwdArgs &x, void *workspace,
                                hipStream_t s);
+// Whether gdr_chunked_fwd takes the cooperative form for a batch of which
+// `per` sequences fit one launch (per = chunked_coop_seqs_per_launch(p)).
+bool coop_runs(const Problem &p, int per);
+// The cooperative form over consecutive launches of `per` sequences on one
+// workspace of chunked_coop_workspace_bytes(p) bytes that is zero where
+// clear_chunked_coop zeroes it (each launch leaves it so); a launch that
+// fails runs the one-launch form for its sequences.
+hipError_t run_coop_batches(const Problem &p, const FwdArgs &x, int per, void *workspace,
+                            hipStream_t s);
 // Zero, on stream s, what launch_chunked_coop needs zero in a workspace of
 // chunked_coop_workspace_bytes(p) bytes (its counters, error words, flags and
 // progress words; not the records), with a fill kernel.

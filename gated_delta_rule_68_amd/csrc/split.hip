@@ -208,6 +208,27 @@ unsigned fill_blocks(int64_t n) {
 
 }  // namespace
 
+Problem segments(const Problem &pr, int segment_len);
+
+// The passes of the rule in bf16 on the matrix cores run in the cooperative
+// form when its launches take the segments as gdr_chunked_fwd would take
+// them (every segment's (segment, key head) group in one launch, or
+// consecutive launches of long enough segments): its workspace, sized for
+// the wider of the two pass shapes, or 0.
+size_t split_coop_bytes(const Problem &pr, int segment_len) {
+  if (pr.mode != kModeRule) return 0;
+  Problem seg = segments(pr, segment_len);
+  Problem segm = seg;
+  segm.d_v = pr.d_k;
+  size_t bytes = 0;
+  for (const Problem *q : {&seg, &segm}) {
+    if (!chunked_mfma_supports(*q) || !coop_runs(*q, chunked_coop_seqs_per_launch(*q))) return 0;
+    const size_t b = chunked_coop_workspace_bytes(*q);
+    bytes = b > bytes ? b : bytes;
+  }
+  return bytes;
+}
+
 // The segments of a batch as one batch: a dense batch of num_seqs * P
 // sequences of segment_len tokens, or for a packed batch a packed batch of
 // NP segment slots whose prefix sums (segcu, written on the device by
@@ -245,7 +266,8 @@ SplitLayout split_layout(const Problem &pr, int segment_len) {
   L.Sin = L.Sloc + round256(st);
   // the M pass writes d_k-wide outputs: into o when d_v == d_k, else here
   L.o_m = L.Sin + round256(st);
-  L.seg_cu = L.o_m + (pr.d_k != pr.d_v ? round256((size_t)pr.total * pr.H_v * pr.d_k * es) : 0);
+  L.coop = L.o_m + (pr.d_k != pr.d_v ? round256((size_t)pr.total * pr.H_v * pr.d_k * es) : 0);
+  L.seg_cu = L.coop + round256(split_coop_bytes(pr, segment_len));
   L.seg_off = L.seg_cu + (pr.cu ? round256((NP + 1) * 4) : 0);
   L.prep = L.seg_off + (pr.cu ? round256(((size_t)pr.num_seqs + 1) * 4) : 0);
   L.bytes = L.prep + round256(kda_two_pass_bytes(segments(pr, segment_len)));
@@ -286,8 +308,23 @@ hipError_t launch_chunked_split(const Problem &pr, const FwdArgs &x, int segment
   void *prep = ws + L.prep;
   const bool two = L.bytes > L.prep;
   if (two && (e = launch_kda_prep(seg, x, prep, s)) != hipSuccess) return e;
+  // the rule in bf16: the cooperative form, its workspace cleared once here
+  // (each of its launches leaves it cleared for the next)
+  void *coop = ws + L.coop;
+  const bool co = L.seg_cu > L.coop;
+  if (co) {
+    Problem first = seg;
+    first.num_seqs = chunked_coop_seqs_per_launch(seg);
+    Problem firstm = segm;
+    firstm.num_seqs = chunked_coop_seqs_per_launch(segm);
+    const Problem &wide = chunked_coop_workspace_bytes(firstm) > chunked_coop_workspace_bytes(first)
+                              ? firstm : first;
+    if ((e = clear_chunked_coop(wide, coop, s)) != hipSuccess) return e;
+  }
   auto chunked = [&](const Problem &q, const FwdArgs &y) {
-    return two ? launch_kda_chain(q, y, prep, s) : chunked_any(q, y, s);
+    if (two) return launch_kda_chain(q, y, prep, s);
+    if (co) return run_coop_batches(q, y, chunked_coop_seqs_per_launch(q), coop, s);
+    return chunked_any(q, y, s);
   };
   // S_loc: from zero on the real v;  M: from I on v = 0  (outputs land in o, or
   // in o_m when they are d_k wide, and o is overwritten by the last launch)
