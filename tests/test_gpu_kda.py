@@ -269,9 +269,9 @@ def test_kda_matrix_core_vs_vector_kernel(lens):
 def test_kda_two_launch_on_the_varlen_batch():
     """The varlen workload (8 packed sequences, about 94k tokens, 48/16
     heads, carried state) through both matrix-core forms: the two-launch
-    form's slot numbering and per-slot sequence lookup at full scale.  The
-    fp64 oracle checks both forms on the smaller cases above; here they are
-    compared with each other per (sequence, head)."""
+    form's slot numbering and per-slot sequence lookup at full scale, the two
+    forms against each other on every (sequence, head) and against the fp64
+    oracle on one head of every sequence."""
     w = synth.workload("varlen")
     inp = synth.kda_inputs(w, 73, device=DEV)
     note(f"[kda] varlen two-launch vs one-launch lens={w.seq_lengths}")
@@ -287,6 +287,13 @@ def test_kda_two_launch_on_the_varlen_batch():
                         U.slice_err(U.to_np(S1[n, h]), U.to_np(S2[n, h])))
     note(f"  two-launch vs one-launch on the varlen batch: {worst:.3e}")
     assert worst <= U.TOL["bf16"]
+    # and both against the fp64 oracle on one value head of every sequence
+    heads = [29]
+    o_ref, S_ref = oracle_of(inp, heads)
+    for name, (o, S) in (("two-launch", (o1, S1)), ("one-launch", (o2, S2))):
+        eo, es = U.compare_full(o[:, heads], S[:, heads], o_ref, S_ref, cu, 1)
+        note(f"  {name} vs oracle (head 29, every sequence): o={eo:.3e} S={es:.3e}")
+        assert eo <= U.TOL["bf16"] and es <= U.TOL["bf16"], (name, eo, es)
 
 
 @pytest.mark.parametrize("form", ["recurrent", "chunked", "chunked_fused"])
