@@ -162,6 +162,19 @@ def main():
     dev_ev[1].record(stream)
     torch.cuda.synchronize(dev)
     dmean_ms = dev_ev[0].elapsed_time(dev_ev[1]) / nsteps
+    # the same steps again with a pair of events around each one (from the
+    # initial state), for the per-step median and spread
+    state.copy_(dinp["initial_state"])
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nsteps)]
+    for s in range(nsteps):
+        step_ev[s][0].record(stream)
+        decode_step(s)
+        step_ev[s][1].record(stream)
+    torch.cuda.synchronize(dev)
+    step_ms = sorted(a.elapsed_time(b) for a, b in step_ev)
+    dmedian_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else \
+        0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     dbytes = decode_bytes(wd.num_seqs, wd.H_k, wd.H_v, wd.d_k, wd.d_v, 2)
     dgbs = dbytes / (dmean_ms / 1e3) / 1e9
 
@@ -280,6 +293,10 @@ def main():
         "decode": {"workload": "256 sequences x 48 value heads (16 key heads), d_k=d_v=128, "
                                "fp32 state in place, bf16 inputs, single-token steps",
                    "steps": nsteps, "mean_step_ms": dmean_ms,
+                   "per_step_events_ms": {"median": dmedian_ms, "min": step_ms[0],
+                                          "max": step_ms[-1],
+                                          "note": "a second pass of the same steps with a pair "
+                                                  "of events around each step"},
                    "tokens_per_s": wd.num_seqs / (dmean_ms / 1e3),
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": dgbs / PEAK_HBM_GBS,
