@@ -117,3 +117,23 @@ def test_coherent_keys_kda(form, eps, tag):
     torch.cuda.synchronize()
     ref = kda_oracle.kda(*(x.cpu() for x in args(inp)), cu_seqlens=inp["cu_host"])
     compare(f"kda {form} {tag}", w, inp, o, S, ref)
+
+
+@pytest.mark.parametrize("eps,tag", EPS, ids=[t for _, t in EPS])
+def test_coherent_keys_split_packed(eps, tag):
+    """gdr_chunked_fwd_split on a packed batch (the segment map formed on the
+    device; the last segment of each sequence partial), its passes on the
+    cooperative form, and the same for the KDA split."""
+    w = workload("bf16", lengths=(2048, 777, 0, 1300))
+    note(f"[coherent] split packed {tag}")
+    inp = inputs(w, 45, eps)
+    o, S = gdr.chunked_fwd_split(*args(inp), segment_len=512, chunk=32,
+                                 cu_seqlens=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    compare(f"split packed {tag}", w, inp, o, S, U.oracle_full(inp, inp["cu_host"]))
+    ik = inputs(w, 46, eps, kda=True)
+    o, S = gdr.kda_chunked_fwd_split(*args(ik), segment_len=512, chunk=32,
+                                     cu_seqlens=ik["cu_seqlens"])
+    torch.cuda.synchronize()
+    ref = kda_oracle.kda(*(x.cpu() for x in args(ik)), cu_seqlens=ik["cu_host"])
+    compare(f"kda split packed {tag}", w, ik, o, S, ref)
