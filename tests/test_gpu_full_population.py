@@ -124,12 +124,34 @@ def test_varlen_every_pair(seed):
     note(f"[full] varlen seed {seed}: lengths {w.seq_lengths}, stress sequences "
          f"{list(w.stress_seqs)}")
     ref = U.oracle_full(inp, inp["cu_host"])
-    for form in ("chunked_one_launch", "recurrent"):
+    for form in ("chunked_coop", "chunked_one_launch", "recurrent"):
         o, S = run_form(form, inp, w)
         torch.cuda.synchronize()
         eo, es = U.compare_full(o, S, ref[0], ref[1], inp["cu_host"], w.H_v)
         note(f"  {form}, all {len(w.seq_lengths) * w.H_v} pairs: worst o={eo:.3e} S={es:.3e}")
         assert eo <= TOL and es <= TOL, (form, eo, es)
+        del o, S
+
+
+def test_varlen_maximum_lengths_sampled():
+    """The varlen workload at the top of its length range: 8 packed
+    sequences of 32768 tokens (262,144 tokens, 48/16 heads, carried state,
+    stress sequences 6 and 7), in the cooperative form the benchmark times
+    and the one-launch form, against the oracle on two value heads of every
+    sequence (byte offsets into v and o past 2^31)."""
+    w = synth.workload("varlen", lengths=[32768] * 8)
+    assert w.total_tokens * w.H_v * w.d_v * 2 > 2 ** 31
+    inp = synth.make_inputs(w, 3, device=DEV)
+    cu = inp["cu_host"]
+    note(f"[full] varlen at the maximum lengths: {w.seq_lengths}")
+    pairs = [(n, h) for n in range(w.num_seqs) for h in (5, 40)]
+    ref = U.oracle_pairs(inp, cu, pairs)
+    for form in ("chunked_coop", "chunked_one_launch"):
+        o, S = run_form(form, inp, w)
+        torch.cuda.synchronize()
+        eo, es, per = U.compare_sampled(o, S, ref, cu)
+        note(f"  {form}, {len(pairs)} pairs: worst o={eo:.3e} S={es:.3e}")
+        assert eo <= TOL and es <= TOL, (form, per)
         del o, S
 
 
