@@ -332,9 +332,10 @@ def pin_streaming_equals_recompute():
 def pin_segment_transition_map(seeds=range(3)):
     """The two-level scan's premise: over a segment the final state is affine
     in the entry state, S_out = M S_in + S_loc, where M is the segment run
-    from S_in = I with v = 0 (d_k = d_v) and S_loc the run from S_in = 0
-    (each step is alpha (I - beta k k^T) S + beta k v^T).  Chaining the maps
-    of consecutive segments reproduces the one long run."""
+    from S_in = I with v = 0 (d_k-wide values, so M is d_k x d_k) and S_loc
+    the run from S_in = 0 (each step is alpha (I - beta k k^T) S + beta k v^T).
+    Chaining the maps of consecutive segments, of equal or unequal length,
+    reproduces the one long run, for d_k = d_v and d_k != d_v."""
     for s in seeds:
         p = rand_problem(800 + s, T=36, H_k=1, H_v=2, d_k=5, d_v=5)
         _, S_full = run_oracle(p)
@@ -352,6 +353,24 @@ def pin_segment_transition_map(seeds=range(3)):
             close(nxt, S_ref, rtol=1e-10, atol=1e-12, what=f"segment map, seed {s}, [{t0},{t1})")
             state = nxt
         close(state, S_full, rtol=1e-10, atol=1e-12, what=f"chained segment maps, seed {s}")
+    # d_k != d_v and segments of unequal length (a packed sequence's last
+    # segment is partial): M is d_k x d_k, the run from S_in = I with d_k-wide
+    # zero values; S_loc and the states are d_k x d_v
+    for s in seeds:
+        p = rand_problem(810 + s, T=29, H_k=1, H_v=2, d_k=5, d_v=3)
+        _, S_full = run_oracle(p)
+        I = np.broadcast_to(np.eye(5), (1, 2, 5, 5)).copy()
+        state = p["initial_state"]
+        for t0, t1 in ((0, 8), (8, 16), (16, 24), (24, 29)):
+            seg = {k: (p[k][t0:t1] if k in ("q", "k", "v", "a", "b") else p[k]) for k in p}
+            zv = np.zeros(seg["v"].shape[:2] + (5,))
+            _, M = oracle.fwd(seg["q"], seg["k"], zv, seg["a"], seg["b"], p["A_log"],
+                              p["dt_bias"], initial_state=I)
+            assert M.shape == (1, 2, 5, 5)
+            _, S_loc = oracle.fwd(seg["q"], seg["k"], seg["v"], seg["a"], seg["b"], p["A_log"],
+                                  p["dt_bias"], initial_state=None)
+            state = np.einsum("nhij,nhjk->nhik", M, state) + S_loc
+        close(state, S_full, rtol=1e-10, atol=1e-12, what=f"chained d_k x d_k maps, seed {s}")
 
 
 def pin_constant_state():
