@@ -1584,6 +1584,13 @@ __device__ __forceinline__ void producer(const MfmaParams &p, unsigned char *sme
       if (prev >= 0) {
         copy_out(prev, buf ^ 1);
         stored = prev;
+        if (prev == phi) {
+          // the first record is flagged as soon as its stores have landed
+          // (the chains wait for it to start), not an iteration later
+          vm_wait<0>();
+          if (lane == 0) flags[j * RING + prev % RING] = (uint32_t)(prev + 1);
+          stored = -1;
+        }
       } else {
         stored = -1;
       }
@@ -1690,14 +1697,15 @@ __device__ __forceinline__ void coop_staging(const MfmaParams &p, Smem &sm, int 
       dma16_l2(rec + 1024 * i + 16 * lane, reinterpret_cast<unsigned char *>(&S.pp.r) + 1024 * i);
   };
   if (which == 0) {
+    // the rows of the first chunks are requested before the wait for their
+    // records' flags, so that they land while the producers form the records
     fetch_flag(2);
     fetch_flag(3);
-    for (int c = 0; c < AHEAD; ++c) {
-      record(c, false);
-      rows(c);
-    }
-    vm_wait<CST0_OPS * (AHEAD - 1)>();  // chunk 0 has landed, flags 2 and 3 too
-    block_sync<CST0_OPS * (AHEAD - 1)>();
+    for (int c = 0; c < AHEAD; ++c) rows(c);
+    for (int c = 0; c < AHEAD; ++c) record(c, false);
+    static_assert(AHEAD == 2, "the wait below leaves only chunk 1's record in flight");
+    vm_wait<REC_DMAS>();  // chunks 0 and 1 have landed but chunk 1's record, flags 2 and 3 too
+    block_sync<REC_DMAS>();
     for (int it = 0; it < nsteps; ++it) {
       fetch_flag(it + AHEAD + 2);
       record(it + AHEAD, true);
