@@ -778,8 +778,8 @@ def cpu_baseline(w, inp, T, cpu_heads):
     (bounded samples, scaled) and 1-thread times for configurations 1-3."""
     import oracle
     import synth
-    # one GPU's share of the host: the GPU boxes give 16 cores to a GPU,
-    # whatever the machine's count
+    # one GPU's share of the host's cores: 16 a GPU on an eight-GPU host,
+    # whatever count the process sees
     threads = min(16, os.cpu_count() or 1)
 
     def run(wl, x, pairs=None, n_threads=threads, dense=None):
